@@ -1,0 +1,172 @@
+"""ctypes binding for libfa.so (argument marshalling only).
+
+Every step of the attention path runs in the library's HIP kernels; this file
+only turns torch tensors into device pointers, picks the current HIP stream,
+and maps status codes to exceptions. If the library is missing the calls
+raise: there is no CPU fallback.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_F16, FA_BF16, FA_FP8_E4M3 = 0, 1, 2
+FA_OUT_F32 = 0x100
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+def lib_path():
+    return os.path.join(_HERE, "libfa.so")
+
+
+def lib():
+    """Load libfa.so once; raise if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise FaError(FA_ERR_HIP, f"{path} not built (run __graft_entry__.build())")
+    L = ctypes.CDLL(path)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    L.fa_fwd.restype = i
+    L.fa_fp8_prep.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp]
+    L.fa_fp8_prep.restype = i
+    L.fa_fp8_packed_bytes.argtypes = [i, i, i, i]
+    L.fa_fp8_packed_bytes.restype = ctypes.c_size_t
+    L.fa_fp8_scales_offset.argtypes = [i, i, i, i]
+    L.fa_fp8_scales_offset.restype = ctypes.c_size_t
+    L.fa_status_string.argtypes = [i]
+    L.fa_status_string.restype = ctypes.c_char_p
+    _LIB = L
+    return L
+
+
+def status_string(status):
+    try:
+        return lib().fa_status_string(int(status)).decode()
+    except FaError:
+        return {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "hip error"}.get(status, "?")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def fwd_raw(q, k, v, o, lse, B, H, N, d, causal, softmax_scale, dtype, stream=None):
+    """Direct call with integer pointers; returns the status code."""
+    return lib().fa_fwd(q, k, v, o, lse, B, H, N, d, int(causal), float(softmax_scale),
+                        int(dtype), stream)
+
+
+def fp8_prep_raw(x, x8, signs, B, H, N, d, block_rows, in_dtype, stream=None):
+    return lib().fa_fp8_prep(x, x8, signs, B, H, N, d, block_rows, in_dtype, stream)
+
+
+def fp8_packed_bytes(B, H, N, d):
+    return int(lib().fa_fp8_packed_bytes(B, H, N, d))
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float16:
+        return FA_F16
+    raise FaError(FA_ERR_UNSUPPORTED, f"dtype {t.dtype}")
+
+
+def fwd(q, k, v, causal=False, softmax_scale=None, out=None, lse=None, out_f32=False):
+    """Attention forward on 16-bit [B,H,N,d] device tensors.
+
+    Returns (o, lse): o has q's dtype (float32 with out_f32=True), lse is
+    float32 [B,H,N].
+    """
+    B, H, N, d = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    code = _dtype_code(q)
+    odt = torch.float32 if out_f32 else q.dtype
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=odt, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out_f32:
+        code |= FA_OUT_F32
+    for t in (q, k, v, out, lse):
+        if not t.is_contiguous():
+            raise FaError(FA_ERR_INVALID_ARG, "tensors must be contiguous")
+    st = fwd_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, causal,
+                 softmax_scale, code, _stream(q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd")
+    return out, lse
+
+
+def fp8_alloc_packed(B, H, N, d, device):
+    return torch.empty(fp8_packed_bytes(B, H, N, d), dtype=torch.uint8, device=device)
+
+
+def fp8_codes_view(packed, B, H, N, d):
+    """The e4m3 codes of a packed fp8 tensor, uint8 [B,H,N,d]."""
+    return packed[: B * H * N * d].view(B, H, N, d)
+
+
+def fp8_scales_view(packed, B, H, N, d):
+    """The float32 block scales of a packed fp8 tensor, [B,H,ceil(N/128)]."""
+    off = int(lib().fa_fp8_scales_offset(B, H, N, d))
+    nb = (N + 127) // 128
+    return packed[off: off + 4 * B * H * nb].view(torch.float32).view(B, H, nb)
+
+
+def fp8_prep(x, signs=None, block_rows=128, out=None):
+    """Random-sign Hadamard (when signs is given) + fp8 e4m3 block quantisation.
+
+    x: 16-bit [B,H,N,d] device tensor; signs: int8 [H,d] device tensor of +-1
+    or None; block_rows: 128, or 0 for one scale per tensor. Returns the
+    packed uint8 tensor (codes then float32 scales) that fwd_fp8 consumes.
+    """
+    B, H, N, d = x.shape
+    if out is None:
+        out = fp8_alloc_packed(B, H, N, d, x.device)
+    st = fp8_prep_raw(_ptr(x), _ptr(out), _ptr(signs), B, H, N, d, block_rows,
+                      _dtype_code(x), _stream(x.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_fp8_prep")
+    return out
+
+
+def fwd_fp8(q8, k8, v8, B, H, N, d, causal=False, softmax_scale=None, out_f32=False,
+            out=None, lse=None):
+    """Attention forward on packed fp8 tensors made by fp8_prep.
+
+    Returns (o, lse) with o bf16 (float32 with out_f32=True).
+    """
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    odt = torch.float32 if out_f32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=odt, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    code = FA_FP8_E4M3 | (FA_OUT_F32 if out_f32 else 0)
+    st = fwd_raw(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(out), _ptr(lse), B, H, N, d, causal,
+                 softmax_scale, code, _stream(q8.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd(fp8)")
+    return out, lse

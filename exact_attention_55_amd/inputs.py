@@ -1,0 +1,70 @@
+"""Seeded synthetic inputs shared by the tests, the bench and the smoke check.
+
+This module only draws random numbers and rounds them to the input dtype; it
+holds none of the attention arithmetic, so both the GPU path and the CPU
+oracle can take their inputs from here without sharing any of the method.
+
+Recipe (the pages measure on synthetic data only: head dim 128 and sequence
+length 8K in the ping-pong ablation of "FlashAttention-3: Fast & Accurate
+Attention with Asynchrony & Low-Precision", section "Overlapping GEMM and
+Softmax", and 0.1% large outliers in its section "Incoherent Processing for
+FP8 Accuracy"):
+
+* numpy.random.default_rng(seed); float32 standard normals of shape
+  [B, H, N, d], drawn in the order Q, K, V;
+* with outliers: after the three base draws, for each of Q, K, V in turn a
+  mask (uniform < p, p = 0.001) and values N(0, sigma^2) with sigma = 10 are
+  drawn and added where the mask is set;
+* the float32 values are rounded once to the 16-bit input dtype (round to
+  nearest even, torch CPU cast). Every consumer reads the rounded values.
+* Hadamard sign vectors: default_rng(seed + 1000), +-1 int8 of shape [H, d].
+"""
+
+import numpy as np
+import torch
+
+# Workloads: (name, B, H, N, d, causal, dtype, seed, outliers)
+CONFIGS = {
+    "tiny_fp16": dict(B=1, H=1, N=256, d=64, causal=False, dtype="fp16", seed=0),
+    "b8h16n2k_d128": dict(B=8, H=16, N=2048, d=128, causal=False, dtype="bf16", seed=1),
+    "b8h16n2k_d128_causal": dict(B=8, H=16, N=2048, d=128, causal=True, dtype="bf16", seed=1),
+    "b4h32n4k_d64": dict(B=4, H=32, N=4096, d=64, causal=False, dtype="bf16", seed=2),
+    "b2h16n8k_d128_causal": dict(B=2, H=16, N=8192, d=128, causal=True, dtype="bf16", seed=5),
+    "b2h8n16k_d256_causal": dict(B=2, H=8, N=16384, d=256, causal=True, dtype="bf16", seed=3),
+    "fp8_b4h16n4k_d128": dict(B=4, H=16, N=4096, d=128, causal=False, dtype="bf16", seed=4,
+                              outliers=True),
+}
+
+TORCH_DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16}
+
+
+def make_qkv(B, H, N, d, seed, dtype="bf16", outliers=False, p_outlier=1e-3,
+             sigma_outlier=10.0, **_):
+    """Return q, k, v as CPU torch tensors of the 16-bit dtype, [B,H,N,d]."""
+    rng = np.random.default_rng(seed)
+    shape = (B, H, N, d)
+    base = [rng.standard_normal(shape, dtype=np.float32) for _ in range(3)]
+    if outliers:
+        for x in base:
+            mask = rng.random(shape, dtype=np.float32) < p_outlier
+            vals = rng.normal(0.0, sigma_outlier, size=shape).astype(np.float32)
+            x += np.where(mask, vals, np.float32(0.0))
+    tdt = TORCH_DTYPES[dtype]
+    return tuple(torch.from_numpy(x).to(tdt) for x in base)
+
+
+def make_signs(H, d, seed):
+    """+-1 sign vectors [H, d] int8 for the random-sign Hadamard."""
+    rng = np.random.default_rng(seed + 1000)
+    return (rng.integers(0, 2, size=(H, d), dtype=np.int8) * 2 - 1).astype(np.int8)
+
+
+def to_f64(t):
+    """Exact float64 copy of a CPU tensor (for the oracle)."""
+    return t.to(torch.float64).numpy()
+
+
+def attention_flops(B, H, N, d, causal):
+    """The metric's work count: 4*B*H*N^2*d, halved for causal."""
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
