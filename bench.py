@@ -1,0 +1,206 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--sweep]
+
+One step runs the whole hot path once, on inputs already resident in HBM:
+  1. bf16 forward, B=8 H=16 N=2048 d=128, non-causal   (16k tokens, hidden 2048)
+  2. bf16 forward, same shape, causal
+  3. fp8 path on B=4 H=16 N=4096 d=128 (0.1% outliers): fa_fp8_prep of Q and K
+     (random-sign Hadamard + 128-row block scales) and V (block scales), then
+     the fp8 forward.
+`value` is the metric work of the step (4*B*H*N^2*d per forward, halved for
+causal) divided by the step time. Every leg is also timed on its own with HIP
+events on the stream it runs on; `legs` reports each. `roofline` is for the
+dominant kernel, the non-causal bf16 forward, against the MI355X dense bf16
+MFMA peak. `cpu_baseline` times the float64 oracle on a bounded sample of the
+same workload (rank 0, N=1 only).
+
+Prints ONE JSON line on stdout.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import exact_attention_55_amd as fa  # noqa: E402
+from exact_attention_55_amd.inputs import CONFIGS, attention_flops, make_qkv, make_signs  # noqa: E402
+
+PEAK_BF16 = 2516.6   # TFLOP/s, MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_FP8 = 5033.2    # TFLOP/s, dense fp8
+PEAK_HBM = 8000.0    # GB/s
+
+MAIN = "b8h16n2k_d128"
+FP8 = "fp8_b4h16n4k_d128"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Leg:
+    def __init__(self, name, fn, flops=0.0, bytes_=0.0):
+        self.name, self.fn, self.flops, self.bytes = name, fn, flops, bytes_
+        self.times = []
+
+    def run(self, timed):
+        if timed:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            self.fn()
+            b.record()
+            return (a, b)
+        self.fn()
+        return None
+
+
+def build_legs(dev):
+    legs = []
+    c = CONFIGS[MAIN]
+    q, k, v = (t.to(dev) for t in make_qkv(**c))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    B, H, N, d = c["B"], c["H"], c["N"], c["d"]
+    fl = attention_flops(B, H, N, d, False)
+    legs.append(Leg("bf16_fwd_b8h16n2k_d128", lambda: fa.fwd(q, k, v, False, out=o, lse=lse), fl))
+    legs.append(Leg("bf16_fwd_b8h16n2k_d128_causal",
+                    lambda: fa.fwd(q, k, v, True, out=o, lse=lse), fl / 2))
+    c8 = CONFIGS[FP8]
+    B8, H8, N8, d8 = c8["B"], c8["H"], c8["N"], c8["d"]
+    q8, k8, v8 = (t.to(dev) for t in make_qkv(**c8))
+    signs = torch.from_numpy(make_signs(H8, d8, c8["seed"])).to(dev)
+    pq, pk, pv = (fa.fp8_alloc_packed(B8, H8, N8, d8, dev) for _ in range(3))
+    o8 = torch.empty((B8, H8, N8, d8), dtype=torch.bfloat16, device=dev)
+    lse8 = torch.empty((B8, H8, N8), dtype=torch.float32, device=dev)
+    nel = B8 * H8 * N8 * d8
+    prep_bytes = 3 * (nel * 2 + nel + B8 * H8 * (N8 // 128) * 4)
+
+    def prep():
+        fa.fp8_prep(q8, signs, 128, out=pq)
+        fa.fp8_prep(k8, signs, 128, out=pk)
+        fa.fp8_prep(v8, None, 128, out=pv)
+
+    legs.append(Leg("fp8_prep_qkv_b4h16n4k_d128", prep, 0.0, prep_bytes))
+    legs.append(Leg("fp8_fwd_b4h16n4k_d128",
+                    lambda: fa.fwd_fp8(pq, pk, pv, B8, H8, N8, d8, False, out=o8, lse=lse8),
+                    attention_flops(B8, H8, N8, d8, False)))
+    keep = (q, k, v, o, lse, q8, k8, v8, signs, pq, pk, pv, o8, lse8)
+    return legs, keep
+
+
+def cpu_baseline(budget_s=12.0):
+    """The float64 oracle on whole heads of the main workload, until the budget
+    is spent (at least one head)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    c = CONFIGS[MAIN]
+    q, k, v = make_qkv(1, 1, c["N"], c["d"], seed=c["seed"], dtype=c["dtype"])
+    q64, k64, v64 = (t.to(torch.float64).numpy() for t in (q, k, v))
+    heads, t0 = 0, time.perf_counter()
+    while True:
+        oracle.attention(q64, k64, v64, False)
+        heads += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or heads >= c["B"] * c["H"]:
+            break
+    fl = attention_flops(1, heads, c["N"], c["d"], False)
+    return {"value": fl / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{heads} of {c['B'] * c['H']} heads of B=8 H=16 N=2048 d=128 non-causal, "
+                      f"float64 numpy oracle, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards over heads with no exchange, see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    fa.lib()
+    log("building inputs")
+    legs, _keep = build_legs(dev)
+    for _ in range(args.warmup):
+        for L in legs:
+            L.run(False)
+    torch.cuda.synchronize()
+    log(f"warmup done; timing {args.steps} steps")
+    events = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        events.append([L.run(True) for L in legs])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for step in events:
+        for L, (a, b) in zip(legs, step):
+            L.times.append(a.elapsed_time(b) * 1e-3)
+    total_flops = sum(L.flops for L in legs)
+    step_s = wall / args.steps
+    legs_out = {}
+    for L in legs:
+        t = float(np.mean(L.times))
+        e = {"ms": t * 1e3, "ms_min": float(np.min(L.times)) * 1e3}
+        if L.flops:
+            peak = PEAK_FP8 if L.name.startswith("fp8") else PEAK_BF16
+            e["tflops"] = L.flops / t / 1e12
+            e["frac_of_peak"] = e["tflops"] / peak
+        if L.bytes:
+            e["gbps"] = L.bytes / t / 1e9
+            e["frac_of_hbm"] = e["gbps"] / PEAK_HBM
+        legs_out[L.name] = e
+    dom = legs[0]
+    t_dom = float(np.mean(dom.times))
+    achieved = dom.flops / t_dom / 1e12
+    roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16, "traffic": None,
+            "kernel": "fa_fwd16_kernel<bf16,128,noncausal>", "launch_ms": t_dom * 1e3}
+    out = {
+        "metric": "attention fwd TFLOP/s (4*B*H*N^2*d, /2 causal), bf16 and fp8",
+        "value": total_flops / step_s / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16+fp8",
+        "data": "synthetic",
+        "config": {"workload": "bf16 fwd B=8 H=16 N=2048 d=128 (non-causal + causal) + fp8 "
+                               "prep/fwd B=4 H=16 N=4096 d=128 (0.1% outliers)",
+                   "global_batch": 8, "seq_len": 2048, "head_dim": 128, "heads": 16,
+                   "parallelism": "single-gpu"},
+        "legs": legs_out,
+        "roofline": roof,
+    }
+    if not args.no_cpu:
+        log("timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

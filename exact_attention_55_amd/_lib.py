@@ -55,10 +55,10 @@ def lib():
 
 
 def status_string(status):
-    try:
-        return lib().fa_status_string(int(status)).decode()
-    except FaError:
-        return {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "hip error"}.get(status, "?")
+    if _LIB is not None:
+        return _LIB.fa_status_string(int(status)).decode()
+    return {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
+            3: "HIP runtime error"}.get(status, "unknown status")
 
 
 def _ptr(t):
@@ -81,6 +81,19 @@ def fp8_prep_raw(x, x8, signs, B, H, N, d, block_rows, in_dtype, stream=None):
 
 def fp8_packed_bytes(B, H, N, d):
     return int(lib().fa_fp8_packed_bytes(B, H, N, d))
+
+
+def _check(cond, what):
+    if not cond:
+        raise FaError(FA_ERR_INVALID_ARG, what)
+
+
+def _check_device(*ts):
+    dev = ts[0].device
+    _check(dev.type == "cuda", "tensors must be on a HIP device")
+    for t in ts:
+        _check(t.device == dev, "tensors on different devices")
+        _check(t.is_contiguous(), "tensors must be contiguous")
 
 
 def _dtype_code(t):
@@ -108,9 +121,11 @@ def fwd(q, k, v, causal=False, softmax_scale=None, out=None, lse=None, out_f32=F
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if out_f32:
         code |= FA_OUT_F32
-    for t in (q, k, v, out, lse):
-        if not t.is_contiguous():
-            raise FaError(FA_ERR_INVALID_ARG, "tensors must be contiguous")
+    _check(q.dim() == 4 and k.shape == q.shape and v.shape == q.shape, "q, k, v shapes differ")
+    _check(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v dtypes differ")
+    _check(out.shape == q.shape and out.dtype == odt, "bad output tensor")
+    _check(lse.shape == (B, H, N) and lse.dtype == torch.float32, "bad lse tensor")
+    _check_device(q, k, v, out, lse)
     st = fwd_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, causal,
                  softmax_scale, code, _stream(q.device))
     if st != FA_OK:
@@ -144,6 +159,13 @@ def fp8_prep(x, signs=None, block_rows=128, out=None):
     B, H, N, d = x.shape
     if out is None:
         out = fp8_alloc_packed(B, H, N, d, x.device)
+    _check(out.dtype == torch.uint8 and out.numel() >= fp8_packed_bytes(B, H, N, d),
+           "packed output too small")
+    if signs is not None:
+        _check(signs.dtype == torch.int8 and tuple(signs.shape) == (H, d), "signs must be int8 [H, d]")
+        _check_device(x, out, signs)
+    else:
+        _check_device(x, out)
     st = fp8_prep_raw(_ptr(x), _ptr(out), _ptr(signs), B, H, N, d, block_rows,
                       _dtype_code(x), _stream(x.device))
     if st != FA_OK:
@@ -165,6 +187,12 @@ def fwd_fp8(q8, k8, v8, B, H, N, d, causal=False, softmax_scale=None, out_f32=Fa
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
     code = FA_FP8_E4M3 | (FA_OUT_F32 if out_f32 else 0)
+    need = fp8_packed_bytes(B, H, N, d)
+    for t in (q8, k8, v8):
+        _check(t.dtype == torch.uint8 and t.numel() >= need, "packed fp8 input too small")
+    _check(out.shape == (B, H, N, d) and out.dtype == odt, "bad output tensor")
+    _check(lse.shape == (B, H, N) and lse.dtype == torch.float32, "bad lse tensor")
+    _check_device(q8, k8, v8, out, lse)
     st = fwd_raw(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(out), _ptr(lse), B, H, N, d, causal,
                  softmax_scale, code, _stream(q8.device))
     if st != FA_OK:

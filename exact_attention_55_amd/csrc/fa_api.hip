@@ -1,0 +1,101 @@
+// fa_api.hip - the C ABI declared in include/fa.h: argument validation,
+// status codes and dispatch to the kernel launchers. All validation happens
+// before the first HIP call, so invalid calls work on hosts without a GPU.
+#include "fa.h"
+#include "fa_internal.h"
+
+#include <math.h>
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool supported_d(int d) { return d == 64 || d == 128 || d == 256; }
+
+// B*H*N*d must stay well inside 64-bit offsets and the grid limits.
+bool sizes_ok(int B, int H, int N, int d) {
+    if (B < 0 || H < 0 || N < 0 || d <= 0) return false;
+    const double elems = (double)B * H * N * d;
+    return elems < 4.0e18;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_fp8_scales_offset(int B, int H, int N, int d) {
+    if (!sizes_ok(B, H, N, d)) return 0;
+    return fa::round_up((size_t)B * H * N * d, 256);
+}
+
+size_t fa_fp8_packed_bytes(int B, int H, int N, int d) {
+    if (!sizes_ok(B, H, N, d)) return 0;
+    const size_t nb = ((size_t)N + fa::kQuantBlockRows - 1) / fa::kQuantBlockRows;
+    return fa::round_up(fa_fp8_scales_offset(B, H, N, d) + (size_t)B * H * nb * 4, 256);
+}
+
+const char* fa_status_string(int status) {
+    switch (status) {
+        case FA_OK: return "ok";
+        case FA_ERR_INVALID_ARG: return "invalid argument";
+        case FA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case FA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+           int d, int causal, float softmax_scale, int dtype, void* stream) {
+    const int base = dtype & 0xff;
+    const int flags = dtype & ~0xff;
+    if ((flags & ~FA_OUT_F32) != 0) return FA_ERR_INVALID_ARG;
+    if (base != FA_F16 && base != FA_BF16 && base != FA_FP8_E4M3) return FA_ERR_INVALID_ARG;
+    if (!sizes_ok(B, H, N, d)) return FA_ERR_INVALID_ARG;
+    if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return FA_ERR_INVALID_ARG;
+    if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * H > 0x7fffffffLL / 2) return FA_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0 || N == 0) return FA_OK;
+    if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+    const size_t qa = base == FA_FP8_E4M3 ? 256 : 16;
+    if (!aligned(q, qa) || !aligned(k, qa) || !aligned(v, qa) || !aligned(o, 16) ||
+        !aligned(lse, 4))
+        return FA_ERR_INVALID_ARG;
+
+    fa::FwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.B = B; a.H = H; a.N = N; a.d = d;
+    a.causal = causal != 0;
+    a.scale = softmax_scale;
+    a.out_f32 = (flags & FA_OUT_F32) != 0;
+    a.scales_off = fa_fp8_scales_offset(B, H, N, d);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();   // do not report an earlier, unrelated error
+    if (base == FA_FP8_E4M3) return from_hip(fa::launch_fwd_fp8(a, s));
+    return from_hip(fa::launch_fwd16(a, base == FA_BF16, s));
+}
+
+int fa_fp8_prep(const void* x, void* x8, const int8_t* signs, int B, int H, int N, int d,
+                int block_rows, int in_dtype, void* stream) {
+    if (in_dtype != FA_BF16 && in_dtype != FA_F16) return FA_ERR_INVALID_ARG;
+    if (!sizes_ok(B, H, N, d)) return FA_ERR_INVALID_ARG;
+    if (block_rows != 0 && block_rows != fa::kQuantBlockRows) return FA_ERR_UNSUPPORTED;
+    if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * H * ((N + 127) / 128) > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0 || N == 0) return FA_OK;
+    if (!x || !x8) return FA_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(x8, 256)) return FA_ERR_INVALID_ARG;
+
+    fa::PrepArgs a;
+    a.x = x; a.x8 = static_cast<uint8_t*>(x8); a.signs = signs;
+    a.B = B; a.H = H; a.N = N; a.d = d;
+    a.block_rows = block_rows;
+    a.bf16 = in_dtype == FA_BF16;
+    a.scales_off = fa_fp8_scales_offset(B, H, N, d);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    return from_hip(fa::launch_fp8_prep(a, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// fa_device.h - gfx950 device primitives shared by the attention kernels.
+//
+// Thin wrappers over the CDNA4 matrix-core, LDS and cross-lane builtins, plus
+// the register-fragment types they use. Nothing here knows about attention.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(8))) int32_t i32x8;
+typedef __attribute__((vector_size(2 * sizeof(int)))) int i32x2v;
+
+#define FA_LDS __attribute__((address_space(3)))
+
+// Element-type traits for the two 16-bit input types.
+template <typename T> struct Elt;
+template <> struct Elt<__bf16> {
+    using x8 = bf16x8;
+    using x2 = bf16x2;
+};
+template <> struct Elt<_Float16> {
+    using x8 = f16x8;
+    using x2 = f16x2;
+};
+
+// D(32x32 f32) += A(32x16) * B(16x32), 16-bit operands, fp32 accumulate.
+// Operand layout (wave64): lane l holds row/column (l % 32) and 8 consecutive
+// k values of k-group (l / 32). Accumulator: lane l holds column l % 32,
+// register r holds row 8*(r/4) + 4*(l/32) + (r%4).
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(const f16x8& a, const f16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// D(32x32 f32) += A(32x64) * B(64x32) with OCP e4m3 operands (32 bytes per
+// lane per operand) and unit block scales (E8M0 127 = 2^0).
+__device__ __forceinline__ f32x16 mfma32_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Transposing LDS read of 16-bit data. Within each group of 16 lanes the 16
+// eight-byte reads form a 4 x 16 tile (lane j supplies row j/4, columns
+// 4*(j%4) .. +3); lane i of the group receives column i, rows 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
+    bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((FA_LDS bf16x4*)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// Same for 8-bit data: the 16 reads form an 8 x 16 tile (lane j supplies row
+// j/2, columns 8*(j%2) .. +7); lane i receives column i, rows 0..7.
+__device__ __forceinline__ u32x2 lds_read_tr8(const void* p) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((FA_LDS i32x2v*)(p)));
+}
+
+// Hardware base-2 exponential (v_exp_f32).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value held by lane (l ^ 32).
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
+
+template <typename V>
+__device__ __forceinline__ V load16(const void* p) {
+    return __builtin_bit_cast(V, *reinterpret_cast<const u32x4*>(p));
+}
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// Score tiles are computed transposed (S^T = K Q^T) with 32x32 MFMA. The key
+// row fed to MFMA row m of a 32-key block is perm(m) = m with bits 2 and 3
+// swapped, so that accumulator register r of a lane in half-wave hi holds key
+//   32*kb + perm(8*(r/4) + 4*hi + r%4) = 32*kb + 16*(r/8) + 8*hi + (r%8):
+// every run of 8 registers is 8 consecutive keys, which is what the
+// transposing LDS reads of V deliver for the P V product.
+__device__ __forceinline__ int krow_perm(int m) {
+    return (m & ~12) | ((m >> 1) & 4) | ((m << 1) & 8);
+}
+__device__ __forceinline__ int key_of(int kb, int r, int hi) {
+    return 32 * kb + 16 * (r >> 3) + 8 * hi + (r & 7);
+}
+
+}  // namespace fa

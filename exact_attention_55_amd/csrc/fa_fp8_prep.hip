@@ -1,0 +1,201 @@
+// fa_fp8_prep.hip - incoherent processing + FP8 e4m3 block quantisation.
+//
+// Sources: "FlashAttention-3: Fast & Accurate Attention with Asynchrony &
+// Low-Precision", section "Incoherent Processing for FP8 Accuracy" (multiply
+// Q and K by a random orthogonal matrix per head, realised as a Hadamard
+// transform with random signs in O(d log d)); review "FlashAttention-3: почему
+// внимание стало быстрее", section "Метод", item 3 (block quantisation, one
+// scale per block).
+//
+// One workgroup per (head, 128-row block). A row of d elements is spread over
+// d/8 lanes, 8 contiguous elements per lane (one 16-byte load). The Sylvester
+// Walsh-Hadamard butterflies of span 1, 2, 4 run inside a lane, spans 8 .. d/2
+// across lanes (xor-partner exchange). The block is held in registers until
+// its amax is known, so the input is read once and the codes written once.
+//
+// Per block: amax = max |y|, scale = amax / 448 (IEEE float32 division; 1 if
+// amax is 0), code = e4m3 round-to-nearest-even of y / scale after clamping to
+// +-448 (the clamp only absorbs the rounding of the scale).
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+
+constexpr float kE4M3Max = 448.0f;
+constexpr int kPrepThreads = 256;
+
+__device__ __forceinline__ float to_f(__bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f(_Float16 x) { return (float)x; }
+
+// Two floats -> two e4m3 bytes (round to nearest even), in the low 16 bits.
+__device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
+    a = fminf(fmaxf(a, -kE4M3Max), kE4M3Max);
+    b = fminf(fmaxf(b, -kE4M3Max), kE4M3Max);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+}
+
+// MODE 0: per-block scales, quantise and store codes + scale.
+// MODE 1: only reduce amax of the whole tensor into *gamax (atomic max on the
+//         float bit pattern; amax >= 0 so integer order equals float order).
+// MODE 2: quantise with the tensor-wide scale from *gamax, store codes only.
+template <typename T, int D, bool HAD, int MODE>
+__global__ void __launch_bounds__(kPrepThreads)
+fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t* __restrict__ signs,
+                float* __restrict__ scales, unsigned* __restrict__ gamax, int N, int H, int nblk)
+{
+    constexpr int LPR = D / 8;                 // lanes per row
+    constexpr int RPP = kPrepThreads / LPR;    // rows per pass
+    constexpr int NPASS = kQuantBlockRows / RPP;
+    __shared__ float red[kPrepThreads / 64];
+
+    const int tid = threadIdx.x;
+    const int j = tid % LPR, rp = tid / LPR;
+    const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
+    const int h = bh % H;
+    const size_t head = (size_t)bh * N * D;
+
+    float sg[8];
+    if (HAD) {
+        const uint32_t* sp = reinterpret_cast<const uint32_t*>(signs + (size_t)h * D + 8 * j);
+        const uint32_t w0 = sp[0], w1 = sp[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sg[e] = (float)(int8_t)((w0 >> (8 * e)) & 0xff);
+            sg[e + 4] = (float)(int8_t)((w1 >> (8 * e)) & 0xff);
+        }
+    }
+
+    float v[NPASS][8];
+    float amax = 0.f;
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+        const int row = blk * kQuantBlockRows + p * RPP + rp;
+        u32x4 raw = u32x4{0, 0, 0, 0};
+        if (row < N) raw = *reinterpret_cast<const u32x4*>(X + head + (size_t)row * D + 8 * j);
+        typedef __attribute__((ext_vector_type(8))) T T8;
+        const T8 x = __builtin_bit_cast(T8, raw);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[p][e] = to_f(x[e]);
+        if (HAD) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[p][e] *= sg[e];
+            // in-lane butterflies, spans 1, 2, 4
+#pragma unroll
+            for (int span = 1; span < 8; span *= 2)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if ((e & span) == 0) {
+                        const float a = v[p][e], b = v[p][e + span];
+                        v[p][e] = a + b;
+                        v[p][e + span] = a - b;
+                    }
+            // cross-lane butterflies, spans 8 .. D/2 (partner lane j ^ m)
+#pragma unroll
+            for (int m = 1; m < LPR; m *= 2) {
+                const bool upper = (j & m) != 0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float other = __shfl_xor(v[p][e], m, 64);
+                    v[p][e] = upper ? (other - v[p][e]) : (v[p][e] + other);
+                }
+            }
+            const float rs = 1.0f / __builtin_sqrtf((float)D);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[p][e] *= rs;
+        }
+        if (row < N) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[p][e]));
+        }
+    }
+
+    if (MODE != 2) {
+        // workgroup amax
+#pragma unroll
+        for (int m = 32; m >= 1; m /= 2) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+        if ((tid & 63) == 0) red[tid >> 6] = amax;
+        __syncthreads();
+        amax = red[0];
+#pragma unroll
+        for (int w = 1; w < kPrepThreads / 64; ++w) amax = fmaxf(amax, red[w]);
+    }
+    if (MODE == 1) {
+        if (tid == 0) atomicMax(gamax, __float_as_uint(amax));
+        return;
+    }
+    if (MODE == 2) amax = __uint_as_float(*gamax);
+
+    const float scale = amax > 0.f ? amax / kE4M3Max : 1.0f;
+    if (MODE == 0 && tid == 0) scales[blockIdx.x] = scale;
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+        const int row = blk * kQuantBlockRows + p * RPP + rp;
+        if (row < N) {
+            const uint32_t w0 = e4m3x2(v[p][0] / scale, v[p][1] / scale) |
+                                (e4m3x2(v[p][2] / scale, v[p][3] / scale) << 16);
+            const uint32_t w1 = e4m3x2(v[p][4] / scale, v[p][5] / scale) |
+                                (e4m3x2(v[p][6] / scale, v[p][7] / scale) << 16);
+            *reinterpret_cast<u32x2*>(X8 + head + (size_t)row * D + 8 * j) = u32x2{w0, w1};
+        }
+    }
+}
+
+__global__ void zero_u32_kernel(unsigned* p) { *p = 0u; }
+
+// One workgroup: read the tensor-wide amax first, then fill every slot.
+__global__ void __launch_bounds__(1024) fill_scales_kernel(float* scales, const unsigned* gamax,
+                                                           long long n) {
+    __shared__ float sc;
+    if (threadIdx.x == 0) {
+        const float amax = __uint_as_float(*gamax);
+        sc = amax > 0.f ? amax / kE4M3Max : 1.0f;
+    }
+    __syncthreads();
+    const float s = sc;
+    for (long long i = threadIdx.x; i < n; i += blockDim.x) scales[i] = s;
+}
+
+template <typename T, int D, bool HAD>
+static hipError_t prep_t(const PrepArgs& a, hipStream_t s) {
+    const int nblk = (a.N + kQuantBlockRows - 1) / kQuantBlockRows;
+    const long long grid = (long long)a.B * a.H * nblk;
+    float* scales = reinterpret_cast<float*>(a.x8 + a.scales_off);
+    const T* x = static_cast<const T*>(a.x);
+    if (a.block_rows != 0) {
+        hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 0>), dim3((unsigned)grid), dim3(kPrepThreads),
+                           0, s, x, a.x8, a.signs, scales, nullptr, a.N, a.H, nblk);
+        return hipGetLastError();
+    }
+    // Per-tensor: the first scale slot serves as the amax accumulator; the
+    // fill kernel reads it before overwriting every slot.
+    unsigned* gamax = reinterpret_cast<unsigned*>(scales);
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(1), 0, s, gamax);
+    hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 1>), dim3((unsigned)grid), dim3(kPrepThreads), 0,
+                       s, x, a.x8, a.signs, scales, gamax, a.N, a.H, nblk);
+    hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 2>), dim3((unsigned)grid), dim3(kPrepThreads), 0,
+                       s, x, a.x8, a.signs, scales, gamax, a.N, a.H, nblk);
+    hipLaunchKernelGGL(fill_scales_kernel, dim3(1), dim3(1024), 0, s, scales,
+                       (const unsigned*)gamax, grid);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t prep_d(const PrepArgs& a, hipStream_t s) {
+    return a.signs ? prep_t<T, D, true>(a, s) : prep_t<T, D, false>(a, s);
+}
+
+template <typename T>
+static hipError_t prep_ty(const PrepArgs& a, hipStream_t s) {
+    switch (a.d) {
+        case 64: return prep_d<T, 64>(a, s);
+        case 128: return prep_d<T, 128>(a, s);
+        case 256: return prep_d<T, 256>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_fp8_prep(const PrepArgs& a, hipStream_t s) {
+    return a.bf16 ? prep_ty<__bf16>(a, s) : prep_ty<_Float16>(a, s);
+}
+
+}  // namespace fa

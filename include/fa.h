@@ -1,0 +1,135 @@
+/*
+ * fa.h - C ABI of libfa.so, the MI355X (gfx950) fused exact-attention forward.
+ *
+ * The operation is exact softmax attention per (batch, head):
+ *     S = softmax_scale * Q K^T,  P = rowsoftmax(S),  O = P V,
+ *     LSE_i = ln sum_j exp(S_ij)
+ * ("FlashAttention - one, two, three!" (Medium), section "Standard
+ * Attention", for S, the softmax and O; section "FlashAttention v1." for
+ * keeping only a few per-row constants - here the log-sum-exp - in global
+ * memory). The library computes it the fused way: tiles of K and V streamed
+ * through on-chip memory, an online softmax with a running row maximum and a
+ * separate denominator, and one normalisation at the end (same page,
+ * sections "FlashAttention v1." and "FlashAttention v2."); the N x N matrix
+ * never reaches device memory.
+ *
+ * The FP8 path follows "FlashAttention-3: Fast & Accurate Attention with
+ * Asynchrony & Low-Precision" (Embodied AI 101 transcript), section
+ * "Incoherent Processing for FP8 Accuracy" (random-sign Hadamard rotation of
+ * Q and K before quantising) and the review "FlashAttention-3: почему внимание
+ * стало быстрее", section "Метод", item 3 (block quantisation; QK^T and PV in
+ * FP8, softmax in higher precision).
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers owned by the caller. The library
+ *    allocates no memory, keeps no pointer after returning and holds no
+ *    mutable global state; calls on different streams may run concurrently.
+ *  - Layout: q, k, v, o are contiguous row-major [B][H][N][d]; lse is
+ *    contiguous [B][H][N] float32. Q and K share N (self-attention shape).
+ *  - Calls are asynchronous: work is enqueued on `stream` (a hipStream_t;
+ *    NULL means the default stream) and the call returns. Faults during
+ *    execution surface at the caller's next synchronisation on that stream.
+ *  - Every argument is validated before any HIP call is made; a bad argument
+ *    returns a status and never aborts. B, H or N equal to 0 is a valid empty
+ *    problem and returns FA_OK without launching anything.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum fa_status {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size or scale   */
+    FA_ERR_UNSUPPORTED = 2,   /* valid request the library has no kernel for */
+    FA_ERR_HIP = 3            /* the HIP runtime rejected a launch            */
+};
+
+/* Element types. FA_OUT_F32 may be OR-ed into fa_fwd's dtype: O is then
+ * written as float32 instead of the default (the input type for 16-bit
+ * inputs, bfloat16 for FP8 inputs). */
+enum fa_dtype {
+    FA_F16 = 0,
+    FA_BF16 = 1,
+    FA_FP8_E4M3 = 2,
+    FA_OUT_F32 = 0x100
+};
+
+/*
+ * fa_fwd - fused attention forward.
+ *
+ *  q, k, v  16-bit inputs [B][H][N][d] (dtype FA_F16 or FA_BF16), or, with
+ *           dtype FA_FP8_E4M3, packed FP8 tensors written by fa_fp8_prep
+ *           (e4m3 codes plus per-block float32 scales, see below). For FP8,
+ *           q and k must have been prepared with the same sign vectors (or
+ *           both without); v without signs.
+ *  o        output [B][H][N][d]: input dtype (16-bit), bfloat16 (FP8), or
+ *           float32 when FA_OUT_F32 is set. 16-byte aligned.
+ *  lse      output [B][H][N] float32: natural-log log-sum-exp of each row of
+ *           softmax_scale * Q K^T over its visible keys. 4-byte aligned.
+ *  B, H, N  batch, heads, sequence length (>= 0; B*H*N*d < 2^62).
+ *  d        head dimension: 64, 128 or 256.
+ *  causal   nonzero: query i sees keys j <= i only.
+ *  softmax_scale  finite and > 0 (usually 1/sqrt(d)); multiplies S before the
+ *           softmax.
+ *  dtype    FA_F16 | FA_BF16 | FA_FP8_E4M3, optionally | FA_OUT_F32.
+ *  stream   hipStream_t or NULL.
+ *
+ * q, k, v must be 16-byte aligned. Returns FA_OK, FA_ERR_INVALID_ARG,
+ * FA_ERR_UNSUPPORTED (d not in {64,128,256}) or FA_ERR_HIP.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, int causal, float softmax_scale, int dtype,
+           void* stream);
+
+/*
+ * fa_fp8_prep - incoherent processing + FP8 block quantisation of one tensor.
+ *
+ *  x        16-bit input [B][H][N][d] (in_dtype FA_BF16 or FA_F16), 16-byte
+ *           aligned.
+ *  x8       output packed FP8 tensor of fa_fp8_packed_bytes(B,H,N,d) bytes,
+ *           256-byte aligned:
+ *             bytes [0, B*H*N*d)            e4m3 codes, [B][H][N][d]
+ *             at fa_fp8_scales_offset(...)  float32 scales [B][H][ceil(N/128)]
+ *  signs    int8 [H][d] of +1/-1: rows are first rotated, x <- x diag(s) H_d
+ *           / sqrt(d) (Sylvester Hadamard H_d, same signs for Q and K of a
+ *           head). NULL: no rotation (V, or the plain baseline).
+ *  block_rows  128: one scale per 128 consecutive rows of a head (the last
+ *           block may be shorter); 0: one scale for the whole tensor (the
+ *           plain per-tensor baseline; the same scale is stored in every
+ *           slot).
+ *  in_dtype FA_BF16 or FA_F16.
+ *
+ * Per block: amax = max |x|, scale = amax / 448 in float32 (1 when amax is
+ * 0), code = e4m3 round-to-nearest-even of x / scale, saturated to +-448.
+ * d must be 64, 128 or 256. Per-tensor mode launches three kernels and uses
+ * the scale slots as its reduction buffer; the tensor is only valid once the
+ * stream reaches the end of the call. Returns FA_OK, FA_ERR_INVALID_ARG,
+ * FA_ERR_UNSUPPORTED or FA_ERR_HIP.
+ */
+int fa_fp8_prep(const void* x, void* x8, const int8_t* signs,
+                int B, int H, int N, int d, int block_rows, int in_dtype,
+                void* stream);
+
+/* Size in bytes of a packed FP8 tensor for [B][H][N][d]; 0 for invalid
+ * sizes. Pure host arithmetic. */
+size_t fa_fp8_packed_bytes(int B, int H, int N, int d);
+
+/* Byte offset of the float32 scales inside a packed FP8 tensor (the codes
+ * size rounded up to 256). Pure host arithmetic. */
+size_t fa_fp8_scales_offset(int B, int H, int N, int d);
+
+/* Static, human-readable text for a status code. */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

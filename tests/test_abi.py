@@ -1,0 +1,115 @@
+"""The C ABI on any host: the library loads, exports every symbol include/fa.h
+declares, and rejects bad arguments with the documented status codes before
+making any HIP call (so these run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_55_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fa.lib_path()):
+        pytest.fail("libfa.so is not built; run __graft_entry__.build()")
+    return fa.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = header_functions()
+    assert {"fa_fwd", "fa_fp8_prep", "fa_fp8_packed_bytes", "fa_fp8_scales_offset",
+            "fa_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported"
+
+
+def test_status_strings(L):
+    for code in (0, 1, 2, 3):
+        assert fa.status_string(code) != "unknown status"
+    assert L.fa_status_string(99).decode() == "unknown status"
+
+
+def test_packed_sizes(L):
+    B, H, N, d = 2, 3, 300, 128
+    off = L.fa_fp8_scales_offset(B, H, N, d)
+    assert off % 256 == 0 and off >= B * H * N * d
+    size = L.fa_fp8_packed_bytes(B, H, N, d)
+    assert size % 256 == 0 and size >= off + 4 * B * H * 3
+    assert L.fa_fp8_packed_bytes(-1, 1, 1, 64) == 0
+
+
+FAKE = 0x10000   # aligned non-null fake device pointer; never dereferenced
+
+
+def fwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, N=128, d=128, causal=0,
+             scale=0.088, dtype=fa.FA_BF16)
+    a.update(kw)
+    return fa.fwd_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                      a["causal"], a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=fa.FA_BF16 | 0x200), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(B=-2), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=-1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=None), fa.FA_ERR_INVALID_ARG),
+    (dict(o=FAKE + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(k=FAKE + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=FAKE + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=fa.FA_FP8_E4M3, q=FAKE + 16), fa.FA_ERR_INVALID_ARG),
+    (dict(B=0), fa.FA_OK),
+    (dict(N=0, q=None), fa.FA_OK),
+])
+def test_fwd_validation(L, kw, status):
+    assert fwd(**kw) == status
+
+
+def prep(**kw):
+    a = dict(x=FAKE, x8=FAKE, signs=None, B=1, H=1, N=128, d=128, block_rows=128,
+             in_dtype=fa.FA_BF16)
+    a.update(kw)
+    return fa.fp8_prep_raw(a["x"], a["x8"], a["signs"], a["B"], a["H"], a["N"], a["d"],
+                           a["block_rows"], a["in_dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(in_dtype=fa.FA_FP8_E4M3), fa.FA_ERR_INVALID_ARG),
+    (dict(block_rows=64), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=-5), fa.FA_ERR_INVALID_ARG),
+    (dict(x=None), fa.FA_ERR_INVALID_ARG),
+    (dict(x8=FAKE + 16), fa.FA_ERR_INVALID_ARG),
+    (dict(x=FAKE + 4), fa.FA_ERR_INVALID_ARG),
+    (dict(H=0), fa.FA_OK),
+])
+def test_prep_validation(L, kw, status):
+    assert prep(**kw) == status
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    """The binding never falls back to CPU code: a missing library is an error."""
+    from exact_attention_55_amd import _lib
+    monkeypatch.setattr(_lib, "_LIB", None)
+    monkeypatch.setattr(_lib, "lib_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(fa.FaError):
+        _lib.lib()

@@ -1,0 +1,147 @@
+"""GPU parity of the FP8 path: fa_fp8_prep (random-sign Hadamard + e4m3 block
+quantisation) against the oracle quantiser, and the fp8 fa_fwd against the
+float64 oracle (exact attention of the unquantised inputs) and the fake-quant
+oracle (exact attention of the oracle's own dequantised inputs).
+
+Quantised codes: without the Hadamard every float32 step of the quantiser is
+reproduced exactly, so the codes must be bit-identical. With it, the GPU's
+float32 butterflies round in a different order than the float64 transform,
+which can move a value lying within a few float32 ulps of an e4m3 rounding
+boundary to the neighbouring code; those codes must still be one of the two
+neighbours of the exact value, and they must be rare.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import exact_attention_55_amd as fa
+from exact_attention_55_amd.inputs import CONFIGS, make_qkv, make_signs, to_f64
+
+from helpers import FP8_RMSE, check_lse, errors, sample_rows
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_prep(x, signs, block_rows):
+    B, H, N, d = x.shape
+    sd = None if signs is None else torch.from_numpy(signs).to(DEV)
+    packed = fa.fp8_prep(x.to(DEV), sd, block_rows)
+    torch.cuda.synchronize()
+    codes = fa.fp8_codes_view(packed, B, H, N, d).cpu().numpy()
+    scales = fa.fp8_scales_view(packed, B, H, N, d).cpu().numpy()
+    return packed, codes, scales
+
+
+def compare_codes(codes, scales, ref_codes, ref_scales, exact):
+    if exact:
+        np.testing.assert_array_equal(scales, ref_scales)
+        np.testing.assert_array_equal(codes, ref_codes)
+        return
+    np.testing.assert_allclose(scales, ref_scales, rtol=2e-6, atol=0)
+    diff = codes != ref_codes
+    frac = diff.mean()
+    assert frac <= 1e-3, f"{frac:.2e} of codes differ"
+    if diff.any():
+        # differing codes must be adjacent on the e4m3 grid
+        a = oracle.e4m3_decode(codes[diff])
+        b = oracle.e4m3_decode(ref_codes[diff])
+        mag = np.maximum(np.maximum(np.abs(a), np.abs(b)), 2.0 ** -6)
+        step = 2.0 ** (np.floor(np.log2(mag)) - 3)
+        assert np.all(np.abs(a - b) <= step)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("had", [False, True])
+@pytest.mark.parametrize("block_rows", [128, 0])
+def test_prep_matches_oracle(d, had, block_rows):
+    say(f"prep d={d} had={had} block_rows={block_rows}")
+    B, H, N = 2, 3, 300
+    x, _, _ = make_qkv(B, H, N, d, seed=21 + d, dtype="bf16", outliers=True)
+    signs = make_signs(H, d, 21) if had else None
+    _, codes, scales = gpu_prep(x, signs, block_rows)
+    rc, rs = oracle.fp8_quantize(to_f64(x), signs, block_rows)
+    compare_codes(codes, scales, rc, rs, exact=not had)
+
+
+def test_prep_fp16_and_zero_block():
+    say("prep fp16 / zero block")
+    x, _, _ = make_qkv(1, 2, 256, 128, seed=5, dtype="fp16")
+    x[0, 1, 128:] = 0
+    _, codes, scales = gpu_prep(x, None, 128)
+    rc, rs = oracle.fp8_quantize(to_f64(x), None, 128)
+    compare_codes(codes, scales, rc, rs, exact=True)
+    assert scales[0, 1, 1] == 1.0 and np.all(codes[0, 1, 128:] == 0)
+
+
+def fp8_run(q, k, v, signs, block_rows, causal, out_f32=True):
+    B, H, N, d = q.shape
+    q8, _, _ = gpu_prep(q, signs, block_rows)
+    k8, _, _ = gpu_prep(k, signs, block_rows)
+    v8, _, _ = gpu_prep(v, None, block_rows)
+    o, lse = fa.fwd_fp8(q8, k8, v8, B, H, N, d, causal=causal, out_f32=out_f32)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", [
+    (1, 2, 300, 64, False), (1, 2, 300, 64, True), (2, 2, 640, 128, False),
+    (1, 2, 520, 128, True), (1, 1, 384, 256, False), (1, 1, 200, 256, True),
+])
+def test_fp8_small_vs_oracles(B, H, N, d, causal):
+    say(f"fp8 small B={B} H={H} N={N} d={d} causal={causal}")
+    q, k, v = make_qkv(B, H, N, d, seed=31 + N, dtype="bf16")
+    signs = make_signs(H, d, 31)
+    q64, k64, v64 = to_f64(q), to_f64(k), to_f64(v)
+    o, lse = fp8_run(q, k, v, signs, 128, causal)
+    o_ref, _ = oracle.attention(q64, k64, v64, causal)
+    _, rmse = errors(o, o_ref)
+    assert rmse <= FP8_RMSE, f"fp8 RMSE {rmse:.3e}"
+    o_fq, lse_fq, *_ = oracle.fake_quant_attention(q64, k64, v64, signs, 128, causal)
+    check_lse(lse, lse_fq)
+    _, rmse_fq = errors(o, o_fq)
+    assert rmse_fq <= FP8_RMSE / 2, f"RMSE vs fake-quant {rmse_fq:.3e}"
+
+
+def test_fp8_workload_outliers():
+    """The outlier workload at full size: Hadamard + block scales stays within
+    the RMSE bound and beats plain per-tensor FP8 (sampled rows)."""
+    cfg = CONFIGS["fp8_b4h16n4k_d128"]
+    B, H, N, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
+    say("fp8 outlier workload")
+    q, k, v = make_qkv(**cfg)
+    signs = make_signs(H, d, cfg["seed"])
+    q64, k64, v64 = to_f64(q), to_f64(k), to_f64(v)
+    res = {}
+    for name, sg, br in [("hadamard_block", signs, 128), ("plain_block", None, 128),
+                         ("plain_tensor", None, 0)]:
+        o, lse = fp8_run(q, k, v, sg, br, False)
+        res[name] = (o, lse)
+    heads = [(0, 0), (B - 1, H - 1), (1, 7)]
+    sq = {n: [] for n in res}
+    for b, h in heads:
+        rows = sample_rows(N, seed=b * 50 + h)
+        o_ref, lse_ref = oracle.attention_rows(q64, k64, v64, b, h, rows, False)
+        for n in res:
+            sq[n].append((res[n][0][b, h, rows] - o_ref) ** 2)
+    rmse = {n: float(np.sqrt(np.mean(np.concatenate(v)))) for n, v in sq.items()}
+    say(f"fp8 sampled RMSE: {rmse}")
+    assert rmse["hadamard_block"] <= FP8_RMSE
+    assert rmse["hadamard_block"] < rmse["plain_tensor"]
+    # LSE against the oracle's own quantised inputs (one head, full quantiser)
+    qc, qs = oracle.fp8_quantize(q64[:1, :1], signs[:1], 128)
+    kc, ks = oracle.fp8_quantize(k64[:1, :1], signs[:1], 128)
+    vc, vs = oracle.fp8_quantize(v64[:1, :1], None, 128)
+    rows = sample_rows(N, seed=3)
+    _, lse_fq = oracle.attention_rows(oracle.fp8_dequantize(qc, qs), oracle.fp8_dequantize(kc, ks),
+                                      oracle.fp8_dequantize(vc, vs), 0, 0, rows, False)
+    check_lse(res["hadamard_block"][1][0, 0, rows], lse_fq)

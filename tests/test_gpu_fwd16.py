@@ -1,0 +1,139 @@
+"""GPU parity of the 16-bit fused forward (fa_fwd through the C ABI) against
+the float64 oracle on the same seeded, 16-bit-rounded inputs.
+
+Small shapes are compared element by element over every output; they span
+several query and key tiles and ragged tails. The full workload shapes, in
+the launch configuration the benchmark times, are compared on sampled rows
+that the oracle computes one by one.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import exact_attention_55_amd as fa
+from exact_attention_55_amd.inputs import CONFIGS, make_qkv, to_f64
+
+from helpers import check_lse, check_o, sample_rows
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run(q, k, v, causal, out_f32, scale=None):
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    o, lse = fa.fwd(qd, kd, vd, causal=causal, softmax_scale=scale, out_f32=out_f32)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+SMALL = [
+    # B, H, N, d, causal, dtype
+    (1, 1, 256, 64, False, "fp16"),       # the tiny oracle-check workload
+    (1, 1, 256, 64, True, "fp16"),
+    (2, 3, 300, 64, False, "bf16"),
+    (2, 3, 300, 64, True, "bf16"),
+    (1, 2, 1000, 128, False, "bf16"),
+    (1, 2, 1000, 128, True, "bf16"),
+    (1, 2, 517, 128, True, "fp16"),
+    (1, 1, 257, 256, False, "bf16"),
+    (1, 1, 700, 256, True, "bf16"),
+    (1, 1, 1, 128, False, "bf16"),
+    (1, 1, 1, 64, True, "bf16"),
+    (3, 1, 33, 64, True, "fp16"),
+    (1, 1, 64, 128, True, "bf16"),
+    (1, 1, 65, 128, False, "bf16"),
+    (1, 1, 256, 128, True, "bf16"),
+    (1, 1, 257, 128, True, "bf16"),
+    (2, 2, 512, 64, True, "bf16"),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,dt", SMALL)
+def test_small_full_compare(B, H, N, d, causal, dt):
+    say(f"small B={B} H={H} N={N} d={d} causal={causal} {dt}")
+    q, k, v = make_qkv(B, H, N, d, seed=100 + N + d, dtype=dt)
+    o_ref, lse_ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), causal)
+    o32, lse = run(q, k, v, causal, True)
+    check_o(o32, o_ref, "f32", "(fp32 out)")
+    check_lse(lse, lse_ref)
+    o16, lse16 = run(q, k, v, causal, False)
+    check_o(o16, o_ref, dt, "(16-bit out)")
+    check_lse(lse16, lse_ref)
+
+
+def test_scale_and_large_logits():
+    """Non-default scale and scores of tens of units: online max must track."""
+    say("large logits")
+    q, k, v = make_qkv(1, 2, 384, 64, seed=7, dtype="bf16")
+    q = (q.float() * 4).to(torch.bfloat16)
+    for causal in (False, True):
+        o_ref, lse_ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), causal, 0.5)
+        o, lse = run(q, k, v, causal, True, scale=0.5)
+        check_o(o, o_ref, "f32")
+        check_lse(lse, lse_ref)
+
+
+def test_constant_v_exact_convex_combination():
+    """Constant V must come back exactly (rows of P sum to one)."""
+    say("constant v")
+    q, k, _ = make_qkv(1, 1, 300, 128, seed=9, dtype="bf16")
+    v = torch.full_like(q, 0.7109375)          # exactly representable in bf16
+    o, _ = run(q, k, v, True, True)
+    assert np.max(np.abs(o - 0.7109375)) <= 2e-6
+
+
+def test_causal_row_zero_is_v0():
+    say("causal row 0")
+    q, k, v = make_qkv(2, 2, 200, 64, seed=10, dtype="bf16")
+    o, lse = run(q, k, v, True, False)
+    assert np.array_equal(o[:, :, 0], to_f64(v)[:, :, 0])
+    s0 = np.sum(to_f64(q)[:, :, 0] * to_f64(k)[:, :, 0], -1) / 8.0
+    assert np.max(np.abs(lse[:, :, 0] - s0)) <= 1e-4
+
+
+FULL = ["b8h16n2k_d128", "b8h16n2k_d128_causal", "b4h32n4k_d64", "b2h16n8k_d128_causal",
+        "b2h8n16k_d256_causal"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    cfg = CONFIGS[name]
+    B, H, N, d, causal = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"]
+    say(f"full {name}")
+    q, k, v = make_qkv(**cfg)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    o16, lse16 = fa.fwd(qd, kd, vd, causal=causal)
+    o32, lse32 = fa.fwd(qd, kd, vd, causal=causal, out_f32=True)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o16).all()) and bool(torch.isfinite(lse16).all())
+    rng = np.random.default_rng(1)
+    heads = [(0, 0), (B - 1, H - 1), (int(rng.integers(B)), int(rng.integers(H)))]
+    q64, k64, v64 = to_f64(q), to_f64(k), to_f64(v)
+    for b, h in heads:
+        rows = sample_rows(N, seed=b * 100 + h)
+        o_ref, lse_ref = oracle.attention_rows(q64, k64, v64, b, h, rows, causal)
+        o_s = o32[b, h, rows].cpu().numpy()
+        check_o(o_s, o_ref, "f32", f"head {b},{h}")
+        check_lse(lse32[b, h, rows].cpu().numpy(), lse_ref, f"head {b},{h}")
+        check_o(o16[b, h, rows].float().cpu().numpy(), o_ref, cfg["dtype"], f"head {b},{h} 16-bit")
+        check_lse(lse16[b, h, rows].cpu().numpy(), lse_ref, f"head {b},{h} 16-bit")
+
+
+def test_many_heads_grid():
+    """B*H large with a ragged N: grid indexing over heads and tiles."""
+    say("many heads")
+    q, k, v = make_qkv(3, 37, 130, 64, seed=12, dtype="bf16")
+    o_ref, lse_ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), True)
+    o, lse = run(q, k, v, True, True)
+    check_o(o, o_ref, "f32")
+    check_lse(lse, lse_ref)
