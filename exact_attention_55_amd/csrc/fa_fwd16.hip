@@ -63,14 +63,142 @@ __device__ __forceinline__ float sum2(f16x2 x, float acc) {
     return __builtin_amdgcn_fdot2(x, one, acc, false);
 }
 
+// Tile configuration per head dimension. NW waves per workgroup, each owning
+// 32*QB query rows; BC keys per K/V tile; WPE = waves per SIMD the register
+// budget is sized for (2: 256 registers per wave, so two waves share a SIMD
+// and one wave's softmax overlaps the other's MFMAs).
+#ifndef FA16_CFG_64
+#define FA16_CFG_64 8, 1, 128, 2
+#endif
+#ifndef FA16_CFG_128
+#define FA16_CFG_128 4, 1, 64, 2
+#endif
+#ifndef FA16_CFG_256
+#define FA16_CFG_256 4, 1, 64, 1
+#endif
+template <int NW_, int QB_, int BC_, int WPE_> struct CfgT {
+    static constexpr int NW = NW_, QB = QB_, BC = BC_, WPE = WPE_;
+};
 template <int D> struct Cfg16;
-//                       waves  query blocks/wave  keys/tile
-template <> struct Cfg16<64>  { static constexpr int NW = 4, QB = 2, BC = 64; };
-template <> struct Cfg16<128> { static constexpr int NW = 4, QB = 2, BC = 64; };
-template <> struct Cfg16<256> { static constexpr int NW = 4, QB = 1, BC = 64; };
+template <> struct Cfg16<64> : CfgT<FA16_CFG_64> {};
+template <> struct Cfg16<128> : CfgT<FA16_CFG_128> {};
+template <> struct Cfg16<256> : CfgT<FA16_CFG_256> {};
+
+// Per-wave running state of the online softmax.
+template <typename T, int D, int QB>
+struct RowState {
+    f32x16 o[QB][D / 32];     // O^T accumulators (unnormalised)
+    float m[QB];              // reference maximum, log2 units
+    float l[QB];              // sum of the rounded P fed to the MFMA
+    float lx[QB];             // sum of the fp32 p (for the log-sum-exp)
+};
+
+// One K/V tile for one wave: S^T = K Q^T, optional mask, online softmax
+// update, O^T += V^T P^T. MASK handles the ragged last tile and the causal
+// diagonal; the main loop instantiates it without.
+template <typename T, int D, int QB, int BC, bool CAUSAL, bool MASK>
+__device__ __forceinline__ void tile_step(RowState<T, D, QB>& st,
+                                          const typename Elt<T>::x8 (&qf)[QB][D / 16],
+                                          const T* kl, const T* vl, int k_off, int v_off,
+                                          int k0, int q0, int N, int hi, int l32, float c)
+{
+    using X8 = typename Elt<T>::x8;
+    using X2 = typename Elt<T>::x2;
+    constexpr int KS = D + 8, VS = D + 16;
+    constexpr int NCH = D / 16, NDB = D / 32, NKB = BC / 32, NPV = BC / 16;
+
+    f32x16 s[QB][NKB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) s[qb][kb] = f32x16{};
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            const X8 a = load16<X8>(kl + k_off + 32 * kb * KS + 16 * ch);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32(a, qf[qb][ch], s[qb][kb]);
+        }
+    }
+    if (MASK) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const int q = q0 + 32 * qb + l32;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + key_of(kb, r, hi);
+                    if (key >= N || (CAUSAL && key > q)) s[qb][kb][r] = -INFINITY;
+                }
+        }
+    }
+    float mt[QB];
+    bool need = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        float mx = s[qb][0][0];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
+        mx = fmaxf(mx, xor32(mx));
+        mt[qb] = mx * c;
+        need |= mt[qb] > st.m[qb] + kTau;
+    }
+    if (wave_any(need)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const float mnew = fmaxf(st.m[qb], mt[qb]);
+            const float alpha = (mnew == -INFINITY) ? 1.f : exp2_hw(st.m[qb] - mnew);
+            st.m[qb] = mnew;
+            st.l[qb] *= alpha;
+            st.lx[qb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) st.o[qb][db] *= alpha;
+        }
+    }
+    X8 pf[QB][NPV];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const float nm = -st.m[qb];
+        float ls = st.l[qb], lx = st.lx[qb];
+#pragma unroll
+        for (int t = 0; t < NPV; ++t) {
+            const int kb = t >> 1, r0 = 8 * (t & 1);
+            X2 pp[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float p0 = exp2_hw(fmaf(s[qb][kb][r0 + 2 * j], c, nm));
+                const float p1 = exp2_hw(fmaf(s[qb][kb][r0 + 2 * j + 1], c, nm));
+                pp[j] = pack2<T>(p0, p1);
+                ls = sum2(pp[j], ls);
+                lx += p0;
+                lx += p1;
+            }
+            pf[qb][t] = X8{pp[0][0], pp[0][1], pp[1][0], pp[1][1],
+                           pp[2][0], pp[2][1], pp[3][0], pp[3][1]};
+        }
+        st.l[qb] = ls;
+        st.lx[qb] = lx;
+    }
+#pragma unroll
+    for (int t = 0; t < NPV; ++t) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const T* vp = vl + v_off + 16 * t * VS + 32 * db;
+            const u32x2 lo = lds_read_tr16(vp);
+            const u32x2 hi4 = lds_read_tr16(vp + 4 * VS);
+            const X8 a = __builtin_bit_cast(X8, u32x4{lo[0], lo[1], hi4[0], hi4[1]});
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) st.o[qb][db] = mfma32(a, pf[qb][t], st.o[qb][db]);
+        }
+    }
+}
 
 template <typename T, int D, bool CAUSAL, bool OUT_F32>
-__global__ void __launch_bounds__(Cfg16<D>::NW * 64, 1)
+__global__ void __launch_bounds__(Cfg16<D>::NW * 64, Cfg16<D>::WPE)
 fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
                 void* __restrict__ Og, float* __restrict__ LSEg, int N, int num_qtiles,
                 int num_blocks, float c)
@@ -83,14 +211,13 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     constexpr int KS = D + 8;              // LDS row stride of K (elements)
     constexpr int VS = D + 16;             // LDS row stride of V (elements)
     constexpr int KT = BC * KS, VT = BC * VS;
-    constexpr int NCH = D / 16;            // k-steps of S^T = K Q^T
-    constexpr int NDB = D / 32;            // 32-row blocks of O^T
-    constexpr int NKB = BC / 32;           // 32-key blocks of S^T
-    constexpr int NPV = BC / 16;           // k-steps of O^T += V^T P^T
+    constexpr int NCH = D / 16;
+    constexpr int NDB = D / 32;
     constexpr int NT = NW * 64;
     constexpr int CPR = D / 8;             // 16-byte chunks per row
     constexpr int CPT = BC * CPR / NT;     // chunks per thread per tile
     static_assert(BC * CPR % NT == 0, "tile must split evenly over threads");
+    static_assert(BC % 32 == 0, "key tile is a multiple of 32");
 
     __shared__ __attribute__((aligned(16))) T smem[2 * (KT + VT)];
 
@@ -128,18 +255,20 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
         }
     }
 
+    // Key tiles [0, nfull) need no mask for any wave of the workgroup; tiles
+    // [nfull, nkt) cross the causal diagonal or the end of the sequence.
     const int kend = CAUSAL ? min(N, qtile0 + BR) : N;
     const int nkt = (kend + BC - 1) / BC;
+    const int nfull = (CAUSAL ? min(qtile0 + 1, N) : N) / BC;
 
-    f32x16 o[QB][NDB];
-    float m_ref[QB], lsum[QB], lexact[QB];
+    RowState<T, D, QB> st;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        m_ref[qb] = -INFINITY;
-        lsum[qb] = 0.f;
-        lexact[qb] = 0.f;
+        st.m[qb] = -INFINITY;
+        st.l[qb] = 0.f;
+        st.lx[qb] = 0.f;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) o[qb][db] = f32x16{};
+        for (int db = 0; db < NDB; ++db) st.o[qb][db] = f32x16{};
     }
 
     u32x4 kst[CPT], vst[CPT];
@@ -178,129 +307,45 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     swrite(0);
     __syncthreads();
 
-    for (int kt = 0; kt < nkt; ++kt) {
+    int kt = 0;
+    for (; kt < nfull; ++kt) {
         const int buf = kt & 1;
         if (kt + 1 < nkt) gload(kt + 1);
         const T* kl = smem + buf * (KT + VT);
-        const T* vl = kl + KT;
+        tile_step<T, D, QB, BC, CAUSAL, false>(st, qf, kl, kl + KT, k_off, v_off, kt * BC, q0, N,
+                                               hi, l32, c);
+        if (kt + 1 < nkt) swrite(buf ^ 1);
+        __syncthreads();
+    }
+    for (; kt < nkt; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nkt) gload(kt + 1);
+        const T* kl = smem + buf * (KT + VT);
         const int k0 = kt * BC;
-        const bool active = !CAUSAL || (k0 <= q0 + QW - 1);
-        if (active) {
-            // ---- S^T = K Q^T ----
-            f32x16 s[QB][NKB];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) s[qb][kb] = f32x16{};
-#pragma unroll
-            for (int ch = 0; ch < NCH; ++ch) {
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) {
-                    const X8 a = load16<X8>(kl + k_off + 32 * kb * KS + 16 * ch);
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32(a, qf[qb][ch], s[qb][kb]);
-                }
-            }
-            // ---- mask: ragged last tile and the causal diagonal ----
-            const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0);
-            if (need_mask) {
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    const int q = q0 + 32 * qb + l32;
-#pragma unroll
-                    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int key = k0 + key_of(kb, r, hi);
-                            if (key >= N || (CAUSAL && key > q)) s[qb][kb][r] = -INFINITY;
-                        }
-                }
-            }
-            // ---- online softmax (base 2) ----
-            float mt[QB];
-            bool need = false;
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                float mx = s[qb][0][0];
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-                mx = fmaxf(mx, xor32(mx));
-                mt[qb] = mx * c;
-                need |= mt[qb] > m_ref[qb] + kTau;
-            }
-            if (wave_any(need)) {
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    const float mnew = fmaxf(m_ref[qb], mt[qb]);
-                    const float alpha = (mnew == -INFINITY) ? 1.f : exp2_hw(m_ref[qb] - mnew);
-                    m_ref[qb] = mnew;
-                    lsum[qb] *= alpha;
-                    lexact[qb] *= alpha;
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) o[qb][db] *= alpha;
-                }
-            }
-            X8 pf[QB][NPV];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const float nm = -m_ref[qb];
-                float ls = lsum[qb], lx = lexact[qb];
-#pragma unroll
-                for (int t = 0; t < NPV; ++t) {
-                    const int kb = t >> 1, r0 = 8 * (t & 1);
-                    X2 pp[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float p0 = exp2_hw(fmaf(s[qb][kb][r0 + 2 * j], c, nm));
-                        const float p1 = exp2_hw(fmaf(s[qb][kb][r0 + 2 * j + 1], c, nm));
-                        pp[j] = pack2<T>(p0, p1);
-                        ls = sum2(pp[j], ls);
-                        lx += p0;
-                        lx += p1;
-                    }
-                    pf[qb][t] = X8{pp[0][0], pp[0][1], pp[1][0], pp[1][1],
-                                   pp[2][0], pp[2][1], pp[3][0], pp[3][1]};
-                }
-                lsum[qb] = ls;
-                lexact[qb] = lx;
-            }
-            // ---- O^T += V^T P^T ----
-#pragma unroll
-            for (int t = 0; t < NPV; ++t) {
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const T* vp = vl + v_off + 16 * t * VS + 32 * db;
-                    const u32x2 lo = lds_read_tr16(vp);
-                    const u32x2 hi4 = lds_read_tr16(vp + 4 * VS);
-                    const X8 a = __builtin_bit_cast(X8, u32x4{lo[0], lo[1], hi4[0], hi4[1]});
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(a, pf[qb][t], o[qb][db]);
-                }
-            }
-        }
+        if (!CAUSAL || k0 <= q0 + QW - 1)       // wave has a visible key in this tile
+            tile_step<T, D, QB, BC, CAUSAL, true>(st, qf, kl, kl + KT, k_off, v_off, k0, q0, N,
+                                                  hi, l32, c);
         if (kt + 1 < nkt) swrite(buf ^ 1);
         __syncthreads();
     }
 
-    // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l) ----
+    // ---- epilogue: O = O^T / l~, LSE = ln2 * (m + log2 l) ----
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        const float l = lsum[qb] + xor32(lsum[qb]);
-        const float lx = lexact[qb] + xor32(lexact[qb]);
+        const float l = st.l[qb] + xor32(st.l[qb]);
+        const float lx = st.lx[qb] + xor32(st.lx[qb]);
         const float inv = 1.0f / l;
         const int row = q0 + 32 * qb + l32;
         if (row < N) {
-            if (hi == 0) LSEg[(size_t)bh * N + row] = (m_ref[qb] + __builtin_amdgcn_logf(lx)) * kLn2;
+            if (hi == 0) LSEg[(size_t)bh * N + row] = (st.m[qb] + __builtin_amdgcn_logf(lx)) * kLn2;
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int dcol = 32 * db + 8 * j + 4 * hi;
                     const size_t off = head + (size_t)row * D + dcol;
-                    const float v0 = o[qb][db][4 * j] * inv, v1 = o[qb][db][4 * j + 1] * inv;
-                    const float v2 = o[qb][db][4 * j + 2] * inv, v3 = o[qb][db][4 * j + 3] * inv;
+                    const float v0 = st.o[qb][db][4 * j] * inv, v1 = st.o[qb][db][4 * j + 1] * inv;
+                    const float v2 = st.o[qb][db][4 * j + 2] * inv, v3 = st.o[qb][db][4 * j + 3] * inv;
                     if (OUT_F32) {
                         *reinterpret_cast<f32x4*>(static_cast<float*>(Og) + off) = f32x4{v0, v1, v2, v3};
                     } else {
