@@ -19,6 +19,8 @@ Prints ONE JSON line on stdout.
 """
 
 import argparse
+import glob
+import hashlib
 import json
 import math
 import os
@@ -40,6 +42,33 @@ PEAK_HBM = 8000.0    # GB/s
 
 MAIN = "b8h16n2k_d128"
 FP8 = "fp8_b4h16n4k_d128"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd16_b8h16n2k_d128_traffic.json")
+
+
+def source_hash():
+    """Hash of everything that defines the compiled kernels (sources, flags)."""
+    h = hashlib.sha256()
+    pkg = os.path.join(ROOT, "exact_attention_55_amd")
+    files = sorted(glob.glob(os.path.join(pkg, "csrc", "*"))) + [os.path.join(pkg, "build.py")]
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or
+    None when the kernels changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
 
 
 def log(msg):
@@ -128,7 +157,15 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="only run a plain 1 GiB device copy three times (HBM counter calibration)")
+    ap.add_argument("--only-main", action="store_true",
+                    help="only launch the bf16 non-causal forward (for counter runs)")
+    ap.add_argument("--source-hash", action="store_true", help="print the kernel source hash")
     args = ap.parse_args()
+    if args.source_hash:
+        print(source_hash())
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards over heads with no exchange, see the design notes)",
@@ -138,9 +175,19 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.copy_calib:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)      # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": src.numel() * 4, "copies": 3}))
+        return
     fa.lib()
     log("building inputs")
     legs, _keep = build_legs(dev)
+    if args.only_main:
+        legs = legs[:1]
     for _ in range(args.warmup):
         for L in legs:
             L.run(False)
@@ -174,7 +221,7 @@ def main():
     t_dom = float(np.mean(dom.times))
     achieved = dom.flops / t_dom / 1e12
     roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16, "unit": "TFLOP/s",
-            "frac": achieved / PEAK_BF16, "traffic": None,
+            "frac": achieved / PEAK_BF16, "traffic": measured_traffic(),
             "kernel": "fa_fwd16_kernel<bf16,128,noncausal>", "launch_ms": t_dom * 1e3}
     out = {
         "metric": "attention fwd TFLOP/s (4*B*H*N^2*d, /2 causal), bf16 and fp8",

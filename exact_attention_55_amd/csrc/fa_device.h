@@ -73,6 +73,18 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 // Value held by lane (l ^ 32).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// max / sum of x over the lane pair (l, l ^ 32), on the VALU: permlane32_swap
+// of (x, x) returns the lower half-wave's values in the first result and the
+// upper half-wave's in the second, in every lane.
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
 
 template <typename V>
@@ -95,5 +107,39 @@ __device__ __forceinline__ int krow_perm(int m) {
 __device__ __forceinline__ int key_of(int kb, int r, int hi) {
     return 32 * kb + 16 * (r >> 3) + 8 * hi + (r & 7);
 }
+
+// LDS tiles hold rows unpadded; the 16-byte chunk c of row r is stored at
+// chunk position c ^ lds_swz(r). With 32 four-byte banks (128 bytes per
+// cycle) this spreads both access patterns over distinct banks: the score
+// MFMA reads one chunk from rows perm(0..7) = {0,1,2,3,8,9,10,11} (values
+// 0,2,4,6,1,3,5,7), and a transposing V read covers rows 4w..4w+3 with two
+// adjacent chunks (bit 0 from hi, bits 1-2 from r % 4).
+__device__ __forceinline__ int lds_swz(int r) { return ((r & 3) << 1) | ((r >> 3) & 1); }
+
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes
+// land at lds + 16*i (lds must be wave-uniform).
+__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
+    __builtin_amdgcn_global_load_lds(g, (FA_LDS void*)(lds), 16, 0, 0);
+}
+
+__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Phase boundary of the ping-pong schedule: nothing is scheduled across it,
+// the wave's LDS reads have returned, then the workgroup barrier. The asm
+// memory clobber also keeps the compiler from moving LDS accesses across.
+__device__ __forceinline__ void phase_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+// Same, after this wave's global loads (direct-to-LDS copies included) landed.
+__device__ __forceinline__ void phase_barrier_vm() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Wait until this wave's global loads (including direct-to-LDS ones) landed.
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 }  // namespace fa
