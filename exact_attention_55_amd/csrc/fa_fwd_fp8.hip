@@ -9,8 +9,10 @@
 // codes plus one float32 scale per 128 rows of a head.
 //
 // Same structure as the 16-bit kernel (transposed score tile S^T = K Q^T,
-// transposed output O^T += V^T P^T, lazy rescale, double-buffered LDS), with
-// 32x32x64 e4m3 MFMA. Scale handling, per query block i and key tile j:
+// transposed output O^T += V^T P^T, lazy rescale, direct global->LDS copies
+// into swizzled double-buffered tiles, score MFMAs of the next tile
+// overlapped with the exponentials of this one), with 32x32x64 e4m3 MFMA.
+// Scale handling, per query block i and key tile j:
 //  * logits: s = acc * sq_i * sk_j * softmax_scale; in the base-2 domain the
 //    product c_j = sq_i * sk_j * softmax_scale * log2(e) is one scalar per
 //    tile, folded into the fma that feeds exp2;
@@ -29,10 +31,33 @@ namespace fa {
 constexpr float kTau8 = 4.0f;       // lazy-rescale threshold (log2 units)
 constexpr float kPScale = 16.0f;    // P multiplier before e4m3 rounding (= 2^(8 - kTau8))
 
+#ifndef FA8_CFG_64
+#define FA8_CFG_64 4, 64, 2
+#endif
+#ifndef FA8_CFG_128
+#define FA8_CFG_128 4, 64, 2
+#endif
+#ifndef FA8_CFG_256
+#define FA8_CFG_256 4, 64, 1
+#endif
+// NW waves of 32 query rows, BC keys per tile, WPE waves per SIMD budget.
+template <int NW_, int BC_, int WPE_> struct Cfg8T {
+    static constexpr int NW = NW_, BC = BC_, WPE = WPE_;
+};
 template <int D> struct Cfg8;
-template <> struct Cfg8<64>  { static constexpr int NW = 4, QB = 2, BC = 64; };
-template <> struct Cfg8<128> { static constexpr int NW = 4, QB = 2, BC = 64; };
-template <> struct Cfg8<256> { static constexpr int NW = 4, QB = 1, BC = 64; };
+template <> struct Cfg8<64> : Cfg8T<FA8_CFG_64> {};
+template <> struct Cfg8<128> : Cfg8T<FA8_CFG_128> {};
+template <> struct Cfg8<256> : Cfg8T<FA8_CFG_256> {};
+
+// LDS chunk swizzle for fp8 tiles (rows of D bytes, 16-byte chunks). With 32
+// four-byte banks, the score MFMA reads one chunk from rows
+// {0,1,2,3,8,9,10,11} per 8 lanes and a transposing V read covers 8
+// consecutive rows of one chunk per 16 lanes; both must hit distinct bank
+// groups. D = 64 packs two rows per 128-byte bank window.
+template <int D> __device__ __forceinline__ int swz8(int r) {
+    if (D == 64) return ((r >> 1) & 3) ^ (((r >> 3) & 1) << 1);
+    return (r & 7) ^ ((r >> 1) & 4);
+}
 
 __device__ __forceinline__ uint32_t cvt4_e4m3(float a, float b, float c, float d) {
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
@@ -40,34 +65,228 @@ __device__ __forceinline__ uint32_t cvt4_e4m3(float a, float b, float c, float d
     return (uint32_t)w;
 }
 
+template <int D, int BC>
+struct Wave8 {
+    static constexpr int RB = D;           // bytes per K / V row in LDS
+    static constexpr int NCH = D / 64;     // k-steps of S^T = K Q^T
+    static constexpr int NDB = D / 32;     // 32-row blocks of O^T
+    static constexpr int NKB = BC / 32;    // 32-key blocks of S^T
+    static constexpr int NPV = BC / 64;    // k-steps of O^T += V^T P'^T
+    static constexpr int NVA = NDB < 4 ? NDB : 4;   // distinct V lane offsets
+    static_assert(NKB == 2 * NPV, "one PV MFMA per two score blocks");
+
+    f32x16 o[NDB];
+    float m, l;
+
+    __device__ __forceinline__ void init() {
+        m = -INFINITY;
+        l = 0.f;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+    }
+
+    // K fragment (ch, kb): row perm(l32) + 32*kb, bytes [64*ch + 32*hi, +32)
+    // = logical chunks 4*ch + 2*hi + e (e = 0, 1). ka[ch & 1][e] holds the
+    // swizzled lane offset; chunk bit 3 (ch >> 1) is an unswizzled 128 bytes.
+    static __device__ __forceinline__ i32x8 kfrag(const char* kl, const int (&ka)[2][2], int ch, int kb) {
+        const char* p = kl + 32 * kb * RB + 128 * (ch >> 1);
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(p + ka[ch & 1][0]);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(p + ka[ch & 1][1]);
+        return i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                     (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+    }
+
+    static __device__ __forceinline__ void qk(f32x16 (&s)[NKB], const i32x8 (&kf)[NKB][NCH],
+                                              const i32x8 (&qf)[NCH], int c0, int c1) {
+#pragma unroll
+        for (int ch = c0; ch < c1; ++ch)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma32_fp8(kf[kb][ch], qf[ch], s[kb]);
+    }
+
+    static __device__ __forceinline__ void scores(f32x16 (&s)[NKB], const char* kl,
+                                                  const int (&ka)[2][2], const i32x8 (&qf)[NCH]) {
+        i32x8 kf[NKB][NCH];
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) kf[kb][ch] = kfrag(kl, ka, ch, kb);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+        qk(s, kf, qf, 0, NCH);
+    }
+
+    template <bool CAUSAL>
+    static __device__ __forceinline__ void mask(f32x16 (&s)[NKB], int k0, int q0, int N, int hi,
+                                                int l32) {
+        const int q = q0 + l32;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = k0 + key_of(kb, r, hi);
+                if (key >= N || (CAUSAL && key > q)) s[kb][r] = -INFINITY;
+            }
+    }
+
+    // Row maximum of the tile in log2 units (cj > 0 commutes with max).
+    static __device__ __forceinline__ float tile_max(const f32x16 (&s)[NKB], float cj) {
+        float part[NKB * 4];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                part[4 * kb + g] = fmaxf(fmaxf(s[kb][4 * g], s[kb][4 * g + 1]),
+                                         fmaxf(s[kb][4 * g + 2], s[kb][4 * g + 3]));
+#pragma unroll
+        for (int w = NKB * 4; w > 1; w /= 2)
+#pragma unroll
+            for (int i = 0; i < w / 2; ++i) part[i] = fmaxf(part[i], part[i + w / 2]);
+        return pair_max(part[0]) * cj;
+    }
+
+    __device__ __forceinline__ void rescale(float mt) {
+        if (wave_any(mt > m + kTau8)) {
+            const float mnew = fmaxf(m, mt);
+            const float alpha = (mnew == -INFINITY) ? 1.f : exp2_hw(m - mnew);
+            m = mnew;
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+        }
+    }
+
+    // P' for score blocks 2t, 2t+1 -> PV operand t. Dword g of the operand
+    // holds the e4m3 bytes of registers 4*(g%4)..+3 of score block 2t + g/4.
+    __device__ __forceinline__ void probs(const f32x16 (&s)[NKB], i32x8 (&pf)[NPV], int t,
+                                          float cj, float bj, float (&ls)[2]) {
+        const float nm = bj - m;
+        uint32_t w[8];
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            const int kb = 2 * t + g / 4, r = 4 * (g % 4);
+            const float p0 = exp2_hw(fmaf(s[kb][r], cj, nm));
+            const float p1 = exp2_hw(fmaf(s[kb][r + 1], cj, nm));
+            const float p2 = exp2_hw(fmaf(s[kb][r + 2], cj, nm));
+            const float p3 = exp2_hw(fmaf(s[kb][r + 3], cj, nm));
+            ls[g & 1] += (p0 + p1) + (p2 + p3);
+            w[g] = cvt4_e4m3(p0, p1, p2, p3);
+        }
+        pf[t] = i32x8{(int)w[0], (int)w[1], (int)w[2], (int)w[3],
+                      (int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+    }
+
+    // V^T fragment (t, db): slots 8c..8c+7 = keys 64t + 16c + 8hi + 0..7 of
+    // d-row 32*db + l32; one transposing read of 8 rows per c.
+    static __device__ __forceinline__ void vfrags(i32x8 (&vf)[NPV][NDB], const char* vl,
+                                                  const int (&va)[NVA]) {
+#pragma unroll
+        for (int t = 0; t < NPV; ++t)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const char* vp = vl + va[db % NVA] + 128 * (db / NVA) + 64 * t * RB;
+                const u32x2 r0 = lds_read_tr8(vp);
+                const u32x2 r1 = lds_read_tr8(vp + 16 * RB);
+                const u32x2 r2 = lds_read_tr8(vp + 32 * RB);
+                const u32x2 r3 = lds_read_tr8(vp + 48 * RB);
+                vf[t][db] = i32x8{(int)r0[0], (int)r0[1], (int)r1[0], (int)r1[1],
+                                  (int)r2[0], (int)r2[1], (int)r3[0], (int)r3[1]};
+            }
+    }
+
+    __device__ __forceinline__ void pv(const i32x8 (&vf)[NPV][NDB], const i32x8 (&pf)[NPV]) {
+#pragma unroll
+        for (int t = 0; t < NPV; ++t)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) o[db] = mfma32_fp8(vf[t][db], pf[t], o[db]);
+    }
+
+    // Softmax + PV of the tile in s (no overlap).
+    __device__ __forceinline__ void finish(const f32x16 (&s)[NKB], const char* vl,
+                                           const int (&va)[NVA], float cj, float bj, float lscale) {
+        rescale(tile_max(s, cj));
+        i32x8 vf[NPV][NDB];
+        vfrags(vf, vl, va);
+        __builtin_amdgcn_sched_barrier(0);
+        i32x8 pf[NPV];
+        float ls[2] = {0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < NPV; ++t) probs(s, pf, t, cj, bj, ls);
+        l += (ls[0] + ls[1]) * lscale;
+        pv(vf, pf);
+    }
+
+    // Pipelined step: exponentials of this tile (maximum already applied)
+    // interleaved with the score MFMAs of the next tile (K fragments at kn);
+    // then the PV MFMAs of this tile interleaved with the row maximum of the
+    // next tile (returned, in log2 units with its own scale cjn).
+    __device__ __forceinline__ float overlap(const f32x16 (&s)[NKB], f32x16 (&sn)[NKB], const char* kn,
+                                             const int (&ka)[2][2], const char* vl,
+                                             const int (&va)[NVA], const i32x8 (&qf)[NCH],
+                                             float cj, float bj, float lscale, float cjn) {
+        constexpr int MF_QK = NCH * NKB;
+        constexpr int MF_PV = NPV * NDB;
+        i32x8 kf[NKB][NCH];
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) kf[kb][ch] = kfrag(kn, ka, ch, kb);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) sn[kb] = f32x16{};
+        i32x8 pf[NPV];
+        float ls[2] = {0.f, 0.f};
+        qk(sn, kf, qf, 0, NCH);
+#pragma unroll
+        for (int t = 0; t < NPV; ++t) probs(s, pf, t, cj, bj, ls);
+        l += (ls[0] + ls[1]) * lscale;
+#pragma unroll
+        for (int i = 0; i < MF_QK; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // twelve VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        i32x8 vf[NPV][NDB];
+        vfrags(vf, vl, va);
+        __builtin_amdgcn_sched_barrier(0);
+        pv(vf, pf);
+        const float mtn = tile_max(sn, cjn);
+#pragma unroll
+        for (int i = 0; i < MF_PV; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        return mtn;
+    }
+};
+
 template <int D, bool CAUSAL, bool OUT_F32>
-__global__ void __launch_bounds__(Cfg8<D>::NW * 64, 1)
+__global__ void __launch_bounds__(Cfg8<D>::NW * 64, Cfg8<D>::WPE)
 fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg,
                   const uint8_t* __restrict__ Vg, void* __restrict__ Og, float* __restrict__ LSEg,
                   int N, int num_qtiles, int num_blocks, int nsb, size_t scales_off, float c)
 {
-    constexpr int NW = Cfg8<D>::NW, QB = Cfg8<D>::QB, BC = Cfg8<D>::BC;
-    constexpr int QW = 32 * QB;
-    constexpr int BR = NW * QW;
-    constexpr int KS = D + 16;              // LDS row stride (bytes)
-    constexpr int VS = D + 16;
-    constexpr int KT = BC * KS, VT = BC * VS;
-    constexpr int NCH = D / 64;             // k-steps of S^T = K Q^T
-    constexpr int NDB = D / 32;             // 32-row blocks of O^T
-    constexpr int NKB = BC / 32;            // 32-key blocks of S^T
-    constexpr int NPV = BC / 64;            // k-steps of O^T += V^T P^T
-    constexpr int NT = NW * 64;
-    constexpr int CPR = D / 16;             // 16-byte chunks per row
-    constexpr int CPT = BC * CPR / NT;
-    static_assert(BC * CPR % NT == 0, "tile must split evenly over threads");
-    static_assert(NKB == 2 * NPV, "one PV MFMA per two score blocks");
+    constexpr int NW = Cfg8<D>::NW, BC = Cfg8<D>::BC;
+    using W = Wave8<D, BC>;
+    constexpr int QW = 32, BR = NW * QW;
+    constexpr int NCH = W::NCH, NDB = W::NDB, NKB = W::NKB, NVA = W::NVA, RB = W::RB;
+    constexpr int TB = BC * RB;            // bytes per K (or V) tile
+    constexpr int NIW = TB / 1024 / NW;    // 1 KB direct loads per wave per tile
+    static_assert(TB % (1024 * NW) == 0, "tile must split into 1 KB loads per wave");
     static_assert(kQuantBlockRows % BC == 0 && kQuantBlockRows % QW == 0, "scale blocks");
 
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (KT + VT)];
+    // LDS: K tiles in slots 0, 1 and V tiles in slots 2, 3 (tile t uses t & 1).
+    __shared__ __attribute__((aligned(1024))) char smem[4 * TB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
+    const int wave_u = wave_uniform(wave);
+    // Tiles are written only by direct global->LDS loads (invisible to the
+    // compiler as stores); a store it cannot rule out keeps the reads alive.
+    if (num_blocks < 0) smem[tid] = 0;
 
     int bid = blockIdx.x;
     if ((num_blocks & 7) == 0) bid = (bid & 7) * (num_blocks >> 3) + (bid >> 3);
@@ -89,16 +308,42 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     float svmax = 0.f;
     for (int i = lane; i < nsb; i += 64) svmax = fmaxf(svmax, Vs[i]);
 #pragma unroll
-    for (int m = 32; m >= 1; m /= 2) svmax = fmaxf(svmax, __shfl_xor(svmax, m, 64));
+    for (int mm = 32; mm >= 1; mm /= 2) svmax = fmaxf(svmax, __shfl_xor(svmax, mm, 64));
+    const float cq = Qs[min(q0, N - 1) / kQuantBlockRows] * c;
 
-    // Q^T fragments: query q0+32*qb+l32, bytes [64*ch + 32*hi, +32)
-    i32x8 qf[QB][NCH];
-    float cq[QB];
+    // Direct-load mapping (see fa_fwd16_kernel), chunk swizzle swz8.
+    int grow[NIW], gcol[NIW];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int row = q0 + 32 * qb + l32;
-        const int rowc = min(q0 + 32 * qb, N - 1);          // wave-uniform scale block
-        cq[qb] = Qs[rowc / kQuantBlockRows] * c;
+    for (int j = 0; j < NIW; ++j) {
+        const int p = (wave * NIW + j) * 1024 + 16 * lane;
+        grow[j] = p / RB;
+        gcol[j] = ((p % RB / 16) ^ swz8<D>(grow[j])) * 16;
+    }
+    const int nkt_total = (N + BC - 1) / BC;
+    auto load_kv = [&](const uint8_t* src, int t, int slot) {
+        if (t >= nkt_total) return;
+        char* dst = smem + slot * TB + wave_u * NIW * 1024;
+#pragma unroll
+        for (int j = 0; j < NIW; ++j) {
+            const int key = min(t * BC + grow[j], N - 1);     // rows past N: any valid row
+            load_lds16(src + (size_t)key * D + gcol[j], dst + j * 1024);
+        }
+    };
+    auto ktile = [&](int t) -> const char* { return smem + (t & 1) * TB; };
+    auto vtile = [&](int t) -> const char* { return smem + (2 + (t & 1)) * TB; };
+    // per-tile scale terms: score multiplier, P exponent offset, l weight
+    auto tile_scales = [&](int t, float& cj, float& bj, float& lscale) {
+        const int sblk = (t * BC) / kQuantBlockRows;
+        const float wv = Vs[sblk] / svmax;                    // (0, 1]
+        cj = cq * Ks[sblk];
+        bj = __builtin_amdgcn_logf(kPScale * wv);            // log2(16 w_j)
+        lscale = 1.0f / (kPScale * wv);
+    };
+
+    // Q^T fragments: query q0 + l32, bytes [64*ch + 32*hi, +32)
+    i32x8 qf[NCH];
+    {
+        const int row = q0 + l32;
 #pragma unroll
         for (int ch = 0; ch < NCH; ++ch) {
             u32x4 a = u32x4{0, 0, 0, 0}, b = u32x4{0, 0, 0, 0};
@@ -107,197 +352,108 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
                 a = *reinterpret_cast<const u32x4*>(p);
                 b = *reinterpret_cast<const u32x4*>(p + 16);
             }
-            qf[qb][ch] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3],
-                               (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+            qf[ch] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3],
+                           (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+        }
+    }
+
+    // Lane offsets into swizzled tiles.
+    int ka[2][2], va[NVA];
+    {
+        const int kr = krow_perm(l32);
+#pragma unroll
+        for (int chl = 0; chl < 2; ++chl)
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                ka[chl][e] = kr * RB + (((4 * chl + 2 * hi + e) ^ swz8<D>(kr)) & (RB / 16 - 1)) * 16;
+        const int vr = 8 * hi + (lane & 15) / 2;
+#pragma unroll
+        for (int db = 0; db < NVA; ++db) {
+            const int chunk = 2 * db + (l32 / 16);
+            va[db] = vr * RB + ((chunk ^ swz8<D>(vr)) * 16) + 8 * (lane & 1);
         }
     }
 
     const int kend = CAUSAL ? min(N, qtile0 + BR) : N;
     const int nkt = (kend + BC - 1) / BC;
+    const int nfull = (CAUSAL ? min(qtile0 + 1, N) : N) / BC;
 
-    f32x16 o[QB][NDB];
-    float m_ref[QB], lsum[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        m_ref[qb] = -INFINITY;
-        lsum[qb] = 0.f;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) o[qb][db] = f32x16{};
-    }
+    W st;
+    st.init();
+    f32x16 s[NKB];
+    float mt = -INFINITY;
 
-    u32x4 kst[CPT], vst[CPT];
-    auto gload = [&](int kt) {
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int idx = tid + i * NT;
-            const int r = idx / CPR, ch = idx % CPR;
-            const int key = kt * BC + r;
-            if (key < N) {
-                kst[i] = *reinterpret_cast<const u32x4*>(K + (size_t)key * D + ch * 16);
-                vst[i] = *reinterpret_cast<const u32x4*>(V + (size_t)key * D + ch * 16);
-            } else {
-                kst[i] = u32x4{0, 0, 0, 0};
-                vst[i] = u32x4{0, 0, 0, 0};
-            }
-        }
-    };
-    auto swrite = [&](int buf) {
-        uint8_t* kl = smem + buf * (KT + VT);
-        uint8_t* vl = kl + KT;
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int idx = tid + i * NT;
-            const int r = idx / CPR, ch = idx % CPR;
-            *reinterpret_cast<u32x4*>(kl + r * KS + ch * 16) = kst[i];
-            *reinterpret_cast<u32x4*>(vl + r * VS + ch * 16) = vst[i];
-        }
-    };
-
-    const int k_off = krow_perm(l32) * KS + 32 * hi;
-    const int v_off = (8 * hi + (lane & 15) / 2) * VS + 16 * (l32 / 16) + 8 * (lane & 1);
-
-    gload(0);
-    swrite(0);
+    load_kv(K, 0, 0);
+    load_kv(V, 0, 2);
+    load_kv(K, 1, 1);
+    wait_vm_all();
     __syncthreads();
-
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nkt) gload(kt + 1);
-        const uint8_t* kl = smem + buf * (KT + VT);
-        const uint8_t* vl = kl + KT;
-        const int k0 = kt * BC;
-        const bool active = !CAUSAL || (k0 <= q0 + QW - 1);
-        if (active) {
-            const int sblk = k0 / kQuantBlockRows;
-            const float sk = Ks[sblk];
-            const float wv = Vs[sblk] / svmax;                  // (0, 1]
-            const float bj = __builtin_amdgcn_logf(kPScale * wv);  // log2(16 w_j)
-            const float lscale = 1.0f / (kPScale * wv);
-            // ---- S^T = K Q^T ----
-            f32x16 s[QB][NKB];
+    if (nfull > 0) {
+        float cj, bj, ls;
+        tile_scales(0, cj, bj, ls);
+        W::scores(s, ktile(0), ka, qf);
+        mt = W::tile_max(s, cj);
+        __syncthreads();                     // all waves done reading K_0's slot
+    }
+    int t = 0;
+    for (; t + 1 < nfull; ++t) {
+        load_kv(K, t + 2, t & 1);
+        load_kv(V, t + 1, 2 + ((t + 1) & 1));
+        float cj, bj, lscale, cjn, bjn, lsn;
+        tile_scales(t, cj, bj, lscale);
+        tile_scales(t + 1, cjn, bjn, lsn);
+        st.rescale(mt);
+        f32x16 sn[NKB];
+        mt = st.overlap(s, sn, ktile(t + 1), ka, vtile(t), va, qf, cj, bj, lscale, cjn);
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) s[qb][kb] = f32x16{};
-#pragma unroll
-            for (int ch = 0; ch < NCH; ++ch) {
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) {
-                    const uint8_t* p = kl + k_off + 32 * kb * KS + 64 * ch;
-                    const u32x4 a0 = *reinterpret_cast<const u32x4*>(p);
-                    const u32x4 a1 = *reinterpret_cast<const u32x4*>(p + 16);
-                    const i32x8 a = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                                          (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32_fp8(a, qf[qb][ch], s[qb][kb]);
-                }
-            }
-            const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0);
-            if (need_mask) {
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    const int q = q0 + 32 * qb + l32;
-#pragma unroll
-                    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int key = k0 + key_of(kb, r, hi);
-                            if (key >= N || (CAUSAL && key > q)) s[qb][kb][r] = -INFINITY;
-                        }
-                }
-            }
-            float cj[QB], mt[QB];
-            bool need = false;
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                cj[qb] = cq[qb] * sk;
-                float mx = s[qb][0][0];
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-                mx = fmaxf(mx, xor32(mx));
-                mt[qb] = mx * cj[qb];
-                need |= mt[qb] > m_ref[qb] + kTau8;
-            }
-            if (wave_any(need)) {
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    const float mnew = fmaxf(m_ref[qb], mt[qb]);
-                    const float alpha = (mnew == -INFINITY) ? 1.f : exp2_hw(m_ref[qb] - mnew);
-                    m_ref[qb] = mnew;
-                    lsum[qb] *= alpha;
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) o[qb][db] *= alpha;
-                }
-            }
-            i32x8 pf[QB][NPV];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const float nm = bj - m_ref[qb];
-                float ls = 0.f;
-#pragma unroll
-                for (int t = 0; t < NPV; ++t) {
-                    uint32_t w[8];
-#pragma unroll
-                    for (int g = 0; g < 8; ++g) {
-                        const int kb = 2 * t + g / 4, r = 4 * (g % 4);
-                        float p[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            p[e] = exp2_hw(fmaf(s[qb][kb][r + e], cj[qb], nm));
-                            ls += p[e];
-                        }
-                        w[g] = cvt4_e4m3(p[0], p[1], p[2], p[3]);
-                    }
-                    pf[qb][t] = i32x8{(int)w[0], (int)w[1], (int)w[2], (int)w[3],
-                                      (int)w[4], (int)w[5], (int)w[6], (int)w[7]};
-                }
-                lsum[qb] += ls * lscale;
-            }
-            // ---- O^T += V^T P'^T ----
-#pragma unroll
-            for (int t = 0; t < NPV; ++t) {
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const uint8_t* vp = vl + v_off + 64 * t * VS + 32 * db;
-                    const u32x2 r0 = lds_read_tr8(vp);
-                    const u32x2 r1 = lds_read_tr8(vp + 16 * VS);
-                    const u32x2 r2 = lds_read_tr8(vp + 32 * VS);
-                    const u32x2 r3 = lds_read_tr8(vp + 48 * VS);
-                    const i32x8 a = i32x8{(int)r0[0], (int)r0[1], (int)r1[0], (int)r1[1],
-                                          (int)r2[0], (int)r2[1], (int)r3[0], (int)r3[1]};
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32_fp8(a, pf[qb][t], o[qb][db]);
-                }
-            }
+        for (int kb = 0; kb < NKB; ++kb) s[kb] = sn[kb];
+        wait_vm_all();
+        __syncthreads();
+    }
+    if (nfull > 0) {                          // last full tile
+        load_kv(V, t + 1, 2 + ((t + 1) & 1));
+        float cj, bj, lscale;
+        tile_scales(t, cj, bj, lscale);
+        st.finish(s, vtile(t), va, cj, bj, lscale);
+        wait_vm_all();
+        __syncthreads();
+        ++t;
+    }
+    for (; t < nkt; ++t) {                    // ragged end / causal diagonal
+        load_kv(K, t + 1, (t + 1) & 1);
+        load_kv(V, t + 1, 2 + ((t + 1) & 1));
+        const int k0 = t * BC;
+        if (!CAUSAL || k0 <= q0 + QW - 1) {
+            float cj, bj, lscale;
+            tile_scales(t, cj, bj, lscale);
+            W::scores(s, ktile(t), ka, qf);
+            W::template mask<CAUSAL>(s, k0, q0, N, hi, l32);
+            st.finish(s, vtile(t), va, cj, bj, lscale);
         }
-        if (kt + 1 < nkt) swrite(buf ^ 1);
+        wait_vm_all();
         __syncthreads();
     }
 
+    // ---- epilogue: O = O_acc * sv_max / (16 l), LSE = ln2 * (m + log2 l) ----
+    const float l = pair_sum(st.l);
+    const float inv = svmax / (kPScale * l);
+    const int row = q0 + l32;
+    if (row < N) {
+        if (hi == 0) LSEg[(size_t)bh * N + row] = (st.m + __builtin_amdgcn_logf(l)) * kLn2;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const float l = lsum[qb] + xor32(lsum[qb]);
-        const float inv = svmax / (kPScale * l);
-        const int row = q0 + 32 * qb + l32;
-        if (row < N) {
-            if (hi == 0) LSEg[(size_t)bh * N + row] = (m_ref[qb] + __builtin_amdgcn_logf(l)) * kLn2;
+        for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int dcol = 32 * db + 8 * j + 4 * hi;
-                    const size_t off = head + (size_t)row * D + dcol;
-                    const float v0 = o[qb][db][4 * j] * inv, v1 = o[qb][db][4 * j + 1] * inv;
-                    const float v2 = o[qb][db][4 * j + 2] * inv, v3 = o[qb][db][4 * j + 3] * inv;
-                    if (OUT_F32) {
-                        *reinterpret_cast<f32x4*>(static_cast<float*>(Og) + off) = f32x4{v0, v1, v2, v3};
-                    } else {
-                        const bf16x2 a = {(__bf16)v0, (__bf16)v1}, b = {(__bf16)v2, (__bf16)v3};
-                        *reinterpret_cast<u32x2*>(static_cast<__bf16*>(Og) + off) =
-                            u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
-                    }
+            for (int j = 0; j < 4; ++j) {
+                const int dcol = 32 * db + 8 * j + 4 * hi;
+                const size_t off = head + (size_t)row * D + dcol;
+                const float v0 = st.o[db][4 * j] * inv, v1 = st.o[db][4 * j + 1] * inv;
+                const float v2 = st.o[db][4 * j + 2] * inv, v3 = st.o[db][4 * j + 3] * inv;
+                if (OUT_F32) {
+                    *reinterpret_cast<f32x4*>(static_cast<float*>(Og) + off) = f32x4{v0, v1, v2, v3};
+                } else {
+                    const bf16x2 a = {(__bf16)v0, (__bf16)v1}, b = {(__bf16)v2, (__bf16)v3};
+                    *reinterpret_cast<u32x2*>(static_cast<__bf16*>(Og) + off) =
+                        u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
                 }
             }
         }
@@ -306,7 +462,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
 
 template <int D, bool CAUSAL, bool OUT_F32>
 static hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
-    constexpr int BR = Cfg8<D>::NW * 32 * Cfg8<D>::QB;
+    constexpr int BR = Cfg8<D>::NW * 32;
     const int num_qtiles = (a.N + BR - 1) / BR;
     const long long nblk = (long long)num_qtiles * a.B * a.H;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
