@@ -109,12 +109,24 @@ __device__ __forceinline__ int key_of(int kb, int r, int hi) {
 }
 
 // LDS tiles hold rows unpadded; the 16-byte chunk c of row r is stored at
-// chunk position c ^ lds_swz(r). With 32 four-byte banks (128 bytes per
-// cycle) this spreads both access patterns over distinct banks: the score
-// MFMA reads one chunk from rows perm(0..7) = {0,1,2,3,8,9,10,11} (values
-// 0,2,4,6,1,3,5,7), and a transposing V read covers rows 4w..4w+3 with two
-// adjacent chunks (bit 0 from hi, bits 1-2 from r % 4).
-__device__ __forceinline__ int lds_swz(int r) { return ((r & 3) << 1) | ((r >> 3) & 1); }
+// chunk position c ^ swz(r). The LDS serves 64 four-byte banks (256 bytes)
+// per cycle: 16 lanes of a 16-byte read or 32 lanes of an 8-byte read. The
+// swizzle makes both access patterns of the kernels hit 16 distinct bank
+// groups: the score MFMA's K reads (one chunk from 16 rows {0..15} of a
+// 32-key block) and the transposing V reads (4 rows x 4 chunks for 16-bit,
+// 8 rows x 2 chunks for 8-bit data, per 32 lanes).
+//   16-bit rows of 2*D bytes:  D = 64 (two rows per 256 bytes):
+//     swz = 4*((r>>1)&1) + ((r>>2)&3);  D >= 128: swz = 4*(r&3) + ((r>>2)&3)
+template <int D> __device__ __forceinline__ int lds_swz16(int r) {
+    if (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+}
+//   8-bit rows of D bytes: D = 64 (four rows per 256 bytes), 128 (two), 256.
+template <int D> __device__ __forceinline__ int lds_swz8(int r) {
+    if (D == 64) return (((r >> 2) & 1) << 1) | ((r >> 3) & 1);
+    if (D == 128) return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+    return ((r & 7) << 1) | ((r >> 3) & 1);
+}
 
 // 16 bytes per lane from global memory straight into LDS: lane i's bytes
 // land at lds + 16*i (lds must be wave-uniform).

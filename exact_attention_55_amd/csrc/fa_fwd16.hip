@@ -88,7 +88,7 @@ template <> struct Cfg16<128> : CfgT<FA16_CFG_128> {};
 template <> struct Cfg16<256> : CfgT<FA16_CFG_256> {};
 
 // Per-wave state and per-tile steps. A wave owns 32*QB query rows; a key
-// tile has BC keys. Swizzled LDS tiles: see lds_swz and the lane offsets ka
+// tile has BC keys. Swizzled LDS tiles: see lds_swz16 and the lane offsets ka
 // (K fragments) and va (transposing V reads) set up in the kernel.
 template <typename T, int D, int QB, int BC>
 struct Wave16 {
@@ -116,9 +116,14 @@ struct Wave16 {
         }
     }
 
+    // Distinct swizzled lane offsets: K fragments repeat every NKA k-steps
+    // (NKA*32 bytes), V^T fragments every NVA d-blocks (NVA*64 bytes).
+    static constexpr int NKA = (D == 64) ? 4 : 8;
+    static constexpr int NVA = (D == 64) ? 2 : 4;
+
     // K fragment (ch, kb): row perm(l32) + 32*kb, logical chunk 2*ch + hi.
-    static __device__ __forceinline__ X8 kfrag(const char* kl, const int (&ka)[4], int ch, int kb) {
-        return load16<X8>(kl + ka[ch & 3] + 128 * (ch >> 2) + 32 * kb * RB);
+    static __device__ __forceinline__ X8 kfrag(const char* kl, const int (&ka)[NKA], int ch, int kb) {
+        return load16<X8>(kl + ka[ch % NKA] + NKA * 32 * (ch / NKA) + 32 * kb * RB);
     }
 
     // S^T for k-steps [c0, c1) with fragments already in registers.
@@ -134,7 +139,7 @@ struct Wave16 {
 
     // Whole score tile: all K fragments requested before the first MFMA.
     static __device__ __forceinline__ void scores(f32x16 (&s)[QB][NKB], const char* kl,
-                                                  const int (&ka)[4], const X8 (&qf)[QB][NCH]) {
+                                                  const int (&ka)[NKA], const X8 (&qf)[QB][NCH]) {
         X8 kf[NKB][NCH];
 #pragma unroll
         for (int ch = 0; ch < NCH; ++ch)
@@ -232,15 +237,17 @@ struct Wave16 {
     }
 
     // V^T fragments (t, db): key rows 16*t + 8*hi + 4*u + (lane%16)/4.
+    // The second read covers rows +4, whose swizzle flips chunk bit 0:
+    // va[NVA] holds that step (4*RB +- 16 bytes) for this lane.
     static __device__ __forceinline__ void vfrags(X8 (&vf)[NPV][NDB], const char* vl,
-                                                  const int (&va)[2]) {
+                                                  const int (&va)[NVA + 1]) {
 #pragma unroll
         for (int t = 0; t < NPV; ++t)
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const char* vp = vl + va[db & 1] + 128 * (db >> 1) + 16 * t * RB;
+                const char* vp = vl + va[db % NVA] + NVA * 64 * (db / NVA) + 16 * t * RB;
                 const u32x2 lo = lds_read_tr16(vp);
-                const u32x2 hi4 = lds_read_tr16(vp + 4 * RB);
+                const u32x2 hi4 = lds_read_tr16(vp + va[NVA]);
                 vf[t][db] = __builtin_bit_cast(X8, u32x4{lo[0], lo[1], hi4[0], hi4[1]});
             }
     }
@@ -273,7 +280,7 @@ struct Wave16 {
 
     // Softmax + PV of a tile whose scores are in s (no overlap).
     __device__ __forceinline__ void finish(const f32x16 (&s)[QB][NKB], const char* vl,
-                                           const int (&va)[2], float c) {
+                                           const int (&va)[NVA + 1], float c) {
         float mt[QB];
         tile_max(s, c, mt);
         rescale(mt);
@@ -297,8 +304,8 @@ struct Wave16 {
     //   halves so the first half's registers are free before the second
     //   lands. sched_group_barrier fixes the MFMA / VALU alternation.
     __device__ __forceinline__ void overlap(const f32x16 (&s)[QB][NKB], f32x16 (&sn)[QB][NKB],
-                                            float (&mtn)[QB], const char* kn, const int (&ka)[4],
-                                            const char* vl, const int (&va)[2],
+                                            float (&mtn)[QB], const char* kn, const int (&ka)[NKA],
+                                            const char* vl, const int (&va)[NVA + 1],
                                             const X8 (&qf)[QB][NCH], float c) {
         constexpr int MF_HALF = (NCH / 2) * NKB * QB;     // score MFMAs per half
         constexpr int MF_PV = NPV * NDB * QB;             // PV MFMAs
@@ -402,13 +409,13 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     // Direct-load mapping: load j of this wave fills bytes
     // [(wave*NIW + j) * 1024, +1024) of a tile; lane i writes 16 bytes at
     // +16*i, i.e. physical chunk cp of row r, which holds logical chunk
-    // cp ^ lds_swz(r) of that key row.
+    // cp ^ lds_swz16(r) of that key row.
     int grow[NIW], gcol[NIW];
 #pragma unroll
     for (int j = 0; j < NIW; ++j) {
         const int p = (wave * NIW + j) * 1024 + 16 * lane;
         grow[j] = p / RB;
-        gcol[j] = ((p % RB / 16) ^ lds_swz(grow[j])) * 8;
+        gcol[j] = ((p % RB / 16) ^ lds_swz16<D>(grow[j])) * 8;
     }
     const int nkt_total = (N + BC - 1) / BC;
     auto load_k = [&](int t) {
@@ -452,21 +459,25 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     const int nkt = (kend + BC - 1) / BC;
     const int nfull = (CAUSAL ? min(qtile0 + 1, N) : N) / BC;
 
-    // Lane byte offsets into a swizzled tile (see lds_swz):
-    //  K fragment (ch, kb): ka[ch & 3] + 128*(ch >> 2) + 32*kb*RB.
+    // Lane byte offsets into a swizzled tile (see lds_swz16):
+    //  K fragment (ch, kb): ka[ch % NKA] + NKA*32*(ch / NKA) + 32*kb*RB.
     //  V^T fragment (t, u, db): row 16*t + 8*hi + 4*u + (lane%16)/4, bytes
-    //    64*db + 32*((lane%32)/16) + 8*(lane%4): va[db & 1] + 128*(db >> 1).
-    int ka[4], va[2];
+    //    64*db + 32*((lane%32)/16) + 8*(lane%4): va[db % NVA] + NVA*64*(db / NVA).
+    int ka[W::NKA], va[W::NVA + 1];
     {
         const int kr = krow_perm(l32);
 #pragma unroll
-        for (int ch = 0; ch < 4; ++ch) ka[ch] = kr * RB + (((2 * ch + hi) ^ lds_swz(kr)) * 16);
+        for (int ch = 0; ch < W::NKA; ++ch)
+            ka[ch] = kr * RB + (((2 * ch + hi) ^ lds_swz16<D>(kr)) * 16);
         const int vr = 8 * hi + (lane & 15) / 4;
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
+        for (int db = 0; db < W::NVA; ++db) {
             const int chunk = 4 * db + 2 * (l32 / 16) + ((lane & 3) >> 1);
-            va[db] = vr * RB + ((chunk ^ lds_swz(vr)) * 16) + 8 * (lane & 1);
+            va[db] = vr * RB + ((chunk ^ lds_swz16<D>(vr)) * 16) + 8 * (lane & 1);
         }
+        // rows vr + 4: swizzle term + 1 (bit 2 of vr is 0), i.e. chunk bit 0
+        // flips; the chunk's bit 0 is (lane & 3) >> 1 for every d-block.
+        va[W::NVA] = 4 * RB + (((lane & 3) >> 1) ? -16 : 16);
     }
 
     W st;
@@ -664,7 +675,7 @@ fa_fwd16_pp_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* 
     for (int j = 0; j < NIL; ++j) {
         const int p = ((wave & 3) * NIL + j) * 1024 + 16 * lane;
         grow[j] = p / RB;
-        gcol[j] = ((p % RB / 16) ^ lds_swz(grow[j])) * 8;
+        gcol[j] = ((p % RB / 16) ^ lds_swz16<D>(grow[j])) * 8;
     }
     const int nkt_total = (N + BC - 1) / BC;
     auto load_k = [&](int t) {
@@ -699,17 +710,21 @@ fa_fwd16_pp_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* 
                 qf[0][ch] = __builtin_bit_cast(X8, u32x4{0, 0, 0, 0});
         }
     }
-    int ka[4], va[2];
+    int ka[W::NKA], va[W::NVA + 1];
     {
         const int kr = krow_perm(l32);
 #pragma unroll
-        for (int ch = 0; ch < 4; ++ch) ka[ch] = kr * RB + (((2 * ch + hi) ^ lds_swz(kr)) * 16);
+        for (int ch = 0; ch < W::NKA; ++ch)
+            ka[ch] = kr * RB + (((2 * ch + hi) ^ lds_swz16<D>(kr)) * 16);
         const int vr = 8 * hi + (lane & 15) / 4;
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
+        for (int db = 0; db < W::NVA; ++db) {
             const int chunk = 4 * db + 2 * (l32 / 16) + ((lane & 3) >> 1);
-            va[db] = vr * RB + ((chunk ^ lds_swz(vr)) * 16) + 8 * (lane & 1);
+            va[db] = vr * RB + ((chunk ^ lds_swz16<D>(vr)) * 16) + 8 * (lane & 1);
         }
+        // rows vr + 4: swizzle term + 1 (bit 2 of vr is 0), i.e. chunk bit 0
+        // flips; the chunk's bit 0 is (lane & 3) >> 1 for every d-block.
+        va[W::NVA] = 4 * RB + (((lane & 3) >> 1) ? -16 : 16);
     }
 
     const int kend = CAUSAL ? min(N, qtile0 + BR) : N;
@@ -749,9 +764,9 @@ fa_fwd16_pp_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* 
             for (int tt = 2 * kb; tt < 2 * kb + 2; ++tt)
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    const char* vp = vl + va[db & 1] + 128 * (db >> 1) + 16 * tt * RB;
+                    const char* vp = vl + va[db % W::NVA] + W::NVA * 64 * (db / W::NVA) + 16 * tt * RB;
                     const u32x2 lo = lds_read_tr16(vp);
-                    const u32x2 hi4 = lds_read_tr16(vp + 4 * RB);
+                    const u32x2 hi4 = lds_read_tr16(vp + va[W::NVA]);
                     vf[tt][db] = __builtin_bit_cast(X8, u32x4{lo[0], lo[1], hi4[0], hi4[1]});
                 }
             __builtin_amdgcn_sched_barrier(0);

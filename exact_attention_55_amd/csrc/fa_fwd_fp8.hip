@@ -49,16 +49,6 @@ template <> struct Cfg8<64> : Cfg8T<FA8_CFG_64> {};
 template <> struct Cfg8<128> : Cfg8T<FA8_CFG_128> {};
 template <> struct Cfg8<256> : Cfg8T<FA8_CFG_256> {};
 
-// LDS chunk swizzle for fp8 tiles (rows of D bytes, 16-byte chunks). With 32
-// four-byte banks, the score MFMA reads one chunk from rows
-// {0,1,2,3,8,9,10,11} per 8 lanes and a transposing V read covers 8
-// consecutive rows of one chunk per 16 lanes; both must hit distinct bank
-// groups. D = 64 packs two rows per 128-byte bank window.
-template <int D> __device__ __forceinline__ int swz8(int r) {
-    if (D == 64) return ((r >> 1) & 3) ^ (((r >> 3) & 1) << 1);
-    return (r & 7) ^ ((r >> 1) & 4);
-}
-
 __device__ __forceinline__ uint32_t cvt4_e4m3(float a, float b, float c, float d) {
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
@@ -72,7 +62,8 @@ struct Wave8 {
     static constexpr int NDB = D / 32;     // 32-row blocks of O^T
     static constexpr int NKB = BC / 32;    // 32-key blocks of S^T
     static constexpr int NPV = BC / 64;    // k-steps of O^T += V^T P'^T
-    static constexpr int NVA = NDB < 4 ? NDB : 4;   // distinct V lane offsets
+    static constexpr int NVA = NDB;        // V lane offsets, one per d-block
+    static constexpr int NKA = NCH;        // K lane offsets, per k-step (x2 chunks)
     static_assert(NKB == 2 * NPV, "one PV MFMA per two score blocks");
 
     f32x16 o[NDB];
@@ -86,12 +77,12 @@ struct Wave8 {
     }
 
     // K fragment (ch, kb): row perm(l32) + 32*kb, bytes [64*ch + 32*hi, +32)
-    // = logical chunks 4*ch + 2*hi + e (e = 0, 1). ka[ch & 1][e] holds the
-    // swizzled lane offset; chunk bit 3 (ch >> 1) is an unswizzled 128 bytes.
-    static __device__ __forceinline__ i32x8 kfrag(const char* kl, const int (&ka)[2][2], int ch, int kb) {
-        const char* p = kl + 32 * kb * RB + 128 * (ch >> 1);
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(p + ka[ch & 1][0]);
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(p + ka[ch & 1][1]);
+    // = logical chunks 4*ch + 2*hi + e (e = 0, 1); ka[ch][e] holds the
+    // swizzled lane offset (see lds_swz8).
+    static __device__ __forceinline__ i32x8 kfrag(const char* kl, const int (&ka)[NKA][2], int ch, int kb) {
+        const char* p = kl + 32 * kb * RB;
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(p + ka[ch][0]);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(p + ka[ch][1]);
         return i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
                      (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
     }
@@ -105,7 +96,7 @@ struct Wave8 {
     }
 
     static __device__ __forceinline__ void scores(f32x16 (&s)[NKB], const char* kl,
-                                                  const int (&ka)[2][2], const i32x8 (&qf)[NCH]) {
+                                                  const int (&ka)[NKA][2], const i32x8 (&qf)[NCH]) {
         i32x8 kf[NKB][NCH];
 #pragma unroll
         for (int ch = 0; ch < NCH; ++ch)
@@ -185,7 +176,7 @@ struct Wave8 {
         for (int t = 0; t < NPV; ++t)
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const char* vp = vl + va[db % NVA] + 128 * (db / NVA) + 64 * t * RB;
+                const char* vp = vl + va[db] + 64 * t * RB;
                 const u32x2 r0 = lds_read_tr8(vp);
                 const u32x2 r1 = lds_read_tr8(vp + 16 * RB);
                 const u32x2 r2 = lds_read_tr8(vp + 32 * RB);
@@ -222,7 +213,7 @@ struct Wave8 {
     // then the PV MFMAs of this tile interleaved with the row maximum of the
     // next tile (returned, in log2 units with its own scale cjn).
     __device__ __forceinline__ float overlap(const f32x16 (&s)[NKB], f32x16 (&sn)[NKB], const char* kn,
-                                             const int (&ka)[2][2], const char* vl,
+                                             const int (&ka)[NKA][2], const char* vl,
                                              const int (&va)[NVA], const i32x8 (&qf)[NCH],
                                              float cj, float bj, float lscale, float cjn) {
         constexpr int MF_QK = NCH * NKB;
@@ -311,13 +302,13 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     for (int mm = 32; mm >= 1; mm /= 2) svmax = fmaxf(svmax, __shfl_xor(svmax, mm, 64));
     const float cq = Qs[min(q0, N - 1) / kQuantBlockRows] * c;
 
-    // Direct-load mapping (see fa_fwd16_kernel), chunk swizzle swz8.
+    // Direct-load mapping (see fa_fwd16_kernel), chunk swizzle lds_swz8.
     int grow[NIW], gcol[NIW];
 #pragma unroll
     for (int j = 0; j < NIW; ++j) {
         const int p = (wave * NIW + j) * 1024 + 16 * lane;
         grow[j] = p / RB;
-        gcol[j] = ((p % RB / 16) ^ swz8<D>(grow[j])) * 16;
+        gcol[j] = ((p % RB / 16) ^ lds_swz8<D>(grow[j])) * 16;
     }
     const int nkt_total = (N + BC - 1) / BC;
     auto load_kv = [&](const uint8_t* src, int t, int slot) {
@@ -358,19 +349,19 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     }
 
     // Lane offsets into swizzled tiles.
-    int ka[2][2], va[NVA];
+    int ka[W::NKA][2], va[NVA];
     {
         const int kr = krow_perm(l32);
 #pragma unroll
-        for (int chl = 0; chl < 2; ++chl)
+        for (int ch = 0; ch < W::NKA; ++ch)
 #pragma unroll
             for (int e = 0; e < 2; ++e)
-                ka[chl][e] = kr * RB + (((4 * chl + 2 * hi + e) ^ swz8<D>(kr)) & (RB / 16 - 1)) * 16;
+                ka[ch][e] = kr * RB + ((4 * ch + 2 * hi + e) ^ lds_swz8<D>(kr)) * 16;
         const int vr = 8 * hi + (lane & 15) / 2;
 #pragma unroll
         for (int db = 0; db < NVA; ++db) {
             const int chunk = 2 * db + (l32 / 16);
-            va[db] = vr * RB + ((chunk ^ swz8<D>(vr)) * 16) + 8 * (lane & 1);
+            va[db] = vr * RB + ((chunk ^ lds_swz8<D>(vr)) * 16) + 8 * (lane & 1);
         }
     }
 
