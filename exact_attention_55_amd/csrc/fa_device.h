@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -65,6 +67,51 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
 // j/2, columns 8*(j%2) .. +7); lane i receives column i, rows 0..7.
 __device__ __forceinline__ u32x2 lds_read_tr8(const void* p) {
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((FA_LDS i32x2v*)(p)));
+}
+
+// The same two reads issued through inline asm, with no wait attached. The
+// compiler cannot tell the LDS tiles apart, so after any direct-to-LDS copy
+// it makes a transposing-read builtin wait for every outstanding copy, a
+// full memory latency in the middle of the key loop. The tiles read here are
+// ordered against the copies by explicit waits and barriers instead. The
+// result is valid only after lgkm_wait() covers the read and lgkm_bind()
+// ties the registers to that wait. OFF is a byte offset < 65536.
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_tr16_async(uint32_t addr) {
+    u32x2 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+    return r;
+}
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_tr8_async(uint32_t addr) {
+    u32x2 r;
+    asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+    return r;
+}
+// Wait until at most N LDS (and scalar-memory) requests of the wave are in
+// flight. LDS requests complete in issue order, so this covers every read
+// issued before the last N.
+template <int N>
+__device__ __forceinline__ void lgkm_wait() {
+    static_assert(N >= 0 && N <= 15, "lgkmcnt is a 4-bit field");
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N));
+}
+// Orders every use of x after the preceding lgkm_wait (both are volatile asm,
+// which the compiler keeps in order).
+__device__ __forceinline__ void lgkm_bind(u32x2& x) { asm volatile("" : "+v"(x)); }
+
+// 32-bit LDS address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const FA_LDS char*)(p);
+}
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i in [I, N).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
 }
 
 // Hardware base-2 exponential (v_exp_f32).
@@ -132,6 +179,21 @@ template <int D> __device__ __forceinline__ int lds_swz8(int r) {
 // land at lds + 16*i (lds must be wave-uniform).
 __device__ __forceinline__ void load_lds16(const void* g, void* lds) {
     __builtin_amdgcn_global_load_lds(g, (FA_LDS void*)(lds), 16, 0, 0);
+}
+
+// Buffer resource over [base, base + bytes): raw (stride 0) byte-addressed
+// loads, range-checked against bytes. On gfx950 the check covers the whole
+// offset (VGPR offset + SGPR offset): a 16-byte read at or past the end
+// returns zeros, also into LDS. bytes must be < 2^31.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+// 16 bytes per lane from a buffer straight into LDS: lane i's bytes come
+// from offset voff + soff (soff wave-uniform) and land at lds + 16*i (lds
+// wave-uniform). No VGPR is written; completion is counted by vmcnt.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff,
+                                                  uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)(lds), 16, (int)voff, (int)soff, 0, 0);
 }
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }

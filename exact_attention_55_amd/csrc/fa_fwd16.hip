@@ -45,7 +45,10 @@
 
 namespace fa {
 
-constexpr float kTau = 8.0f;      // lazy-rescale threshold (log2 units)
+// A tile whose exponentials sum past kBig in some lane is redone with its
+// exact row maximum (see Wave16::settle); every p is then <= kBig, which
+// fp16 P (max 65504) and the fp32 accumulators hold with room to spare.
+constexpr float kBig = 16384.0f;
 
 template <typename T> __device__ __forceinline__ typename Elt<T>::x2 pack2(float a, float b);
 template <> __device__ __forceinline__ bf16x2 pack2<__bf16>(float a, float b) {
@@ -190,28 +193,22 @@ struct Wave16 {
         }
     }
 
-    // Lazy rescale: the reference maximum moves only when the tile maximum
-    // exceeds it by more than kTau (then p <= 2^kTau always holds).
-    __device__ __forceinline__ void rescale(const float (&mt)[QB]) {
-        bool need = false;
+    // Moves the reference maximum to max(m, mt), rescaling O, l and lx.
+    __device__ __forceinline__ void raise_max(const float (&mt)[QB]) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) need |= mt[qb] > m[qb] + kTau;
-        if (wave_any(need)) {
+        for (int qb = 0; qb < QB; ++qb) {
+            const float mnew = fmaxf(m[qb], mt[qb]);
+            const float alpha = (mnew == -INFINITY) ? 1.f : exp2_hw(m[qb] - mnew);
+            m[qb] = mnew;
+            l[qb] *= alpha;
+            lx[qb] *= alpha;
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const float mnew = fmaxf(m[qb], mt[qb]);
-                const float alpha = (mnew == -INFINITY) ? 1.f : exp2_hw(m[qb] - mnew);
-                m[qb] = mnew;
-                l[qb] *= alpha;
-                lx[qb] *= alpha;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) o[qb][db] *= alpha;
-            }
+            for (int db = 0; db < NDB; ++db) o[qb][db] *= alpha;
         }
     }
 
     // P for score block kb (16 keys per lane -> two PV operands), with the
-    // row sums in independent partial accumulators.
+    // tile's row sums in independent partial accumulators.
     __device__ __forceinline__ void probs(const f32x16 (&s)[QB][NKB], X8 (&pf)[QB][NPV], int kb,
                                           float c, float (&ls)[QB][2], float (&lxs)[QB][2]) {
 #pragma unroll
@@ -236,79 +233,101 @@ struct Wave16 {
         }
     }
 
-    // V^T fragments (t, db): key rows 16*t + 8*hi + 4*u + (lane%16)/4.
-    // The second read covers rows +4, whose swizzle flips chunk bit 0:
-    // va[NVA] holds that step (4*RB +- 16 bytes) for this lane.
-    static __device__ __forceinline__ void vfrags(X8 (&vf)[NPV][NDB], const char* vl,
-                                                  const int (&va)[NVA + 1]) {
+    static __device__ __forceinline__ void zero_sums(float (&ls)[QB][2], float (&lxs)[QB][2]) {
 #pragma unroll
-        for (int t = 0; t < NPV; ++t)
+        for (int qb = 0; qb < QB; ++qb) ls[qb][0] = ls[qb][1] = lxs[qb][0] = lxs[qb][1] = 0.f;
+    }
+
+    // The reference maximum is not moved per tile. Exponentials are taken
+    // against it directly; a tile is redone with its exact maximum only when
+    // its sum in some lane exceeds kBig (every p is then <= kBig: no
+    // overflow in fp16 P or in the fp32 accumulators). The exact softmax is
+    // unchanged: O, l and lx share the reference (FlashAttention v1/v2
+    // rescaling, done only when needed).
+    __device__ __forceinline__ void settle(const f32x16 (&s)[QB][NKB], X8 (&pf)[QB][NPV], float c,
+                                           float (&ls)[QB][2], float (&lxs)[QB][2]) {
+        bool big = false;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) big |= lxs[qb][0] + lxs[qb][1] > kBig;
+        if (wave_any(big)) {
+            float mt[QB];
+            tile_max(s, c, mt);
+            raise_max(mt);
+            zero_sums(ls, lxs);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) probs(s, pf, kb, c, ls, lxs);
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            l[qb] += ls[qb][0] + ls[qb][1];
+            lx[qb] += lxs[qb][0] + lxs[qb][1];
+        }
+    }
+
+    // V^T fragments (t, db): key rows 16*t + 8*hi + 4*u + (lane%16)/4, read
+    // without waits in (t, db) order, rows +0..3 (base b0) then +4..7 (base
+    // b1, whose swizzle differs); pv_async waits for each k-step's share.
+    static __device__ __forceinline__ void vfrags_async(u32x2 (&vlo)[NPV][NDB], u32x2 (&vhi)[NPV][NDB],
+                                                        const uint32_t (&b0)[NVA],
+                                                        const uint32_t (&b1)[NVA]) {
+        static_for<0, NPV>([&](auto tc) {
+            constexpr int t = decltype(tc)::value;
+            static_for<0, NDB>([&](auto dc) {
+                constexpr int db = decltype(dc)::value;
+                constexpr int off = NVA * 64 * (db / NVA) + 16 * t * RB;
+                vlo[t][db] = lds_tr16_async<off>(b0[db % NVA]);
+                vhi[t][db] = lds_tr16_async<off>(b1[db % NVA]);
+            });
+        });
+    }
+
+    __device__ __forceinline__ void pv_async(u32x2 (&vlo)[NPV][NDB], u32x2 (&vhi)[NPV][NDB],
+                                             const X8 (&pf)[QB][NPV]) {
+        static_for<0, NPV>([&](auto tc) {
+            constexpr int t = decltype(tc)::value;
+            constexpr int later = 2 * NDB * (NPV - 1 - t);     // reads issued after step t's
+            lgkm_wait<(later > 15 ? 15 : later)>();
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const char* vp = vl + va[db % NVA] + NVA * 64 * (db / NVA) + 16 * t * RB;
-                const u32x2 lo = lds_read_tr16(vp);
-                const u32x2 hi4 = lds_read_tr16(vp + va[NVA]);
-                vf[t][db] = __builtin_bit_cast(X8, u32x4{lo[0], lo[1], hi4[0], hi4[1]});
+                lgkm_bind(vlo[t][db]);
+                lgkm_bind(vhi[t][db]);
             }
-    }
-
-    __device__ __forceinline__ void pv(const X8 (&vf)[NPV][NDB], const X8 (&pf)[QB][NPV]) {
 #pragma unroll
-        for (int t = 0; t < NPV; ++t)
+            for (int db = 0; db < NDB; ++db) {
+                const X8 v = __builtin_bit_cast(
+                    X8, u32x4{vlo[t][db][0], vlo[t][db][1], vhi[t][db][0], vhi[t][db][1]});
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(vf[t][db], pf[qb][t], o[qb][db]);
-    }
-
-    __device__ __forceinline__ void begin_sums(float (&ls)[QB][2], float (&lxs)[QB][2]) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            ls[qb][0] = l[qb];
-            ls[qb][1] = 0.f;
-            lxs[qb][0] = lx[qb];
-            lxs[qb][1] = 0.f;
-        }
-    }
-    __device__ __forceinline__ void end_sums(const float (&ls)[QB][2], const float (&lxs)[QB][2]) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            l[qb] = ls[qb][0] + ls[qb][1];
-            lx[qb] = lxs[qb][0] + lxs[qb][1];
-        }
+                for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(v, pf[qb][t], o[qb][db]);
+            }
+        });
     }
 
     // Softmax + PV of a tile whose scores are in s (no overlap).
-    __device__ __forceinline__ void finish(const f32x16 (&s)[QB][NKB], const char* vl,
-                                           const int (&va)[NVA + 1], float c) {
-        float mt[QB];
-        tile_max(s, c, mt);
-        rescale(mt);
-        X8 vf[NPV][NDB];
-        vfrags(vf, vl, va);
-        __builtin_amdgcn_sched_barrier(0);
+    __device__ __forceinline__ void finish(const f32x16 (&s)[QB][NKB], const uint32_t (&b0)[NVA],
+                                           const uint32_t (&b1)[NVA], float c) {
         X8 pf[QB][NPV];
         float ls[QB][2], lxs[QB][2];
-        begin_sums(ls, lxs);
+        zero_sums(ls, lxs);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) probs(s, pf, kb, c, ls, lxs);
-        end_sums(ls, lxs);
-        pv(vf, pf);
+        settle(s, pf, c, ls, lxs);
+        u32x2 vlo[NPV][NDB], vhi[NPV][NDB];
+        vfrags_async(vlo, vhi, b0, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        pv_async(vlo, vhi, pf);
     }
 
-    // Pipelined step, all in one wave's instruction stream:
-    //   score MFMAs of the next tile (K fragments at kn) interleaved with the
-    //   exponentials of this tile (scores s, maximum already applied), then
-    //   the PV MFMAs of this tile interleaved with the row maximum of the next
-    //   tile (returned in mtn). The next tile's K fragments come in two
-    //   halves so the first half's registers are free before the second
-    //   lands. sched_group_barrier fixes the MFMA / VALU alternation.
+    // Pipelined step, all in one wave's instruction stream: the score MFMAs
+    // of the next tile (K fragments at kn) interleaved with the exponentials
+    // of this tile (scores s), then the PV MFMAs of this tile. The next
+    // tile's K fragments come in two halves so the first half's registers
+    // are free before the second lands. sched_group_barrier fixes the
+    // MFMA / VALU alternation.
     __device__ __forceinline__ void overlap(const f32x16 (&s)[QB][NKB], f32x16 (&sn)[QB][NKB],
-                                            float (&mtn)[QB], const char* kn, const int (&ka)[NKA],
-                                            const char* vl, const int (&va)[NVA + 1],
+                                            const char* kn, const int (&ka)[NKA],
+                                            const uint32_t (&b0)[NVA], const uint32_t (&b1)[NVA],
                                             const X8 (&qf)[QB][NCH], float c) {
         constexpr int MF_HALF = (NCH / 2) * NKB * QB;     // score MFMAs per half
-        constexpr int MF_PV = NPV * NDB * QB;             // PV MFMAs
         X8 kf[NKB][NCH];
 #pragma unroll
         for (int ch = 0; ch < NCH / 2; ++ch)
@@ -321,14 +340,14 @@ struct Wave16 {
             for (int kb = 0; kb < NKB; ++kb) sn[qb][kb] = f32x16{};
         X8 pf[QB][NPV];
         float ls[QB][2], lxs[QB][2];
-        begin_sums(ls, lxs);
+        zero_sums(ls, lxs);
         qk(sn, kf, qf, 0, NCH / 2);
 #pragma unroll
         for (int kb = 0; kb < NKB / 2; ++kb) probs(s, pf, kb, c, ls, lxs);
 #pragma unroll
         for (int i = 0; i < MF_HALF; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // eight VALU
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -339,23 +358,17 @@ struct Wave16 {
         qk(sn, kf, qf, NCH / 2, NCH);
 #pragma unroll
         for (int kb = NKB / 2; kb < NKB; ++kb) probs(s, pf, kb, c, ls, lxs);
-        end_sums(ls, lxs);
 #pragma unroll
         for (int i = 0; i < MF_HALF; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        X8 vf[NPV][NDB];
-        vfrags(vf, vl, va);
+        settle(s, pf, c, ls, lxs);
+        u32x2 vlo[NPV][NDB], vhi[NPV][NDB];
+        vfrags_async(vlo, vhi, b0, b1);
         __builtin_amdgcn_sched_barrier(0);
-        pv(vf, pf);
-        tile_max(sn, c, mtn);
-#pragma unroll
-        for (int i = 0; i < MF_PV; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-        }
+        pv_async(vlo, vhi, pf);
         __builtin_amdgcn_sched_barrier(0);
     }
 };
@@ -372,7 +385,7 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     using W = Wave16<T, D, QB, BC>;
     constexpr int QW = 32 * QB;            // query rows per wave
     constexpr int BR = NW * QW;            // query rows per workgroup
-    constexpr int NCH = W::NCH, NDB = W::NDB, NKB = W::NKB, RB = W::RB;
+    constexpr int NCH = W::NCH, NDB = W::NDB, NKB = W::NKB, RB = W::RB, NVA = W::NVA;
     constexpr int TB = BC * RB;            // bytes per K (or V) tile
     constexpr int NIW = TB / 1024 / NW;    // 1 KB direct loads per wave per tile
     static_assert(TB % (1024 * NW) == 0, "tile must split into 1 KB loads per wave");
@@ -401,43 +414,33 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
 
     const size_t head = (size_t)bh * N * D;
     const T* Q = Qg + head;
-    const T* K = Kg + head;
-    const T* V = Vg + head;
     const int qtile0 = qt * BR;
     const int q0 = qtile0 + wave * QW;
 
-    // Direct-load mapping: load j of this wave fills bytes
+    // K / V tiles: buffer loads over this head's rows (rows at or past N
+    // read as zeros) straight into LDS. Load j of this wave fills bytes
     // [(wave*NIW + j) * 1024, +1024) of a tile; lane i writes 16 bytes at
     // +16*i, i.e. physical chunk cp of row r, which holds logical chunk
-    // cp ^ lds_swz16(r) of that key row.
-    int grow[NIW], gcol[NIW];
+    // cp ^ lds_swz16(r) of that key row. The tile's row offset is the
+    // wave-uniform SGPR offset, so a load costs no vector instructions.
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kg + head, N * RB);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vg + head, N * RB);
+    uint32_t voff[NIW];
 #pragma unroll
     for (int j = 0; j < NIW; ++j) {
         const int p = (wave * NIW + j) * 1024 + 16 * lane;
-        grow[j] = p / RB;
-        gcol[j] = ((p % RB / 16) ^ lds_swz16<D>(grow[j])) * 8;
+        const int row = p / RB;
+        voff[j] = row * RB + ((p % RB / 16) ^ lds_swz16<D>(row)) * 16;
     }
     const int nkt_total = (N + BC - 1) / BC;
-    auto load_k = [&](int t) {
-        if (t >= nkt_total) return;
-        char* dst = smem + (t & 1) * TB + wave_u * NIW * 1024;
+    auto issue = [&](__amdgpu_buffer_rsrc_t rs, int t, int slot) {
+        char* dst = smem + slot * TB + wave_u * NIW * 1024;
 #pragma unroll
-        for (int j = 0; j < NIW; ++j) {
-            const int key = min(t * BC + grow[j], N - 1);     // rows past N: any valid row
-            load_lds16(K + (size_t)key * D + gcol[j], dst + j * 1024);
-        }
+        for (int j = 0; j < NIW; ++j) buffer_load_lds16(rs, dst + j * 1024, voff[j], t * TB);
     };
-    auto load_v = [&](int t) {
-        if (t >= nkt_total) return;
-        char* dst = smem + (2 + (t & 1)) * TB + wave_u * NIW * 1024;
-#pragma unroll
-        for (int j = 0; j < NIW; ++j) {
-            const int key = min(t * BC + grow[j], N - 1);
-            load_lds16(V + (size_t)key * D + gcol[j], dst + j * 1024);
-        }
-    };
+    auto load_k = [&](int t) { if (t < nkt_total) issue(krs, t, t & 1); };
+    auto load_v = [&](int t) { if (t < nkt_total) issue(vrs, t, 2 + (t & 1)); };
     auto ktile = [&](int t) -> const char* { return smem + (t & 1) * TB; };
-    auto vtile = [&](int t) -> const char* { return smem + (2 + (t & 1)) * TB; };
 
     // Q^T fragments (B operand): lane holds query q0+32*qb+l32, d = 16*ch + 8*hi .. +7
     X8 qf[QB][NCH];
@@ -462,8 +465,11 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     // Lane byte offsets into a swizzled tile (see lds_swz16):
     //  K fragment (ch, kb): ka[ch % NKA] + NKA*32*(ch / NKA) + 32*kb*RB.
     //  V^T fragment (t, u, db): row 16*t + 8*hi + 4*u + (lane%16)/4, bytes
-    //    64*db + 32*((lane%32)/16) + 8*(lane%4): va[db % NVA] + NVA*64*(db / NVA).
-    int ka[W::NKA], va[W::NVA + 1];
+    //    64*db + 32*((lane%32)/16) + 8*(lane%4): va[db % NVA] + NVA*64*(db / NVA)
+    //    for u = 0; u = 1 (rows + 4) flips the chunk's bit 0 in the swizzle,
+    //    so its offset is va + 4*RB +- 16 (vstep).
+    int ka[W::NKA];
+    uint32_t va[NVA], vstep;
     {
         const int kr = krow_perm(l32);
 #pragma unroll
@@ -471,14 +477,21 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
             ka[ch] = kr * RB + (((2 * ch + hi) ^ lds_swz16<D>(kr)) * 16);
         const int vr = 8 * hi + (lane & 15) / 4;
 #pragma unroll
-        for (int db = 0; db < W::NVA; ++db) {
+        for (int db = 0; db < NVA; ++db) {
             const int chunk = 4 * db + 2 * (l32 / 16) + ((lane & 3) >> 1);
             va[db] = vr * RB + ((chunk ^ lds_swz16<D>(vr)) * 16) + 8 * (lane & 1);
         }
-        // rows vr + 4: swizzle term + 1 (bit 2 of vr is 0), i.e. chunk bit 0
-        // flips; the chunk's bit 0 is (lane & 3) >> 1 for every d-block.
-        va[W::NVA] = 4 * RB + (((lane & 3) >> 1) ? -16 : 16);
+        vstep = 4 * RB + (((lane & 3) >> 1) ? -16 : 16);
     }
+    const uint32_t sbase = lds_addr(smem);
+    // V read bases of a tile at LDS address base.
+    auto vbases = [&](uint32_t base, uint32_t (&b0)[NVA], uint32_t (&b1)[NVA]) {
+#pragma unroll
+        for (int i = 0; i < NVA; ++i) {
+            b0[i] = base + va[i];
+            b1[i] = b0[i] + vstep;
+        }
+    };
 
     W st;
     st.init();
@@ -492,10 +505,11 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     load_k(1);
     wait_vm_all();
     __syncthreads();
-    float mt[QB];
     if (nfull > 0) {
         W::scores(s, ktile(0), ka, qf);
-        W::tile_max(s, c, mt);
+        float mt[QB];
+        W::tile_max(s, c, mt);                // first reference maximum: exact
+        st.raise_max(mt);
         __syncthreads();                     // all waves done reading K_0's slot
     }
     int t = 0;
@@ -504,9 +518,10 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     for (; t + 1 < nfull; ++t) {
         load_k(t + 2);
         load_v(t + 1);
-        st.rescale(mt);
+        uint32_t b0[NVA], b1[NVA];
+        vbases(sbase + (2 + (t & 1)) * TB, b0, b1);
         f32x16 sn[QB][NKB];
-        st.overlap(s, sn, mt, ktile(t + 1), ka, vtile(t), va, qf, c);
+        st.overlap(s, sn, ktile(t + 1), ka, b0, b1, qf, c);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -516,7 +531,9 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     }
     if (nfull > 0) {                          // last full tile: no next scores
         load_v(t + 1);
-        st.finish(s, vtile(t), va, c);
+        uint32_t b0[NVA], b1[NVA];
+        vbases(sbase + (2 + (t & 1)) * TB, b0, b1);
+        st.finish(s, b0, b1, c);
         wait_vm_all();
         __syncthreads();
         ++t;
@@ -529,7 +546,14 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
         if (!CAUSAL || k0 <= q0 + QW - 1) {   // wave has a visible key in this tile
             W::scores(s, ktile(t), ka, qf);
             W::template mask<CAUSAL>(s, k0, q0, N, hi, l32);
-            st.finish(s, vtile(t), va, c);
+            if (t == 0) {                      // first reference maximum: exact
+                float mt[QB];
+                W::tile_max(s, c, mt);
+                st.raise_max(mt);
+            }
+            uint32_t b0[NVA], b1[NVA];
+            vbases(sbase + (2 + (t & 1)) * TB, b0, b1);
+            st.finish(s, b0, b1, c);
         }
         wait_vm_all();
         __syncthreads();
@@ -565,295 +589,8 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     }
 }
 
-// ---------------------------------------------------------------------------
-// Ping-pong kernel (head dims 64 and 128): eight waves in two groups of four
-// (one wave of each group per SIMD). Per key tile a group runs four phases,
-//   QK  : score MFMAs (K fragments already in registers)
-//   VS  : V^T fragments LDS -> registers, then the softmax (VALU)
-//   PV  : PV MFMAs
-//   LK  : next tile's K fragments LDS -> registers
-// and the second group runs the same sequence one phase later, so in every
-// phase one wave of each SIMD issues MFMAs while the other reads LDS and runs
-// the exponentials. Workgroup barriers separate the phases ("FlashAttention-3:
-// Fast & Accurate Attention with Asynchrony & Low-Precision", section
-// "Overlapping GEMM and Softmax (Asynchrony)": inter-warpgroup ping-pong).
-// The MFMA phases run at raised wave priority (s_setprio).
-//
-// Both groups run the same loop body; the second group enters it one phase
-// later (its first phase only reads K_0's fragments) and the first group
-// ends with one empty phase, so both pass the same number of barriers.
-//
-// Global -> LDS: K tile t and V tile t in slots t & 1. The first group issues
-// all copies: V_{t+1} and K_{t+2} in global phase 4t+1, waited for (vmcnt)
-// at the end of phase 4t+4, before the barrier that starts the first phase
-// reading them. Slot reuse: V_{t+1} overwrites V_{t-1} (last read in phase
-// 4t-2), K_{t+2} overwrites K_t (last read in phase 4t).
-// ---------------------------------------------------------------------------
-#ifndef FA16_PP_BC
-#define FA16_PP_BC 64
-#endif
-#ifndef FA16_PP_PRIO
-#define FA16_PP_PRIO 1
-#endif
-
-template <typename T, int D, bool CAUSAL, bool OUT_F32>
-__device__ __forceinline__ void store_rows(const Wave16<T, D, 1, FA16_PP_BC>& st, void* Og,
-                                           float* LSEg, size_t head, int bh, int N, int q0,
-                                           int l32, int hi)
-{
-    using X2 = typename Elt<T>::x2;
-    constexpr int NDB = D / 32;
-    const float l = pair_sum(st.l[0]);
-    const float lx = pair_sum(st.lx[0]);
-    const float inv = 1.0f / l;
-    const int row = q0 + l32;
-    if (row >= N) return;
-    if (hi == 0) LSEg[(size_t)bh * N + row] = (st.m[0] + __builtin_amdgcn_logf(lx)) * kLn2;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int dcol = 32 * db + 8 * j + 4 * hi;
-            const size_t off = head + (size_t)row * D + dcol;
-            const float v0 = st.o[0][db][4 * j] * inv, v1 = st.o[0][db][4 * j + 1] * inv;
-            const float v2 = st.o[0][db][4 * j + 2] * inv, v3 = st.o[0][db][4 * j + 3] * inv;
-            if (OUT_F32) {
-                *reinterpret_cast<f32x4*>(static_cast<float*>(Og) + off) = f32x4{v0, v1, v2, v3};
-            } else {
-                const X2 a = pack2<T>(v0, v1), b = pack2<T>(v2, v3);
-                *reinterpret_cast<u32x2*>(static_cast<T*>(Og) + off) =
-                    u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
-            }
-        }
-    }
-}
-
-__device__ __forceinline__ void prio_hi() { if (FA16_PP_PRIO) __builtin_amdgcn_s_setprio(1); }
-__device__ __forceinline__ void prio_lo() { if (FA16_PP_PRIO) __builtin_amdgcn_s_setprio(0); }
-
-template <typename T, int D, bool CAUSAL, bool OUT_F32>
-__global__ void __launch_bounds__(512, 2)
-fa_fwd16_pp_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
-                   void* __restrict__ Og, float* __restrict__ LSEg, int N, int num_qtiles,
-                   int num_blocks, float c)
-{
-    using X8 = typename Elt<T>::x8;
-    constexpr int NW = 8, QB = 1, BC = FA16_PP_BC;
-    using W = Wave16<T, D, QB, BC>;
-    constexpr int QW = 32, BR = NW * QW;
-    constexpr int NCH = W::NCH, NDB = W::NDB, NKB = W::NKB, NPV = W::NPV, RB = W::RB;
-    constexpr int TB = BC * RB;
-    static_assert(TB % (1024 * 4) == 0, "tile must split into 1 KB loads per wave");
-
-    __shared__ __attribute__((aligned(1024))) char smem[4 * TB];   // K: slots 0,1; V: 2,3
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int l32 = lane & 31, hi = lane >> 5;
-    const int wave_u = wave_uniform(wave);
-    const int group = wave_u >> 2;
-    if (num_blocks < 0) smem[tid] = 0;   // see fa_fwd16_kernel
-
-    int bid = blockIdx.x;
-    if ((num_blocks & 7) == 0) bid = (bid & 7) * (num_blocks >> 3) + (bid >> 3);
-    const int bh = bid / num_qtiles;
-    int qt = bid - bh * num_qtiles;
-    if (CAUSAL) qt = num_qtiles - 1 - qt;
-
-    const size_t head = (size_t)bh * N * D;
-    const T* Q = Qg + head;
-    const T* K = Kg + head;
-    const T* V = Vg + head;
-    const int qtile0 = qt * BR;
-    const int q0 = qtile0 + wave * QW;
-
-    // Direct-load mapping (first group only): load j of wave w fills bytes
-    // [(w*NIL + j) * 1024, +1024) of a tile; lane i writes 16 bytes at +16*i.
-    constexpr int NIL = TB / 1024 / 4;
-    int grow[NIL], gcol[NIL];
-#pragma unroll
-    for (int j = 0; j < NIL; ++j) {
-        const int p = ((wave & 3) * NIL + j) * 1024 + 16 * lane;
-        grow[j] = p / RB;
-        gcol[j] = ((p % RB / 16) ^ lds_swz16<D>(grow[j])) * 8;
-    }
-    const int nkt_total = (N + BC - 1) / BC;
-    auto load_k = [&](int t) {
-        if (t >= nkt_total) return;
-        char* dst = smem + (t & 1) * TB + (wave_u & 3) * NIL * 1024;
-#pragma unroll
-        for (int j = 0; j < NIL; ++j) {
-            const int key = min(t * BC + grow[j], N - 1);
-            load_lds16(K + (size_t)key * D + gcol[j], dst + j * 1024);
-        }
-    };
-    auto load_v = [&](int t) {
-        if (t >= nkt_total) return;
-        char* dst = smem + (2 + (t & 1)) * TB + (wave_u & 3) * NIL * 1024;
-#pragma unroll
-        for (int j = 0; j < NIL; ++j) {
-            const int key = min(t * BC + grow[j], N - 1);
-            load_lds16(V + (size_t)key * D + gcol[j], dst + j * 1024);
-        }
-    };
-    auto ktile = [&](int t) -> const char* { return smem + (t & 1) * TB; };
-    auto vtile = [&](int t) -> const char* { return smem + (2 + (t & 1)) * TB; };
-
-    X8 qf[QB][NCH];
-    {
-        const int row = q0 + l32;
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) {
-            if (row < N)
-                qf[0][ch] = load16<X8>(Q + (size_t)row * D + 16 * ch + 8 * hi);
-            else
-                qf[0][ch] = __builtin_bit_cast(X8, u32x4{0, 0, 0, 0});
-        }
-    }
-    int ka[W::NKA], va[W::NVA + 1];
-    {
-        const int kr = krow_perm(l32);
-#pragma unroll
-        for (int ch = 0; ch < W::NKA; ++ch)
-            ka[ch] = kr * RB + (((2 * ch + hi) ^ lds_swz16<D>(kr)) * 16);
-        const int vr = 8 * hi + (lane & 15) / 4;
-#pragma unroll
-        for (int db = 0; db < W::NVA; ++db) {
-            const int chunk = 4 * db + 2 * (l32 / 16) + ((lane & 3) >> 1);
-            va[db] = vr * RB + ((chunk ^ lds_swz16<D>(vr)) * 16) + 8 * (lane & 1);
-        }
-        // rows vr + 4: swizzle term + 1 (bit 2 of vr is 0), i.e. chunk bit 0
-        // flips; the chunk's bit 0 is (lane & 3) >> 1 for every d-block.
-        va[W::NVA] = 4 * RB + (((lane & 3) >> 1) ? -16 : 16);
-    }
-
-    const int kend = CAUSAL ? min(N, qtile0 + BR) : N;
-    const int nkt = (kend + BC - 1) / BC;
-
-    W st;
-    st.init();
-    X8 kf[NKB][NCH];
-    X8 vf[NPV][NDB];
-    f32x16 s[QB][NKB];
-    X8 pf[QB][NPV];
-
-    auto lk = [&](int t) {
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch)
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) kf[kb][ch] = W::kfrag(ktile(t), ka, ch, kb);
-    };
-    auto qk = [&]() {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) s[0][kb] = f32x16{};
-        W::qk(s, kf, qf, 0, NCH);
-    };
-    // Softmax of tile t with the V^T fragment reads spread over it: each
-    // score block's exponentials run while the next batch of V reads lands.
-    auto vsm = [&](int t, bool masked) {
-        if (masked) W::template mask<CAUSAL>(s, t * BC, q0, N, hi, l32);
-        float mt[QB];
-        W::tile_max(s, c, mt);
-        st.rescale(mt);
-        float ls[QB][2], lxs[QB][2];
-        st.begin_sums(ls, lxs);
-        const char* vl = vtile(t);
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-            for (int tt = 2 * kb; tt < 2 * kb + 2; ++tt)
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const char* vp = vl + va[db % W::NVA] + W::NVA * 64 * (db / W::NVA) + 16 * tt * RB;
-                    const u32x2 lo = lds_read_tr16(vp);
-                    const u32x2 hi4 = lds_read_tr16(vp + va[W::NVA]);
-                    vf[tt][db] = __builtin_bit_cast(X8, u32x4{lo[0], lo[1], hi4[0], hi4[1]});
-                }
-            __builtin_amdgcn_sched_barrier(0);
-            st.probs(s, pf, kb, c, ls, lxs);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        st.end_sums(ls, lxs);
-    };
-    auto pv = [&]() { st.pv(vf, pf); };
-
-    // prologue: K_0, V_0, K_1 in LDS; the first group reads K_0's fragments,
-    // then the second group does (its phase shift).
-    if (group == 0) {
-        load_k(0);
-        load_v(0);
-        load_k(1);
-    }
-    phase_barrier_vm();
-    if (group == 0) lk(0);
-    phase_barrier();
-    if (group == 1) {
-        lk(0);
-        phase_barrier();
-    }
-    // Tiles [0, nact) hold a key visible to this wave; with causal masking
-    // the wave then only keeps the barrier / copy schedule for the rest.
-    // (Unconditional work inside the first loop keeps the compiler from
-    // carrying fragment registers across iterations.)
-    const int nact = CAUSAL ? min(nkt, (q0 + QW - 1) / BC + 1) : nkt;
-    int t = 0;
-    for (; t < nact; ++t) {
-        const int k0 = t * BC;
-        const bool msk = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0);
-        // phase 0: QK (first group: global phase 4t)
-        prio_hi();
-        qk();
-        prio_lo();
-        if (group == 0) phase_barrier_vm();
-        else phase_barrier();
-        // phase 1: V fragments + softmax; first group streams V_{t+1}, K_{t+2}
-        if (group == 0) {
-            load_v(t + 1);
-            load_k(t + 2);
-        }
-        vsm(t, msk);
-        phase_barrier();
-        // phase 2: PV
-        prio_hi();
-        pv();
-        prio_lo();
-        phase_barrier();
-        // phase 3: next K fragments (a stale slot when t + 1 == nkt: unused)
-        lk(t + 1);
-        phase_barrier();
-    }
-    for (; t < nkt; ++t) {
-        if (group == 0) phase_barrier_vm();
-        else phase_barrier();
-        if (group == 0) {
-            load_v(t + 1);
-            load_k(t + 2);
-        }
-        phase_barrier();
-        phase_barrier();
-        phase_barrier();
-    }
-    if (group == 0) phase_barrier();
-    store_rows<T, D, CAUSAL, OUT_F32>(st, Og, LSEg, head, bh, N, q0, l32, hi);
-}
-
-#ifndef FA16_PINGPONG
-#define FA16_PINGPONG 0
-#endif
-
 template <typename T, int D, bool CAUSAL, bool OUT_F32>
 static hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
-    if constexpr (FA16_PINGPONG && D <= 128) {
-        constexpr int BR = 256;
-        const int num_qtiles = (a.N + BR - 1) / BR;
-        const long long nblk = (long long)num_qtiles * a.B * a.H;
-        if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((fa_fwd16_pp_kernel<T, D, CAUSAL, OUT_F32>), dim3((unsigned)nblk),
-                           dim3(512), 0, s, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                           static_cast<const T*>(a.v), a.o, a.lse, a.N, num_qtiles, (int)nblk,
-                           a.scale * kLog2e);
-        return hipGetLastError();
-    }
     constexpr int BR = Cfg16<D>::NW * 32 * Cfg16<D>::QB;
     const int num_qtiles = (a.N + BR - 1) / BR;
     const long long nblk = (long long)num_qtiles * a.B * a.H;

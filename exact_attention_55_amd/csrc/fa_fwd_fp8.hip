@@ -170,42 +170,54 @@ struct Wave8 {
 
     // V^T fragment (t, db): slots 8c..8c+7 = keys 64t + 16c + 8hi + 0..7 of
     // d-row 32*db + l32; one transposing read of 8 rows per c.
-    static __device__ __forceinline__ void vfrags(i32x8 (&vf)[NPV][NDB], const char* vl,
-                                                  const int (&va)[NVA]) {
-#pragma unroll
-        for (int t = 0; t < NPV; ++t)
+    // Read without waits, in (t, db, row-group) order; pv_async waits for
+    // each fragment before its MFMA.
+    static __device__ __forceinline__ void vfrags_async(u32x2 (&vr)[NPV][NDB][4], const char* vl,
+                                                        const int (&va)[NVA]) {
+        const uint32_t base = lds_addr(vl);
+        static_for<0, NPV>([&](auto tc) {
+            constexpr int t = decltype(tc)::value;
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const char* vp = vl + va[db] + 64 * t * RB;
-                const u32x2 r0 = lds_read_tr8(vp);
-                const u32x2 r1 = lds_read_tr8(vp + 16 * RB);
-                const u32x2 r2 = lds_read_tr8(vp + 32 * RB);
-                const u32x2 r3 = lds_read_tr8(vp + 48 * RB);
-                vf[t][db] = i32x8{(int)r0[0], (int)r0[1], (int)r1[0], (int)r1[1],
-                                  (int)r2[0], (int)r2[1], (int)r3[0], (int)r3[1]};
+                const uint32_t a = base + va[db];
+                vr[t][db][0] = lds_tr8_async<64 * t * RB>(a);
+                vr[t][db][1] = lds_tr8_async<64 * t * RB + 16 * RB>(a);
+                vr[t][db][2] = lds_tr8_async<64 * t * RB + 32 * RB>(a);
+                vr[t][db][3] = lds_tr8_async<64 * t * RB + 48 * RB>(a);
             }
+        });
     }
 
-    __device__ __forceinline__ void pv(const i32x8 (&vf)[NPV][NDB], const i32x8 (&pf)[NPV]) {
+    __device__ __forceinline__ void pv_async(u32x2 (&vr)[NPV][NDB][4], const i32x8 (&pf)[NPV]) {
+        static_for<0, NPV>([&](auto tc) {
+            constexpr int t = decltype(tc)::value;
+            static_for<0, NDB>([&](auto dc) {
+                constexpr int db = decltype(dc)::value;
+                constexpr int later = 4 * (NDB * (NPV - t) - db - 1);   // reads issued after this one
+                lgkm_wait<(later > 15 ? 15 : later)>();
 #pragma unroll
-        for (int t = 0; t < NPV; ++t)
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) o[db] = mfma32_fp8(vf[t][db], pf[t], o[db]);
+                for (int g = 0; g < 4; ++g) lgkm_bind(vr[t][db][g]);
+                const i32x8 v = {(int)vr[t][db][0][0], (int)vr[t][db][0][1], (int)vr[t][db][1][0],
+                                 (int)vr[t][db][1][1], (int)vr[t][db][2][0], (int)vr[t][db][2][1],
+                                 (int)vr[t][db][3][0], (int)vr[t][db][3][1]};
+                o[db] = mfma32_fp8(v, pf[t], o[db]);
+            });
+        });
     }
 
     // Softmax + PV of the tile in s (no overlap).
     __device__ __forceinline__ void finish(const f32x16 (&s)[NKB], const char* vl,
                                            const int (&va)[NVA], float cj, float bj, float lscale) {
         rescale(tile_max(s, cj));
-        i32x8 vf[NPV][NDB];
-        vfrags(vf, vl, va);
+        u32x2 vr[NPV][NDB][4];
+        vfrags_async(vr, vl, va);
         __builtin_amdgcn_sched_barrier(0);
         i32x8 pf[NPV];
         float ls[2] = {0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < NPV; ++t) probs(s, pf, t, cj, bj, ls);
         l += (ls[0] + ls[1]) * lscale;
-        pv(vf, pf);
+        pv_async(vr, pf);
     }
 
     // Pipelined step: exponentials of this tile (maximum already applied)
@@ -238,10 +250,10 @@ struct Wave8 {
             __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // twelve VALU
         }
         __builtin_amdgcn_sched_barrier(0);
-        i32x8 vf[NPV][NDB];
-        vfrags(vf, vl, va);
+        u32x2 vr[NPV][NDB][4];
+        vfrags_async(vr, vl, va);
         __builtin_amdgcn_sched_barrier(0);
-        pv(vf, pf);
+        pv_async(vr, pf);
         const float mtn = tile_max(sn, cjn);
 #pragma unroll
         for (int i = 0; i < MF_PV; ++i) {
