@@ -21,6 +21,10 @@ bool sizes_ok(int B, int H, int N, int d) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
+// Largest K or V of one head in bytes (N * d * 2): the kernels address a
+// head through 31-bit buffer offsets, with one tile of headroom.
+constexpr long long kMaxHeadBytes = 0x7fffffffLL - (1 << 16);
+
 }  // namespace
 
 extern "C" {
@@ -56,6 +60,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return FA_ERR_INVALID_ARG;
     if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
     if ((long long)B * H > 0x7fffffffLL / 2) return FA_ERR_UNSUPPORTED;
+    // K and V of one head are read through 32-bit range-checked offsets.
+    if ((long long)N * d * 2 > kMaxHeadBytes) return FA_ERR_UNSUPPORTED;
     if (B == 0 || H == 0 || N == 0) return FA_OK;
     if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
     const size_t qa = base == FA_FP8_E4M3 ? 256 : 16;

@@ -16,11 +16,12 @@
 //  * Workgroup = NW waves, each wave owns QW = 32*QB query rows. The wave
 //    keeps its Q rows in registers as MFMA B operands for the whole kernel.
 //  * K and V tiles of BC keys go straight from global memory into LDS
-//    (global_load_lds, 16 bytes per lane, no staging registers), double
-//    buffered: tile j+1 is in flight while tile j is computed, with one
-//    workgroup barrier per tile. Rows are stored unpadded with their 16-byte
-//    chunks XOR-swizzled (see lds_chunk), which keeps both the K fragment
-//    reads and the transposing V reads free of bank conflicts.
+//    (buffer loads with an LDS destination, 16 bytes per lane, no staging
+//    registers; the tile's offset is a scalar operand and rows at or past N
+//    read as zeros), double buffered: tile j+1 is in flight while tile j is
+//    computed, with one workgroup barrier per tile. Rows are stored unpadded
+//    with their 16-byte chunks XOR-swizzled (see lds_swz16), which keeps both
+//    the K fragment reads and the transposing V reads free of bank conflicts.
 //  * Scores are computed transposed, S^T = K Q^T, with 32x32x16 MFMA: each
 //    lane then owns one query (column) and 16 keys per 32-key block, so the
 //    row max and row sum are mostly lane-local; the two half-waves that share
@@ -32,10 +33,12 @@
 //    row index swapped) so that every lane's P^T slots cover 8 consecutive
 //    keys; V^T fragments then come from LDS with transposing reads.
 //  * Softmax in the base-2 domain: p = exp2(s*c - m), c = scale*log2(e),
-//    hardware v_exp_f32. The reference maximum m is only moved when a tile's
-//    row maximum exceeds it by more than TAU (p then stays <= 2^TAU), which
-//    skips almost all rescales of the O accumulators; the result is the same
-//    exact softmax up to rounding because l and O use the same m.
+//    hardware v_exp_f32. The reference maximum m is the exact row maximum of
+//    the first key tile; later tiles take their exponentials against it
+//    without computing their own maximum. Only when a tile's sum of p in some
+//    lane exceeds kBig is that tile redone with its exact maximum (moving m
+//    and rescaling O and the sums). The result is the same exact softmax up
+//    to rounding because l and O always share m.
 //  * Two row sums: l~ from the rounded P actually fed to the PV MFMA (dot2
 //    with ones) normalises O, which makes O an exact convex combination of V
 //    rows even when one key dominates; l from the fp32 p gives the

@@ -82,7 +82,8 @@ enum fa_dtype {
  *  stream   hipStream_t or NULL.
  *
  * q, k, v must be 16-byte aligned. Returns FA_OK, FA_ERR_INVALID_ARG,
- * FA_ERR_UNSUPPORTED (d not in {64,128,256}) or FA_ERR_HIP.
+ * FA_ERR_UNSUPPORTED (d not in {64,128,256}, or N*d*2 > 2^31 - 2^16 - 1:
+ * one head's K or V must be addressable with 31-bit offsets) or FA_ERR_HIP.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, int causal, float softmax_scale, int dtype,

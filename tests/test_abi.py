@@ -65,6 +65,9 @@ def fwd(**kw):
     (dict(dtype=fa.FA_BF16 | 0x200), fa.FA_ERR_INVALID_ARG),
     (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    # one head's K/V past 2^31 - 2^16 - 1 bytes (31-bit buffer offsets)
+    (dict(N=8388352, d=128), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=1 << 23, d=256), fa.FA_ERR_UNSUPPORTED),
     (dict(N=-1), fa.FA_ERR_INVALID_ARG),
     (dict(B=-2), fa.FA_ERR_INVALID_ARG),
     (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
