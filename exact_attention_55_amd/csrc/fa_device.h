@@ -184,16 +184,25 @@ __device__ __forceinline__ void load_lds16(const void* g, void* lds) {
 // Buffer resource over [base, base + bytes): raw (stride 0) byte-addressed
 // loads, range-checked against bytes. On gfx950 the check covers the whole
 // offset (VGPR offset + SGPR offset): a 16-byte read at or past the end
-// returns zeros, also into LDS. bytes must be < 2^31.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+// returns zeros, also into LDS. bytes must be < 2^31; base wave-uniform.
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                 __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xffff),
+                 __builtin_amdgcn_readfirstlane(bytes), 0x00020000};
 }
 // 16 bytes per lane from a buffer straight into LDS: lane i's bytes come
-// from offset voff + soff (soff wave-uniform) and land at lds + 16*i (lds
-// wave-uniform). No VGPR is written; completion is counted by vmcnt.
-__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff,
+// from offset voff + soff and land at LDS address lds + 16*i (lds and soff
+// wave-uniform). Issued through inline asm so that the compiler does not
+// track it: otherwise it makes LDS reads wait for every outstanding copy,
+// because it cannot tell the tiles apart. Completion is awaited explicitly
+// (wait_vm_all) before the barrier that publishes the tile. Nothing else in
+// the kernels keeps a value in M0.
+__device__ __forceinline__ void buffer_load_lds16(i32x4 rsrc, uint32_t lds, uint32_t voff,
                                                   uint32_t soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)(lds), 16, (int)voff, (int)soff, 0, 0);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
 }
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -212,6 +221,9 @@ __device__ __forceinline__ void phase_barrier_vm() {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 }
+
+// s_waitcnt immediate (gfx9 encoding) for vmcnt(0), other counters ignored.
+constexpr int kVmcnt0 = 0x0f70;
 
 // Wait until this wave's global loads (including direct-to-LDS ones) landed.
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

@@ -53,6 +53,10 @@ namespace fa {
 // fp16 P (max 65504) and the fp32 accumulators hold with room to spare.
 constexpr float kBig = 16384.0f;
 
+#ifndef FA16_SCHED
+#define FA16_SCHED 1
+#endif
+
 template <typename T> __device__ __forceinline__ typename Elt<T>::x2 pack2(float a, float b);
 template <> __device__ __forceinline__ bf16x2 pack2<__bf16>(float a, float b) {
     bf16x2 r = {(__bf16)a, (__bf16)b};
@@ -77,7 +81,7 @@ __device__ __forceinline__ float sum2(f16x2 x, float acc) {
 // budget is sized for (2: 256 registers per wave, so two waves share a SIMD
 // and one wave's softmax overlaps the other's MFMAs).
 #ifndef FA16_CFG_64
-#define FA16_CFG_64 8, 1, 128, 2
+#define FA16_CFG_64 4, 1, 64, 2
 #endif
 #ifndef FA16_CFG_128
 #define FA16_CFG_128 4, 1, 64, 2
@@ -344,6 +348,10 @@ struct Wave16 {
         X8 pf[QB][NPV];
         float ls[QB][2], lxs[QB][2];
         zero_sums(ls, lxs);
+        // The MFMA + exponential phase runs at raised wave priority: of the
+        // two waves sharing a SIMD, the one in this phase issues first and the
+        // other (in its PV phase) fills the matrix core around it.
+        __builtin_amdgcn_s_setprio(1);
         qk(sn, kf, qf, 0, NCH / 2);
 #pragma unroll
         for (int kb = 0; kb < NKB / 2; ++kb) probs(s, pf, kb, c, ls, lxs);
@@ -367,12 +375,116 @@ struct Wave16 {
             __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
         settle(s, pf, c, ls, lxs);
         u32x2 vlo[NPV][NDB], vhi[NPV][NDB];
         vfrags_async(vlo, vhi, b0, b1);
         __builtin_amdgcn_sched_barrier(0);
         pv_async(vlo, vhi, pf);
         __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- fine-grained schedule (compiler-visible LDS reads) ----
+    __device__ __forceinline__ void pv(const X8 (&vf)[NPV][NDB], const X8 (&pf)[QB][NPV]) {
+#pragma unroll
+        for (int t = 0; t < NPV; ++t)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(vf[t][db], pf[qb][t], o[qb][db]);
+    }
+
+    // V^T fragment (t, db) with two transposing reads: rows +0..3 at
+    // va[db % NVA] + NVA*64*(db / NVA) + 16*t*RB, rows +4..7 vstep further.
+    static __device__ __forceinline__ X8 vfrag(const char* vl, const int (&va)[NVA], int vstep,
+                                               int t, int db) {
+        const char* vp = vl + va[db % NVA] + NVA * 64 * (db / NVA) + 16 * t * RB;
+        const u32x2 lo = lds_read_tr16(vp);
+        const u32x2 hi4 = lds_read_tr16(vp + vstep);
+        return __builtin_bit_cast(X8, u32x4{lo[0], lo[1], hi4[0], hi4[1]});
+    }
+
+    // One exponential pair of the tile: scores 8*h + 2*j, +1 of block kb.
+    __device__ __forceinline__ void prob_pair(const f32x16 (&s)[QB][NKB], X2 (&pp)[QB][NKB][2][4],
+                                              int kb, int h, int j, float c, float (&ls)[QB][2],
+                                              float (&lxs)[QB][2]) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const float p0 = exp2_hw(fmaf(s[qb][kb][8 * h + 2 * j], c, -m[qb]));
+            const float p1 = exp2_hw(fmaf(s[qb][kb][8 * h + 2 * j + 1], c, -m[qb]));
+            pp[qb][kb][h][j] = pack2<T>(p0, p1);
+            ls[qb][h] = sum2(pp[qb][kb][h][j], ls[qb][h]);
+            lxs[qb][h] += p0 + p1;
+        }
+    }
+
+    // Pipelined step as one instruction stream in program order (every
+    // chunk ends in a scheduling barrier):
+    //   NQK chunks, each: one LDS read KPD fragments ahead (K of the next
+    //   tile; in the last VPD chunks the first V^T fragments of this tile),
+    //   one score MFMA of the next tile, and an even share of this tile's
+    //   exponentials, which run in the MFMA's shadow;
+    //   the overflow check (a branch, rarely taken);
+    //   NPVM chunks, each: the reads of the V^T fragment VPD ahead, one PV
+    //   MFMA, and a share of the copy of the next scores into s.
+    __device__ __forceinline__ void step(f32x16 (&s)[QB][NKB], const char* kn, const int (&ka)[NKA],
+                                         const char* vl, const int (&va)[NVA], int vstep,
+                                         const X8 (&qf)[QB][NCH], float c) {
+        static_assert(QB == 1, "one 32-row query block per wave");
+        constexpr int NKF = NCH * NKB;      // K fragments = score MFMAs per tile
+        constexpr int NVF = NPV * NDB;      // V^T fragments = PV MFMAs per tile
+        constexpr int NPAIR = NKB * 8;      // exponential pairs per lane per tile
+        constexpr int KPD = 4;
+        constexpr int VPD = 4;
+        static_assert(NKF >= KPD + VPD && NVF > VPD, "tile too small for the read-ahead");
+        X8 kf[NKB][NCH];
+        f32x16 sn[QB][NKB];
+        X8 vf[NPV][NDB];
+        X2 pp[QB][NKB][2][4];
+        float ls[QB][2], lxs[QB][2];
+        zero_sums(ls, lxs);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) sn[0][kb] = f32x16{};
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int f = 0; f < KPD; ++f) kf[f % NKB][f / NKB] = kfrag(kn, ka, f / NKB, f % NKB);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NKF; ++i) {
+            const int f = i + KPD;                      // fragment read in this chunk
+            if (f < NKF) {
+                kf[f % NKB][f / NKB] = kfrag(kn, ka, f / NKB, f % NKB);
+            } else {
+                const int v = f - NKF;                  // V^T fragment (t, db) = (v / NDB, v % NDB)
+                vf[v / NDB][v % NDB] = vfrag(vl, va, vstep, v / NDB, v % NDB);
+            }
+            const int ch = i / NKB, kb = i % NKB;
+            sn[0][kb] = mfma32(kf[kb][ch], qf[0][ch], sn[0][kb]);
+#pragma unroll
+            for (int q = i * NPAIR / NKF; q < (i + 1) * NPAIR / NKF; ++q)
+                prob_pair(s, pp, q / 8, (q / 4) % 2, q % 4, c, ls, lxs);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_s_setprio(0);
+        X8 pf[QB][NPV];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const X2 (&w)[4] = pp[0][kb][h];
+                pf[0][2 * kb + h] = X8{w[0][0], w[0][1], w[1][0], w[1][1], w[2][0], w[2][1], w[3][0], w[3][1]};
+            }
+        settle(s, pf, c, ls, lxs);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < NVF; ++j) {
+            const int v = j + VPD;
+            if (v < NVF) vf[v / NDB][v % NDB] = vfrag(vl, va, vstep, v / NDB, v % NDB);
+            const int t = j / NDB, db = j % NDB;
+            o[0][db] = mfma32(vf[t][db], pf[0][t], o[0][db]);
+            if (j < NKB) s[0][j] = sn[0][j];
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 };
 
@@ -426,8 +538,8 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     // +16*i, i.e. physical chunk cp of row r, which holds logical chunk
     // cp ^ lds_swz16(r) of that key row. The tile's row offset is the
     // wave-uniform SGPR offset, so a load costs no vector instructions.
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kg + head, N * RB);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vg + head, N * RB);
+    const i32x4 krs = make_rsrc(Kg + head, N * RB);
+    const i32x4 vrs = make_rsrc(Vg + head, N * RB);
     uint32_t voff[NIW];
 #pragma unroll
     for (int j = 0; j < NIW; ++j) {
@@ -436,8 +548,9 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
         voff[j] = row * RB + ((p % RB / 16) ^ lds_swz16<D>(row)) * 16;
     }
     const int nkt_total = (N + BC - 1) / BC;
-    auto issue = [&](__amdgpu_buffer_rsrc_t rs, int t, int slot) {
-        char* dst = smem + slot * TB + wave_u * NIW * 1024;
+    const uint32_t sbase = lds_addr(smem);
+    auto issue = [&](const i32x4& rs, int t, int slot) {
+        const uint32_t dst = sbase + slot * TB + wave_u * NIW * 1024;
 #pragma unroll
         for (int j = 0; j < NIW; ++j) buffer_load_lds16(rs, dst + j * 1024, voff[j], t * TB);
     };
@@ -458,6 +571,11 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
                 qf[qb][ch] = __builtin_bit_cast(X8, u32x4{0, 0, 0, 0});
         }
     }
+    // Q has landed before any tile copy is issued. (A wait the compiler can
+    // see: otherwise it keeps Q's loads pending on paths that skip the first
+    // use and re-waits inside the key loop, where vmcnt also counts the
+    // tile copies in flight.)
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
 
     // Key tiles [0, nfull) need no mask for any wave of the workgroup; tiles
     // [nfull, nkt) cross the causal diagonal or the end of the sequence.
@@ -486,7 +604,10 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
         }
         vstep = 4 * RB + (((lane & 3) >> 1) ? -16 : 16);
     }
-    const uint32_t sbase = lds_addr(smem);
+    int vai[NVA];
+#pragma unroll
+    for (int i = 0; i < NVA; ++i) vai[i] = (int)va[i];
+    const int vsi = (int)vstep;
     // V read bases of a tile at LDS address base.
     auto vbases = [&](uint32_t base, uint32_t (&b0)[NVA], uint32_t (&b1)[NVA]) {
 #pragma unroll
@@ -521,6 +642,9 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     for (; t + 1 < nfull; ++t) {
         load_k(t + 2);
         load_v(t + 1);
+#if FA16_SCHED
+        st.step(s, ktile(t + 1), ka, smem + (2 + (t & 1)) * TB, vai, vsi, qf, c);
+#else
         uint32_t b0[NVA], b1[NVA];
         vbases(sbase + (2 + (t & 1)) * TB, b0, b1);
         f32x16 sn[QB][NKB];
@@ -529,6 +653,7 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) s[qb][kb] = sn[qb][kb];
+#endif
         wait_vm_all();
         __syncthreads();
     }
