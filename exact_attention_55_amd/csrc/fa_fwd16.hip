@@ -56,6 +56,12 @@ constexpr float kBig = 16384.0f;
 #ifndef FA16_SCHED
 #define FA16_SCHED 1
 #endif
+#ifndef FA16_KPD
+#define FA16_KPD 4
+#endif
+#ifndef FA16_VPD
+#define FA16_VPD 4
+#endif
 
 template <typename T> __device__ __forceinline__ typename Elt<T>::x2 pack2(float a, float b);
 template <> __device__ __forceinline__ bf16x2 pack2<__bf16>(float a, float b) {
@@ -430,12 +436,11 @@ struct Wave16 {
     __device__ __forceinline__ void step(f32x16 (&s)[QB][NKB], const char* kn, const int (&ka)[NKA],
                                          const char* vl, const int (&va)[NVA], int vstep,
                                          const X8 (&qf)[QB][NCH], float c) {
-        static_assert(QB == 1, "one 32-row query block per wave");
         constexpr int NKF = NCH * NKB;      // K fragments = score MFMAs per tile
         constexpr int NVF = NPV * NDB;      // V^T fragments = PV MFMAs per tile
         constexpr int NPAIR = NKB * 8;      // exponential pairs per lane per tile
-        constexpr int KPD = 4;
-        constexpr int VPD = 4;
+        constexpr int KPD = FA16_KPD;       // K fragments read ahead of their MFMA
+        constexpr int VPD = FA16_VPD;       // V^T fragments read ahead of their MFMA
         static_assert(NKF >= KPD + VPD && NVF > VPD, "tile too small for the read-ahead");
         X8 kf[NKB][NCH];
         f32x16 sn[QB][NKB];
@@ -444,7 +449,9 @@ struct Wave16 {
         float ls[QB][2], lxs[QB][2];
         zero_sums(ls, lxs);
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) sn[0][kb] = f32x16{};
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) sn[qb][kb] = f32x16{};
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int f = 0; f < KPD; ++f) kf[f % NKB][f / NKB] = kfrag(kn, ka, f / NKB, f % NKB);
@@ -459,7 +466,8 @@ struct Wave16 {
                 vf[v / NDB][v % NDB] = vfrag(vl, va, vstep, v / NDB, v % NDB);
             }
             const int ch = i / NKB, kb = i % NKB;
-            sn[0][kb] = mfma32(kf[kb][ch], qf[0][ch], sn[0][kb]);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) sn[qb][kb] = mfma32(kf[kb][ch], qf[qb][ch], sn[qb][kb]);
 #pragma unroll
             for (int q = i * NPAIR / NKF; q < (i + 1) * NPAIR / NKF; ++q)
                 prob_pair(s, pp, q / 8, (q / 4) % 2, q % 4, c, ls, lxs);
@@ -468,12 +476,15 @@ struct Wave16 {
         __builtin_amdgcn_s_setprio(0);
         X8 pf[QB][NPV];
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const X2 (&w)[4] = pp[0][kb][h];
-                pf[0][2 * kb + h] = X8{w[0][0], w[0][1], w[1][0], w[1][1], w[2][0], w[2][1], w[3][0], w[3][1]};
-            }
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const X2 (&w)[4] = pp[qb][kb][h];
+                    pf[qb][2 * kb + h] =
+                        X8{w[0][0], w[0][1], w[1][0], w[1][1], w[2][0], w[2][1], w[3][0], w[3][1]};
+                }
         settle(s, pf, c, ls, lxs);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -481,8 +492,9 @@ struct Wave16 {
             const int v = j + VPD;
             if (v < NVF) vf[v / NDB][v % NDB] = vfrag(vl, va, vstep, v / NDB, v % NDB);
             const int t = j / NDB, db = j % NDB;
-            o[0][db] = mfma32(vf[t][db], pf[0][t], o[0][db]);
-            if (j < NKB) s[0][j] = sn[0][j];
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(vf[t][db], pf[qb][t], o[qb][db]);
+            if (j < QB * NKB) s[j / NKB][j % NKB] = sn[j / NKB][j % NKB];
             __builtin_amdgcn_sched_barrier(0);
         }
     }

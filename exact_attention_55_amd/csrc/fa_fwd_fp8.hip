@@ -9,27 +9,30 @@
 // codes plus one float32 scale per 128 rows of a head.
 //
 // Same structure as the 16-bit kernel (transposed score tile S^T = K Q^T,
-// transposed output O^T += V^T P^T, lazy rescale, direct global->LDS copies
-// into swizzled double-buffered tiles, score MFMAs of the next tile
-// overlapped with the exponentials of this one), with 32x32x64 e4m3 MFMA.
+// transposed output O^T += V^T P^T, reference maximum from the first tile
+// with an overflow-checked redo, buffer loads straight into swizzled
+// double-buffered LDS tiles, a hand-ordered pipeline of the next tile's
+// score MFMAs with this tile's exponentials), with 32x32x64 e4m3 MFMA.
 // Scale handling, per query block i and key tile j:
 //  * logits: s = acc * sq_i * sk_j * softmax_scale; in the base-2 domain the
 //    product c_j = sq_i * sk_j * softmax_scale * log2(e) is one scalar per
 //    tile, folded into the fma that feeds exp2;
-//  * P is quantised to e4m3 for the PV MFMA as P' = p * 16 * w_j with
+//  * P is quantised to e4m3 for the PV MFMA as P' = p * 8 * w_j with
 //    w_j = sv_j / sv_max (sv_max = largest V block scale of the head): the
-//    factor is folded into the exponent, p' = exp2(s*c - m + log2(16 w_j)), so
-//    the V block scale costs no extra VALU work. With the lazy-rescale bound
-//    p <= 2^4 this keeps P' <= 256 < 448, and p >= 2^-10 stays normal;
-//  * the row sum l accumulates the unquantised p (rowsum(P') / (16 w_j));
-//  * epilogue: O = O_acc * sv_max / (16 l).
+//    factor is folded into the exponent, p' = exp2(s*c - m + log2(8 w_j)), so
+//    the V block scale costs no extra VALU work. A tile whose P' sum in some
+//    lane exceeds kBig8 = 384 is redone with its exact maximum, so every P'
+//    is <= 384 < 448 (e4m3 maximum); at the reference maximum a lane's 32
+//    values sum to at most 256, and p >= 2^-9 stays normal;
+//  * the row sum l accumulates the unquantised p (rowsum(P') / (8 w_j));
+//  * epilogue: O = O_acc * sv_max / (8 l).
 #include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
 
-constexpr float kTau8 = 4.0f;       // lazy-rescale threshold (log2 units)
-constexpr float kPScale = 16.0f;    // P multiplier before e4m3 rounding (= 2^(8 - kTau8))
+constexpr float kPScale = 8.0f;     // P multiplier before e4m3 rounding
+constexpr float kBig8 = 384.0f;     // per-lane tile sum of P' that forces the exact-maximum path
 
 #ifndef FA8_CFG_64
 #define FA8_CFG_64 4, 64, 2
@@ -137,131 +140,142 @@ struct Wave8 {
         return pair_max(part[0]) * cj;
     }
 
-    __device__ __forceinline__ void rescale(float mt) {
-        if (wave_any(mt > m + kTau8)) {
-            const float mnew = fmaxf(m, mt);
-            const float alpha = (mnew == -INFINITY) ? 1.f : exp2_hw(m - mnew);
-            m = mnew;
-            l *= alpha;
+    // Moves the reference maximum to max(m, mt), rescaling O and l.
+    __device__ __forceinline__ void raise_max(float mt) {
+        const float mnew = fmaxf(m, mt);
+        const float alpha = (mnew == -INFINITY) ? 1.f : exp2_hw(m - mnew);
+        m = mnew;
+        l *= alpha;
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-        }
+        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
     }
 
     // P' for score blocks 2t, 2t+1 -> PV operand t. Dword g of the operand
-    // holds the e4m3 bytes of registers 4*(g%4)..+3 of score block 2t + g/4.
-    __device__ __forceinline__ void probs(const f32x16 (&s)[NKB], i32x8 (&pf)[NPV], int t,
-                                          float cj, float bj, float (&ls)[2]) {
+    // holds the e4m3 bytes of registers 4*(g%4)..+3 of score block 2t + g/4;
+    // group q = 8t + g of the tile.
+    __device__ __forceinline__ void prob_group(const f32x16 (&s)[NKB], uint32_t (&w)[NPV][8], int q,
+                                               float cj, float bj, float (&ls)[2]) {
+        const int t = q / 8, g = q % 8;
+        const int kb = 2 * t + g / 4, r = 4 * (g % 4);
         const float nm = bj - m;
-        uint32_t w[8];
+        const float p0 = exp2_hw(fmaf(s[kb][r], cj, nm));
+        const float p1 = exp2_hw(fmaf(s[kb][r + 1], cj, nm));
+        const float p2 = exp2_hw(fmaf(s[kb][r + 2], cj, nm));
+        const float p3 = exp2_hw(fmaf(s[kb][r + 3], cj, nm));
+        ls[g & 1] += (p0 + p1) + (p2 + p3);
+        w[t][g] = cvt4_e4m3(p0, p1, p2, p3);
+    }
+    static __device__ __forceinline__ void pack_p(const uint32_t (&w)[NPV][8], i32x8 (&pf)[NPV]) {
 #pragma unroll
-        for (int g = 0; g < 8; ++g) {
-            const int kb = 2 * t + g / 4, r = 4 * (g % 4);
-            const float p0 = exp2_hw(fmaf(s[kb][r], cj, nm));
-            const float p1 = exp2_hw(fmaf(s[kb][r + 1], cj, nm));
-            const float p2 = exp2_hw(fmaf(s[kb][r + 2], cj, nm));
-            const float p3 = exp2_hw(fmaf(s[kb][r + 3], cj, nm));
-            ls[g & 1] += (p0 + p1) + (p2 + p3);
-            w[g] = cvt4_e4m3(p0, p1, p2, p3);
+        for (int t = 0; t < NPV; ++t)
+            pf[t] = i32x8{(int)w[t][0], (int)w[t][1], (int)w[t][2], (int)w[t][3],
+                          (int)w[t][4], (int)w[t][5], (int)w[t][6], (int)w[t][7]};
+    }
+
+    // Exponentials against the reference maximum; a tile whose P' sum in
+    // some lane exceeds kBig8 is redone with its exact maximum (moving m,
+    // rescaling O and l). Then l takes the tile's unquantised row sum.
+    __device__ __forceinline__ void settle(const f32x16 (&s)[NKB], uint32_t (&w)[NPV][8], float cj,
+                                           float bj, float lscale, float (&ls)[2]) {
+        if (wave_any(ls[0] + ls[1] > kBig8)) {
+            raise_max(tile_max(s, cj));
+            ls[0] = ls[1] = 0.f;
+#pragma unroll
+            for (int q = 0; q < 8 * NPV; ++q) prob_group(s, w, q, cj, bj, ls);
         }
-        pf[t] = i32x8{(int)w[0], (int)w[1], (int)w[2], (int)w[3],
-                      (int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+        l += (ls[0] + ls[1]) * lscale;
     }
 
     // V^T fragment (t, db): slots 8c..8c+7 = keys 64t + 16c + 8hi + 0..7 of
     // d-row 32*db + l32; one transposing read of 8 rows per c.
-    // Read without waits, in (t, db, row-group) order; pv_async waits for
-    // each fragment before its MFMA.
-    static __device__ __forceinline__ void vfrags_async(u32x2 (&vr)[NPV][NDB][4], const char* vl,
-                                                        const int (&va)[NVA]) {
-        const uint32_t base = lds_addr(vl);
-        static_for<0, NPV>([&](auto tc) {
-            constexpr int t = decltype(tc)::value;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const uint32_t a = base + va[db];
-                vr[t][db][0] = lds_tr8_async<64 * t * RB>(a);
-                vr[t][db][1] = lds_tr8_async<64 * t * RB + 16 * RB>(a);
-                vr[t][db][2] = lds_tr8_async<64 * t * RB + 32 * RB>(a);
-                vr[t][db][3] = lds_tr8_async<64 * t * RB + 48 * RB>(a);
-            }
-        });
-    }
-
-    __device__ __forceinline__ void pv_async(u32x2 (&vr)[NPV][NDB][4], const i32x8 (&pf)[NPV]) {
-        static_for<0, NPV>([&](auto tc) {
-            constexpr int t = decltype(tc)::value;
-            static_for<0, NDB>([&](auto dc) {
-                constexpr int db = decltype(dc)::value;
-                constexpr int later = 4 * (NDB * (NPV - t) - db - 1);   // reads issued after this one
-                lgkm_wait<(later > 15 ? 15 : later)>();
-#pragma unroll
-                for (int g = 0; g < 4; ++g) lgkm_bind(vr[t][db][g]);
-                const i32x8 v = {(int)vr[t][db][0][0], (int)vr[t][db][0][1], (int)vr[t][db][1][0],
-                                 (int)vr[t][db][1][1], (int)vr[t][db][2][0], (int)vr[t][db][2][1],
-                                 (int)vr[t][db][3][0], (int)vr[t][db][3][1]};
-                o[db] = mfma32_fp8(v, pf[t], o[db]);
-            });
-        });
+    static __device__ __forceinline__ i32x8 vfrag(const char* vl, const int (&va)[NVA], int t, int db) {
+        const char* vp = vl + va[db] + 64 * t * RB;
+        const u32x2 r0 = lds_read_tr8(vp);
+        const u32x2 r1 = lds_read_tr8(vp + 16 * RB);
+        const u32x2 r2 = lds_read_tr8(vp + 32 * RB);
+        const u32x2 r3 = lds_read_tr8(vp + 48 * RB);
+        return i32x8{(int)r0[0], (int)r0[1], (int)r1[0], (int)r1[1],
+                     (int)r2[0], (int)r2[1], (int)r3[0], (int)r3[1]};
     }
 
     // Softmax + PV of the tile in s (no overlap).
     __device__ __forceinline__ void finish(const f32x16 (&s)[NKB], const char* vl,
                                            const int (&va)[NVA], float cj, float bj, float lscale) {
-        rescale(tile_max(s, cj));
-        u32x2 vr[NPV][NDB][4];
-        vfrags_async(vr, vl, va);
-        __builtin_amdgcn_sched_barrier(0);
-        i32x8 pf[NPV];
+        uint32_t w[NPV][8];
         float ls[2] = {0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < NPV; ++t) probs(s, pf, t, cj, bj, ls);
-        l += (ls[0] + ls[1]) * lscale;
-        pv_async(vr, pf);
+        for (int q = 0; q < 8 * NPV; ++q) prob_group(s, w, q, cj, bj, ls);
+        settle(s, w, cj, bj, lscale, ls);
+        i32x8 pf[NPV];
+        pack_p(w, pf);
+        i32x8 vf[NPV][NDB];
+#pragma unroll
+        for (int t = 0; t < NPV; ++t)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) vf[t][db] = vfrag(vl, va, t, db);
+#pragma unroll
+        for (int t = 0; t < NPV; ++t)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) o[db] = mfma32_fp8(vf[t][db], pf[t], o[db]);
     }
 
-    // Pipelined step: exponentials of this tile (maximum already applied)
-    // interleaved with the score MFMAs of the next tile (K fragments at kn);
-    // then the PV MFMAs of this tile interleaved with the row maximum of the
-    // next tile (returned, in log2 units with its own scale cjn).
-    __device__ __forceinline__ float overlap(const f32x16 (&s)[NKB], f32x16 (&sn)[NKB], const char* kn,
-                                             const int (&ka)[NKA][2], const char* vl,
-                                             const int (&va)[NVA], const i32x8 (&qf)[NCH],
-                                             float cj, float bj, float lscale, float cjn) {
-        constexpr int MF_QK = NCH * NKB;
-        constexpr int MF_PV = NPV * NDB;
+    // Pipelined step as one instruction stream in program order (every chunk
+    // ends in a scheduling barrier): per score MFMA of the next tile (K at
+    // kn), the LDS reads of the fragment KPD ahead (in the last chunks the
+    // first VPD V^T fragments of this tile) and an even share of this tile's
+    // exponential groups; the overflow check; per PV MFMA of this tile, the
+    // reads of the V^T fragment VPD ahead and a share of the copy of the next
+    // scores into s.
+    __device__ __forceinline__ void step(f32x16 (&s)[NKB], const char* kn, const int (&ka)[NKA][2],
+                                         const char* vl, const int (&va)[NVA], const i32x8 (&qf)[NCH],
+                                         float cj, float bj, float lscale) {
+        constexpr int NKF = NCH * NKB;      // K fragments = score MFMAs per tile
+        constexpr int NVF = NPV * NDB;      // V^T fragments = PV MFMAs per tile
+        constexpr int NG = 8 * NPV;         // exponential groups (4 each) per lane
+        constexpr int KPD = NKF >= 4 ? 2 : 1;
+        constexpr int VPD = (NKF - KPD) < 2 ? (NKF - KPD) : 2;
+        static_assert(VPD >= 1 && VPD < NVF, "tile too small for the read-ahead");
         i32x8 kf[NKB][NCH];
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch)
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) kf[kb][ch] = kfrag(kn, ka, ch, kb);
-        __builtin_amdgcn_sched_barrier(0);
+        f32x16 sn[NKB];
+        i32x8 vf[NPV][NDB];
+        uint32_t w[NPV][8];
+        float ls[2] = {0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) sn[kb] = f32x16{};
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int f = 0; f < KPD; ++f) kf[f % NKB][f / NKB] = kfrag(kn, ka, f / NKB, f % NKB);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NKF; ++i) {
+            const int f = i + KPD;
+            if (f < NKF) {
+                kf[f % NKB][f / NKB] = kfrag(kn, ka, f / NKB, f % NKB);
+            } else if (f - NKF < VPD) {
+                const int v = f - NKF;
+                vf[v / NDB][v % NDB] = vfrag(vl, va, v / NDB, v % NDB);
+            }
+            const int ch = i / NKB, kb = i % NKB;
+            sn[kb] = mfma32_fp8(kf[kb][ch], qf[ch], sn[kb]);
+#pragma unroll
+            for (int q = i * NG / NKF; q < (i + 1) * NG / NKF; ++q) prob_group(s, w, q, cj, bj, ls);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_s_setprio(0);
+        settle(s, w, cj, bj, lscale, ls);
         i32x8 pf[NPV];
-        float ls[2] = {0.f, 0.f};
-        qk(sn, kf, qf, 0, NCH);
+        pack_p(w, pf);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int t = 0; t < NPV; ++t) probs(s, pf, t, cj, bj, ls);
-        l += (ls[0] + ls[1]) * lscale;
+        for (int j = 0; j < NVF; ++j) {
+            const int v = j + VPD;
+            if (v < NVF) vf[v / NDB][v % NDB] = vfrag(vl, va, v / NDB, v % NDB);
+            const int t = j / NDB, db = j % NDB;
+            o[db] = mfma32_fp8(vf[t][db], pf[t], o[db]);
 #pragma unroll
-        for (int i = 0; i < MF_QK; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // twelve VALU
+            for (int kb = j * NKB / NVF; kb < (j + 1) * NKB / NVF; ++kb) s[kb] = sn[kb];
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        u32x2 vr[NPV][NDB][4];
-        vfrags_async(vr, vl, va);
-        __builtin_amdgcn_sched_barrier(0);
-        pv_async(vr, pf);
-        const float mtn = tile_max(sn, cjn);
-#pragma unroll
-        for (int i = 0; i < MF_PV; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        return mtn;
     }
 };
 
@@ -314,23 +328,24 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     for (int mm = 32; mm >= 1; mm /= 2) svmax = fmaxf(svmax, __shfl_xor(svmax, mm, 64));
     const float cq = Qs[min(q0, N - 1) / kQuantBlockRows] * c;
 
-    // Direct-load mapping (see fa_fwd16_kernel), chunk swizzle lds_swz8.
-    int grow[NIW], gcol[NIW];
+    // Tile copies: buffer loads straight into LDS (see fa_fwd16_kernel),
+    // chunk swizzle lds_swz8; rows at or past N read as zeros.
+    const i32x4 krs = make_rsrc(K, N * RB);
+    const i32x4 vrs = make_rsrc(V, N * RB);
+    uint32_t voff[NIW];
 #pragma unroll
     for (int j = 0; j < NIW; ++j) {
         const int p = (wave * NIW + j) * 1024 + 16 * lane;
-        grow[j] = p / RB;
-        gcol[j] = ((p % RB / 16) ^ lds_swz8<D>(grow[j])) * 16;
+        const int row = p / RB;
+        voff[j] = row * RB + ((p % RB / 16) ^ lds_swz8<D>(row)) * 16;
     }
     const int nkt_total = (N + BC - 1) / BC;
-    auto load_kv = [&](const uint8_t* src, int t, int slot) {
+    const uint32_t sbase = lds_addr(smem);
+    auto load_kv = [&](const i32x4& rs, int t, int slot) {
         if (t >= nkt_total) return;
-        char* dst = smem + slot * TB + wave_u * NIW * 1024;
+        const uint32_t dst = sbase + slot * TB + wave_u * NIW * 1024;
 #pragma unroll
-        for (int j = 0; j < NIW; ++j) {
-            const int key = min(t * BC + grow[j], N - 1);     // rows past N: any valid row
-            load_lds16(src + (size_t)key * D + gcol[j], dst + j * 1024);
-        }
+        for (int j = 0; j < NIW; ++j) buffer_load_lds16(rs, dst + j * 1024, voff[j], t * TB);
     };
     auto ktile = [&](int t) -> const char* { return smem + (t & 1) * TB; };
     auto vtile = [&](int t) -> const char* { return smem + (2 + (t & 1)) * TB; };
@@ -339,7 +354,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
         const int sblk = (t * BC) / kQuantBlockRows;
         const float wv = Vs[sblk] / svmax;                    // (0, 1]
         cj = cq * Ks[sblk];
-        bj = __builtin_amdgcn_logf(kPScale * wv);            // log2(16 w_j)
+        bj = __builtin_amdgcn_logf(kPScale * wv);            // log2(8 w_j)
         lscale = 1.0f / (kPScale * wv);
     };
 
@@ -359,6 +374,9 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
                            (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
         }
     }
+    // Q has landed before any tile copy is issued (a wait the compiler sees;
+    // see fa_fwd16_kernel).
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
 
     // Lane offsets into swizzled tiles.
     int ka[W::NKA][2], va[NVA];
@@ -384,37 +402,31 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     W st;
     st.init();
     f32x16 s[NKB];
-    float mt = -INFINITY;
 
-    load_kv(K, 0, 0);
-    load_kv(V, 0, 2);
-    load_kv(K, 1, 1);
+    load_kv(krs, 0, 0);
+    load_kv(vrs, 0, 2);
+    load_kv(krs, 1, 1);
     wait_vm_all();
     __syncthreads();
     if (nfull > 0) {
         float cj, bj, ls;
         tile_scales(0, cj, bj, ls);
         W::scores(s, ktile(0), ka, qf);
-        mt = W::tile_max(s, cj);
+        st.raise_max(W::tile_max(s, cj));    // first reference maximum: exact
         __syncthreads();                     // all waves done reading K_0's slot
     }
     int t = 0;
     for (; t + 1 < nfull; ++t) {
-        load_kv(K, t + 2, t & 1);
-        load_kv(V, t + 1, 2 + ((t + 1) & 1));
-        float cj, bj, lscale, cjn, bjn, lsn;
+        load_kv(krs, t + 2, t & 1);
+        load_kv(vrs, t + 1, 2 + ((t + 1) & 1));
+        float cj, bj, lscale;
         tile_scales(t, cj, bj, lscale);
-        tile_scales(t + 1, cjn, bjn, lsn);
-        st.rescale(mt);
-        f32x16 sn[NKB];
-        mt = st.overlap(s, sn, ktile(t + 1), ka, vtile(t), va, qf, cj, bj, lscale, cjn);
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) s[kb] = sn[kb];
+        st.step(s, ktile(t + 1), ka, vtile(t), va, qf, cj, bj, lscale);
         wait_vm_all();
         __syncthreads();
     }
     if (nfull > 0) {                          // last full tile
-        load_kv(V, t + 1, 2 + ((t + 1) & 1));
+        load_kv(vrs, t + 1, 2 + ((t + 1) & 1));
         float cj, bj, lscale;
         tile_scales(t, cj, bj, lscale);
         st.finish(s, vtile(t), va, cj, bj, lscale);
@@ -423,21 +435,22 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
         ++t;
     }
     for (; t < nkt; ++t) {                    // ragged end / causal diagonal
-        load_kv(K, t + 1, (t + 1) & 1);
-        load_kv(V, t + 1, 2 + ((t + 1) & 1));
+        load_kv(krs, t + 1, (t + 1) & 1);
+        load_kv(vrs, t + 1, 2 + ((t + 1) & 1));
         const int k0 = t * BC;
         if (!CAUSAL || k0 <= q0 + QW - 1) {
             float cj, bj, lscale;
             tile_scales(t, cj, bj, lscale);
             W::scores(s, ktile(t), ka, qf);
             W::template mask<CAUSAL>(s, k0, q0, N, hi, l32);
+            if (t == 0) st.raise_max(W::tile_max(s, cj));   // first reference maximum: exact
             st.finish(s, vtile(t), va, cj, bj, lscale);
         }
         wait_vm_all();
         __syncthreads();
     }
 
-    // ---- epilogue: O = O_acc * sv_max / (16 l), LSE = ln2 * (m + log2 l) ----
+    // ---- epilogue: O = O_acc * sv_max / (8 l), LSE = ln2 * (m + log2 l) ----
     const float l = pair_sum(st.l);
     const float inv = svmax / (kPScale * l);
     const int row = q0 + l32;
