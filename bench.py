@@ -71,6 +71,61 @@ def measured_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
+def traffic_summary(run_dir):
+    """Build the HBM-traffic summary of the dominant kernel from four
+    rocprofv3 counter runs under run_dir (pmc_FETCH_SIZE/{main,copy} and
+    pmc_WRITE_SIZE/{main,copy}, see TRAFFIC_COMMANDS) and write it to
+    TRAFFIC_FILE. FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by
+    what the same counter reads for a plain 1 GiB device copy."""
+    import csv
+
+    def per_dispatch(path, name_part):
+        vals = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if name_part in r["Kernel_Name"]:
+                    vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        return vals
+
+    out = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        main = per_dispatch(os.path.join(run_dir, f"pmc_{c}", "main_counter_collection.csv"),
+                            "fa_fwd16_kernel")
+        copy = per_dispatch(os.path.join(run_dir, f"pmc_{c}", "copy_counter_collection.csv"), "")
+        copy_kib = sorted(copy.values())[-2]          # median of the three 1 GiB copies
+        ideal_kib = (1 << 30) / 1024.0                # each copy reads and writes 1 GiB
+        out[c] = {"kib_per_dispatch": float(np.mean(list(main.values()))), "dispatches": len(main),
+                  "copy_kib": copy_kib, "scale": ideal_kib / copy_kib}
+    c = CONFIGS[MAIN]
+    B, H, N, d = c["B"], c["H"], c["N"], c["d"]
+    algorithmic = 4 * B * H * N * d * 2 + B * H * N * 4          # Q, K, V in, O out (bf16), LSE
+    fetch = out["FETCH_SIZE"]["kib_per_dispatch"] * 1024 * out["FETCH_SIZE"]["scale"]
+    write = out["WRITE_SIZE"]["kib_per_dispatch"] * 1024 * out["WRITE_SIZE"]["scale"]
+    summary = {
+        "kernel": "fa_fwd16_kernel<bf16, d=128, non-causal, bf16 out>",
+        "workload": "B=8 H=16 N=2048 d=128 bf16 non-causal forward (bench.py main leg)",
+        "commands": TRAFFIC_COMMANDS + [f"python3 bench.py --traffic-summary <out>"],
+        "counters": out,
+        "hbm_fetch_bytes_per_launch": fetch,
+        "hbm_write_bytes_per_launch": write,
+        "hbm_bytes_per_launch": fetch + write,
+        "algorithmic_bytes_per_launch": algorithmic,
+        "traffic_over_algorithmic": (fetch + write) / algorithmic,
+        "source_sha256": source_hash(),
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(summary, f, indent=1)
+    print(json.dumps(summary, indent=1))
+
+
+TRAFFIC_COMMANDS = [
+    "rocprofv3 --pmc FETCH_SIZE -d <out>/pmc_FETCH_SIZE -o main -f csv -- python3 bench.py --only-main --steps 3 --warmup 1 --no-cpu",
+    "rocprofv3 --pmc FETCH_SIZE -d <out>/pmc_FETCH_SIZE -o copy -f csv -- python3 bench.py --copy-calib",
+    "rocprofv3 --pmc WRITE_SIZE -d <out>/pmc_WRITE_SIZE -o main -f csv -- python3 bench.py --only-main --steps 3 --warmup 1 --no-cpu",
+    "rocprofv3 --pmc WRITE_SIZE -d <out>/pmc_WRITE_SIZE -o copy -f csv -- python3 bench.py --copy-calib",
+]
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -162,9 +217,14 @@ def main():
     ap.add_argument("--only-main", action="store_true",
                     help="only launch the bf16 non-causal forward (for counter runs)")
     ap.add_argument("--source-hash", action="store_true", help="print the kernel source hash")
+    ap.add_argument("--traffic-summary", metavar="DIR",
+                    help="write the HBM-traffic summary from the counter runs under DIR (no GPU)")
     args = ap.parse_args()
     if args.source_hash:
         print(source_hash())
+        return
+    if args.traffic_summary:
+        traffic_summary(args.traffic_summary)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
