@@ -19,7 +19,6 @@ Prints ONE JSON line on stdout.
 """
 
 import argparse
-import glob
 import hashlib
 import json
 import math
@@ -46,15 +45,24 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd16_b8h16n2k_d128_traffic.json"
 
 
 def source_hash():
-    """Hash of everything that defines the compiled kernels (sources, flags)."""
-    h = hashlib.sha256()
-    pkg = os.path.join(ROOT, "exact_attention_55_amd")
-    files = sorted(glob.glob(os.path.join(pkg, "csrc", "*"))) + [os.path.join(pkg, "build.py")]
-    for f in files:
-        h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()
+    """SHA-256 of the device code in the built library (the ELF section
+    .hip_fatbin of libfa.so): it changes exactly when the compiled kernels
+    change, not with comments or host-side code."""
+    import struct
+    path = os.path.join(ROOT, "exact_attention_55_amd", "libfa.so")
+    with open(path, "rb") as f:
+        elf = f.read()
+    shoff, = struct.unpack_from("<Q", elf, 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", elf, 0x3A)
+    def section(i):
+        name, _, _, _, off, size = struct.unpack_from("<IIQQQQ", elf, shoff + i * shentsize)
+        return name, off, size
+    _, stroff, _ = section(shstrndx)
+    for i in range(shnum):
+        name, off, size = section(i)
+        if elf[stroff + name:elf.index(b"\0", stroff + name)] == b".hip_fatbin":
+            return hashlib.sha256(elf[off:off + size]).hexdigest()
+    raise RuntimeError(f"no .hip_fatbin section in {path}")
 
 
 def measured_traffic():

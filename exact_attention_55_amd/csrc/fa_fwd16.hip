@@ -43,6 +43,16 @@
 //    with ones) normalises O, which makes O an exact convex combination of V
 //    rows even when one key dominates; l from the fp32 p gives the
 //    log-sum-exp, free of the 16-bit rounding of P.
+//  * Schedule ("FlashAttention-3: ...", "Overlapping GEMM and Softmax"): two
+//    waves share each SIMD, and inside a wave one step overlaps the score
+//    MFMAs of key tile j+1 with the exponentials of tile j, then runs the PV
+//    MFMAs of tile j. The step is written as a fixed instruction order
+//    (Wave16::step): every score MFMA is preceded by the LDS read of the K
+//    fragment four MFMAs ahead and followed by its share of exponentials,
+//    and every PV MFMA by the reads of the V^T fragment four ahead. The
+//    score phase runs at raised wave priority. FA16_SCHED=0 selects the
+//    earlier two-half schedule left to the compiler (Wave16::overlap), kept
+//    as an ablation.
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -53,7 +63,7 @@ namespace fa {
 // fp16 P (max 65504) and the fp32 accumulators hold with room to spare.
 constexpr float kBig = 16384.0f;
 
-#ifndef FA16_SCHED
+#ifndef FA16_SCHED                 // 1: hand-ordered step; 0: compiler-scheduled overlap
 #define FA16_SCHED 1
 #endif
 #ifndef FA16_KPD
