@@ -26,6 +26,7 @@ Modules:
     hadamard    fast Walsh-Hadamard transform with random signs
     fp8         OCP e4m3 ("fn") rounding / encoding from the format definition
     quant       block / per-tensor fp8 quantisation and fake-quant attention
+    backward    gradients dQ, dK, dV of exact attention (chain rule, materialised)
 
 Parity pins for every function live in tests/test_oracle_*.py. Functions whose
 result has no independent pin are marked "parity unpinned" in their docstring.
@@ -36,3 +37,4 @@ from .online import attention_online  # noqa: F401
 from .hadamard import fwht, random_sign_hadamard  # noqa: F401
 from .fp8 import e4m3_round, e4m3_encode, e4m3_decode, E4M3_MAX  # noqa: F401
 from .quant import fp8_quantize, fp8_dequantize, fake_quant_attention  # noqa: F401
+from .backward import attention_backward, attention_delta  # noqa: F401
