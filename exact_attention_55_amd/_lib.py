@@ -42,6 +42,8 @@ def lib():
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     L.fa_fwd.restype = i
+    L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    L.fa_bwd.restype = i
     L.fa_fp8_prep.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp]
     L.fa_fp8_prep.restype = i
     L.fa_fp8_packed_bytes.argtypes = [i, i, i, i]
@@ -73,6 +75,13 @@ def fwd_raw(q, k, v, o, lse, B, H, N, d, causal, softmax_scale, dtype, stream=No
     """Direct call with integer pointers; returns the status code."""
     return lib().fa_fwd(q, k, v, o, lse, B, H, N, d, int(causal), float(softmax_scale),
                         int(dtype), stream)
+
+
+def bwd_raw(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, causal, softmax_scale, dtype,
+            stream=None):
+    """Direct call with integer pointers; returns the status code."""
+    return lib().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, int(causal),
+                        float(softmax_scale), int(dtype), stream)
 
 
 def fp8_prep_raw(x, x8, signs, B, H, N, d, block_rows, in_dtype, stream=None):
@@ -131,6 +140,39 @@ def fwd(q, k, v, causal=False, softmax_scale=None, out=None, lse=None, out_f32=F
     if st != FA_OK:
         raise FaError(st, "fa_fwd")
     return out, lse
+
+
+def bwd(q, k, v, o, lse, dout, causal=False, softmax_scale=None, out_f32=False, grads=None,
+        delta=None):
+    """Gradients (dq, dk, dv) of the forward on 16-bit [B,H,N,d] device tensors.
+
+    o and lse are the forward's outputs; dout is dL/do. The gradients have
+    q's dtype (float32 with out_f32=True). delta is the float32 [B,H,N]
+    scratch the call overwrites (allocated when not given).
+    """
+    B, H, N, d = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    code = _dtype_code(q)
+    gdt = torch.float32 if out_f32 else q.dtype
+    if grads is None:
+        grads = tuple(torch.empty((B, H, N, d), dtype=gdt, device=q.device) for _ in range(3))
+    dq, dk, dv = grads
+    if delta is None:
+        delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out_f32:
+        code |= FA_OUT_F32
+    _check(q.dim() == 4 and all(t.shape == q.shape for t in (k, v, o, dout)), "shapes differ")
+    _check(all(t.dtype == q.dtype for t in (k, v, o, dout)), "dtypes differ")
+    _check(all(t.shape == q.shape and t.dtype == gdt for t in grads), "bad gradient tensors")
+    _check(lse.shape == (B, H, N) and lse.dtype == torch.float32, "bad lse tensor")
+    _check(delta.shape == (B, H, N) and delta.dtype == torch.float32, "bad delta tensor")
+    _check_device(q, k, v, o, lse, dout, dq, dk, dv, delta)
+    st = bwd_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                 _ptr(dv), _ptr(delta), B, H, N, d, causal, softmax_scale, code, _stream(q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv
 
 
 def fp8_alloc_packed(B, H, N, d, device):

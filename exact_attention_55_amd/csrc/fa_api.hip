@@ -82,6 +82,38 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     return from_hip(fa::launch_fwd16(a, base == FA_BF16, s));
 }
 
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int N,
+           int d, int causal, float softmax_scale, int dtype, void* stream) {
+    const int base = dtype & 0xff;
+    const int flags = dtype & ~0xff;
+    if ((flags & ~FA_OUT_F32) != 0) return FA_ERR_INVALID_ARG;
+    if (base != FA_F16 && base != FA_BF16) return FA_ERR_INVALID_ARG;
+    if (!sizes_ok(B, H, N, d)) return FA_ERR_INVALID_ARG;
+    if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * H > 0x7fffffffLL / 2) return FA_ERR_UNSUPPORTED;
+    if ((long long)N * d * 2 > kMaxHeadBytes) return FA_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0 || N == 0) return FA_OK;
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta)
+        return FA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+        !aligned(lse, 4) || !aligned(delta, 4))
+        return FA_ERR_INVALID_ARG;
+
+    fa::BwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.delta = delta;
+    a.B = B; a.H = H; a.N = N; a.d = d;
+    a.causal = causal != 0;
+    a.scale = softmax_scale;
+    a.out_f32 = (flags & FA_OUT_F32) != 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    return from_hip(fa::launch_bwd16(a, base == FA_BF16, s));
+}
+
 int fa_fp8_prep(const void* x, void* x8, const int8_t* signs, int B, int H, int N, int d,
                 int block_rows, int in_dtype, void* stream) {
     if (in_dtype != FA_BF16 && in_dtype != FA_F16) return FA_ERR_INVALID_ARG;

@@ -1,0 +1,525 @@
+// fa_bwd16.hip - gradients of the fused attention forward (bf16 / fp16, gfx950).
+//
+// Method: the attention probabilities are not stored by the forward; they
+// are recomputed from Q, K and the saved per-row log-sum-exp ("FlashAttention
+// - one, two, three!" (Medium), section "FlashAttention v1.": recomputation
+// instead of keeping intermediate results, with a few per-row constants in
+// global memory). The gradient is the chain rule through the "Standard
+// Attention" definition of O = softmax(scale * Q K^T) V (same page):
+//     P  = exp(scale * Q K^T - LSE)        (recomputed per tile)
+//     dV = P^T dO,   dP = dO V^T,   D_i = sum_c dO_ic O_ic,
+//     dS = P * (dP - D),   dQ = scale * dS K,   dK = scale * dS^T Q.
+//
+// Three kernels, no atomics and no scratch beyond the caller's D array:
+//  * bwd_delta_kernel: D = rowsum(dO * O) in fp32.
+//  * bwd_dq_kernel (one workgroup per 128 query rows, the forward's
+//    structure): per key tile S^T = K Q^T and dP^T = V dO^T with K and V
+//    rows read from LDS, dS^T in registers, dQ^T += K^T dS^T with K^T read
+//    from the same LDS tile by transposing reads.
+//  * bwd_dkv_kernel (one workgroup per 128 keys, the mirror image): per
+//    query tile S = Q K^T and dP = dO V^T with Q and dO rows from LDS,
+//    dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T by transposing
+//    reads. This costs two more GEMMs than a single pass with atomic dQ
+//    updates (7 instead of 5 per tile pair) and keeps the result
+//    deterministic.
+// Tiles go global -> LDS by buffer loads (see fa_fwd16.hip); the LDS
+// swizzle, the row permutation of the A operand (krow_perm) and the lane
+// layouts are those of the forward.
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+template <typename T> struct Bw;
+template <> struct Bw<__bf16> {
+    using x8 = bf16x8;
+    using x2 = bf16x2;
+    static __device__ __forceinline__ x2 pack(float a, float b) { return x2{(__bf16)a, (__bf16)b}; }
+};
+template <> struct Bw<_Float16> {
+    using x8 = f16x8;
+    using x2 = f16x2;
+    static __device__ __forceinline__ x2 pack(float a, float b) { return x2{(_Float16)a, (_Float16)b}; }
+};
+
+// Shared tile geometry: rows of 2*D bytes, 16-byte chunks XOR-swizzled with
+// lds_swz16<D>. kfrag: A-operand fragment of a 32-row block, rows permuted
+// by krow_perm (so that accumulator runs of 8 registers are 8 consecutive
+// rows); tfrag: transposed A-operand fragment (d rows x 16 tile rows) by
+// two transposing reads.
+template <typename T, int D>
+struct Tile {
+    using X8 = typename Bw<T>::x8;
+    static constexpr int RB = 2 * D;
+    static constexpr int NCH = D / 16;
+    static constexpr int NDB = D / 32;
+    static constexpr int NKA = (D == 64) ? 4 : 8;
+    static constexpr int NVA = (D == 64) ? 2 : 4;
+
+    // row-fragment lane offsets (ka) and transposed-fragment offsets (va, vstep)
+    int ka[NKA], va[NVA], vstep;
+
+    __device__ __forceinline__ void init(int lane) {
+        const int l32 = lane & 31, hi = lane >> 5;
+        const int kr = krow_perm(l32);
+#pragma unroll
+        for (int ch = 0; ch < NKA; ++ch) ka[ch] = kr * RB + (((2 * ch + hi) ^ lds_swz16<D>(kr)) * 16);
+        const int vr = 8 * hi + (lane & 15) / 4;
+#pragma unroll
+        for (int db = 0; db < NVA; ++db) {
+            const int chunk = 4 * db + 2 * (l32 / 16) + ((lane & 3) >> 1);
+            va[db] = vr * RB + ((chunk ^ lds_swz16<D>(vr)) * 16) + 8 * (lane & 1);
+        }
+        vstep = 4 * RB + (((lane & 3) >> 1) ? -16 : 16);
+    }
+    __device__ __forceinline__ X8 kfrag(const char* tl, int ch, int blk) const {
+        return load16<X8>(tl + ka[ch % NKA] + NKA * 32 * (ch / NKA) + 32 * blk * RB);
+    }
+    // rows 16*t + 8*hi + (0..7) of d-block db
+    __device__ __forceinline__ X8 tfrag(const char* tl, int t, int db) const {
+        const char* p = tl + va[db % NVA] + NVA * 64 * (db / NVA) + 16 * t * RB;
+        const u32x2 lo = lds_read_tr16(p);
+        const u32x2 hi4 = lds_read_tr16(p + vstep);
+        return __builtin_bit_cast(X8, u32x4{lo[0], lo[1], hi4[0], hi4[1]});
+    }
+};
+
+// Global -> LDS tile copies for a [rows, D] tile of one head (see fa_fwd16).
+template <int D, int TROWS, int NW>
+struct Copier {
+    static constexpr int RB = 2 * D;
+    static constexpr int TB = TROWS * RB;
+    static constexpr int NIW = TB / 1024 / NW;
+    static_assert(TB % (1024 * NW) == 0, "tile must split into 1 KB loads per wave");
+    uint32_t voff[NIW];
+    uint32_t dst0;
+    __device__ __forceinline__ void init(int wave, int lane, uint32_t sbase, int wave_u) {
+#pragma unroll
+        for (int j = 0; j < NIW; ++j) {
+            const int p = (wave * NIW + j) * 1024 + 16 * lane;
+            const int row = p / RB;
+            voff[j] = row * RB + ((p % RB / 16) ^ lds_swz16<D>(row)) * 16;
+        }
+        dst0 = sbase + wave_u * NIW * 1024;
+    }
+    __device__ __forceinline__ void issue(const i32x4& rs, int tile, int slot) const {
+#pragma unroll
+        for (int j = 0; j < NIW; ++j) buffer_load_lds16(rs, dst0 + slot * TB + j * 1024, voff[j], tile * TB);
+    }
+};
+
+// Workgroup -> (head, tile): consecutive workgroups land on different XCDs;
+// regroup so each XCD walks whole heads.
+__device__ __forceinline__ int xcd_block(int num_blocks) {
+    int bid = blockIdx.x;
+    if ((num_blocks & 7) == 0) bid = (bid & 7) * (num_blocks >> 3) + (bid >> 3);
+    return bid;
+}
+
+// 16-bit row of the head-major output for the transposed accumulator of a
+// lane (lane = row, register r of d-block db = column 32*db + 8*(r/4) +
+// 4*hi + r%4), scaled.
+template <typename T, int D, bool OUT_F32>
+__device__ __forceinline__ void store_rowT(void* out, size_t off_row, const f32x16 (&acc)[D / 32],
+                                           float mul, int hi) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const size_t off = off_row + 32 * db + 8 * j + 4 * hi;
+            const float v0 = acc[db][4 * j] * mul, v1 = acc[db][4 * j + 1] * mul;
+            const float v2 = acc[db][4 * j + 2] * mul, v3 = acc[db][4 * j + 3] * mul;
+            if (OUT_F32) {
+                *reinterpret_cast<f32x4*>(static_cast<float*>(out) + off) = f32x4{v0, v1, v2, v3};
+            } else {
+                const auto a = Bw<T>::pack(v0, v1), b = Bw<T>::pack(v2, v3);
+                *reinterpret_cast<u32x2*>(static_cast<T*>(out) + off) =
+                    u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
+// D = rowsum(dO * O): 8 lanes of 8 elements (d = 64) or 16 lanes (d = 128)
+// per row, fp32 accumulation.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) bwd_delta_kernel(const T* __restrict__ O, const T* __restrict__ dO,
+                                                        float* __restrict__ Dout, long long rows) {
+    using X8 = typename Bw<T>::x8;
+    constexpr int LPR = D / 8;                         // lanes per row
+    const long long tid = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long row = tid / LPR;
+    const int part = (int)(tid % LPR);
+    float acc = 0.f;
+    if (row < rows) {
+        const X8 a = load16<X8>(O + row * D + 8 * part);
+        const X8 b = load16<X8>(dO + row * D + 8 * part);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc = fmaf((float)a[i], (float)b[i], acc);
+    }
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m, 64);
+    if (row < rows && part == 0) Dout[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup = 4 waves x 32 query rows; key tiles of 64.
+template <typename T, int D, bool CAUSAL, bool OUT_F32>
+__global__ void __launch_bounds__(256, 2)
+bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
+              const T* __restrict__ dOg, const float* __restrict__ LSEg, const float* __restrict__ Dg,
+              void* __restrict__ dQg, int N, int num_qtiles, int num_blocks, float c, float scale)
+{
+    using X8 = typename Bw<T>::x8;
+    using TL = Tile<T, D>;
+    constexpr int NW = 4, QW = 32, BR = NW * QW, BC = 64;
+    constexpr int NCH = TL::NCH, NDB = TL::NDB, RB = TL::RB;
+    constexpr int NKB = BC / 32, NPV = BC / 16;
+    using CP = Copier<D, BC, NW>;
+    constexpr int TB = CP::TB;
+    __shared__ __attribute__((aligned(1024))) char smem[4 * TB];   // K: slots 0,1; V: 2,3
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+    if (num_blocks < 0) smem[tid] = 0;     // keeps the LDS reads alive (tiles come by DMA)
+
+    const int bid = xcd_block(num_blocks);
+    const int bh = bid / num_qtiles;
+    int qt = bid - bh * num_qtiles;
+    if (CAUSAL) qt = num_qtiles - 1 - qt;
+    const size_t head = (size_t)bh * N * D;
+    const int qtile0 = qt * BR, q0 = qtile0 + wave * QW;
+    const int row = q0 + l32;
+
+    const uint32_t sbase = lds_addr(smem);
+    CP cp;
+    cp.init(wave, lane, sbase, wave_uniform(wave));
+    const i32x4 krs = make_rsrc(Kg + head, N * RB), vrs = make_rsrc(Vg + head, N * RB);
+    const int nkt_total = (N + BC - 1) / BC;
+    auto load_kv = [&](int t) {
+        if (t < nkt_total) {
+            cp.issue(krs, t, t & 1);
+            cp.issue(vrs, t, 2 + (t & 1));
+        }
+    };
+    auto ktile = [&](int t) -> const char* { return smem + (t & 1) * TB; };
+    auto vtile = [&](int t) -> const char* { return smem + (2 + (t & 1)) * TB; };
+
+    // Q^T and dO^T fragments (B operands): lane = query, d = 16*ch + 8*hi .. +7
+    X8 qf[NCH], of[NCH];
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+        const X8 z = __builtin_bit_cast(X8, u32x4{0, 0, 0, 0});
+        qf[ch] = row < N ? load16<X8>(Qg + head + (size_t)row * D + 16 * ch + 8 * hi) : z;
+        of[ch] = row < N ? load16<X8>(dOg + head + (size_t)row * D + 16 * ch + 8 * hi) : z;
+    }
+    const float lse2 = row < N ? LSEg[(size_t)bh * N + row] * kLog2e : 0.f;
+    const float dd = row < N ? Dg[(size_t)bh * N + row] : 0.f;
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+
+    TL tl;
+    tl.init(lane);
+    f32x16 acc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+
+    const int kend = CAUSAL ? min(N, qtile0 + BR) : N;
+    const int nkt = (kend + BC - 1) / BC;
+    load_kv(0);
+    wait_vm_all();
+    __syncthreads();
+    for (int t = 0; t < nkt; ++t) {
+        load_kv(t + 1);
+        const int k0 = t * BC;
+        if (!CAUSAL || k0 <= q0 + QW - 1) {
+            // S^T = K Q^T and dP^T = V dO^T (lane = query, registers = keys)
+            f32x16 s[NKB], dp[NKB];
+            {
+                X8 kf[NKB][NCH];
+#pragma unroll
+                for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb) kf[kb][ch] = tl.kfrag(ktile(t), ch, kb);
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+                for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma32(kf[kb][ch], qf[ch], s[kb]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            {
+                X8 vf[NKB][NCH];
+#pragma unroll
+                for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb) vf[kb][ch] = tl.kfrag(vtile(t), ch, kb);
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) dp[kb] = f32x16{};
+#pragma unroll
+                for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb) dp[kb] = mfma32(vf[kb][ch], of[ch], dp[kb]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // dS^T = P^T (dP^T - D), P^T = exp2(c S^T - lse2); masked keys give 0
+            const bool masked = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0);
+            X8 dsf[NPV];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    typename Bw<T>::x2 w[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float x[2];
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            const int r = 8 * h + 2 * j + e;
+                            float p = exp2_hw(fmaf(s[kb][r], c, -lse2));
+                            if (masked) {
+                                const int key = k0 + key_of(kb, r, hi);
+                                if (key >= N || (CAUSAL && key > row)) p = 0.f;
+                            }
+                            x[e] = p * (dp[kb][r] - dd);
+                        }
+                        w[j] = Bw<T>::pack(x[0], x[1]);
+                    }
+                    dsf[2 * kb + h] = X8{w[0][0], w[0][1], w[1][0], w[1][1],
+                                         w[2][0], w[2][1], w[3][0], w[3][1]};
+                }
+            __builtin_amdgcn_sched_barrier(0);
+            // dQ^T += K^T dS^T
+#pragma unroll
+            for (int tt = 0; tt < NPV; ++tt) {
+                X8 kt[NDB];
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) kt[db] = tl.tfrag(ktile(t), tt, db);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) acc[db] = mfma32(kt[db], dsf[tt], acc[db]);
+            }
+        }
+        wait_vm_all();
+        __syncthreads();
+    }
+    if (row < N) store_rowT<T, D, OUT_F32>(dQg, head + (size_t)row * D, acc, scale, hi);
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup = 4 waves x 32 keys; query tiles of 32. One wave per
+// SIMD (the two 32 x d accumulators and the K, V operands need ~300
+// registers).
+template <typename T, int D, bool CAUSAL, bool OUT_F32>
+__global__ void __launch_bounds__(256, 1)
+bwd_dkv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
+               const T* __restrict__ dOg, const float* __restrict__ LSEg, const float* __restrict__ Dg,
+               void* __restrict__ dKg, void* __restrict__ dVg, int N, int num_ktiles,
+               int num_blocks, float c, float scale)
+{
+    using X8 = typename Bw<T>::x8;
+    using TL = Tile<T, D>;
+    constexpr int NW = 4, KW = 32, BK = NW * KW, BQ = 32;
+    constexpr int NCH = TL::NCH, NDB = TL::NDB, RB = TL::RB;
+    constexpr int NPV = BQ / 16;
+    using CP = Copier<D, BQ, NW>;
+    constexpr int TB = CP::TB;
+    __shared__ __attribute__((aligned(1024))) char smem[4 * TB];   // Q: slots 0,1; dO: 2,3
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+    if (num_blocks < 0) smem[tid] = 0;
+
+    const int bid = xcd_block(num_blocks);
+    const int bh = bid / num_ktiles;
+    const int kt = bid - bh * num_ktiles;
+    const size_t head = (size_t)bh * N * D;
+    const int kblk0 = kt * BK, k0 = kblk0 + wave * KW;
+    const int key = k0 + l32;
+
+    const uint32_t sbase = lds_addr(smem);
+    CP cp;
+    cp.init(wave, lane, sbase, wave_uniform(wave));
+    const i32x4 qrs = make_rsrc(Qg + head, N * RB), ors = make_rsrc(dOg + head, N * RB);
+    const int nqt = (N + BQ - 1) / BQ;
+    auto load_qo = [&](int i) {
+        if (i < nqt) {
+            cp.issue(qrs, i, i & 1);
+            cp.issue(ors, i, 2 + (i & 1));
+        }
+    };
+    auto qtile = [&](int i) -> const char* { return smem + (i & 1) * TB; };
+    auto otile = [&](int i) -> const char* { return smem + (2 + (i & 1)) * TB; };
+
+    // K^T and V^T fragments (B operands): lane = key, d = 16*ch + 8*hi .. +7
+    X8 kf[NCH], vf[NCH];
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+        const X8 z = __builtin_bit_cast(X8, u32x4{0, 0, 0, 0});
+        kf[ch] = key < N ? load16<X8>(Kg + head + (size_t)key * D + 16 * ch + 8 * hi) : z;
+        vf[ch] = key < N ? load16<X8>(Vg + head + (size_t)key * D + 16 * ch + 8 * hi) : z;
+    }
+    // per-row LSE and D of a query tile, range-checked (rows >= N read 0):
+    // register r of a lane half holds row 16*(r/8) + 8*hi + r%8 of the tile
+    const __amdgpu_buffer_rsrc_t lrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(LSEg + (size_t)bh * N), (short)0, N * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t drs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Dg + (size_t)bh * N), (short)0, N * 4, 0x00020000);
+    auto row_consts = [&](int i, float (&lv)[16], float (&dv)[16]) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int off = (i * BQ + 16 * (g / 2) + 8 * hi + 4 * (g % 2)) * 4;
+            const f32x4 a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(lrs, off, 0, 0));
+            const f32x4 b = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(drs, off, 0, 0));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                lv[4 * g + e] = a[e] * kLog2e;
+                dv[4 * g + e] = b[e];
+            }
+        }
+    };
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+
+    TL tl;
+    tl.init(lane);
+    f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dk[db] = dv[db] = f32x16{};
+
+    const int i0 = CAUSAL ? kblk0 / BQ : 0;
+    float lc[16], dc[16];
+    row_consts(i0, lc, dc);
+    load_qo(i0);
+    wait_vm_all();
+    __syncthreads();
+    for (int i = i0; i < nqt; ++i) {
+        float ln[16], dn[16];
+        row_consts(i + 1, ln, dn);                 // next tile's constants (range-checked)
+        load_qo(i + 1);
+        const int q0 = i * BQ;
+        if (!CAUSAL || q0 + BQ - 1 >= k0) {        // this wave has a visible pair
+            // S = Q K^T and dP = dO V^T (lane = key, registers = queries)
+            f32x16 s = f32x16{}, dp = f32x16{};
+            {
+                X8 qa[NCH];
+#pragma unroll
+                for (int ch = 0; ch < NCH; ++ch) qa[ch] = tl.kfrag(qtile(i), ch, 0);
+#pragma unroll
+                for (int ch = 0; ch < NCH; ++ch) s = mfma32(qa[ch], kf[ch], s);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            {
+                X8 oa[NCH];
+#pragma unroll
+                for (int ch = 0; ch < NCH; ++ch) oa[ch] = tl.kfrag(otile(i), ch, 0);
+#pragma unroll
+                for (int ch = 0; ch < NCH; ++ch) dp = mfma32(oa[ch], vf[ch], dp);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            const bool masked = (q0 + BQ > N) || (CAUSAL && q0 < k0 + KW - 1);
+            X8 pf[NPV], dsf[NPV];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                typename Bw<T>::x2 wp[4], wd[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float p2[2], d2[2];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int r = 8 * h + 2 * j + e;
+                        float p = exp2_hw(fmaf(s[r], c, -lc[r]));
+                        if (masked) {
+                            const int q = q0 + key_of(0, r, hi);
+                            if (q >= N || (CAUSAL && key > q)) p = 0.f;
+                        }
+                        p2[e] = p;
+                        d2[e] = p * (dp[r] - dc[r]);
+                    }
+                    wp[j] = Bw<T>::pack(p2[0], p2[1]);
+                    wd[j] = Bw<T>::pack(d2[0], d2[1]);
+                }
+                pf[h] = X8{wp[0][0], wp[0][1], wp[1][0], wp[1][1], wp[2][0], wp[2][1], wp[3][0], wp[3][1]};
+                dsf[h] = X8{wd[0][0], wd[0][1], wd[1][0], wd[1][1], wd[2][0], wd[2][1], wd[3][0], wd[3][1]};
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // dV^T += dO^T P,  dK^T += Q^T dS
+#pragma unroll
+            for (int tt = 0; tt < NPV; ++tt) {
+                X8 ot[NDB], qt[NDB];
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    ot[db] = tl.tfrag(otile(i), tt, db);
+                    qt[db] = tl.tfrag(qtile(i), tt, db);
+                }
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    dv[db] = mfma32(ot[db], pf[tt], dv[db]);
+                    dk[db] = mfma32(qt[db], dsf[tt], dk[db]);
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            lc[r] = ln[r];
+            dc[r] = dn[r];
+        }
+        wait_vm_all();
+        __syncthreads();
+    }
+    if (key < N) {
+        store_rowT<T, D, OUT_F32>(dKg, head + (size_t)key * D, dk, scale, hi);
+        store_rowT<T, D, OUT_F32>(dVg, head + (size_t)key * D, dv, 1.0f, hi);
+    }
+}
+
+template <typename T, int D, bool CAUSAL, bool OUT_F32>
+hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
+    const long long rows = (long long)a.B * a.H * a.N;
+    const long long nthr = rows * (D / 8);
+    hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const T*>(a.o), static_cast<const T*>(a.dout), a.delta, rows);
+    const float c = a.scale * kLog2e;
+    {
+        const int nqt = (a.N + 127) / 128;
+        const long long nblk = (long long)nqt * a.B * a.H;
+        if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, OUT_F32>), dim3((unsigned)nblk), dim3(256), 0, s,
+                           static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                           static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
+                           a.dq, a.N, nqt, (int)nblk, c, a.scale);
+    }
+    {
+        const int nkt = (a.N + 127) / 128;
+        const long long nblk = (long long)nkt * a.B * a.H;
+        if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((bwd_dkv_kernel<T, D, CAUSAL, OUT_F32>), dim3((unsigned)nblk), dim3(256), 0, s,
+                           static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                           static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
+                           a.dk, a.dv, a.N, nkt, (int)nblk, c, a.scale);
+    }
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_d(const BwdArgs& a, hipStream_t s) {
+    if (a.causal)
+        return a.out_f32 ? launch_t<T, D, true, true>(a, s) : launch_t<T, D, true, false>(a, s);
+    return a.out_f32 ? launch_t<T, D, false, true>(a, s) : launch_t<T, D, false, false>(a, s);
+}
+
+template <typename T>
+hipError_t launch_ty(const BwdArgs& a, hipStream_t s) {
+    switch (a.d) {
+        case 64: return launch_d<T, 64>(a, s);
+        case 128: return launch_d<T, 128>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_bwd16(const BwdArgs& a, bool bf16, hipStream_t s) {
+    return bf16 ? launch_ty<__bf16>(a, s) : launch_ty<_Float16>(a, s);
+}
+
+}  // namespace fa

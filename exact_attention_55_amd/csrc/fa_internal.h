@@ -41,6 +41,25 @@ struct PrepArgs {
 };
 hipError_t launch_fp8_prep(const PrepArgs& a, hipStream_t s);
 
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const float* lse;
+    const void* dout;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* delta;       // caller scratch [B][H][N]: rowsum(dO * O)
+    int B, H, N, d;
+    bool causal;
+    float scale;
+    bool out_f32;       // gradients as float32
+};
+// 16-bit backward (bf16 = true: bfloat16, else float16), d = 64 or 128.
+hipError_t launch_bwd16(const BwdArgs& a, bool bf16, hipStream_t s);
+
 inline size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
 
 }  // namespace fa

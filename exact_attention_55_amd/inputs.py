@@ -53,6 +53,14 @@ def make_qkv(B, H, N, d, seed, dtype="bf16", outliers=False, p_outlier=1e-3,
     return tuple(torch.from_numpy(x).to(tdt) for x in base)
 
 
+def make_dout(B, H, N, d, seed, dtype="bf16"):
+    """Upstream gradient dL/dO for the backward: float32 standard normals
+    [B,H,N,d] from default_rng(seed), one RNE cast to the 16-bit dtype."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    return torch.from_numpy(x).to(TORCH_DTYPES[dtype])
+
+
 def make_signs(H, d, seed):
     """+-1 sign vectors [H, d] int8 for the random-sign Hadamard."""
     rng = np.random.default_rng(seed + 1000)

@@ -90,6 +90,37 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            void* stream);
 
 /*
+ * fa_bwd - gradients dQ, dK, dV of the 16-bit forward.
+ *
+ * Recomputes the attention probabilities from q, k and the forward's log-sum-
+ * exp instead of storing them ("FlashAttention - one, two, three!",
+ * "FlashAttention v1.": recomputation for the backward pass); the gradient
+ * is the chain rule through softmax(softmax_scale * Q K^T) V:
+ *   dV = P^T dO, dP = dO V^T, D = rowsum(dO * O), dS = P * (dP - D),
+ *   dQ = softmax_scale * dS K, dK = softmax_scale * dS^T Q.
+ *
+ *  q, k, v  the forward's 16-bit inputs [B][H][N][d] (dtype FA_F16 or
+ *           FA_BF16), 16-byte aligned.
+ *  o, lse   the forward's output (same dtype) and log-sum-exp [B][H][N].
+ *  dout     gradient of the loss with respect to o, [B][H][N][d], same dtype.
+ *  dq, dk, dv  outputs [B][H][N][d]: the input dtype, or float32 when
+ *           FA_OUT_F32 is set in dtype. 16-byte aligned.
+ *  delta    caller-owned scratch, float32 [B][H][N], 4-byte aligned;
+ *           overwritten with rowsum(dout * o).
+ *  B, H, N, causal, softmax_scale  as for fa_fwd.
+ *  d        64 or 128 (256 returns FA_ERR_UNSUPPORTED).
+ *  stream   hipStream_t or NULL.
+ *
+ * Launches three kernels on stream (D, then dQ, then dK/dV); no atomics, so
+ * the result is deterministic. Returns FA_OK, FA_ERR_INVALID_ARG,
+ * FA_ERR_UNSUPPORTED or FA_ERR_HIP.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, float* delta,
+           int B, int H, int N, int d, int causal, float softmax_scale, int dtype,
+           void* stream);
+
+/*
  * fa_fp8_prep - incoherent processing + FP8 block quantisation of one tensor.
  *
  *  x        16-bit input [B][H][N][d] (in_dtype FA_BF16 or FA_F16), 16-byte
