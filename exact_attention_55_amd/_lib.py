@@ -147,8 +147,9 @@ def bwd(q, k, v, o, lse, dout, causal=False, softmax_scale=None, out_f32=False, 
     """Gradients (dq, dk, dv) of the forward on 16-bit [B,H,N,d] device tensors.
 
     o and lse are the forward's outputs; dout is dL/do. The gradients have
-    q's dtype (float32 with out_f32=True). delta is the float32 [B,H,N]
-    scratch the call overwrites (allocated when not given).
+    q's dtype (float32 with out_f32=True). delta is the float32 [2,B,H,N]
+    scratch of per-row constants the call overwrites (allocated when not
+    given).
     """
     B, H, N, d = q.shape
     if softmax_scale is None:
@@ -159,14 +160,14 @@ def bwd(q, k, v, o, lse, dout, causal=False, softmax_scale=None, out_f32=False, 
         grads = tuple(torch.empty((B, H, N, d), dtype=gdt, device=q.device) for _ in range(3))
     dq, dk, dv = grads
     if delta is None:
-        delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        delta = torch.empty((2, B, H, N), dtype=torch.float32, device=q.device)
     if out_f32:
         code |= FA_OUT_F32
     _check(q.dim() == 4 and all(t.shape == q.shape for t in (k, v, o, dout)), "shapes differ")
     _check(all(t.dtype == q.dtype for t in (k, v, o, dout)), "dtypes differ")
     _check(all(t.shape == q.shape and t.dtype == gdt for t in grads), "bad gradient tensors")
     _check(lse.shape == (B, H, N) and lse.dtype == torch.float32, "bad lse tensor")
-    _check(delta.shape == (B, H, N) and delta.dtype == torch.float32, "bad delta tensor")
+    _check(delta.shape == (2, B, H, N) and delta.dtype == torch.float32, "bad delta tensor")
     _check_device(q, k, v, o, lse, dout, dq, dk, dv, delta)
     st = bwd_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
                  _ptr(dv), _ptr(delta), B, H, N, d, causal, softmax_scale, code, _stream(q.device))

@@ -99,7 +99,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
         return FA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
         !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
-        !aligned(lse, 4) || !aligned(delta, 4))
+        !aligned(lse, 4) || !aligned(delta, 16))
         return FA_ERR_INVALID_ARG;
 
     fa::BwdArgs a;

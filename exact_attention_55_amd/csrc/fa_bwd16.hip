@@ -10,14 +10,16 @@
 //     dV = P^T dO,   dP = dO V^T,   D_i = sum_c dO_ic O_ic,
 //     dS = P * (dP - D),   dQ = scale * dS K,   dK = scale * dS^T Q.
 //
-// Three kernels, no atomics and no scratch beyond the caller's D array:
-//  * bwd_delta_kernel: D = rowsum(dO * O) in fp32.
+// Three kernels, no atomics and no scratch beyond the caller's row-constant
+// array (D and -LSE/scale, 2 floats per row):
+//  * bwd_delta_kernel: D = rowsum(dO * O) in fp32, and -LSE / scale.
 //  * bwd_dq_kernel (one workgroup per 128 query rows, the forward's
 //    structure): per key tile S^T = K Q^T and dP^T = V dO^T with K and V
 //    rows read from LDS, dS^T in registers, dQ^T += K^T dS^T with K^T read
 //    from the same LDS tile by transposing reads.
 //  * bwd_dkv_kernel (one workgroup per 128 keys, the mirror image): per
-//    query tile S = Q K^T and dP = dO V^T with Q and dO rows from LDS,
+//    query tile S = Q K^T and dP = dO V^T with Q and dO rows from LDS
+//    (accumulators started from the row constants),
 //    dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T by transposing
 //    reads. This costs two more GEMMs than a single pass with atomic dQ
 //    updates (7 instead of 5 per tile pair) and keeps the result
@@ -141,11 +143,16 @@ __device__ __forceinline__ void store_rowT(void* out, size_t off_row, const f32x
 }
 
 // ---------------------------------------------------------------------------
-// D = rowsum(dO * O): 8 lanes of 8 elements (d = 64) or 16 lanes (d = 128)
-// per row, fp32 accumulation.
+// Per-row constants: D = rowsum(dO * O) (fp32, 8 lanes of 8 elements for
+// d = 64, 16 for d = 128) and Lr = -LSE / scale, the value the key-parallel
+// kernel starts its score accumulator from (so that scale * (acc) is the
+// log-probability). Both land in the caller's scratch: D at [0, rows),
+// Lr at [rows, 2 rows).
 template <typename T, int D>
 __global__ void __launch_bounds__(256) bwd_delta_kernel(const T* __restrict__ O, const T* __restrict__ dO,
-                                                        float* __restrict__ Dout, long long rows) {
+                                                        const float* __restrict__ LSE,
+                                                        float* __restrict__ Dout, long long rows,
+                                                        float inv_scale) {
     using X8 = typename Bw<T>::x8;
     constexpr int LPR = D / 8;                         // lanes per row
     const long long tid = (long long)blockIdx.x * 256 + threadIdx.x;
@@ -160,7 +167,10 @@ __global__ void __launch_bounds__(256) bwd_delta_kernel(const T* __restrict__ O,
     }
 #pragma unroll
     for (int m = LPR / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m, 64);
-    if (row < rows && part == 0) Dout[row] = acc;
+    if (row < rows && part == 0) {
+        Dout[row] = acc;
+        Dout[rows + row] = -LSE[row] * inv_scale;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -307,15 +317,18 @@ bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __res
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup = 4 waves x 32 keys; query tiles of 32. One wave per
-// SIMD (the two 32 x d accumulators and the K, V operands need ~300
-// registers).
+// dK, dV: one workgroup = 4 waves x 32 keys; query tiles of 32, two waves
+// per SIMD. Per tile the copies bring the Q and dO rows and the tile's row
+// constants Lr = -LSE/scale and D (1 KB each: rows beyond the tile are not
+// used) into LDS. The score accumulator starts from Lr and the dP
+// accumulator from -D (read from LDS into the accumulator registers), so
+// P = exp2(c * S') and dS = P * dP' need no per-row registers.
 template <typename T, int D, bool CAUSAL, bool OUT_F32>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(256, 2)
 bwd_dkv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
-               const T* __restrict__ dOg, const float* __restrict__ LSEg, const float* __restrict__ Dg,
-               void* __restrict__ dKg, void* __restrict__ dVg, int N, int num_ktiles,
-               int num_blocks, float c, float scale)
+               const T* __restrict__ dOg, const float* __restrict__ Cg, void* __restrict__ dKg,
+               void* __restrict__ dVg, int N, long long rows, int num_ktiles, int num_blocks,
+               float c, float scale)
 {
     using X8 = typename Bw<T>::x8;
     using TL = Tile<T, D>;
@@ -324,7 +337,12 @@ bwd_dkv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __re
     constexpr int NPV = BQ / 16;
     using CP = Copier<D, BQ, NW>;
     constexpr int TB = CP::TB;
-    __shared__ __attribute__((aligned(1024))) char smem[4 * TB];   // Q: slots 0,1; dO: 2,3
+    constexpr int CB = 1024;                 // bytes per row-constant slot
+    constexpr int VB = KW * RB;              // bytes of one wave's V rows
+    // Q: slots 0,1; dO: 2,3; then [parity][Lr, D] constant slots; then each
+    // wave's 32 V rows (B operand of dP, read per tile instead of held in
+    // registers)
+    __shared__ __attribute__((aligned(1024))) char smem[4 * TB + 4 * CB + NW * VB];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
@@ -335,50 +353,62 @@ bwd_dkv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __re
     const int kt = bid - bh * num_ktiles;
     const size_t head = (size_t)bh * N * D;
     const int kblk0 = kt * BK, k0 = kblk0 + wave * KW;
-    const int key = k0 + l32;
+    // lane -> key: permuted within the wave's 32 keys like the A-operand rows,
+    // so the K fragments in registers and the V fragments read from LDS (with
+    // the row-permuted fragment read) agree
+    const int key = k0 + krow_perm(l32);
 
     const uint32_t sbase = lds_addr(smem);
+    const int wave_u = wave_uniform(wave);
     CP cp;
-    cp.init(wave, lane, sbase, wave_uniform(wave));
+    cp.init(wave, lane, sbase, wave_u);
     const i32x4 qrs = make_rsrc(Qg + head, N * RB), ors = make_rsrc(dOg + head, N * RB);
+    const i32x4 lrs = make_rsrc(Cg + rows + (size_t)bh * N, N * 4);     // Lr of this head
+    const i32x4 drs = make_rsrc(Cg + (size_t)bh * N, N * 4);            // D of this head
+    const uint32_t cslot = sbase + 4 * TB;
     const int nqt = (N + BQ - 1) / BQ;
     auto load_qo = [&](int i) {
         if (i < nqt) {
             cp.issue(qrs, i, i & 1);
             cp.issue(ors, i, 2 + (i & 1));
+            if (wave_u == 0) {
+                const uint32_t dst = cslot + (i & 1) * 2 * CB;
+                buffer_load_lds16(lrs, dst, 16 * lane, i * BQ * 4);
+                buffer_load_lds16(drs, dst + CB, 16 * lane, i * BQ * 4);
+            }
         }
     };
     auto qtile = [&](int i) -> const char* { return smem + (i & 1) * TB; };
     auto otile = [&](int i) -> const char* { return smem + (2 + (i & 1)) * TB; };
+    // accumulator start: register r holds tile row 16*(r/8) + 8*hi + r%8
+    auto acc_init = [&](int i, int which, float sign) -> f32x16 {
+        const char* base = smem + 4 * TB + (i & 1) * 2 * CB + which * CB;
+        f32x16 a;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 v = load16<f32x4>(base + 4 * (16 * (g / 2) + 8 * hi + 4 * (g % 2)));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[4 * g + e] = sign * v[e];
+        }
+        return a;
+    };
 
-    // K^T and V^T fragments (B operands): lane = key, d = 16*ch + 8*hi .. +7
-    X8 kf[NCH], vf[NCH];
+    // K^T fragments (B operand of S): lane = key, d = 16*ch + 8*hi .. +7
+    X8 kf[NCH];
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
         const X8 z = __builtin_bit_cast(X8, u32x4{0, 0, 0, 0});
         kf[ch] = key < N ? load16<X8>(Kg + head + (size_t)key * D + 16 * ch + 8 * hi) : z;
-        vf[ch] = key < N ? load16<X8>(Vg + head + (size_t)key * D + 16 * ch + 8 * hi) : z;
     }
-    // per-row LSE and D of a query tile, range-checked (rows >= N read 0):
-    // register r of a lane half holds row 16*(r/8) + 8*hi + r%8 of the tile
-    const __amdgpu_buffer_rsrc_t lrs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(LSEg + (size_t)bh * N), (short)0, N * 4, 0x00020000);
-    const __amdgpu_buffer_rsrc_t drs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(Dg + (size_t)bh * N), (short)0, N * 4, 0x00020000);
-    auto row_consts = [&](int i, float (&lv)[16], float (&dv)[16]) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int off = (i * BQ + 16 * (g / 2) + 8 * hi + 4 * (g % 2)) * 4;
-            const f32x4 a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(lrs, off, 0, 0));
-            const f32x4 b = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(drs, off, 0, 0));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                lv[4 * g + e] = a[e] * kLog2e;
-                dv[4 * g + e] = b[e];
-            }
-        }
-    };
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    // this wave's V rows k0 .. k0+31 into its LDS slot (rows >= N read 0)
+    const char* vw = smem + 4 * TB + 4 * CB + wave * VB;
+    {
+        Copier<D, KW, 1> vcp;
+        vcp.init(0, lane, sbase + 4 * TB + 4 * CB + wave_u * VB, 0);
+        const i32x4 vrs = make_rsrc(Vg + head + (size_t)k0 * D, max(N - k0, 0) * RB);
+        vcp.issue(vrs, 0, 0);
+    }
 
     TL tl;
     tl.init(lane);
@@ -387,35 +417,38 @@ bwd_dkv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __re
     for (int db = 0; db < NDB; ++db) dk[db] = dv[db] = f32x16{};
 
     const int i0 = CAUSAL ? kblk0 / BQ : 0;
-    float lc[16], dc[16];
-    row_consts(i0, lc, dc);
     load_qo(i0);
     wait_vm_all();
     __syncthreads();
     for (int i = i0; i < nqt; ++i) {
-        float ln[16], dn[16];
-        row_consts(i + 1, ln, dn);                 // next tile's constants (range-checked)
         load_qo(i + 1);
         const int q0 = i * BQ;
         if (!CAUSAL || q0 + BQ - 1 >= k0) {        // this wave has a visible pair
-            // S = Q K^T and dP = dO V^T (lane = key, registers = queries)
-            f32x16 s = f32x16{}, dp = f32x16{};
-            {
-                X8 qa[NCH];
+            // S' = Q K^T + Lr and dP' = dO V^T - D (lane = key, registers =
+            // queries); operands in half batches to bound the live registers
+            f32x16 s = acc_init(i, 0, 1.0f);
 #pragma unroll
-                for (int ch = 0; ch < NCH; ++ch) qa[ch] = tl.kfrag(qtile(i), ch, 0);
+            for (int half = 0; half < 2; ++half) {
+                X8 qa[NCH / 2];
 #pragma unroll
-                for (int ch = 0; ch < NCH; ++ch) s = mfma32(qa[ch], kf[ch], s);
+                for (int ch = 0; ch < NCH / 2; ++ch) qa[ch] = tl.kfrag(qtile(i), half * NCH / 2 + ch, 0);
+#pragma unroll
+                for (int ch = 0; ch < NCH / 2; ++ch) s = mfma32(qa[ch], kf[half * NCH / 2 + ch], s);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
-            {
-                X8 oa[NCH];
+            f32x16 dp = acc_init(i, 1, -1.0f);
 #pragma unroll
-                for (int ch = 0; ch < NCH; ++ch) oa[ch] = tl.kfrag(otile(i), ch, 0);
+            for (int half = 0; half < 2; ++half) {
+                X8 oa[NCH / 2];
 #pragma unroll
-                for (int ch = 0; ch < NCH; ++ch) dp = mfma32(oa[ch], vf[ch], dp);
+                for (int ch = 0; ch < NCH / 2; ++ch) oa[ch] = tl.kfrag(otile(i), half * NCH / 2 + ch, 0);
+                X8 vb[NCH / 2];
+#pragma unroll
+                for (int ch = 0; ch < NCH / 2; ++ch) vb[ch] = tl.kfrag(vw, half * NCH / 2 + ch, 0);
+#pragma unroll
+                for (int ch = 0; ch < NCH / 2; ++ch) dp = mfma32(oa[ch], vb[ch], dp);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
             const bool masked = (q0 + BQ > N) || (CAUSAL && q0 < k0 + KW - 1);
             X8 pf[NPV], dsf[NPV];
 #pragma unroll
@@ -427,13 +460,13 @@ bwd_dkv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __re
 #pragma unroll
                     for (int e = 0; e < 2; ++e) {
                         const int r = 8 * h + 2 * j + e;
-                        float p = exp2_hw(fmaf(s[r], c, -lc[r]));
+                        float p = exp2_hw(s[r] * c);
                         if (masked) {
                             const int q = q0 + key_of(0, r, hi);
                             if (q >= N || (CAUSAL && key > q)) p = 0.f;
                         }
                         p2[e] = p;
-                        d2[e] = p * (dp[r] - dc[r]);
+                        d2[e] = p * dp[r];
                     }
                     wp[j] = Bw<T>::pack(p2[0], p2[1]);
                     wd[j] = Bw<T>::pack(d2[0], d2[1]);
@@ -445,23 +478,23 @@ bwd_dkv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __re
             // dV^T += dO^T P,  dK^T += Q^T dS
 #pragma unroll
             for (int tt = 0; tt < NPV; ++tt) {
-                X8 ot[NDB], qt[NDB];
+                {
+                    X8 ot[NDB];
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    ot[db] = tl.tfrag(otile(i), tt, db);
-                    qt[db] = tl.tfrag(qtile(i), tt, db);
-                }
+                    for (int db = 0; db < NDB; ++db) ot[db] = tl.tfrag(otile(i), tt, db);
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    dv[db] = mfma32(ot[db], pf[tt], dv[db]);
-                    dk[db] = mfma32(qt[db], dsf[tt], dk[db]);
+                    for (int db = 0; db < NDB; ++db) dv[db] = mfma32(ot[db], pf[tt], dv[db]);
                 }
+                __builtin_amdgcn_sched_barrier(0);
+                {
+                    X8 qt[NDB];
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) qt[db] = tl.tfrag(qtile(i), tt, db);
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) dk[db] = mfma32(qt[db], dsf[tt], dk[db]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            lc[r] = ln[r];
-            dc[r] = dn[r];
         }
         wait_vm_all();
         __syncthreads();
@@ -477,7 +510,8 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
     const long long rows = (long long)a.B * a.H * a.N;
     const long long nthr = rows * (D / 8);
     hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, s,
-                       static_cast<const T*>(a.o), static_cast<const T*>(a.dout), a.delta, rows);
+                       static_cast<const T*>(a.o), static_cast<const T*>(a.dout), a.lse, a.delta, rows,
+                       1.0f / a.scale);
     const float c = a.scale * kLog2e;
     {
         const int nqt = (a.N + 127) / 128;
@@ -494,8 +528,8 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
         if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
         hipLaunchKernelGGL((bwd_dkv_kernel<T, D, CAUSAL, OUT_F32>), dim3((unsigned)nblk), dim3(256), 0, s,
                            static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                           static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
-                           a.dk, a.dv, a.N, nkt, (int)nblk, c, a.scale);
+                           static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.delta,
+                           a.dk, a.dv, a.N, rows, nkt, (int)nblk, c, a.scale);
     }
     return hipGetLastError();
 }

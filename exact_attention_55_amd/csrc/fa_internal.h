@@ -51,7 +51,7 @@ struct BwdArgs {
     void* dq;
     void* dk;
     void* dv;
-    float* delta;       // caller scratch [B][H][N]: rowsum(dO * O)
+    float* delta;       // caller scratch [2][B][H][N]: rowsum(dO * O), -LSE / scale
     int B, H, N, d;
     bool causal;
     float scale;

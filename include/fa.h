@@ -105,8 +105,9 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *  dout     gradient of the loss with respect to o, [B][H][N][d], same dtype.
  *  dq, dk, dv  outputs [B][H][N][d]: the input dtype, or float32 when
  *           FA_OUT_F32 is set in dtype. 16-byte aligned.
- *  delta    caller-owned scratch, float32 [B][H][N], 4-byte aligned;
- *           overwritten with rowsum(dout * o).
+ *  delta    caller-owned scratch, float32 [2][B][H][N], 16-byte aligned;
+ *           overwritten with the per-row constants rowsum(dout * o) and
+ *           -lse / softmax_scale.
  *  B, H, N, causal, softmax_scale  as for fa_fwd.
  *  d        64 or 128 (256 returns FA_ERR_UNSUPPORTED).
  *  stream   hipStream_t or NULL.
