@@ -1,6 +1,6 @@
 """Benchmark of the fused attention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--sweep]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-next]
 
 One step runs the whole hot path once, on inputs already resident in HBM:
   1. bf16 forward, B=8 H=16 N=2048 d=128, non-causal   (16k tokens, hidden 2048)
@@ -14,6 +14,11 @@ events on the stream it runs on; `legs` reports each. `roofline` is for the
 dominant kernel, the non-causal bf16 forward, against the MI355X dense bf16
 MFMA peak. `cpu_baseline` times the float64 oracle on a bounded sample of the
 same workload (rank 0, N=1 only).
+
+After the step, the rows built beyond the forward are timed on their own with
+the same events and reported under `next_rows` (not part of `value`): the
+16-bit backward (dQ, dK, dV from the saved LSE) on the main shape, its work
+counted as 10*B*H*N^2*d (the five GEMMs of the gradient, halved for causal).
 
 Prints ONE JSON line on stdout.
 """
@@ -33,7 +38,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import exact_attention_55_amd as fa  # noqa: E402
-from exact_attention_55_amd.inputs import CONFIGS, attention_flops, make_qkv, make_signs  # noqa: E402
+from exact_attention_55_amd.inputs import (CONFIGS, attention_flops, make_dout, make_qkv,  # noqa: E402
+                                           make_signs)
 
 PEAK_BF16 = 2516.6   # TFLOP/s, MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 PEAK_FP8 = 5033.2    # TFLOP/s, dense fp8
@@ -44,25 +50,66 @@ FP8 = "fp8_b4h16n4k_d128"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd16_b8h16n2k_d128_traffic.json")
 
 
-def source_hash():
-    """SHA-256 of the device code in the built library (the ELF section
-    .hip_fatbin of libfa.so): it changes exactly when the compiled kernels
-    change, not with comments or host-side code."""
+MAIN_SYMBOL = "_ZN2fa15fa_fwd16_kernelIDF16bLi128ELb0ELb0EEEvPKT_S3_S3_PvPfiiif"
+
+
+def _elf_sections(elf):
+    """(name, address, file offset, size) of every section of a little-endian
+    ELF64 image, in section-index order."""
+    import struct
+    shoff, = struct.unpack_from("<Q", elf, 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", elf, 0x3A)
+    raw = [struct.unpack_from("<IIQQQQ", elf, shoff + i * shentsize) for i in range(shnum)]
+    stroff = raw[shstrndx][4]
+    return [(elf[stroff + r[0]:elf.index(b"\0", stroff + r[0])].decode(), r[3], r[4], r[5])
+            for r in raw]
+
+
+def source_hash(symbol=MAIN_SYMBOL):
+    """SHA-256 of one kernel's machine code in the built library: the bytes of
+    its function and of its kernel descriptor (with the position-dependent
+    entry offset cleared), taken from the gfx950 code object inside the
+    .hip_fatbin section of libfa.so. It changes exactly when that kernel's
+    compiled code changes, not with comments, host code or other kernels."""
     import struct
     path = os.path.join(ROOT, "exact_attention_55_amd", "libfa.so")
     with open(path, "rb") as f:
         elf = f.read()
-    shoff, = struct.unpack_from("<Q", elf, 0x28)
-    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", elf, 0x3A)
-    def section(i):
-        name, _, _, _, off, size = struct.unpack_from("<IIQQQQ", elf, shoff + i * shentsize)
-        return name, off, size
-    _, stroff, _ = section(shstrndx)
-    for i in range(shnum):
-        name, off, size = section(i)
-        if elf[stroff + name:elf.index(b"\0", stroff + name)] == b".hip_fatbin":
-            return hashlib.sha256(elf[off:off + size]).hexdigest()
-    raise RuntimeError(f"no .hip_fatbin section in {path}")
+    fat = [(o, n) for name, _, o, n in _elf_sections(elf) if name == ".hip_fatbin"]
+    if not fat:
+        raise RuntimeError(f"no .hip_fatbin section in {path}")
+    bundle = elf[fat[0][0]:fat[0][0] + fat[0][1]]
+    count, = struct.unpack_from("<Q", bundle, 24)          # clang offload bundle
+    pos, code = 32, None
+    for _ in range(count):
+        off, size, tlen = struct.unpack_from("<QQQ", bundle, pos)
+        triple = bundle[pos + 24:pos + 24 + tlen].decode()
+        pos += 24 + tlen
+        if triple.endswith("gfx950"):
+            code = bundle[off:off + size]
+    if code is None:
+        raise RuntimeError("no gfx950 code object in the fat binary")
+    shdrs = _elf_sections(code)
+    secs = {name: (o, n) for name, _, o, n in shdrs}
+    symoff, symsize = secs[".symtab"]
+    stroff = secs[".strtab"][0]
+    h = hashlib.sha256()
+    found = 0
+    for j in range(symsize // 24):
+        st_name, _, _, shndx, value, size = struct.unpack_from("<IBBHQQ", code, symoff + j * 24)
+        name = code[stroff + st_name:code.index(b"\0", stroff + st_name)].decode()
+        if name not in (symbol, symbol + ".kd") or size == 0:
+            continue
+        _, addr, soff, _ = shdrs[shndx]
+        start = soff + value - addr                # file offset of the symbol
+        blob = bytearray(code[start:start + size])
+        if name.endswith(".kd"):
+            blob[16:24] = bytes(8)                 # kernel_code_entry_byte_offset
+        h.update(name.encode() + bytes(blob))
+        found += 1
+    if found != 2:
+        raise RuntimeError(f"kernel {symbol} not found in the code object")
+    return h.hexdigest()
 
 
 def measured_traffic():
@@ -74,7 +121,7 @@ def measured_traffic():
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256") != source_hash():
+    if t.get("code_sha256") != source_hash():
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -119,7 +166,7 @@ def traffic_summary(run_dir):
         "hbm_bytes_per_launch": fetch + write,
         "algorithmic_bytes_per_launch": algorithmic,
         "traffic_over_algorithmic": (fetch + write) / algorithmic,
-        "source_sha256": source_hash(),
+        "code_sha256": source_hash(),
     }
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(summary, f, indent=1)
@@ -189,6 +236,51 @@ def build_legs(dev):
     return legs, keep
 
 
+def build_next_legs(dev):
+    """Legs of the rows beyond the forward; timed apart from the step."""
+    legs = []
+    c = CONFIGS[MAIN]
+    B, H, N, d = c["B"], c["H"], c["N"], c["d"]
+    q, k, v = (t.to(dev) for t in make_qkv(**c))
+    do = make_dout(B, H, N, d, c["seed"] + 500, c["dtype"]).to(dev)
+    grads = tuple(torch.empty_like(q) for _ in range(3))
+    delta = torch.empty((2, B, H, N), dtype=torch.float32, device=dev)
+    keep = [q, k, v, do, grads, delta]
+    for causal in (False, True):
+        o, lse = fa.fwd(q, k, v, causal)
+        keep += [o, lse]
+        fl = 2.5 * attention_flops(B, H, N, d, causal)
+        name = "bf16_bwd_b8h16n2k_d128" + ("_causal" if causal else "")
+        legs.append(Leg(name, lambda o=o, lse=lse, causal=causal: fa.bwd(
+            q, k, v, o, lse, do, causal, grads=grads, delta=delta), fl))
+    return legs, keep
+
+
+def time_legs(legs, steps, warmup):
+    for _ in range(warmup):
+        for L in legs:
+            L.run(False)
+    torch.cuda.synchronize()
+    events = [[L.run(True) for L in legs] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for step in events:
+        for L, (a, b) in zip(legs, step):
+            L.times.append(a.elapsed_time(b) * 1e-3)
+
+
+def leg_summary(L):
+    t = float(np.mean(L.times))
+    e = {"ms": t * 1e3, "ms_min": float(np.min(L.times)) * 1e3}
+    if L.flops:
+        peak = PEAK_FP8 if L.name.startswith("fp8") else PEAK_BF16
+        e["tflops"] = L.flops / t / 1e12
+        e["frac_of_peak"] = e["tflops"] / peak
+    if L.bytes:
+        e["gbps"] = L.bytes / t / 1e9
+        e["frac_of_hbm"] = e["gbps"] / PEAK_HBM
+    return e
+
+
 def cpu_baseline(budget_s=12.0):
     """The float64 oracle on whole heads of the main workload, until the budget
     is spent (at least one head)."""
@@ -220,6 +312,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the rows beyond the forward (backward)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device copy three times (HBM counter calibration)")
     ap.add_argument("--only-main", action="store_true",
@@ -273,18 +367,7 @@ def main():
             L.times.append(a.elapsed_time(b) * 1e-3)
     total_flops = sum(L.flops for L in legs)
     step_s = wall / args.steps
-    legs_out = {}
-    for L in legs:
-        t = float(np.mean(L.times))
-        e = {"ms": t * 1e3, "ms_min": float(np.min(L.times)) * 1e3}
-        if L.flops:
-            peak = PEAK_FP8 if L.name.startswith("fp8") else PEAK_BF16
-            e["tflops"] = L.flops / t / 1e12
-            e["frac_of_peak"] = e["tflops"] / peak
-        if L.bytes:
-            e["gbps"] = L.bytes / t / 1e9
-            e["frac_of_hbm"] = e["gbps"] / PEAK_HBM
-        legs_out[L.name] = e
+    legs_out = {L.name: leg_summary(L) for L in legs}
     dom = legs[0]
     t_dom = float(np.mean(dom.times))
     achieved = dom.flops / t_dom / 1e12
@@ -311,6 +394,11 @@ def main():
         "legs": legs_out,
         "roofline": roof,
     }
+    if not args.only_main and not args.no_next:
+        log("timing the rows beyond the forward")
+        nlegs, _nkeep = build_next_legs(dev)
+        time_legs(nlegs, args.steps, args.warmup)
+        out["next_rows"] = {L.name: leg_summary(L) for L in nlegs}
     if not args.no_cpu:
         log("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline()
