@@ -27,6 +27,8 @@ Modules:
     fp8         OCP e4m3 ("fn") rounding / encoding from the format definition
     quant       block / per-tensor fp8 quantisation and fake-quant attention
     backward    gradients dQ, dK, dV of exact attention (chain rule, materialised)
+    decode      the same attention for few query rows over a long, ragged key
+                history (grouped key/value heads, bottom-right causal)
 
 Parity pins for every function live in tests/test_oracle_*.py. Functions whose
 result has no independent pin are marked "parity unpinned" in their docstring.
@@ -38,3 +40,4 @@ from .hadamard import fwht, random_sign_hadamard  # noqa: F401
 from .fp8 import e4m3_round, e4m3_encode, e4m3_decode, E4M3_MAX  # noqa: F401
 from .quant import fp8_quantize, fp8_dequantize, fake_quant_attention  # noqa: F401
 from .backward import attention_backward, attention_delta  # noqa: F401
+from .decode import attention_decode, visible_keys  # noqa: F401
