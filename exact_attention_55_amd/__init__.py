@@ -1,11 +1,12 @@
-"""MI355X (gfx950) fused exact attention: forward pass and its gradients.
+"""MI355X (gfx950) fused exact attention: forward pass, its gradients, and a
+decode-shaped (split-key) forward.
 
 The compute lives in ``libfa.so`` (hand-written HIP for gfx950 behind a C ABI
 declared in ``include/fa.h``). This package is a thin ctypes binding: it passes
 torch device pointers and the current HIP stream to the library and does no
 arithmetic of its own.
 
-    from exact_attention_55_amd import fwd, bwd, fp8_prep
+    from exact_attention_55_amd import fwd, bwd, fwd_decode, fp8_prep
 """
 
 from ._lib import (  # noqa: F401
@@ -13,4 +14,5 @@ from ._lib import (  # noqa: F401
     FA_F16, FA_BF16, FA_FP8_E4M3, FA_OUT_F32,
     FaError, lib, lib_path, fwd, fwd_raw, bwd, bwd_raw, fwd_fp8, fp8_prep, fp8_prep_raw, fp8_packed_bytes,
     fp8_alloc_packed, fp8_scales_view, fp8_codes_view, status_string,
+    fwd_decode, decode_raw, decode_splits, decode_workspace_bytes,
 )

@@ -44,6 +44,13 @@ def lib():
     L.fa_fwd.restype = i
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     L.fa_bwd.restype = i
+    L.fa_fwd_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                i, i, i, i, i, i, i, f, i, i, vp]
+    L.fa_fwd_decode.restype = i
+    L.fa_decode_splits.argtypes = [i, i, i, i, i, i]
+    L.fa_decode_splits.restype = i
+    L.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.fa_decode_workspace_bytes.restype = ctypes.c_size_t
     L.fa_fp8_prep.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp]
     L.fa_fp8_prep.restype = i
     L.fa_fp8_packed_bytes.argtypes = [i, i, i, i]
@@ -82,6 +89,22 @@ def bwd_raw(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, causal, softma
     """Direct call with integer pointers; returns the status code."""
     return lib().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, int(causal),
                         float(softmax_scale), int(dtype), stream)
+
+
+def decode_raw(q, k, v, o, lse, seqlens_k, workspace, workspace_bytes, B, H, H_kv, Nq, Nk, d,
+               causal, softmax_scale, num_splits, dtype, stream=None):
+    """Direct call with integer pointers; returns the status code."""
+    return lib().fa_fwd_decode(q, k, v, o, lse, seqlens_k, workspace, workspace_bytes, B, H, H_kv,
+                               Nq, Nk, d, int(causal), float(softmax_scale), int(num_splits),
+                               int(dtype), stream)
+
+
+def decode_splits(B, H, H_kv, Nq, Nk, d):
+    return int(lib().fa_decode_splits(B, H, H_kv, Nq, Nk, d))
+
+
+def decode_workspace_bytes(B, H, Nq, d, num_splits):
+    return int(lib().fa_decode_workspace_bytes(B, H, Nq, d, num_splits))
 
 
 def fp8_prep_raw(x, x8, signs, B, H, N, d, block_rows, in_dtype, stream=None):
@@ -174,6 +197,56 @@ def bwd(q, k, v, o, lse, dout, causal=False, softmax_scale=None, out_f32=False, 
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
     return dq, dk, dv
+
+
+def fwd_decode(q, k, v, causal=False, softmax_scale=None, seqlens_k=None, num_splits=0,
+               out=None, lse=None, out_f32=False, workspace=None):
+    """Decode-shaped forward: q [B,H,Nq,d] against k, v [B,H_kv,Nk,d] (16-bit
+    device tensors, H a multiple of H_kv).
+
+    seqlens_k: optional int32 [B] device tensor of keys per sequence.
+    num_splits: 0 picks the library's suggestion. workspace: optional uint8
+    device tensor of at least decode_workspace_bytes(...) bytes (allocated
+    when needed and not given). Returns (o, lse): o [B,H,Nq,d] in q's dtype
+    (float32 with out_f32=True), lse float32 [B,H,Nq].
+    """
+    B, H, Nq, d = q.shape
+    _check(k.dim() == 4 and k.shape == v.shape, "k, v shapes differ")
+    Bk, H_kv, Nk, dk = k.shape
+    _check(Bk == B and dk == d, "k, v must be [B, H_kv, Nk, d]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if num_splits == 0:
+        num_splits = decode_splits(B, H, H_kv, Nq, Nk, d)
+    code = _dtype_code(q)
+    odt = torch.float32 if out_f32 else q.dtype
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=odt, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if out_f32:
+        code |= FA_OUT_F32
+    need = decode_workspace_bytes(B, H, Nq, d, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v dtypes differ")
+    _check(out.shape == (B, H, Nq, d) and out.dtype == odt, "bad output tensor")
+    _check(lse.shape == (B, H, Nq) and lse.dtype == torch.float32, "bad lse tensor")
+    extra = []
+    if seqlens_k is not None:
+        _check(seqlens_k.dtype == torch.int32 and tuple(seqlens_k.shape) == (B,), "seqlens_k must be int32 [B]")
+        extra.append(seqlens_k)
+    if workspace is not None:
+        _check(workspace.dtype == torch.uint8, "workspace must be uint8")
+        extra.append(workspace)
+    _check_device(q, k, v, out, lse, *extra)
+    wbytes = 0 if workspace is None else workspace.numel()
+    st = decode_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(seqlens_k), _ptr(workspace),
+                    wbytes, B, H, H_kv, Nq, Nk, d, causal, softmax_scale, num_splits, code,
+                    _stream(q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_decode")
+    return out, lse
 
 
 def fp8_alloc_packed(B, H, N, d, device):

@@ -22,7 +22,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libfa.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["fa_api.hip", "fa_fwd16.hip", "fa_fwd_fp8.hip", "fa_fp8_prep.hip", "fa_bwd16.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd16.hip", "fa_fwd_fp8.hip", "fa_fp8_prep.hip", "fa_bwd16.hip",
+           "fa_decode16.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -25,6 +25,9 @@ int from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 // head through 31-bit buffer offsets, with one tile of headroom.
 constexpr long long kMaxHeadBytes = 0x7fffffffLL - (1 << 16);
 
+// Most key splits of one decode call.
+constexpr int kMaxSplits = 256;
+
 }  // namespace
 
 extern "C" {
@@ -112,6 +115,57 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     return from_hip(fa::launch_bwd16(a, base == FA_BF16, s));
+}
+
+int fa_decode_splits(int B, int H, int H_kv, int Nq, int Nk, int d) {
+    if (B <= 0 || H <= 0 || H_kv <= 0 || Nq <= 0 || Nk <= 0 || H % H_kv != 0) return 1;
+    if (!supported_d(d)) return 1;
+    return fa::decode_default_splits(B, H, H_kv, Nq, Nk, d);
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int Nq, int d, int num_splits) {
+    if (!sizes_ok(B, H, Nq, d) || num_splits <= 1 || num_splits > kMaxSplits) return 0;
+    return fa::decode_workspace_bytes((long long)B * H * Nq, num_splits, d);
+}
+
+int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int* seqlens_k, void* workspace, size_t workspace_bytes, int B, int H,
+                  int H_kv, int Nq, int Nk, int d, int causal, float softmax_scale, int num_splits,
+                  int dtype, void* stream) {
+    const int base = dtype & 0xff;
+    const int flags = dtype & ~0xff;
+    if ((flags & ~FA_OUT_F32) != 0) return FA_ERR_INVALID_ARG;
+    if (base != FA_F16 && base != FA_BF16) return FA_ERR_INVALID_ARG;
+    if (!sizes_ok(B, H, Nq, d) || !sizes_ok(B, H_kv, Nk, d)) return FA_ERR_INVALID_ARG;
+    if (H > 0 && (H_kv <= 0 || H % H_kv != 0)) return FA_ERR_INVALID_ARG;
+    if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return FA_ERR_INVALID_ARG;
+    if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_INVALID_ARG;
+    if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
+    if ((long long)Nk * d * 2 > kMaxHeadBytes) return FA_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0 || Nq == 0) return FA_OK;
+    const long long rgroups = ((long long)(H / H_kv) * Nq + 31) / 32;
+    if ((long long)B * H_kv * rgroups * num_splits > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(lse, 4) || !aligned(seqlens_k, 4))
+        return FA_ERR_INVALID_ARG;
+    if (num_splits > 1) {
+        const size_t need = fa::decode_workspace_bytes((long long)B * H * Nq, num_splits, d);
+        if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return FA_ERR_INVALID_ARG;
+    }
+
+    fa::DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.seqlens = seqlens_k;
+    a.workspace = workspace;
+    a.B = B; a.H = H; a.Hkv = H_kv; a.Nq = Nq; a.Nk = Nk; a.d = d;
+    a.causal = causal != 0;
+    a.scale = softmax_scale;
+    a.out_f32 = (flags & FA_OUT_F32) != 0;
+    a.splits = num_splits;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    return from_hip(fa::launch_decode16(a, base == FA_BF16, s));
 }
 
 int fa_fp8_prep(const void* x, void* x8, const int8_t* signs, int B, int H, int N, int d,

@@ -38,6 +38,26 @@ template <> struct Elt<_Float16> {
     using x2 = f16x2;
 };
 
+// Two floats rounded (RNE) to the 16-bit type, packed.
+template <typename T> __device__ __forceinline__ typename Elt<T>::x2 pack2(float a, float b);
+template <> __device__ __forceinline__ bf16x2 pack2<__bf16>(float a, float b) {
+    bf16x2 r = {(__bf16)a, (__bf16)b};
+    return r;
+}
+template <> __device__ __forceinline__ f16x2 pack2<_Float16>(float a, float b) {
+    f16x2 r = {(_Float16)a, (_Float16)b};
+    return r;
+}
+// x.x + x.y + acc in fp32 (v_dot2 with ones)
+__device__ __forceinline__ float sum2(bf16x2 x, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(x, one, acc, false);
+}
+__device__ __forceinline__ float sum2(f16x2 x, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(x, one, acc, false);
+}
+
 // D(32x32 f32) += A(32x16) * B(16x32), 16-bit operands, fp32 accumulate.
 // Operand layout (wave64): lane l holds row/column (l % 32) and 8 consecutive
 // k values of k-group (l / 32). Accumulator: lane l holds column l % 32,

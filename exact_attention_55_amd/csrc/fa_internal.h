@@ -62,4 +62,26 @@ hipError_t launch_bwd16(const BwdArgs& a, bool bf16, hipStream_t s);
 
 inline size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
 
+struct DecodeArgs {
+    const void* q;      // [B][H][Nq][d]
+    const void* k;      // [B][Hkv][Nk][d]
+    const void* v;
+    void* o;            // [B][H][Nq][d]
+    float* lse;         // [B][H][Nq]
+    const int* seqlens; // [B] keys per sequence (clamped to [0, Nk]), or null: Nk
+    void* workspace;    // partial results when splits > 1
+    int B, H, Hkv, Nq, Nk, d;
+    bool causal;
+    float scale;
+    bool out_f32;
+    int splits;
+};
+// Bytes of the partial-O block at the start of the workspace, and of the
+// whole workspace (partial O, then partial LSE), for rows = B*H*Nq.
+size_t decode_partial_o_bytes(long long rows, int splits, int d);
+size_t decode_workspace_bytes(long long rows, int splits, int d);
+int decode_default_splits(int B, int H, int Hkv, int Nq, int Nk, int d);
+// Decode-shaped 16-bit forward (bf16 = true: bfloat16, else float16).
+hipError_t launch_decode16(const DecodeArgs& a, bool bf16, hipStream_t s);
+
 }  // namespace fa

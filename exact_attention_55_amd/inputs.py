@@ -35,6 +35,18 @@ CONFIGS = {
                               outliers=True),
 }
 
+# Decode workloads (few new query rows against a long key/value history; the
+# pages name autoregressive sampling but give no shapes): B sequences, H query
+# heads sharing Hkv key/value heads, Nq new rows, Nk cached keys; with
+# ragged=True the key count of each sequence is drawn uniformly from
+# [Nk/8, Nk].
+DECODE_CONFIGS = {
+    "decode_b8h16_nk16k_d128": dict(B=8, H=16, Hkv=16, Nq=1, Nk=16384, d=128, causal=True,
+                                    dtype="bf16", seed=6),
+    "decode_gqa_b16h64kv8_nk8k_ragged": dict(B=16, H=64, Hkv=8, Nq=1, Nk=8192, d=128, causal=True,
+                                             dtype="bf16", seed=7, ragged=True),
+}
+
 TORCH_DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16}
 
 
@@ -59,6 +71,21 @@ def make_dout(B, H, N, d, seed, dtype="bf16"):
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((B, H, N, d), dtype=np.float32)
     return torch.from_numpy(x).to(TORCH_DTYPES[dtype])
+
+
+def make_decode(B, H, Hkv, Nq, Nk, d, seed, dtype="bf16", ragged=False, **_):
+    """Decode inputs: q [B,H,Nq,d], k and v [B,Hkv,Nk,d] (float32 standard
+    normals drawn in the order q, k, v from default_rng(seed), one RNE cast to
+    the 16-bit dtype), and seqlens (int32 [B] drawn afterwards from
+    [Nk // 8, Nk] when ragged, else None)."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, Nq, d), dtype=np.float32)
+    k = rng.standard_normal((B, Hkv, Nk, d), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, Nk, d), dtype=np.float32)
+    lens = rng.integers(Nk // 8, Nk + 1, size=B).astype(np.int32) if ragged else None
+    tdt = TORCH_DTYPES[dtype]
+    out = tuple(torch.from_numpy(x).to(tdt) for x in (q, k, v))
+    return out + (None if lens is None else torch.from_numpy(lens),)
 
 
 def make_signs(H, d, seed):

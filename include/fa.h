@@ -122,6 +122,55 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            void* stream);
 
 /*
+ * fa_fwd_decode - attention forward for a few query rows per head against a
+ * long key/value history (token-by-token generation, "FlashAttention-3: Fast
+ * & Accurate Attention with Asynchrony & Low-Precision", "Performance
+ * Results"). Same function as fa_fwd ("FlashAttention - one, two, three!",
+ * "Standard Attention"); the keys are split over num_splits parts whose
+ * partial results are merged by their log-sum-exp (the block-wise softmax
+ * of the same page's "FlashAttention v1.", across parts).
+ *
+ *  q        16-bit queries [B][H][Nq][d] (dtype FA_F16 or FA_BF16).
+ *  k, v     keys and values [B][H_kv][Nk][d], same dtype. Query head h reads
+ *           key/value head h / (H / H_kv); H_kv == H is plain multi-head.
+ *  o        output [B][H][Nq][d]: input dtype, or float32 with FA_OUT_F32.
+ *  lse      output [B][H][Nq] float32, natural log; -inf for a row that sees
+ *           no key (its o row is then 0).
+ *  seqlens_k  device int32 [B]: keys 0 .. seqlens_k[b]-1 of batch b are the
+ *           sequence (values are clamped to [0, Nk]); NULL: all Nk keys.
+ *  workspace, workspace_bytes  caller-owned device scratch of at least
+ *           fa_decode_workspace_bytes(B, H, Nq, d, num_splits) bytes,
+ *           16-byte aligned (partial O and LSE per split); may be NULL when
+ *           num_splits == 1.
+ *  B, H, H_kv, Nq, Nk  >= 0, H a multiple of H_kv (>= 1 when H > 0).
+ *  d        64, 128 or 256.
+ *  causal   nonzero: the Nq query rows are the last Nq positions of the
+ *           sequence: query i sees keys j <= L - Nq + i (L = the sequence's
+ *           key count); rows with L - Nq + i < 0 see no key.
+ *  softmax_scale  finite and > 0.
+ *  num_splits  1 .. 256; fa_decode_splits() suggests one for the shape.
+ *  dtype    FA_F16 | FA_BF16, optionally | FA_OUT_F32.
+ *  stream   hipStream_t or NULL.
+ *
+ * q, k, v, o 16-byte aligned, lse and seqlens_k 4-byte aligned. Launches one
+ * kernel (num_splits == 1) or two (splits, then the merge). Returns FA_OK,
+ * FA_ERR_INVALID_ARG (also for a workspace that is missing or too small),
+ * FA_ERR_UNSUPPORTED (d, or Nk*d*2 > 2^31 - 2^16 - 1) or FA_ERR_HIP.
+ */
+int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int* seqlens_k, void* workspace, size_t workspace_bytes,
+                  int B, int H, int H_kv, int Nq, int Nk, int d, int causal,
+                  float softmax_scale, int num_splits, int dtype, void* stream);
+
+/* Suggested num_splits for fa_fwd_decode (enough parts to fill the GPU, each
+ * at least 256 keys). Returns 1 for invalid or empty shapes. */
+int fa_decode_splits(int B, int H, int H_kv, int Nq, int Nk, int d);
+
+/* Workspace bytes fa_fwd_decode needs for num_splits (0 when num_splits <= 1
+ * or the arguments are invalid). */
+size_t fa_decode_workspace_bytes(int B, int H, int Nq, int d, int num_splits);
+
+/*
  * fa_fp8_prep - incoherent processing + FP8 block quantisation of one tensor.
  *
  *  x        16-bit input [B][H][N][d] (in_dtype FA_BF16 or FA_F16), 16-byte

@@ -116,3 +116,81 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "lib_path", lambda: str(tmp_path / "missing.so"))
     with pytest.raises(fa.FaError):
         _lib.lib()
+
+
+def bwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+             delta=FAKE, B=1, H=1, N=128, d=128, causal=0, scale=0.088, dtype=fa.FA_BF16)
+    a.update(kw)
+    return fa.bwd_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+                      a["delta"], a["B"], a["H"], a["N"], a["d"], a["causal"], a["scale"],
+                      a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=fa.FA_FP8_E4M3), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=fa.FA_BF16 | 0x400), fa.FA_ERR_INVALID_ARG),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=8388352, d=128), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(do=None), fa.FA_ERR_INVALID_ARG),
+    (dict(delta=None), fa.FA_ERR_INVALID_ARG),
+    (dict(dv=FAKE + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(delta=FAKE + 4), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=FAKE + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(H=0, q=None), fa.FA_OK),
+])
+def test_bwd_validation(L, kw, status):
+    assert bwd(**kw) == status
+
+
+def decode(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, seqlens=None, ws=FAKE, ws_bytes=1 << 30,
+             B=2, H=8, H_kv=2, Nq=1, Nk=4096, d=128, causal=0, scale=0.088, splits=4,
+             dtype=fa.FA_BF16)
+    a.update(kw)
+    return fa.decode_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["seqlens"], a["ws"],
+                         a["ws_bytes"], a["B"], a["H"], a["H_kv"], a["Nq"], a["Nk"], a["d"],
+                         a["causal"], a["scale"], a["splits"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=fa.FA_FP8_E4M3), fa.FA_ERR_INVALID_ARG),
+    (dict(H_kv=3), fa.FA_ERR_INVALID_ARG),          # H not a multiple of H_kv
+    (dict(H_kv=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(splits=0), fa.FA_ERR_INVALID_ARG),
+    (dict(splits=257), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(Nk=8388352), fa.FA_ERR_UNSUPPORTED),
+    (dict(ws=None), fa.FA_ERR_INVALID_ARG),           # splits > 1 needs a workspace
+    (dict(ws_bytes=1024), fa.FA_ERR_INVALID_ARG),     # too small
+    (dict(ws=FAKE + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(seqlens=FAKE + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(k=None), fa.FA_ERR_INVALID_ARG),
+    (dict(o=FAKE + 4), fa.FA_ERR_INVALID_ARG),
+    (dict(B=0), fa.FA_OK),
+    (dict(Nq=0, q=None), fa.FA_OK),
+])
+def test_decode_validation(L, kw, status):
+    assert decode(**kw) == status
+
+
+def test_decode_sizes(L):
+    # workspace: partial O (fp32) then partial LSE, each rounded to 256 bytes
+    B, H, Nq, d, S = 2, 8, 3, 128, 5
+    rows = B * H * Nq
+    o_bytes = -(-rows * S * d * 4 // 256) * 256
+    l_bytes = -(-rows * S * 4 // 256) * 256
+    assert fa.decode_workspace_bytes(B, H, Nq, d, S) == o_bytes + l_bytes
+    assert fa.decode_workspace_bytes(B, H, Nq, d, 1) == 0
+    assert fa.decode_workspace_bytes(B, H, Nq, d, 300) == 0
+    # suggested splits: at least 1, at most 64, and short histories are not split
+    assert fa.decode_splits(8, 16, 16, 1, 16384, 128) > 1
+    assert fa.decode_splits(8, 16, 16, 1, 200, 128) == 1
+    assert 1 <= fa.decode_splits(1, 1, 1, 1, 1 << 20, 64) <= 64
+    assert fa.decode_splits(1, 3, 2, 1, 100, 128) == 1
