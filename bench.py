@@ -18,7 +18,11 @@ same workload (rank 0, N=1 only).
 After the step, the rows built beyond the forward are timed on their own with
 the same events and reported under `next_rows` (not part of `value`): the
 16-bit backward (dQ, dK, dV from the saved LSE) on the main shape, its work
-counted as 10*B*H*N^2*d (the five GEMMs of the gradient, halved for causal).
+counted as 10*B*H*N^2*d (the five GEMMs of the gradient, halved for causal);
+and the decode-shaped forward on its two workloads (B=8 H=16 sequences of
+16384 keys; B=16 with 64 query heads over 8 key/value heads and ragged key
+counts), in GB/s of the bytes it must move (K and V of every sequence's keys,
+Q, O, LSE) against the HBM peak.
 
 Prints ONE JSON line on stdout.
 """
@@ -38,8 +42,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import exact_attention_55_amd as fa  # noqa: E402
-from exact_attention_55_amd.inputs import (CONFIGS, attention_flops, make_dout, make_qkv,  # noqa: E402
-                                           make_signs)
+from exact_attention_55_amd.inputs import (CONFIGS, DECODE_CONFIGS, attention_flops,  # noqa: E402
+                                           make_decode, make_dout, make_qkv, make_signs)
 
 PEAK_BF16 = 2516.6   # TFLOP/s, MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 PEAK_FP8 = 5033.2    # TFLOP/s, dense fp8
@@ -253,6 +257,23 @@ def build_next_legs(dev):
         name = "bf16_bwd_b8h16n2k_d128" + ("_causal" if causal else "")
         legs.append(Leg(name, lambda o=o, lse=lse, causal=causal: fa.bwd(
             q, k, v, o, lse, do, causal, grads=grads, delta=delta), fl))
+    for name, c in sorted(DECODE_CONFIGS.items()):
+        B, H, Hkv, Nq, Nk, d = c["B"], c["H"], c["Hkv"], c["Nq"], c["Nk"], c["d"]
+        qh, kh, vh, sl = make_decode(**c)
+        qd, kd, vd = (t.to(dev) for t in (qh, kh, vh))
+        sld = None if sl is None else sl.to(dev)
+        splits = fa.decode_splits(B, H, Hkv, Nq, Nk, d)
+        ws = torch.empty(max(1, fa.decode_workspace_bytes(B, H, Nq, d, splits)), dtype=torch.uint8,
+                         device=dev)
+        od = torch.empty((B, H, Nq, d), dtype=qd.dtype, device=dev)
+        ld = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+        keys = Nk * B if sl is None else int(sl.sum())
+        nbytes = keys * Hkv * d * 2 * 2 + 2 * B * H * Nq * d * 2 + 4 * B * H * Nq
+        legs.append(Leg("bf16_" + name, lambda qd=qd, kd=kd, vd=vd, sld=sld, od=od, ld=ld, ws=ws,
+                        s=splits, causal=c["causal"]: fa.fwd_decode(
+                            qd, kd, vd, causal, seqlens_k=sld, num_splits=s, out=od, lse=ld,
+                            workspace=ws), 0.0, nbytes))
+        keep += [qd, kd, vd, sld, od, ld, ws]
     return legs, keep
 
 
@@ -313,7 +334,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-next", action="store_true",
-                    help="skip the rows beyond the forward (backward)")
+                    help="skip the rows beyond the forward (backward, decode)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device copy three times (HBM counter calibration)")
     ap.add_argument("--only-main", action="store_true",

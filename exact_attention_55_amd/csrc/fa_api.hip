@@ -143,6 +143,8 @@ int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* l
     if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
     if ((long long)Nk * d * 2 > kMaxHeadBytes) return FA_ERR_UNSUPPORTED;
     if (B == 0 || H == 0 || Nq == 0) return FA_OK;
+    // the query rows sharing one key/value head are addressed with 31-bit offsets
+    if ((long long)(H / H_kv) * Nq * d * 2 > kMaxHeadBytes) return FA_ERR_UNSUPPORTED;
     const long long rgroups = ((long long)(H / H_kv) * Nq + 31) / 32;
     if ((long long)B * H_kv * rgroups * num_splits > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
     if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;

@@ -34,16 +34,34 @@ namespace {
 
 // Stages per wave: all in flight at the top of a block except the one being
 // read. The vmcnt field holds 63 outstanding loads (NST-1 blocks of
-// 2*RB/32 loads each).
+// 2*RB/32 loads each). Measured at d = 128: 2, 3 and 4 stages (5, 3 and 2
+// waves per CU by LDS) stream within noise of each other and above a plain
+// device copy.
+#ifndef FA_DEC_NST64
+#define FA_DEC_NST64 4
+#endif
+#ifndef FA_DEC_NST128
+#define FA_DEC_NST128 2
+#endif
+#ifndef FA_DEC_NST256
+#define FA_DEC_NST256 2
+#endif
 template <int D> struct DecCfg;
-template <> struct DecCfg<64> { static constexpr int NST = 4; };
-template <> struct DecCfg<128> { static constexpr int NST = 4; };
-template <> struct DecCfg<256> { static constexpr int NST = 2; };
+template <> struct DecCfg<64> { static constexpr int NST = FA_DEC_NST64; };
+template <> struct DecCfg<128> { static constexpr int NST = FA_DEC_NST128; };
+template <> struct DecCfg<256> { static constexpr int NST = FA_DEC_NST256; };
 
 template <int N>
 __device__ __forceinline__ void vm_wait() {
     static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit field");
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// 16 bytes per lane from a buffer into registers, untracked by the compiler:
+// the result is valid only after an explicit vm_wait covers the load.
+__device__ __forceinline__ u32x4 buffer_load16_async(i32x4 rsrc, uint32_t voff) {
+    u32x4 r;
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(r) : "v"(voff), "s"(rsrc) : "memory");
+    return r;
 }
 // Every LDS read of the wave has returned (before a copy overwrites a stage).
 __device__ __forceinline__ void lds_reads_done() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
@@ -101,12 +119,15 @@ decode16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     const int klim = CAUSAL ? L - Nq + qi : L - 1;       // last key this row sees
     const int kfree = CAUSAL ? L - Nq + 1 : L;           // keys below: seen by every row
 
-    X8 qf[NCH];
+    // Q^T fragments (B operand): lane holds d = 16 ch + 8 hi .. +7 of its row.
+    // The group's M rows are contiguous (heads hkv*g .. hkv*g + g - 1, Nq rows
+    // each); rows >= M fall outside the buffer range and read as zeros. The
+    // loads go through asm so that the compiler does not add its own
+    // (stricter) wait for them; see the wait after the first copies.
+    const i32x4 qrs = make_rsrc(Qg + ((long long)b * H + hkv * g) * Nq * D, M * RB);
+    u32x4 qraw[NCH];
 #pragma unroll
-    for (int ch = 0; ch < NCH; ++ch)
-        qf[ch] = rv ? load16<X8>(Qg + qrow * D + 16 * ch + 8 * hi)
-                    : __builtin_bit_cast(X8, u32x4{0, 0, 0, 0});
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);   // Q landed before the copies start counting
+    for (int ch = 0; ch < NCH; ++ch) qraw[ch] = buffer_load16_async(qrs, r * RB + 32 * ch + 16 * hi);
 
     // Copies: buffer loads over the sequence's L rows (rows >= L read as
     // zeros) straight into LDS; load j fills bytes [1024 j, +1024) of a block,
@@ -157,9 +178,20 @@ decode16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     float l = 0.f;         // sum of the rounded P fed to the MFMA
     float lx = 0.f;        // sum of the fp32 p (for the log-sum-exp)
 
+    // The first NST-1 blocks are requested while Q is still in flight; the
+    // wait below covers Q (issued before them) but not the copies.
 #pragma unroll
-    for (int j = 0; j < NST; ++j)
+    for (int j = 0; j < NST - 1; ++j)
         if (j < nblk) issue(j);
+    if (NST - 1 < nblk) vm_wait<LPB * (NST - 1)>();
+    else vm_wait<0>();
+    X8 qf[NCH];
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+        asm volatile("" : "+v"(qraw[ch]));           // Q is used only after the wait
+        qf[ch] = __builtin_bit_cast(X8, qraw[ch]);
+    }
+    if (NST - 1 < nblk) issue(NST - 1);
 
     for (int j = 0; j < nblk; ++j) {
         if (j + NST - 1 < nblk) vm_wait<LPB * (NST - 1)>();
@@ -347,12 +379,12 @@ size_t decode_workspace_bytes(long long rows, int splits, int d) {
 }
 
 int decode_default_splits(int B, int H, int Hkv, int Nq, int Nk, int d) {
-    // Enough waves for two rounds over the chip (256 CUs; the LDS stages
-    // allow two waves per CU at d >= 128, four at d = 64), each split at
-    // least 8 blocks of 32 keys, at most 64 splits.
+    // About 1024 waves (four per CU of 256), each split at least 8 blocks
+    // of 32 keys, at most 64 splits. Measured on two workloads of 128
+    // (batch, key/value head) units: 8 splits beat 4, 6, 12 and 16.
     const int g = H / Hkv;
     const long long units = (long long)B * Hkv * ((g * Nq + 31) / 32);
-    const long long waves = 2LL * 256 * (d == 64 ? 4 : 2);
+    const long long waves = 1024;
     long long s = (waves + units - 1) / units;
     const long long by_len = (long long)((Nk + 31) / 32) / 8;
     s = s < by_len ? s : by_len;
