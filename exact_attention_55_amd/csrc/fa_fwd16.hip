@@ -39,10 +39,13 @@
 //    lane exceeds kBig is that tile redone with its exact maximum (moving m
 //    and rescaling O and the sums). The result is the same exact softmax up
 //    to rounding because l and O always share m.
-//  * Two row sums: l~ from the rounded P actually fed to the PV MFMA (dot2
-//    with ones) normalises O, which makes O an exact convex combination of V
-//    rows even when one key dominates; l from the fp32 p gives the
-//    log-sum-exp, free of the 16-bit rounding of P.
+//  * Row sums: l~ of the rounded P actually fed to the PV MFMA (dot2 with
+//    ones) normalises O, which makes O an exact convex combination of V rows
+//    even when one key dominates. For fp16 it also gives the log-sum-exp
+//    (relative error at most fp16's rounding of P, 2^-11: within the LSE
+//    tolerance). bf16's rounding (2^-9) is not, so bf16 keeps a second,
+//    fp32 sum for the log-sum-exp: two more adds per pair of exponentials
+//    (2.5-5.5 % of the kernel time; FA16_XSUM=1 forces it for fp16 too).
 //  * Schedule ("FlashAttention-3: ...", "Overlapping GEMM and Softmax"): two
 //    waves share each SIMD, and inside a wave one step overlaps the score
 //    MFMAs of key tile j+1 with the exponentials of tile j, then runs the PV
@@ -65,6 +68,9 @@ constexpr float kBig = 16384.0f;
 
 #ifndef FA16_SCHED                 // 1: hand-ordered step; 0: compiler-scheduled overlap
 #define FA16_SCHED 1
+#endif
+#ifndef FA16_XSUM                 // 1: separate fp32 row sum for the log-sum-exp also for fp16
+#define FA16_XSUM 0
 #endif
 #ifndef FA16_KPD
 #define FA16_KPD 4
@@ -106,6 +112,9 @@ struct Wave16 {
     static constexpr int NDB = D / 32;     // 32-row blocks of O^T
     static constexpr int NKB = BC / 32;    // 32-key blocks of S^T
     static constexpr int NPV = BC / 16;    // k-steps of O^T += V^T P^T
+
+    // separate fp32 row sum for the log-sum-exp (see the file header)
+    static constexpr bool XS = FA16_XSUM || std::is_same<T, __bf16>::value;
 
     f32x16 o[QB][NDB];   // O^T accumulators (unnormalised)
     float m[QB];         // reference maximum, log2 units
@@ -227,10 +236,10 @@ struct Wave16 {
                     const float p0 = exp2_hw(fmaf(s[qb][kb][8 * h + 2 * j], c, nm));
                     const float p1 = exp2_hw(fmaf(s[qb][kb][8 * h + 2 * j + 1], c, nm));
                     pp[j] = pack2<T>(p0, p1);
-                    xs += p0 + p1;
+                    if (XS) xs += p0 + p1;
                 }
                 ls[qb][h] = sum2(pp[3], sum2(pp[2], sum2(pp[1], sum2(pp[0], ls[qb][h]))));
-                lxs[qb][h] += xs;
+                if (XS) lxs[qb][h] += xs;
                 pf[qb][2 * kb + h] = X8{pp[0][0], pp[0][1], pp[1][0], pp[1][1],
                                         pp[2][0], pp[2][1], pp[3][0], pp[3][1]};
             }
@@ -252,7 +261,8 @@ struct Wave16 {
                                            float (&ls)[QB][2], float (&lxs)[QB][2]) {
         bool big = false;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) big |= lxs[qb][0] + lxs[qb][1] > kBig;
+        for (int qb = 0; qb < QB; ++qb)
+            big |= (XS ? lxs[qb][0] + lxs[qb][1] : ls[qb][0] + ls[qb][1]) > kBig;
         if (wave_any(big)) {
             float mt[QB];
             tile_max(s, c, mt);
@@ -264,7 +274,7 @@ struct Wave16 {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             l[qb] += ls[qb][0] + ls[qb][1];
-            lx[qb] += lxs[qb][0] + lxs[qb][1];
+            if (XS) lx[qb] += lxs[qb][0] + lxs[qb][1];
         }
     }
 
@@ -411,7 +421,7 @@ struct Wave16 {
             const float p1 = exp2_hw(fmaf(s[qb][kb][8 * h + 2 * j + 1], c, -m[qb]));
             pp[qb][kb][h][j] = pack2<T>(p0, p1);
             ls[qb][h] = sum2(pp[qb][kb][h][j], ls[qb][h]);
-            lxs[qb][h] += p0 + p1;
+            if (XS) lxs[qb][h] += p0 + p1;
         }
     }
 
@@ -550,15 +560,16 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
         const int row = p / RB;
         voff[j] = row * RB + ((p % RB / 16) ^ lds_swz16<D>(row)) * 16;
     }
-    const int nkt_total = (N + BC - 1) / BC;
+    // tiles this workgroup reads: up to its last query row (causal) or N
+    const int nkt_use = ((CAUSAL ? min(N, qtile0 + BR) : N) + BC - 1) / BC;
     const uint32_t sbase = lds_addr(smem);
     auto issue = [&](const i32x4& rs, int t, int slot) {
         const uint32_t dst = sbase + slot * TB + wave_u * NIW * 1024;
 #pragma unroll
         for (int j = 0; j < NIW; ++j) buffer_load_lds16(rs, dst + j * 1024, voff[j], t * TB);
     };
-    auto load_k = [&](int t) { if (t < nkt_total) issue(krs, t, t & 1); };
-    auto load_v = [&](int t) { if (t < nkt_total) issue(vrs, t, 2 + (t & 1)); };
+    auto load_k = [&](int t) { if (t < nkt_use) issue(krs, t, t & 1); };
+    auto load_v = [&](int t) { if (t < nkt_use) issue(vrs, t, 2 + (t & 1)); };
     auto ktile = [&](int t) -> const char* { return smem + (t & 1) * TB; };
 
     // Q^T fragments (B operand): lane holds query q0+32*qb+l32, d = 16*ch + 8*hi .. +7
@@ -623,6 +634,7 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     W st;
     st.init();
     f32x16 s[QB][NKB];
+
 
     // Invariant at the top of step t: K_t, V_t and (if any) K_{t+1} are in
     // LDS. Step t fills the slots of K_{t-1}/K_t and V_{t-1} that every wave
@@ -694,7 +706,7 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const float l = pair_sum(st.l[qb]);
-        const float lx = pair_sum(st.lx[qb]);
+        const float lx = W::XS ? pair_sum(st.lx[qb]) : l;
         const float inv = 1.0f / l;
         const int row = q0 + 32 * qb + l32;
         if (row < N) {
