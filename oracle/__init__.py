@@ -17,7 +17,7 @@ says otherwise. Sources, cited by page title and section:
 * "FlashAttention-3: Fast & Accurate Attention with Asynchrony &
   Low-Precision" (Embodied AI 101 transcript), section "Incoherent Processing
   for FP8 Accuracy": random-sign Hadamard rotation of Q and K before FP8
-  quantisation; and the review "FlashAttention-3: почему внимание стало
+  quantisation, fused into the rotary-embedding step; and the review "FlashAttention-3: почему внимание стало
   быстрее", section "Метод", item 3: block quantisation.
 
 Modules:
@@ -27,6 +27,7 @@ Modules:
     fp8         OCP e4m3 ("fn") rounding / encoding from the format definition
     quant       block / per-tensor fp8 quantisation and fake-quant attention
     backward    gradients dQ, dK, dV of exact attention (chain rule, materialised)
+    rope        rotary position embedding (interleaved or half pairing)
     decode      the same attention for few query rows over a long, ragged key
                 history (grouped key/value heads, bottom-right causal)
 
@@ -41,3 +42,4 @@ from .fp8 import e4m3_round, e4m3_encode, e4m3_decode, E4M3_MAX  # noqa: F401
 from .quant import fp8_quantize, fp8_dequantize, fake_quant_attention  # noqa: F401
 from .backward import attention_backward, attention_delta  # noqa: F401
 from .decode import attention_decode, visible_keys  # noqa: F401
+from .rope import rope, rope_angles, rope_cos_sin, rope_frequencies  # noqa: F401

@@ -33,27 +33,34 @@ import numpy as np
 
 from .fp8 import E4M3_MAX, e4m3_encode, e4m3_decode
 from .hadamard import random_sign_hadamard
+from .rope import rope as rotary
 
 
-def _rotated_f32(x, signs):
-    """The values that get quantised: x, or x M, rounded once to float32."""
+def _rotated_f32(x, signs, rope=None):
+    """The values that get quantised: x, optionally after the rotary
+    embedding (rope = (style, base, pos0)), then x M when signs are given,
+    rounded once to float32."""
     x = np.asarray(x, dtype=np.float64)
+    if rope is not None:
+        x = rotary(x, *rope)
     if signs is not None:
         x = random_sign_hadamard(x, signs)
     return x.astype(np.float32)
 
 
-def fp8_quantize(x, signs=None, block_rows=128):
+def fp8_quantize(x, signs=None, block_rows=128, rope=None):
     """Quantise x [B, H, N, d] to e4m3 codes with float32 scales.
 
     signs: [H, d] of +-1 to apply the random-sign Hadamard first (Q and K), or
     None (V, and the plain baseline).
     block_rows: rows per block (128), or 0 for one scale per tensor.
+    rope: None, or (style, base, pos0) to apply the rotary embedding first
+    (the fused rotary + Hadamard + quantisation step).
     Returns (codes uint8 [B,H,N,d], scales float32 [B,H,ceil(N/block_rows)];
     per-tensor mode returns the same scale in every slot of a
     [B,H,ceil(N/128)] array so both modes have one layout).
     """
-    y = _rotated_f32(x, signs)
+    y = _rotated_f32(x, signs, rope)
     B, H, N, d = y.shape
     br = block_rows if block_rows > 0 else 128
     nb = (N + br - 1) // br
@@ -83,7 +90,7 @@ def fp8_dequantize(codes, scales, block_rows=128):
 
 
 def fake_quant_attention(q, k, v, signs=None, block_rows=128, causal=False,
-                         scale=None):
+                         scale=None, rope=None):
     """Exact float64 attention on the dequantised fp8 inputs.
 
     Q and K are rotated by the same random-sign Hadamard (when signs is given)
@@ -91,15 +98,16 @@ def fake_quant_attention(q, k, v, signs=None, block_rows=128, causal=False,
     orthogonal, the attention of the rotated, unquantised inputs equals the
     plain attention; what remains is the quantisation error alone. This is the
     reference for the fp8 kernel's log-sum-exp (which never sees the rounding
-    of P) and a diagnostic for its output.
+    of P) and a diagnostic for its output. With rope = (style, base, pos0)
+    Q and K get the rotary embedding before the rotation and quantisation.
     Returns (O, LSE, (qc, qs), (kc, ks), (vc, vs)).
     """
     from .attention import attention
     d = np.asarray(q).shape[-1]
     if scale is None:
         scale = 1.0 / np.sqrt(d)
-    qc, qs = fp8_quantize(q, signs, block_rows)
-    kc, ks = fp8_quantize(k, signs, block_rows)
+    qc, qs = fp8_quantize(q, signs, block_rows, rope)
+    kc, ks = fp8_quantize(k, signs, block_rows, rope)
     vc, vs = fp8_quantize(v, None, block_rows)
     o, lse = attention(fp8_dequantize(qc, qs, block_rows),
                        fp8_dequantize(kc, ks, block_rows),
