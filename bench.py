@@ -19,7 +19,9 @@ After the step, the rows built beyond the forward are timed on their own with
 the same events and reported under `next_rows` (not part of `value`): the
 16-bit backward (dQ, dK, dV from the saved LSE) on the main shape, its work
 counted as 10*B*H*N^2*d (the five GEMMs of the gradient, halved for causal);
-and the decode-shaped forward on its two workloads (B=8 H=16 sequences of
+the fused rotary + Hadamard + fp8 block quantisation of Q and K of the fp8
+workload (half pairing, GB/s of bytes read and written); and the
+decode-shaped forward on its two workloads (B=8 H=16 sequences of
 16384 keys; B=16 with 64 query heads over 8 key/value heads and ragged key
 counts), in GB/s of the bytes it must move (K and V of every sequence's keys,
 Q, O, LSE) against the HBM peak.
@@ -257,6 +259,20 @@ def build_next_legs(dev):
         name = "bf16_bwd_b8h16n2k_d128" + ("_causal" if causal else "")
         legs.append(Leg(name, lambda o=o, lse=lse, causal=causal: fa.bwd(
             q, k, v, o, lse, do, causal, grads=grads, delta=delta), fl))
+    c8 = CONFIGS[FP8]
+    B8, H8, N8, d8 = c8["B"], c8["H"], c8["N"], c8["d"]
+    q8, k8, _ = (t.to(dev) for t in make_qkv(**c8))
+    signs = torch.from_numpy(make_signs(H8, d8, c8["seed"])).to(dev)
+    pq, pk = (fa.fp8_alloc_packed(B8, H8, N8, d8, dev) for _ in range(2))
+    nel = B8 * H8 * N8 * d8
+    rope_bytes = 2 * (nel * 2 + nel + B8 * H8 * (N8 // 128) * 4)
+
+    def prep_rope():
+        fa.fp8_prep(q8, signs, 128, out=pq, rope=("half", 10000.0, 0))
+        fa.fp8_prep(k8, signs, 128, out=pk, rope=("half", 10000.0, 0))
+
+    legs.append(Leg("fp8_prep_rope_qk_b4h16n4k_d128", prep_rope, 0.0, rope_bytes))
+    keep += [q8, k8, signs, pq, pk]
     for name, c in sorted(DECODE_CONFIGS.items()):
         B, H, Hkv, Nq, Nk, d = c["B"], c["H"], c["Hkv"], c["Nq"], c["Nk"], c["d"]
         qh, kh, vh, sl = make_decode(**c)
@@ -334,7 +350,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-next", action="store_true",
-                    help="skip the rows beyond the forward (backward, decode)")
+                    help="skip the rows beyond the forward (backward, rotary prep, decode)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device copy three times (HBM counter calibration)")
     ap.add_argument("--only-main", action="store_true",

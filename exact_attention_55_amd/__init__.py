@@ -15,4 +15,5 @@ from ._lib import (  # noqa: F401
     FaError, lib, lib_path, fwd, fwd_raw, bwd, bwd_raw, fwd_fp8, fp8_prep, fp8_prep_raw, fp8_packed_bytes,
     fp8_alloc_packed, fp8_scales_view, fp8_codes_view, status_string,
     fwd_decode, decode_raw, decode_splits, decode_workspace_bytes,
+    fp8_prep_rope_raw, FA_ROPE_NONE, FA_ROPE_INTERLEAVED, FA_ROPE_HALF,
 )

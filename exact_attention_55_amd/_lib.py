@@ -15,6 +15,8 @@ import torch
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 FA_F16, FA_BF16, FA_FP8_E4M3 = 0, 1, 2
 FA_OUT_F32 = 0x100
+FA_ROPE_NONE, FA_ROPE_INTERLEAVED, FA_ROPE_HALF = 0, 1, 2
+ROPE_STYLES = {"interleaved": FA_ROPE_INTERLEAVED, "half": FA_ROPE_HALF}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -52,6 +54,8 @@ def lib():
     L.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     L.fa_decode_workspace_bytes.restype = ctypes.c_size_t
     L.fa_fp8_prep.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp]
+    L.fa_fp8_prep_rope.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+    L.fa_fp8_prep_rope.restype = i
     L.fa_fp8_prep.restype = i
     L.fa_fp8_packed_bytes.argtypes = [i, i, i, i]
     L.fa_fp8_packed_bytes.restype = ctypes.c_size_t
@@ -109,6 +113,12 @@ def decode_workspace_bytes(B, H, Nq, d, num_splits):
 
 def fp8_prep_raw(x, x8, signs, B, H, N, d, block_rows, in_dtype, stream=None):
     return lib().fa_fp8_prep(x, x8, signs, B, H, N, d, block_rows, in_dtype, stream)
+
+
+def fp8_prep_rope_raw(x, x8, signs, B, H, N, d, block_rows, in_dtype, rope_style, rope_base, pos0,
+                      stream=None):
+    return lib().fa_fp8_prep_rope(x, x8, signs, B, H, N, d, block_rows, in_dtype, int(rope_style),
+                                  float(rope_base), int(pos0), stream)
 
 
 def fp8_packed_bytes(B, H, N, d):
@@ -265,12 +275,14 @@ def fp8_scales_view(packed, B, H, N, d):
     return packed[off: off + 4 * B * H * nb].view(torch.float32).view(B, H, nb)
 
 
-def fp8_prep(x, signs=None, block_rows=128, out=None):
+def fp8_prep(x, signs=None, block_rows=128, out=None, rope=None):
     """Random-sign Hadamard (when signs is given) + fp8 e4m3 block quantisation.
 
     x: 16-bit [B,H,N,d] device tensor; signs: int8 [H,d] device tensor of +-1
-    or None; block_rows: 128, or 0 for one scale per tensor. Returns the
-    packed uint8 tensor (codes then float32 scales) that fwd_fp8 consumes.
+    or None; block_rows: 128, or 0 for one scale per tensor; rope: None, or
+    (style, base, pos0) with style "interleaved" or "half" to apply the
+    rotary embedding first, in the same pass. Returns the packed uint8 tensor
+    (codes then float32 scales) that fwd_fp8 consumes.
     """
     B, H, N, d = x.shape
     if out is None:
@@ -282,8 +294,14 @@ def fp8_prep(x, signs=None, block_rows=128, out=None):
         _check_device(x, out, signs)
     else:
         _check_device(x, out)
-    st = fp8_prep_raw(_ptr(x), _ptr(out), _ptr(signs), B, H, N, d, block_rows,
-                      _dtype_code(x), _stream(x.device))
+    if rope is None:
+        st = fp8_prep_raw(_ptr(x), _ptr(out), _ptr(signs), B, H, N, d, block_rows,
+                          _dtype_code(x), _stream(x.device))
+    else:
+        style, base, pos0 = rope
+        _check(style in ROPE_STYLES, f"rope style must be one of {sorted(ROPE_STYLES)}")
+        st = fp8_prep_rope_raw(_ptr(x), _ptr(out), _ptr(signs), B, H, N, d, block_rows,
+                               _dtype_code(x), ROPE_STYLES[style], base, pos0, _stream(x.device))
     if st != FA_OK:
         raise FaError(st, "fa_fp8_prep")
     return out

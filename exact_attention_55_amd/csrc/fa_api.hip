@@ -170,10 +170,17 @@ int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* l
     return from_hip(fa::launch_decode16(a, base == FA_BF16, s));
 }
 
-int fa_fp8_prep(const void* x, void* x8, const int8_t* signs, int B, int H, int N, int d,
-                int block_rows, int in_dtype, void* stream) {
+int fa_fp8_prep_rope(const void* x, void* x8, const int8_t* signs, int B, int H, int N, int d,
+                     int block_rows, int in_dtype, int rope_style, float rope_base, int pos0,
+                     void* stream) {
     if (in_dtype != FA_BF16 && in_dtype != FA_F16) return FA_ERR_INVALID_ARG;
     if (!sizes_ok(B, H, N, d)) return FA_ERR_INVALID_ARG;
+    if (rope_style != FA_ROPE_NONE && rope_style != FA_ROPE_INTERLEAVED && rope_style != FA_ROPE_HALF)
+        return FA_ERR_INVALID_ARG;
+    if (rope_style != FA_ROPE_NONE) {
+        if (!(rope_base > 0.0f) || !isfinite(rope_base)) return FA_ERR_INVALID_ARG;
+        if (pos0 < 0 || (long long)pos0 + N > (1LL << 24)) return FA_ERR_INVALID_ARG;
+    }
     if (block_rows != 0 && block_rows != fa::kQuantBlockRows) return FA_ERR_UNSUPPORTED;
     if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
     if ((long long)B * H * ((N + 127) / 128) > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
@@ -187,9 +194,19 @@ int fa_fp8_prep(const void* x, void* x8, const int8_t* signs, int B, int H, int 
     a.block_rows = block_rows;
     a.bf16 = in_dtype == FA_BF16;
     a.scales_off = fa_fp8_scales_offset(B, H, N, d);
+    a.rope_style = rope_style;
+    a.rope.pos0 = pos0;
+    for (int i = 0; i < 128; ++i)
+        a.rope.w[i] = i < d / 2 ? (float)pow((double)rope_base, -2.0 * i / d) : 0.0f;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     return from_hip(fa::launch_fp8_prep(a, s));
+}
+
+int fa_fp8_prep(const void* x, void* x8, const int8_t* signs, int B, int H, int N, int d,
+                int block_rows, int in_dtype, void* stream) {
+    return fa_fp8_prep_rope(x, x8, signs, B, H, N, d, block_rows, in_dtype, FA_ROPE_NONE, 1.0f, 0,
+                            stream);
 }
 
 }  // extern "C"

@@ -16,6 +16,16 @@
 // Per block: amax = max |y|, scale = amax / 448 (IEEE float32 division; 1 if
 // amax is 0), code = e4m3 round-to-nearest-even of y / scale after clamping to
 // +-448 (the clamp only absorbs the rounding of the scale).
+//
+// Rotary embedding (ROPE 1: pairs (2i, 2i+1); ROPE 2: pairs (i, i + d/2)):
+// the same section notes that the Hadamard step is fused into the rotary
+// step, both being memory-bound passes over Q and K. Before the signs, each
+// pair (a, b) of the row at position p = pos0 + row turns into
+// (a c - b s, a s + b c), c and s the float32 cosine and sine of the float32
+// product p * w_i; the frequencies w_i = base^(-2i/d) are rounded to float32
+// on the host and passed by value. Interleaved pairs sit inside a lane; for
+// the half pairing the partner of element e of lane j is element e of lane
+// j ^ (d/16).
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -38,10 +48,11 @@ __device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
 // MODE 1: only reduce amax of the whole tensor into *gamax (atomic max on the
 //         float bit pattern; amax >= 0 so integer order equals float order).
 // MODE 2: quantise with the tensor-wide scale from *gamax, store codes only.
-template <typename T, int D, bool HAD, int MODE>
+template <typename T, int D, bool HAD, int MODE, int ROPE>
 __global__ void __launch_bounds__(kPrepThreads)
 fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t* __restrict__ signs,
-                float* __restrict__ scales, unsigned* __restrict__ gamax, int N, int H, int nblk)
+                float* __restrict__ scales, unsigned* __restrict__ gamax, int N, int H, int nblk,
+                RopeFreqs rf)
 {
     constexpr int LPR = D / 8;                 // lanes per row
     constexpr int RPP = kPrepThreads / LPR;    // rows per pass
@@ -76,6 +87,41 @@ fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t*
         const T8 x = __builtin_bit_cast(T8, raw);
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[p][e] = to_f(x[e]);
+        if (ROPE != 0) {
+            const float pos = (float)(rf.pos0 + row);
+            if (ROPE == 1) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    float sn, cs;
+                    sincosf(pos * rf.w[4 * j + k], &sn, &cs);
+                    const float a = v[p][2 * k], b = v[p][2 * k + 1];
+                    v[p][2 * k] = a * cs - b * sn;
+                    v[p][2 * k + 1] = a * sn + b * cs;
+                }
+            } else {
+                // Lanes j and j ^ (LPR/2) need the same 8 angles: each takes
+                // the cosine and sine of 4 of them and trades with the other.
+                const bool second = j >= LPR / 2;
+                const int i0 = (8 * j) % (D / 2);
+                float cs[8], sn[8];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int e = second ? 4 + k : k;
+                    sincosf(pos * rf.w[i0 + e], &sn[e], &cs[e]);
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int mine = second ? 4 + k : k, theirs = second ? k : 4 + k;
+                    cs[theirs] = __shfl_xor(cs[mine], LPR / 2, 64);
+                    sn[theirs] = __shfl_xor(sn[mine], LPR / 2, 64);
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float other = __shfl_xor(v[p][e], LPR / 2, 64);
+                    v[p][e] = second ? v[p][e] * cs[e] + other * sn[e] : v[p][e] * cs[e] - other * sn[e];
+                }
+            }
+        }
         if (HAD) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[p][e] *= sg[e];
@@ -155,33 +201,43 @@ __global__ void __launch_bounds__(1024) fill_scales_kernel(float* scales, const 
     for (long long i = threadIdx.x; i < n; i += blockDim.x) scales[i] = s;
 }
 
-template <typename T, int D, bool HAD>
+template <typename T, int D, bool HAD, int ROPE>
 static hipError_t prep_t(const PrepArgs& a, hipStream_t s) {
     const int nblk = (a.N + kQuantBlockRows - 1) / kQuantBlockRows;
     const long long grid = (long long)a.B * a.H * nblk;
     float* scales = reinterpret_cast<float*>(a.x8 + a.scales_off);
     const T* x = static_cast<const T*>(a.x);
     if (a.block_rows != 0) {
-        hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 0>), dim3((unsigned)grid), dim3(kPrepThreads),
-                           0, s, x, a.x8, a.signs, scales, nullptr, a.N, a.H, nblk);
+        hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 0, ROPE>), dim3((unsigned)grid),
+                           dim3(kPrepThreads), 0, s, x, a.x8, a.signs, scales, nullptr, a.N, a.H, nblk,
+                           a.rope);
         return hipGetLastError();
     }
     // Per-tensor: the first scale slot serves as the amax accumulator; the
     // fill kernel reads it before overwriting every slot.
     unsigned* gamax = reinterpret_cast<unsigned*>(scales);
     hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(1), 0, s, gamax);
-    hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 1>), dim3((unsigned)grid), dim3(kPrepThreads), 0,
-                       s, x, a.x8, a.signs, scales, gamax, a.N, a.H, nblk);
-    hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 2>), dim3((unsigned)grid), dim3(kPrepThreads), 0,
-                       s, x, a.x8, a.signs, scales, gamax, a.N, a.H, nblk);
+    hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 1, ROPE>), dim3((unsigned)grid), dim3(kPrepThreads),
+                       0, s, x, a.x8, a.signs, scales, gamax, a.N, a.H, nblk, a.rope);
+    hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 2, ROPE>), dim3((unsigned)grid), dim3(kPrepThreads),
+                       0, s, x, a.x8, a.signs, scales, gamax, a.N, a.H, nblk, a.rope);
     hipLaunchKernelGGL(fill_scales_kernel, dim3(1), dim3(1024), 0, s, scales,
                        (const unsigned*)gamax, grid);
     return hipGetLastError();
 }
 
+template <typename T, int D, int ROPE>
+static hipError_t prep_r(const PrepArgs& a, hipStream_t s) {
+    return a.signs ? prep_t<T, D, true, ROPE>(a, s) : prep_t<T, D, false, ROPE>(a, s);
+}
+
 template <typename T, int D>
 static hipError_t prep_d(const PrepArgs& a, hipStream_t s) {
-    return a.signs ? prep_t<T, D, true>(a, s) : prep_t<T, D, false>(a, s);
+    switch (a.rope_style) {
+        case 1: return prep_r<T, D, 1>(a, s);
+        case 2: return prep_r<T, D, 2>(a, s);
+    }
+    return prep_r<T, D, 0>(a, s);
 }
 
 template <typename T>

@@ -30,6 +30,13 @@ hipError_t launch_fwd16(const FwdArgs& a, bool bf16, hipStream_t s);
 // FP8 e4m3 forward on packed tensors.
 hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t s);
 
+// Rotary frequencies w_i (float32, i < d/2) and the first row's position,
+// passed to the prep kernel by value.
+struct RopeFreqs {
+    float w[128];
+    int pos0;
+};
+
 struct PrepArgs {
     const void* x;
     uint8_t* x8;
@@ -38,6 +45,8 @@ struct PrepArgs {
     int block_rows;     // 128 or 0 (per tensor)
     bool bf16;
     size_t scales_off;
+    int rope_style;     // 0 none, 1 interleaved pairs, 2 half pairs
+    RopeFreqs rope;
 };
 hipError_t launch_fp8_prep(const PrepArgs& a, hipStream_t s);
 

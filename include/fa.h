@@ -199,6 +199,40 @@ int fa_fp8_prep(const void* x, void* x8, const int8_t* signs,
                 int B, int H, int N, int d, int block_rows, int in_dtype,
                 void* stream);
 
+/* Rotary pairings for fa_fp8_prep_rope. */
+enum fa_rope_style {
+    FA_ROPE_NONE = 0,
+    FA_ROPE_INTERLEAVED = 1,   /* pairs (2i, 2i+1) */
+    FA_ROPE_HALF = 2           /* pairs (i, i + d/2) */
+};
+
+/*
+ * fa_fp8_prep_rope - rotary embedding fused into fa_fp8_prep: the rotary
+ * step, the random-sign Hadamard and the FP8 block quantisation of Q or K in
+ * one pass over the tensor ("FlashAttention-3: Fast & Accurate Attention
+ * with Asynchrony & Low-Precision", "Incoherent Processing for FP8
+ * Accuracy": the Hadamard is fused into the memory-bound rotary step).
+ *
+ * Row n of every head is at position p = pos0 + n; each coordinate pair
+ * (a, b) (pairing rope_style) becomes (a cos t - b sin t, a sin t + b cos t)
+ * with t = p * w_i, w_i = rope_base^(-2i/d) for pair i < d/2. w_i and t are
+ * float32 (w_i rounded once from double precision, t the float32 product),
+ * cos t and sin t float32. Then as fa_fp8_prep (signs may be NULL: rotary +
+ * quantisation only).
+ *
+ *  rope_style  FA_ROPE_INTERLEAVED or FA_ROPE_HALF (FA_ROPE_NONE: same as
+ *           fa_fp8_prep).
+ *  rope_base   finite and > 0 (10000 in most models).
+ *  pos0     position of row 0, >= 0; pos0 + N <= 2^24 (positions exact in
+ *           float32).
+ *  other arguments as for fa_fp8_prep.
+ *
+ * Returns FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED or FA_ERR_HIP.
+ */
+int fa_fp8_prep_rope(const void* x, void* x8, const int8_t* signs,
+                     int B, int H, int N, int d, int block_rows, int in_dtype,
+                     int rope_style, float rope_base, int pos0, void* stream);
+
 /* Size in bytes of a packed FP8 tensor for [B][H][N][d]; 0 for invalid
  * sizes. Pure host arithmetic. */
 size_t fa_fp8_packed_bytes(int B, int H, int N, int d);

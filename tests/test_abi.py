@@ -194,3 +194,31 @@ def test_decode_sizes(L):
     assert fa.decode_splits(8, 16, 16, 1, 200, 128) == 1
     assert 1 <= fa.decode_splits(1, 1, 1, 1, 1 << 20, 64) <= 64
     assert fa.decode_splits(1, 3, 2, 1, 100, 128) == 1
+
+
+def prep_rope(**kw):
+    a = dict(x=FAKE, x8=FAKE, signs=None, B=1, H=1, N=128, d=128, block_rows=128,
+             in_dtype=fa.FA_BF16, style=fa.FA_ROPE_HALF, base=10000.0, pos0=0)
+    a.update(kw)
+    return fa.fp8_prep_rope_raw(a["x"], a["x8"], a["signs"], a["B"], a["H"], a["N"], a["d"],
+                                a["block_rows"], a["in_dtype"], a["style"], a["base"], a["pos0"],
+                                None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(style=3), fa.FA_ERR_INVALID_ARG),
+    (dict(style=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(base=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(base=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(pos0=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(pos0=(1 << 24) - 100), fa.FA_ERR_INVALID_ARG),     # positions past 2^24
+    (dict(in_dtype=fa.FA_FP8_E4M3), fa.FA_ERR_INVALID_ARG),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(block_rows=64), fa.FA_ERR_UNSUPPORTED),
+    (dict(x8=FAKE + 16), fa.FA_ERR_INVALID_ARG),
+    (dict(x=None), fa.FA_ERR_INVALID_ARG),
+    (dict(N=0), fa.FA_OK),
+    (dict(style=fa.FA_ROPE_NONE, base=0.0, pos0=-5, N=0), fa.FA_OK),   # no rotary: not checked
+])
+def test_prep_rope_validation(L, kw, status):
+    assert prep_rope(**kw) == status

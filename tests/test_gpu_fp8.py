@@ -32,10 +32,10 @@ def say(msg):
     sys.stdout.flush()
 
 
-def gpu_prep(x, signs, block_rows):
+def gpu_prep(x, signs, block_rows, rope=None):
     B, H, N, d = x.shape
     sd = None if signs is None else torch.from_numpy(signs).to(DEV)
-    packed = fa.fp8_prep(x.to(DEV), sd, block_rows)
+    packed = fa.fp8_prep(x.to(DEV), sd, block_rows, rope=rope)
     torch.cuda.synchronize()
     codes = fa.fp8_codes_view(packed, B, H, N, d).cpu().numpy()
     scales = fa.fp8_scales_view(packed, B, H, N, d).cpu().numpy()
@@ -83,10 +83,10 @@ def test_prep_fp16_and_zero_block():
     assert scales[0, 1, 1] == 1.0 and np.all(codes[0, 1, 128:] == 0)
 
 
-def fp8_run(q, k, v, signs, block_rows, causal, out_f32=True):
+def fp8_run(q, k, v, signs, block_rows, causal, out_f32=True, rope=None):
     B, H, N, d = q.shape
-    q8, _, _ = gpu_prep(q, signs, block_rows)
-    k8, _, _ = gpu_prep(k, signs, block_rows)
+    q8, _, _ = gpu_prep(q, signs, block_rows, rope)
+    k8, _, _ = gpu_prep(k, signs, block_rows, rope)
     v8, _, _ = gpu_prep(v, None, block_rows)
     o, lse = fa.fwd_fp8(q8, k8, v8, B, H, N, d, causal=causal, out_f32=out_f32)
     torch.cuda.synchronize()
@@ -145,3 +145,58 @@ def test_fp8_workload_outliers():
     _, lse_fq = oracle.attention_rows(oracle.fp8_dequantize(qc, qs), oracle.fp8_dequantize(kc, ks),
                                       oracle.fp8_dequantize(vc, vs), 0, 0, rows, False)
     check_lse(res["hadamard_block"][1][0, 0, rows], lse_fq)
+
+
+# ---- rotary embedding fused into the prep (cos/sin are float32 on both
+# sides but the GPU's sincosf may differ from the correctly rounded values in
+# the last bit, so codes are compared like the Hadamard case) ----
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("style", ["interleaved", "half"])
+@pytest.mark.parametrize("had", [False, True])
+def test_prep_rope_matches_oracle(d, style, had):
+    say(f"prep rope d={d} style={style} had={had}")
+    B, H, N = 2, 2, 300
+    x, _, _ = make_qkv(B, H, N, d, seed=41 + d, dtype="bf16", outliers=True)
+    signs = make_signs(H, d, 41) if had else None
+    rope = (style, 10000.0, 1000)
+    _, codes, scales = gpu_prep(x, signs, 128, rope)
+    rc, rs = oracle.fp8_quantize(to_f64(x), signs, 128, rope)
+    compare_codes(codes, scales, rc, rs, exact=False)
+
+
+@pytest.mark.parametrize("style", ["interleaved", "half"])
+def test_prep_rope_large_positions_and_tensor_scale(style):
+    """Positions near 2^24 (large angles) and the per-tensor scale."""
+    say(f"prep rope large positions {style}")
+    B, H, N, d = 1, 2, 256, 128
+    x, _, _ = make_qkv(B, H, N, d, seed=47, dtype="fp16")
+    rope = (style, 500000.0, (1 << 24) - N)
+    signs = make_signs(H, d, 47)
+    for br in (128, 0):
+        _, codes, scales = gpu_prep(x, signs, br, rope)
+        rc, rs = oracle.fp8_quantize(to_f64(x), signs, br, rope)
+        compare_codes(codes, scales, rc, rs, exact=False)
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,style", [
+    (1, 2, 300, 64, False, "interleaved"), (1, 2, 520, 128, True, "half"),
+    (2, 2, 640, 128, False, "interleaved"), (1, 1, 200, 256, True, "half"),
+])
+def test_fp8_rope_forward_vs_oracles(B, H, N, d, causal, style):
+    """prep (rotary + Hadamard + block quantisation) of Q and K, prep of V,
+    fp8 forward: within the fp8 RMSE bound of the exact attention of the
+    rotary-embedded inputs, LSE within 1e-3 of the fake-quant oracle."""
+    say(f"fp8 rope forward B={B} H={H} N={N} d={d} causal={causal} {style}")
+    q, k, v = make_qkv(B, H, N, d, seed=51 + N, dtype="bf16")
+    signs = make_signs(H, d, 51)
+    rope = (style, 10000.0, 7)
+    q64, k64, v64 = to_f64(q), to_f64(k), to_f64(v)
+    o, lse = fp8_run(q, k, v, signs, 128, causal, rope=rope)
+    o_ref, _ = oracle.attention(oracle.rope(q64, *rope), oracle.rope(k64, *rope), v64, causal)
+    _, rmse = errors(o, o_ref)
+    assert rmse <= FP8_RMSE, f"fp8 RMSE {rmse:.3e}"
+    o_fq, lse_fq, *_ = oracle.fake_quant_attention(q64, k64, v64, signs, 128, causal, rope=rope)
+    check_lse(lse, lse_fq)
+    _, rmse_fq = errors(o, o_fq)
+    assert rmse_fq <= FP8_RMSE / 2, f"RMSE vs fake-quant {rmse_fq:.3e}"
