@@ -34,6 +34,63 @@ namespace fa {
 constexpr float kE4M3Max = 448.0f;
 constexpr int kPrepThreads = 256;
 
+// Value of x held by lane (l ^ M). Distances inside a row of 16 lanes go
+// through DPP moves (VALU): xor 1 and 2 are quad permutations; xor 4 is the
+// half-row mirror (l ^ 7) followed by the quad reversal (^ 3); xor 8 is the
+// row mirror (l ^ 15) followed by the half-row mirror (^ 7). Longer
+// distances use the LDS permute.
+template <int M>
+__device__ __forceinline__ float lane_xor(float x) {
+    const int v = __float_as_int(x);
+    if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true));
+    if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true));
+    if constexpr (M == 4) {
+        const int h = __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true);
+        return __int_as_float(__builtin_amdgcn_mov_dpp(h, 0x1B, 0xF, 0xF, true));
+    }
+    if constexpr (M == 8) {
+        const int r = __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, true);
+        return __int_as_float(__builtin_amdgcn_mov_dpp(r, 0x141, 0xF, 0xF, true));
+    }
+    if constexpr (M >= 16) return __shfl_xor(x, M, 64);
+}
+
+// sin and cos of a float32 angle t, |t| < 2^25. Reduction t = k (pi/2) + r
+// in double precision with pi/2 split into two doubles (the error of r is far
+// below a float32 ulp even for k near 2^24), then the Taylor series of sin
+// and cos on |r| <= pi/4 in float32 (truncation below 1e-11), and the
+// quadrant k mod 4 selects and signs the pair.
+__device__ __forceinline__ void sincos_f32(float t, float* sn, float* cs) {
+    constexpr double kPio2Hi = 1.5707963267948966;          // nearest double to pi/2
+    constexpr double kPio2Lo = 6.123233995736766e-17;       // pi/2 - kPio2Hi
+    constexpr double k2OverPi = 0.63661977236758134;
+    const double td = (double)t;
+    const double k = __builtin_rint(td * k2OverPi);
+    const double rd = __builtin_fma(-k, kPio2Lo, __builtin_fma(-k, kPio2Hi, td));
+    const float r = (float)rd;
+    const float r2 = r * r;
+    // sin r = r (1 - r^2/3! + r^4/5! - ... - r^10/11!)
+    float ps = -1.0f / 39916800.0f;
+    ps = fmaf(ps, r2, 1.0f / 362880.0f);
+    ps = fmaf(ps, r2, -1.0f / 5040.0f);
+    ps = fmaf(ps, r2, 1.0f / 120.0f);
+    ps = fmaf(ps, r2, -1.0f / 6.0f);
+    const float s0 = fmaf(r * r2, ps, r);
+    // cos r = 1 - r^2/2! + r^4/4! - ... + r^12/12!
+    float pc = 1.0f / 479001600.0f;
+    pc = fmaf(pc, r2, -1.0f / 3628800.0f);
+    pc = fmaf(pc, r2, 1.0f / 40320.0f);
+    pc = fmaf(pc, r2, -1.0f / 720.0f);
+    pc = fmaf(pc, r2, 1.0f / 24.0f);
+    pc = fmaf(pc, r2, -0.5f);
+    const float c0 = fmaf(r2, pc, 1.0f);
+    const int q = (int)(long long)k & 3;
+    const float a = (q & 1) ? c0 : s0;      // sin for q = 0, 2; cos for q = 1, 3
+    const float b = (q & 1) ? s0 : c0;
+    *sn = (q & 2) ? -a : a;
+    *cs = ((q + 1) & 2) ? -b : b;           // cos negated for q = 1, 2
+}
+
 __device__ __forceinline__ float to_f(__bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f(_Float16 x) { return (float)x; }
 
@@ -93,7 +150,7 @@ fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t*
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     float sn, cs;
-                    sincosf(pos * rf.w[4 * j + k], &sn, &cs);
+                    sincos_f32(pos * rf.w[4 * j + k], &sn, &cs);
                     const float a = v[p][2 * k], b = v[p][2 * k + 1];
                     v[p][2 * k] = a * cs - b * sn;
                     v[p][2 * k + 1] = a * sn + b * cs;
@@ -107,17 +164,17 @@ fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t*
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const int e = second ? 4 + k : k;
-                    sincosf(pos * rf.w[i0 + e], &sn[e], &cs[e]);
+                    sincos_f32(pos * rf.w[i0 + e], &sn[e], &cs[e]);
                 }
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const int mine = second ? 4 + k : k, theirs = second ? k : 4 + k;
-                    cs[theirs] = __shfl_xor(cs[mine], LPR / 2, 64);
-                    sn[theirs] = __shfl_xor(sn[mine], LPR / 2, 64);
+                    cs[theirs] = lane_xor<LPR / 2>(cs[mine]);
+                    sn[theirs] = lane_xor<LPR / 2>(sn[mine]);
                 }
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float other = __shfl_xor(v[p][e], LPR / 2, 64);
+                    const float other = lane_xor<LPR / 2>(v[p][e]);
                     v[p][e] = second ? v[p][e] * cs[e] + other * sn[e] : v[p][e] * cs[e] - other * sn[e];
                 }
             }
@@ -136,15 +193,17 @@ fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t*
                         v[p][e + span] = a - b;
                     }
             // cross-lane butterflies, spans 8 .. D/2 (partner lane j ^ m)
+            static_for<0, 5>([&](auto mc) {
+                constexpr int m = 1 << decltype(mc)::value;
+                if constexpr (m < LPR) {
+                    const bool upper = (j & m) != 0;
 #pragma unroll
-            for (int m = 1; m < LPR; m *= 2) {
-                const bool upper = (j & m) != 0;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float other = __shfl_xor(v[p][e], m, 64);
-                    v[p][e] = upper ? (other - v[p][e]) : (v[p][e] + other);
+                    for (int e = 0; e < 8; ++e) {
+                        const float other = lane_xor<m>(v[p][e]);
+                        v[p][e] = upper ? (other - v[p][e]) : (v[p][e] + other);
+                    }
                 }
-            }
+            });
             const float rs = 1.0f / __builtin_sqrtf((float)D);
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[p][e] *= rs;
