@@ -28,6 +28,7 @@ Modules:
     quant       block / per-tensor fp8 quantisation and fake-quant attention
     backward    gradients dQ, dK, dV of exact attention (chain rule, materialised)
     rope        rotary position embedding (interleaved or half pairing)
+    mx          microscaled e4m3 quantisation (power-of-two scale per 32 elements)
     decode      the same attention for few query rows over a long, ragged key
                 history (grouped key/value heads, bottom-right causal)
 
@@ -43,3 +44,4 @@ from .quant import fp8_quantize, fp8_dequantize, fake_quant_attention  # noqa: F
 from .backward import attention_backward, attention_delta  # noqa: F401
 from .decode import attention_decode, visible_keys  # noqa: F401
 from .rope import rope, rope_angles, rope_cos_sin, rope_frequencies  # noqa: F401
+from .mx import mx_quantize, mx_dequantize, fake_quant_attention_mx  # noqa: F401
