@@ -56,13 +56,6 @@ __device__ __forceinline__ void vm_wait() {
     static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit field");
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-// 16 bytes per lane from a buffer into registers, untracked by the compiler:
-// the result is valid only after an explicit vm_wait covers the load.
-__device__ __forceinline__ u32x4 buffer_load16_async(i32x4 rsrc, uint32_t voff) {
-    u32x4 r;
-    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(r) : "v"(voff), "s"(rsrc) : "memory");
-    return r;
-}
 // Every LDS read of the wave has returned (before a copy overwrites a stage).
 __device__ __forceinline__ void lds_reads_done() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
@@ -119,15 +112,15 @@ decode16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     const int klim = CAUSAL ? L - Nq + qi : L - 1;       // last key this row sees
     const int kfree = CAUSAL ? L - Nq + 1 : L;           // keys below: seen by every row
 
-    // Q^T fragments (B operand): lane holds d = 16 ch + 8 hi .. +7 of its row.
-    // The group's M rows are contiguous (heads hkv*g .. hkv*g + g - 1, Nq rows
-    // each); rows >= M fall outside the buffer range and read as zeros. The
-    // loads go through asm so that the compiler does not add its own
-    // (stricter) wait for them; see the wait after the first copies.
-    const i32x4 qrs = make_rsrc(Qg + ((long long)b * H + hkv * g) * Nq * D, M * RB);
-    u32x4 qraw[NCH];
+    // Q^T fragments (B operand): lane holds d = 16 ch + 8 hi .. +7 of its row;
+    // rows >= M are zeros. Waited for (a wait the compiler sees) before the
+    // first copy is issued.
+    X8 qf[NCH];
 #pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) qraw[ch] = buffer_load16_async(qrs, r * RB + 32 * ch + 16 * hi);
+    for (int ch = 0; ch < NCH; ++ch)
+        qf[ch] = rv ? load16<X8>(Qg + qrow * D + 16 * ch + 8 * hi)
+                    : __builtin_bit_cast(X8, u32x4{0, 0, 0, 0});
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
 
     // Copies: buffer loads over the sequence's L rows (rows >= L read as
     // zeros) straight into LDS; load j fills bytes [1024 j, +1024) of a block,
@@ -178,20 +171,9 @@ decode16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     float l = 0.f;         // sum of the rounded P fed to the MFMA
     float lx = 0.f;        // sum of the fp32 p (for the log-sum-exp)
 
-    // The first NST-1 blocks are requested while Q is still in flight; the
-    // wait below covers Q (issued before them) but not the copies.
 #pragma unroll
-    for (int j = 0; j < NST - 1; ++j)
+    for (int j = 0; j < NST; ++j)
         if (j < nblk) issue(j);
-    if (NST - 1 < nblk) vm_wait<LPB * (NST - 1)>();
-    else vm_wait<0>();
-    X8 qf[NCH];
-#pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) {
-        asm volatile("" : "+v"(qraw[ch]));           // Q is used only after the wait
-        qf[ch] = __builtin_bit_cast(X8, qraw[ch]);
-    }
-    if (NST - 1 < nblk) issue(NST - 1);
 
     for (int j = 0; j < nblk; ++j) {
         if (j + NST - 1 < nblk) vm_wait<LPB * (NST - 1)>();
