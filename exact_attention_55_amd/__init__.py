@@ -16,4 +16,5 @@ from ._lib import (  # noqa: F401
     fp8_alloc_packed, fp8_scales_view, fp8_codes_view, status_string,
     fwd_decode, decode_raw, decode_splits, decode_workspace_bytes,
     fp8_prep_rope_raw, FA_ROPE_NONE, FA_ROPE_INTERLEAVED, FA_ROPE_HALF,
+    FA_FP8_MX, FA_MX_ALONG_D, FA_MX_ALONG_N, mx_prep, mx_prep_raw, mx_packed_bytes, mx_scales_view,
 )

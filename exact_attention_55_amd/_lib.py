@@ -13,7 +13,8 @@ import os
 import torch
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
-FA_F16, FA_BF16, FA_FP8_E4M3 = 0, 1, 2
+FA_F16, FA_BF16, FA_FP8_E4M3, FA_FP8_MX = 0, 1, 2, 3
+FA_MX_ALONG_D, FA_MX_ALONG_N = 0, 1
 FA_OUT_F32 = 0x100
 FA_ROPE_NONE, FA_ROPE_INTERLEAVED, FA_ROPE_HALF = 0, 1, 2
 ROPE_STYLES = {"interleaved": FA_ROPE_INTERLEAVED, "half": FA_ROPE_HALF}
@@ -54,6 +55,10 @@ def lib():
     L.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     L.fa_decode_workspace_bytes.restype = ctypes.c_size_t
     L.fa_fp8_prep.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp]
+    L.fa_mx_prep.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp]
+    L.fa_mx_prep.restype = i
+    L.fa_mx_packed_bytes.argtypes = [i, i, i, i]
+    L.fa_mx_packed_bytes.restype = ctypes.c_size_t
     L.fa_fp8_prep_rope.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
     L.fa_fp8_prep_rope.restype = i
     L.fa_fp8_prep.restype = i
@@ -119,6 +124,14 @@ def fp8_prep_rope_raw(x, x8, signs, B, H, N, d, block_rows, in_dtype, rope_style
                       stream=None):
     return lib().fa_fp8_prep_rope(x, x8, signs, B, H, N, d, block_rows, in_dtype, int(rope_style),
                                   float(rope_base), int(pos0), stream)
+
+
+def mx_prep_raw(x, x8, signs, B, H, N, d, axis, in_dtype, stream=None):
+    return lib().fa_mx_prep(x, x8, signs, B, H, N, d, int(axis), in_dtype, stream)
+
+
+def mx_packed_bytes(B, H, N, d):
+    return int(lib().fa_mx_packed_bytes(B, H, N, d))
 
 
 def fp8_packed_bytes(B, H, N, d):
@@ -307,9 +320,46 @@ def fp8_prep(x, signs=None, block_rows=128, out=None, rope=None):
     return out
 
 
+def mx_prep(x, signs=None, axis="d", out=None):
+    """fp8 e4m3 quantisation with a power-of-two scale per 32 elements,
+    along d (axis "d": Q and K, optionally after the random-sign Hadamard)
+    or along the sequence (axis "n": V). Returns the packed uint8 tensor
+    (codes, then E8M0 scale bytes) that fwd_fp8(..., mx=True) consumes."""
+    B, H, N, d = x.shape
+    _check(axis in ("d", "n"), "axis must be 'd' or 'n'")
+    if out is None:
+        out = torch.empty(mx_packed_bytes(B, H, N, d), dtype=torch.uint8, device=x.device)
+    _check(out.dtype == torch.uint8 and out.numel() >= mx_packed_bytes(B, H, N, d),
+           "packed output too small")
+    if signs is not None:
+        _check(signs.dtype == torch.int8 and tuple(signs.shape) == (H, d), "signs must be int8 [H, d]")
+        _check_device(x, out, signs)
+    else:
+        _check_device(x, out)
+    st = mx_prep_raw(_ptr(x), _ptr(out), _ptr(signs), B, H, N, d,
+                     FA_MX_ALONG_D if axis == "d" else FA_MX_ALONG_N, _dtype_code(x),
+                     _stream(x.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_mx_prep")
+    return out
+
+
+def mx_scales_view(packed, B, H, N, d, axis):
+    """E8M0 scale bytes of a packed microscaled tensor: [B,H,N,d/32] for
+    axis "d"; [B,H,ceil(N/32),32,d/32] for axis "n" (column c of a 32-row
+    block at [c % 32, c // 32])."""
+    off = int(lib().fa_fp8_scales_offset(B, H, N, d))
+    if axis == "d":
+        n = B * H * N * (d // 32)
+        return packed[off: off + n].view(B, H, N, d // 32)
+    nb = (N + 31) // 32
+    return packed[off: off + B * H * nb * d].view(B, H, nb, 32, d // 32)
+
+
 def fwd_fp8(q8, k8, v8, B, H, N, d, causal=False, softmax_scale=None, out_f32=False,
-            out=None, lse=None):
-    """Attention forward on packed fp8 tensors made by fp8_prep.
+            out=None, lse=None, mx=False):
+    """Attention forward on packed fp8 tensors made by fp8_prep (mx=False)
+    or by mx_prep (mx=True: q and k along d, v along n).
 
     Returns (o, lse) with o bf16 (float32 with out_f32=True).
     """
@@ -320,8 +370,8 @@ def fwd_fp8(q8, k8, v8, B, H, N, d, causal=False, softmax_scale=None, out_f32=Fa
         out = torch.empty((B, H, N, d), dtype=odt, device=q8.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
-    code = FA_FP8_E4M3 | (FA_OUT_F32 if out_f32 else 0)
-    need = fp8_packed_bytes(B, H, N, d)
+    code = (FA_FP8_MX if mx else FA_FP8_E4M3) | (FA_OUT_F32 if out_f32 else 0)
+    need = mx_packed_bytes(B, H, N, d) if mx else fp8_packed_bytes(B, H, N, d)
     for t in (q8, k8, v8):
         _check(t.dtype == torch.uint8 and t.numel() >= need, "packed fp8 input too small")
     _check(out.shape == (B, H, N, d) and out.dtype == odt, "bad output tensor")

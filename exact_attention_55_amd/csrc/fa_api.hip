@@ -58,7 +58,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     const int base = dtype & 0xff;
     const int flags = dtype & ~0xff;
     if ((flags & ~FA_OUT_F32) != 0) return FA_ERR_INVALID_ARG;
-    if (base != FA_F16 && base != FA_BF16 && base != FA_FP8_E4M3) return FA_ERR_INVALID_ARG;
+    if (base != FA_F16 && base != FA_BF16 && base != FA_FP8_E4M3 && base != FA_FP8_MX)
+        return FA_ERR_INVALID_ARG;
     if (!sizes_ok(B, H, N, d)) return FA_ERR_INVALID_ARG;
     if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return FA_ERR_INVALID_ARG;
     if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
@@ -67,7 +68,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     if ((long long)N * d * 2 > kMaxHeadBytes) return FA_ERR_UNSUPPORTED;
     if (B == 0 || H == 0 || N == 0) return FA_OK;
     if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
-    const size_t qa = base == FA_FP8_E4M3 ? 256 : 16;
+    const bool fp8 = base == FA_FP8_E4M3 || base == FA_FP8_MX;
+    const size_t qa = fp8 ? 256 : 16;
     if (!aligned(q, qa) || !aligned(k, qa) || !aligned(v, qa) || !aligned(o, 16) ||
         !aligned(lse, 4))
         return FA_ERR_INVALID_ARG;
@@ -79,9 +81,10 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     a.scale = softmax_scale;
     a.out_f32 = (flags & FA_OUT_F32) != 0;
     a.scales_off = fa_fp8_scales_offset(B, H, N, d);
+    a.mx = base == FA_FP8_MX;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();   // do not report an earlier, unrelated error
-    if (base == FA_FP8_E4M3) return from_hip(fa::launch_fwd_fp8(a, s));
+    if (fp8) return from_hip(fa::launch_fwd_fp8(a, s));
     return from_hip(fa::launch_fwd16(a, base == FA_BF16, s));
 }
 
@@ -195,9 +198,44 @@ int fa_fp8_prep_rope(const void* x, void* x8, const int8_t* signs, int B, int H,
     a.bf16 = in_dtype == FA_BF16;
     a.scales_off = fa_fp8_scales_offset(B, H, N, d);
     a.rope_style = rope_style;
+    a.mx = fa::kMxNone;
     a.rope.pos0 = pos0;
     for (int i = 0; i < 128; ++i)
         a.rope.w[i] = i < d / 2 ? (float)pow((double)rope_base, -2.0 * i / d) : 0.0f;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    return from_hip(fa::launch_fp8_prep(a, s));
+}
+
+size_t fa_mx_packed_bytes(int B, int H, int N, int d) {
+    if (!sizes_ok(B, H, N, d) || d % 32 != 0) return 0;
+    const size_t rows = (size_t)B * H * N * (d / 32);
+    const size_t cols = (size_t)B * H * ((N + 31) / 32) * d;
+    return fa::round_up(fa_fp8_scales_offset(B, H, N, d) + (rows > cols ? rows : cols), 256);
+}
+
+int fa_mx_prep(const void* x, void* x8, const int8_t* signs, int B, int H, int N, int d, int axis,
+               int in_dtype, void* stream) {
+    if (in_dtype != FA_BF16 && in_dtype != FA_F16) return FA_ERR_INVALID_ARG;
+    if (axis != FA_MX_ALONG_D && axis != FA_MX_ALONG_N) return FA_ERR_INVALID_ARG;
+    if (axis == FA_MX_ALONG_N && signs) return FA_ERR_INVALID_ARG;
+    if (!sizes_ok(B, H, N, d)) return FA_ERR_INVALID_ARG;
+    if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * H * ((N + 31) / 32) > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0 || N == 0) return FA_OK;
+    if (!x || !x8) return FA_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(x8, 256)) return FA_ERR_INVALID_ARG;
+
+    fa::PrepArgs a;
+    a.x = x; a.x8 = static_cast<uint8_t*>(x8); a.signs = signs;
+    a.B = B; a.H = H; a.N = N; a.d = d;
+    a.block_rows = fa::kQuantBlockRows;
+    a.bf16 = in_dtype == FA_BF16;
+    a.scales_off = fa_fp8_scales_offset(B, H, N, d);
+    a.rope_style = 0;
+    a.rope.pos0 = 0;
+    for (int i = 0; i < 128; ++i) a.rope.w[i] = 0.0f;
+    a.mx = axis == FA_MX_ALONG_D ? fa::kMxAlongD : fa::kMxAlongN;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     return from_hip(fa::launch_fp8_prep(a, s));

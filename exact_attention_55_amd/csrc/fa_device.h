@@ -74,6 +74,12 @@ __device__ __forceinline__ f32x16 mfma32(const f16x8& a, const f16x8& b, const f
 __device__ __forceinline__ f32x16 mfma32_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
+// Same with per-lane E8M0 scales: lane l's 32 A values (row l % 32, k-half
+// l / 32) are multiplied by 2^(sa - 127), its 32 B values by 2^(sb - 127).
+__device__ __forceinline__ f32x16 mfma32_fp8s(const i32x8& a, const i32x8& b, const f32x16& c, int sa,
+                                              int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
 
 // Transposing LDS read of 16-bit data. Within each group of 16 lanes the 16
 // eight-byte reads form a 4 x 16 tile (lane j supplies row j/4, columns

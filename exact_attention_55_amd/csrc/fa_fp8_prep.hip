@@ -91,6 +91,18 @@ __device__ __forceinline__ void sincos_f32(float t, float* sn, float* cs) {
     *cs = ((q + 1) & 2) ? -b : b;           // cos negated for q = 1, 2
 }
 
+// Microscaling exponent of a block with maximum magnitude a: floor(log2 a)
+// minus 8 (the exponent of 448, the largest e4m3 normal), clamped to the
+// E8M0 range [-127, 127]; -127 for a = 0 or a subnormal a (the block then
+// quantises to zeros). floor(log2 a) of a normal float is its biased
+// exponent field minus 127.
+__device__ __forceinline__ int mx_exponent(float a) {
+    const int field = (__float_as_int(a) >> 23) & 0xff;
+    if (field == 0) return -127;
+    const int e = field - 127 - 8;
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
 __device__ __forceinline__ float to_f(__bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f(_Float16 x) { return (float)x; }
 
@@ -105,6 +117,9 @@ __device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
 // MODE 1: only reduce amax of the whole tensor into *gamax (atomic max on the
 //         float bit pattern; amax >= 0 so integer order equals float order).
 // MODE 2: quantise with the tensor-wide scale from *gamax, store codes only.
+// MODE 3: microscaling along d: one power-of-two scale per 32 columns of a
+//         row (4 lanes), stored as the E8M0 byte e + 127 at
+//         scales[row of the tensor][column block] (see mx_exponent).
 template <typename T, int D, bool HAD, int MODE, int ROPE>
 __global__ void __launch_bounds__(kPrepThreads)
 fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t* __restrict__ signs,
@@ -214,6 +229,33 @@ fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t*
         }
     }
 
+    if (MODE == 3) {
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+            const int row = blk * kQuantBlockRows + p * RPP + rp;
+            float la = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) la = fmaxf(la, fabsf(v[p][e]));
+            la = fmaxf(la, lane_xor<1>(la));
+            la = fmaxf(la, lane_xor<2>(la));
+            const int ex = mx_exponent(la);
+            if (row < N) {
+                uint32_t w[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const float* x = &v[p][4 * h];
+                    w[h] = e4m3x2(__builtin_ldexpf(x[0], -ex), __builtin_ldexpf(x[1], -ex)) |
+                           (e4m3x2(__builtin_ldexpf(x[2], -ex), __builtin_ldexpf(x[3], -ex)) << 16);
+                }
+                *reinterpret_cast<u32x2*>(X8 + head + (size_t)row * D + 8 * j) = u32x2{w[0], w[1]};
+                if ((j & 3) == 0)
+                    reinterpret_cast<uint8_t*>(scales)[((size_t)bh * N + row) * (D / 32) + j / 4] =
+                        (uint8_t)(ex + 127);
+            }
+        }
+        return;
+    }
+
     if (MODE != 2) {
         // workgroup amax
 #pragma unroll
@@ -245,6 +287,37 @@ fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t*
     }
 }
 
+// Microscaling along the sequence (V): one workgroup per (head, 32-row
+// block), one lane per column; the block's scale for column c is stored at
+// byte (c % 32) * (D / 32) + c / 32 of the block's D scale bytes, the order
+// in which a lane of the PV matrix instruction wants its column scales.
+template <typename T, int D>
+__global__ void __launch_bounds__(D)
+mx_prep_cols_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, uint8_t* __restrict__ scales,
+                    int N, int nkb)
+{
+    const int c = threadIdx.x;
+    const int bh = blockIdx.x / nkb, kb = blockIdx.x % nkb;
+    const int r0 = kb * 32;
+    const int nr = min(32, N - r0);
+    const size_t head = (size_t)bh * N * D;
+    float x[32];
+    float a = 0.f;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+        x[r] = r < nr ? to_f(X[head + (size_t)(r0 + r) * D + c]) : 0.f;
+        a = fmaxf(a, fabsf(x[r]));
+    }
+    const int ex = mx_exponent(a);
+#pragma unroll
+    for (int r = 0; r < 32; r += 2) {
+        const uint32_t w = e4m3x2(__builtin_ldexpf(x[r], -ex), __builtin_ldexpf(x[r + 1], -ex));
+        if (r < nr) X8[head + (size_t)(r0 + r) * D + c] = (uint8_t)(w & 0xff);
+        if (r + 1 < nr) X8[head + (size_t)(r0 + r + 1) * D + c] = (uint8_t)(w >> 8);
+    }
+    scales[((size_t)bh * nkb + kb) * D + (c % 32) * (D / 32) + c / 32] = (uint8_t)(ex + 127);
+}
+
 __global__ void zero_u32_kernel(unsigned* p) { *p = 0u; }
 
 // One workgroup: read the tensor-wide amax first, then fill every slot.
@@ -266,6 +339,18 @@ static hipError_t prep_t(const PrepArgs& a, hipStream_t s) {
     const long long grid = (long long)a.B * a.H * nblk;
     float* scales = reinterpret_cast<float*>(a.x8 + a.scales_off);
     const T* x = static_cast<const T*>(a.x);
+    if (a.mx == kMxAlongN) {
+        const int nkb = (a.N + 31) / 32;
+        hipLaunchKernelGGL((mx_prep_cols_kernel<T, D>), dim3((unsigned)((long long)a.B * a.H * nkb)),
+                           dim3(D), 0, s, x, a.x8, a.x8 + a.scales_off, a.N, nkb);
+        return hipGetLastError();
+    }
+    if (a.mx == kMxAlongD) {
+        hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 3, ROPE>), dim3((unsigned)grid),
+                           dim3(kPrepThreads), 0, s, x, a.x8, a.signs, scales, nullptr, a.N, a.H, nblk,
+                           a.rope);
+        return hipGetLastError();
+    }
     if (a.block_rows != 0) {
         hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 0, ROPE>), dim3((unsigned)grid),
                            dim3(kPrepThreads), 0, s, x, a.x8, a.signs, scales, nullptr, a.N, a.H, nblk,

@@ -26,12 +26,21 @@
 //    values sum to at most 256, and p >= 2^-9 stays normal;
 //  * the row sum l accumulates the unquantised p (rowsum(P') / (8 w_j));
 //  * epilogue: O = O_acc * sv_max / (8 l).
+// Microscaled inputs (fa_mx_prep: one power-of-two E8M0 scale per 32
+// elements, along d for Q and K, along the sequence for V) take the scaled
+// form of the same MFMA, which applies a per-lane scale byte to each 32
+// k-values of A and of B: the score MFMAs take the Q and K bytes of their
+// d-block, the PV MFMAs the V bytes of their 32-key block and 2^-3 for P'
+// (so P' = 8p exactly as above, without w_j), the logits only the softmax
+// scale, and the epilogue is O = O_acc / l. The scale bytes of a tile travel
+// into LDS with the tile.
 #include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
 
 constexpr float kPScale = 8.0f;     // P multiplier before e4m3 rounding
+constexpr int kPScaleE8M0 = 124;    // 2^-3: the microscaled PV MFMA undoes kPScale
 constexpr float kBig8 = 384.0f;     // per-lane tile sum of P' that forces the exact-maximum path
 
 #ifndef FA8_CFG_64
@@ -58,7 +67,22 @@ __device__ __forceinline__ uint32_t cvt4_e4m3(float a, float b, float c, float d
     return (uint32_t)w;
 }
 
-template <int D, int BC>
+// Per-lane E8M0 scale bytes of one tile for the microscaled path, kept as
+// the loaded words (SW = ceil(d/128) words of 4 bytes): k[kb] holds the key
+// row's bytes shifted right by 8*hi, so the score MFMA of k-step ch takes
+// byte 2*ch of it; v holds the V bytes of the lane's d-row, byte db for
+// d-block db. Unused (and optimised away) on the block-scaled path.
+template <int NKB, int SW>
+struct TileScales {
+    uint32_t k[NKB][SW];
+    uint32_t v[SW];
+    __device__ __forceinline__ int kbyte(int kb, int ch) const {
+        return (k[kb][ch >> 1] >> (16 * (ch & 1))) & 0xff;
+    }
+    __device__ __forceinline__ int vbyte(int db) const { return (v[db >> 2] >> (8 * (db & 3))) & 0xff; }
+};
+
+template <int D, int BC, bool MX>
 struct Wave8 {
     static constexpr int RB = D;           // bytes per K / V row in LDS
     static constexpr int NCH = D / 64;     // k-steps of S^T = K Q^T
@@ -68,6 +92,14 @@ struct Wave8 {
     static constexpr int NVA = NDB;        // V lane offsets, one per d-block
     static constexpr int NKA = NCH;        // K lane offsets, per k-step (x2 chunks)
     static_assert(NKB == 2 * NPV, "one PV MFMA per two score blocks");
+    using TS = TileScales<NKB, (D + 127) / 128>;
+
+    // MFMA with the tile's scales (microscaled) or unit scales.
+    static __device__ __forceinline__ f32x16 mm(const i32x8& a, const i32x8& b, const f32x16& c, int sa,
+                                                int sb) {
+        if constexpr (MX) return mfma32_fp8s(a, b, c, sa, sb);
+        else return mfma32_fp8(a, b, c);
+    }
 
     f32x16 o[NDB];
     float m, l;
@@ -79,9 +111,13 @@ struct Wave8 {
         for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
     }
 
-    // K fragment (ch, kb): row perm(l32) + 32*kb, bytes [64*ch + 32*hi, +32)
-    // = logical chunks 4*ch + 2*hi + e (e = 0, 1); ka[ch][e] holds the
-    // swizzled lane offset (see lds_swz8).
+    // K fragment (ch, kb): row perm(l32) + 32*kb, 16-byte logical chunks
+    // 4*ch + 2*hi + e (block-scaled path) or 4*ch + hi + 2*e (microscaled
+    // path), e = 0, 1; ka[ch][e] holds the swizzled lane offset (see
+    // lds_swz8). The 64 k-values of one 8-bit MFMA operand are bytes 0-15 of
+    // both half-waves for k 0-31 and bytes 16-31 for k 32-63, and the scale
+    // of half-wave h covers k [32h, 32h + 32): with the microscaled chunk
+    // order that range is d-block 2*ch + h of the row.
     static __device__ __forceinline__ i32x8 kfrag(const char* kl, const int (&ka)[NKA][2], int ch, int kb) {
         const char* p = kl + 32 * kb * RB;
         const u32x4 a0 = *reinterpret_cast<const u32x4*>(p + ka[ch][0]);
@@ -91,15 +127,17 @@ struct Wave8 {
     }
 
     static __device__ __forceinline__ void qk(f32x16 (&s)[NKB], const i32x8 (&kf)[NKB][NCH],
-                                              const i32x8 (&qf)[NCH], int c0, int c1) {
+                                              const i32x8 (&qf)[NCH], int c0, int c1, const TS& ts,
+                                              const int (&qs)[NCH]) {
 #pragma unroll
         for (int ch = c0; ch < c1; ++ch)
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma32_fp8(kf[kb][ch], qf[ch], s[kb]);
+            for (int kb = 0; kb < NKB; ++kb) s[kb] = mm(kf[kb][ch], qf[ch], s[kb], ts.kbyte(kb, ch), qs[ch]);
     }
 
     static __device__ __forceinline__ void scores(f32x16 (&s)[NKB], const char* kl,
-                                                  const int (&ka)[NKA][2], const i32x8 (&qf)[NCH]) {
+                                                  const int (&ka)[NKA][2], const i32x8 (&qf)[NCH],
+                                                  const TS& ts, const int (&qs)[NCH]) {
         i32x8 kf[NKB][NCH];
 #pragma unroll
         for (int ch = 0; ch < NCH; ++ch)
@@ -108,7 +146,7 @@ struct Wave8 {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
-        qk(s, kf, qf, 0, NCH);
+        qk(s, kf, qf, 0, NCH, ts, qs);
     }
 
     template <bool CAUSAL>
@@ -187,7 +225,9 @@ struct Wave8 {
     }
 
     // V^T fragment (t, db): slots 8c..8c+7 = keys 64t + 16c + 8hi + 0..7 of
-    // d-row 32*db + l32; one transposing read of 8 rows per c.
+    // d-row 32*db + l32; one transposing read of 8 rows per c. Bytes 0-15 of
+    // both half-waves are keys 64t + [0, 32), bytes 16-31 keys 64t + [32, 64):
+    // the two 32-key V scale blocks of the microscaled PV MFMA.
     static __device__ __forceinline__ i32x8 vfrag(const char* vl, const int (&va)[NVA], int t, int db) {
         const char* vp = vl + va[db] + 64 * t * RB;
         const u32x2 r0 = lds_read_tr8(vp);
@@ -200,7 +240,8 @@ struct Wave8 {
 
     // Softmax + PV of the tile in s (no overlap).
     __device__ __forceinline__ void finish(const f32x16 (&s)[NKB], const char* vl,
-                                           const int (&va)[NVA], float cj, float bj, float lscale) {
+                                           const int (&va)[NVA], float cj, float bj, float lscale,
+                                           const TS& ts) {
         uint32_t w[NPV][8];
         float ls[2] = {0.f, 0.f};
 #pragma unroll
@@ -216,7 +257,7 @@ struct Wave8 {
 #pragma unroll
         for (int t = 0; t < NPV; ++t)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) o[db] = mfma32_fp8(vf[t][db], pf[t], o[db]);
+            for (int db = 0; db < NDB; ++db) o[db] = mm(vf[t][db], pf[t], o[db], ts.vbyte(db), kPScaleE8M0);
     }
 
     // Pipelined step as one instruction stream in program order (every chunk
@@ -226,9 +267,11 @@ struct Wave8 {
     // exponential groups; the overflow check; per PV MFMA of this tile, the
     // reads of the V^T fragment VPD ahead and a share of the copy of the next
     // scores into s.
+    // tsn: scales of the next tile's score MFMAs; ts: this tile's PV scales.
     __device__ __forceinline__ void step(f32x16 (&s)[NKB], const char* kn, const int (&ka)[NKA][2],
                                          const char* vl, const int (&va)[NVA], const i32x8 (&qf)[NCH],
-                                         float cj, float bj, float lscale) {
+                                         float cj, float bj, float lscale, const TS& tsn, const TS& ts,
+                                         const int (&qs)[NCH]) {
         constexpr int NKF = NCH * NKB;      // K fragments = score MFMAs per tile
         constexpr int NVF = NPV * NDB;      // V^T fragments = PV MFMAs per tile
         constexpr int NG = 8 * NPV;         // exponential groups (4 each) per lane
@@ -256,7 +299,7 @@ struct Wave8 {
                 vf[v / NDB][v % NDB] = vfrag(vl, va, v / NDB, v % NDB);
             }
             const int ch = i / NKB, kb = i % NKB;
-            sn[kb] = mfma32_fp8(kf[kb][ch], qf[ch], sn[kb]);
+            sn[kb] = mm(kf[kb][ch], qf[ch], sn[kb], tsn.kbyte(kb, ch), qs[ch]);
 #pragma unroll
             for (int q = i * NG / NKF; q < (i + 1) * NG / NKF; ++q) prob_group(s, w, q, cj, bj, ls);
             __builtin_amdgcn_sched_barrier(0);
@@ -271,7 +314,7 @@ struct Wave8 {
             const int v = j + VPD;
             if (v < NVF) vf[v / NDB][v % NDB] = vfrag(vl, va, v / NDB, v % NDB);
             const int t = j / NDB, db = j % NDB;
-            o[db] = mfma32_fp8(vf[t][db], pf[t], o[db]);
+            o[db] = mm(vf[t][db], pf[t], o[db], ts.vbyte(db), kPScaleE8M0);
 #pragma unroll
             for (int kb = j * NKB / NVF; kb < (j + 1) * NKB / NVF; ++kb) s[kb] = sn[kb];
             __builtin_amdgcn_sched_barrier(0);
@@ -279,14 +322,25 @@ struct Wave8 {
     }
 };
 
-template <int D, bool CAUSAL, bool OUT_F32>
+// 4 bytes per lane from a buffer straight into LDS (lane i at lds + 4*i),
+// like buffer_load_lds16; used for the microscaled path's scale bytes, which
+// travel with their tile through the same wait and barrier.
+__device__ __forceinline__ void buffer_load_lds4(i32x4 rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+
+template <int D, bool CAUSAL, bool OUT_F32, bool MX>
 __global__ void __launch_bounds__(Cfg8<D>::NW * 64, Cfg8<D>::WPE)
 fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg,
                   const uint8_t* __restrict__ Vg, void* __restrict__ Og, float* __restrict__ LSEg,
                   int N, int num_qtiles, int num_blocks, int nsb, size_t scales_off, float c)
 {
     constexpr int NW = Cfg8<D>::NW, BC = Cfg8<D>::BC;
-    using W = Wave8<D, BC>;
+    using W = Wave8<D, BC, MX>;
+    using TS = typename W::TS;
+    constexpr int SBY = D / 32;            // microscaling: scale bytes per row of Q or K
+    static_assert(!MX || W::NPV == 1, "microscaled V scales are held for one PV k-step per tile");
     constexpr int QW = 32, BR = NW * QW;
     constexpr int NCH = W::NCH, NDB = W::NDB, NKB = W::NKB, NVA = W::NVA, RB = W::RB;
     constexpr int TB = BC * RB;            // bytes per K (or V) tile
@@ -294,8 +348,15 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     static_assert(TB % (1024 * NW) == 0, "tile must split into 1 KB loads per wave");
     static_assert(kQuantBlockRows % BC == 0 && kQuantBlockRows % QW == 0, "scale blocks");
 
-    // LDS: K tiles in slots 0, 1 and V tiles in slots 2, 3 (tile t uses t & 1).
-    __shared__ __attribute__((aligned(1024))) char smem[4 * TB];
+    // LDS: K tiles in slots 0, 1 and V tiles in slots 2, 3 (tile t uses t & 1);
+    // microscaled path: then the tiles' scale bytes, K in slots 0, 1 and V
+    // in slots 2, 3 of SCB bytes each.
+    constexpr int KSB = BC * (D / 32);     // K scale bytes of a tile (one row per key)
+    constexpr int VSB = (BC / 32) * D;     // V scale bytes of a tile (32-key blocks)
+    constexpr int SCB = (KSB > 256 ? KSB : 256);
+    static_assert(SBY % 4 == 0 || KSB + 4 <= SCB, "room for the dword-aligned start of 2-byte scale rows");
+    static_assert(KSB == VSB, "one scale slot size for K and V");
+    __shared__ __attribute__((aligned(1024))) char smem[4 * TB + (MX ? 4 * SCB : 0)];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -321,12 +382,17 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     const int qtile0 = qt * BR;
     const int q0 = qtile0 + wave * QW;
 
-    // largest V block scale of the head
-    float svmax = 0.f;
-    for (int i = lane; i < nsb; i += 64) svmax = fmaxf(svmax, Vs[i]);
+    // Block-scaled path: largest V block scale of the head. Microscaled
+    // path: the matrix instructions apply every scale, the logits only take
+    // softmax_scale * log2(e).
+    float svmax = 1.f, cq = c;
+    if constexpr (!MX) {
+        svmax = 0.f;
+        for (int i = lane; i < nsb; i += 64) svmax = fmaxf(svmax, Vs[i]);
 #pragma unroll
-    for (int mm = 32; mm >= 1; mm /= 2) svmax = fmaxf(svmax, __shfl_xor(svmax, mm, 64));
-    const float cq = Qs[min(q0, N - 1) / kQuantBlockRows] * c;
+        for (int mm = 32; mm >= 1; mm /= 2) svmax = fmaxf(svmax, __shfl_xor(svmax, mm, 64));
+        cq = Qs[min(q0, N - 1) / kQuantBlockRows] * c;
+    }
 
     // Tile copies: buffer loads straight into LDS (see fa_fwd16_kernel),
     // chunk swizzle lds_swz8; rows at or past N read as zeros.
@@ -339,10 +405,61 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
         const int row = p / RB;
         voff[j] = row * RB + ((p % RB / 16) ^ lds_swz8<D>(row)) * 16;
     }
+    // row of the K tile this lane feeds to MFMA row l32 of score block 0
+    const int krow0 = krow_perm(l32);
+    // Microscaled path: E8M0 scale bytes. K of key row k: bytes
+    // [k*SBY, +SBY) of the head's K scales; V of 32-key block kb, d-row r:
+    // bytes [kb*D + (r % 32)*SBY, +SBY) (one byte per d-block). A tile's
+    // bytes are contiguous in both (KSB = VSB bytes) and are copied into LDS
+    // with the tile (wave 0, 4 bytes per lane, rows past the end read as
+    // zeros). A lane of the score MFMA for key block kb, k-step ch takes K
+    // byte 2*ch + hi of its key row; of the PV MFMA, V byte db of block
+    // 2t + hi. With d = 64 (2 bytes per row) a head's K scales may start
+    // 2 bytes into a dword and end inside one: the copy starts at the dword
+    // below (kdelta bytes early, read back at +kdelta) and covers whole
+    // dwords (bounds are checked per dword); the extra bytes lie inside the
+    // packed buffer (its scale area is at least 2 bytes longer than the Q/K
+    // scales whenever their total is not a whole number of dwords).
+    const size_t nkb32 = ((size_t)N + 31) / 32;
+    const size_t kso = (size_t)bh * N * SBY;
+    const int kdelta = (int)(kso & 3);
+    const i32x4 ksrs = make_rsrc(Kg + scales_off + kso - kdelta, MX ? (kdelta + N * SBY + 3) & ~3 : 0);
+    const i32x4 vsrs = make_rsrc(Vg + scales_off + (size_t)bh * nkb32 * D, MX ? (int)(nkb32 * D) : 0);
+    const uint32_t scbase = lds_addr(smem) + 4 * TB;
+    auto load_sc = [&](const i32x4& rs, int t, int slot) {
+        if (wave_u != 0) return;
+        // 256 bytes per instruction; with KSB < 256 the upper lanes copy the
+        // next tile's bytes (or zeros) into the unused end of the slot
+#pragma unroll
+        for (int i = 0; i < (KSB + 255) / 256; ++i)
+            buffer_load_lds4(rs, scbase + slot * SCB + 256 * i, 4 * lane, t * KSB + 256 * i);
+    };
+    constexpr int SW = (SBY + 3) / 4;
+    // scale words of the lane for the tile in K slot ks / V slot vs
+    auto read_k = [&](TS& ts, int ks) {
+        const char* p = smem + 4 * TB + ks * SCB + kdelta;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            const char* q = p + (32 * kb + krow0) * SBY;
+            uint32_t w0, w1 = 0;
+            if constexpr (SBY == 2) w0 = *reinterpret_cast<const uint16_t*>(q);
+            else if constexpr (SBY == 4) w0 = *reinterpret_cast<const uint32_t*>(q);
+            else { const u32x2 x = *reinterpret_cast<const u32x2*>(q); w0 = x[0]; w1 = x[1]; }
+            ts.k[kb][0] = w0 >> (8 * hi);
+            if constexpr (SW > 1) ts.k[kb][1] = w1 >> (8 * hi);
+        }
+    };
+    auto read_v = [&](TS& ts, int vs) {
+        const char* q = smem + 4 * TB + (2 + vs) * SCB + hi * D + l32 * SBY;
+        if constexpr (SBY == 2) ts.v[0] = *reinterpret_cast<const uint16_t*>(q);
+        else if constexpr (SBY == 4) ts.v[0] = *reinterpret_cast<const uint32_t*>(q);
+        else { const u32x2 x = *reinterpret_cast<const u32x2*>(q); ts.v[0] = x[0]; ts.v[SW - 1] = x[1]; }
+    };
     const int nkt_total = (N + BC - 1) / BC;
     const uint32_t sbase = lds_addr(smem);
     auto load_kv = [&](const i32x4& rs, int t, int slot) {
         if (t >= nkt_total) return;
+        if constexpr (MX) load_sc(slot < 2 ? ksrs : vsrs, t, slot);
         const uint32_t dst = sbase + slot * TB + wave_u * NIW * 1024;
 #pragma unroll
         for (int j = 0; j < NIW; ++j) buffer_load_lds16(rs, dst + j * 1024, voff[j], t * TB);
@@ -351,24 +468,47 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     auto vtile = [&](int t) -> const char* { return smem + (2 + (t & 1)) * TB; };
     // per-tile scale terms: score multiplier, P exponent offset, l weight
     auto tile_scales = [&](int t, float& cj, float& bj, float& lscale) {
-        const int sblk = (t * BC) / kQuantBlockRows;
-        const float wv = Vs[sblk] / svmax;                    // (0, 1]
-        cj = cq * Ks[sblk];
-        bj = __builtin_amdgcn_logf(kPScale * wv);            // log2(8 w_j)
-        lscale = 1.0f / (kPScale * wv);
+        if constexpr (MX) {
+            cj = c;
+            bj = 3.0f;                                         // log2(kPScale)
+            lscale = 1.0f / kPScale;
+        } else {
+            const int sblk = (t * BC) / kQuantBlockRows;
+            const float wv = Vs[sblk] / svmax;                // (0, 1]
+            cj = cq * Ks[sblk];
+            bj = __builtin_amdgcn_logf(kPScale * wv);        // log2(8 w_j)
+            lscale = 1.0f / (kPScale * wv);
+        }
     };
-
-    // Q^T fragments: query q0 + l32, bytes [64*ch + 32*hi, +32)
+    // Q^T fragments: query q0 + l32, bytes [64*ch + 32*hi, +32) (microscaled:
+    // [64*ch + 16*hi, +16) and [64*ch + 32 + 16*hi, +16), the chunk order of
+    // the K fragments); its MX scale byte 2*ch + hi of the row
     i32x8 qf[NCH];
+    int qs[NCH];
     {
         const int row = q0 + l32;
+        uint32_t qw[2] = {0x7f7f7f7fu, 0x7f7f7f7fu};
+        if (MX && row < N) {
+            const uint8_t* sp = Qg + scales_off + ((size_t)bh * N + row) * SBY;
+            if constexpr (SBY == 2) {
+                qw[0] = *reinterpret_cast<const uint16_t*>(sp);
+            } else if constexpr (SBY == 4) {
+                qw[0] = *reinterpret_cast<const uint32_t*>(sp);
+            } else {
+                const u32x2 x = *reinterpret_cast<const u32x2*>(sp);
+                qw[0] = x[0];
+                qw[1] = x[1];
+            }
+        }
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch) qs[ch] = (qw[ch >> 1] >> (16 * (ch & 1) + 8 * hi)) & 0xff;
 #pragma unroll
         for (int ch = 0; ch < NCH; ++ch) {
             u32x4 a = u32x4{0, 0, 0, 0}, b = u32x4{0, 0, 0, 0};
             if (row < N) {
-                const uint8_t* p = Q + (size_t)row * D + 64 * ch + 32 * hi;
+                const uint8_t* p = Q + (size_t)row * D + 64 * ch + (MX ? 16 : 32) * hi;
                 a = *reinterpret_cast<const u32x4*>(p);
-                b = *reinterpret_cast<const u32x4*>(p + 16);
+                b = *reinterpret_cast<const u32x4*>(p + (MX ? 32 : 16));
             }
             qf[ch] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3],
                            (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
@@ -381,12 +521,12 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     // Lane offsets into swizzled tiles.
     int ka[W::NKA][2], va[NVA];
     {
-        const int kr = krow_perm(l32);
+        const int kr = krow0;
 #pragma unroll
         for (int ch = 0; ch < W::NKA; ++ch)
 #pragma unroll
             for (int e = 0; e < 2; ++e)
-                ka[ch][e] = kr * RB + ((4 * ch + 2 * hi + e) ^ lds_swz8<D>(kr)) * 16;
+                ka[ch][e] = kr * RB + (((MX ? 4 * ch + hi + 2 * e : 4 * ch + 2 * hi + e)) ^ lds_swz8<D>(kr)) * 16;
         const int vr = 8 * hi + (lane & 15) / 2;
 #pragma unroll
         for (int db = 0; db < NVA; ++db) {
@@ -403,16 +543,26 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     st.init();
     f32x16 s[NKB];
 
+    // Scale registers (microscaled path): tk holds the K scales of the tile
+    // whose scores come next, tv the V scales of the tile whose PV comes
+    // next; the scales of a tile are requested with its copy and read after
+    // the barrier that publishes it.
+    TS tk, tv;
     load_kv(krs, 0, 0);
     load_kv(vrs, 0, 2);
     load_kv(krs, 1, 1);
     wait_vm_all();
     __syncthreads();
+    if constexpr (MX) {
+        read_k(tk, 0);
+        read_v(tv, 0);
+    }
     if (nfull > 0) {
         float cj, bj, ls;
         tile_scales(0, cj, bj, ls);
-        W::scores(s, ktile(0), ka, qf);
+        W::scores(s, ktile(0), ka, qf, tk, qs);
         st.raise_max(W::tile_max(s, cj));    // first reference maximum: exact
+        if constexpr (MX) read_k(tk, 1);
         __syncthreads();                     // all waves done reading K_0's slot
     }
     int t = 0;
@@ -421,17 +571,22 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
         load_kv(vrs, t + 1, 2 + ((t + 1) & 1));
         float cj, bj, lscale;
         tile_scales(t, cj, bj, lscale);
-        st.step(s, ktile(t + 1), ka, vtile(t), va, qf, cj, bj, lscale);
+        st.step(s, ktile(t + 1), ka, vtile(t), va, qf, cj, bj, lscale, tk, tv, qs);
         wait_vm_all();
         __syncthreads();
+        if constexpr (MX) {
+            read_k(tk, t & 1);                 // tile t + 2
+            read_v(tv, (t + 1) & 1);           // tile t + 1
+        }
     }
     if (nfull > 0) {                          // last full tile
         load_kv(vrs, t + 1, 2 + ((t + 1) & 1));
         float cj, bj, lscale;
         tile_scales(t, cj, bj, lscale);
-        st.finish(s, vtile(t), va, cj, bj, lscale);
+        st.finish(s, vtile(t), va, cj, bj, lscale, tv);
         wait_vm_all();
         __syncthreads();
+        if constexpr (MX) read_v(tv, (t + 1) & 1);   // the K scales of t + 1 are in tk already
         ++t;
     }
     for (; t < nkt; ++t) {                    // ragged end / causal diagonal
@@ -441,18 +596,23 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
         if (!CAUSAL || k0 <= q0 + QW - 1) {
             float cj, bj, lscale;
             tile_scales(t, cj, bj, lscale);
-            W::scores(s, ktile(t), ka, qf);
+            W::scores(s, ktile(t), ka, qf, tk, qs);
             W::template mask<CAUSAL>(s, k0, q0, N, hi, l32);
             if (t == 0) st.raise_max(W::tile_max(s, cj));   // first reference maximum: exact
-            st.finish(s, vtile(t), va, cj, bj, lscale);
+            st.finish(s, vtile(t), va, cj, bj, lscale, tv);
         }
         wait_vm_all();
         __syncthreads();
+        if constexpr (MX) {
+            read_k(tk, (t + 1) & 1);
+            read_v(tv, (t + 1) & 1);
+        }
     }
 
-    // ---- epilogue: O = O_acc * sv_max / (8 l), LSE = ln2 * (m + log2 l) ----
+    // ---- epilogue: O = O_acc * sv_max / (8 l) (microscaled: O_acc / l, the
+    // PV instruction already applied 2^-3), LSE = ln2 * (m + log2 l) ----
     const float l = pair_sum(st.l);
-    const float inv = svmax / (kPScale * l);
+    const float inv = MX ? 1.0f / l : svmax / (kPScale * l);
     const int row = q0 + l32;
     if (row < N) {
         if (hi == 0) LSEg[(size_t)bh * N + row] = (st.m + __builtin_amdgcn_logf(l)) * kLn2;
@@ -476,25 +636,30 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     }
 }
 
-template <int D, bool CAUSAL, bool OUT_F32>
+template <int D, bool CAUSAL, bool OUT_F32, bool MX>
 static hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
     constexpr int BR = Cfg8<D>::NW * 32;
     const int num_qtiles = (a.N + BR - 1) / BR;
     const long long nblk = (long long)num_qtiles * a.B * a.H;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const int nsb = (a.N + kQuantBlockRows - 1) / kQuantBlockRows;
-    hipLaunchKernelGGL((fa_fwd_fp8_kernel<D, CAUSAL, OUT_F32>), dim3((unsigned)nblk),
+    hipLaunchKernelGGL((fa_fwd_fp8_kernel<D, CAUSAL, OUT_F32, MX>), dim3((unsigned)nblk),
                        dim3(Cfg8<D>::NW * 64), 0, s, static_cast<const uint8_t*>(a.q),
                        static_cast<const uint8_t*>(a.k), static_cast<const uint8_t*>(a.v), a.o,
                        a.lse, a.N, num_qtiles, (int)nblk, nsb, a.scales_off, a.scale * kLog2e);
     return hipGetLastError();
 }
 
+template <int D, bool MX>
+static hipError_t launch_m(const FwdArgs& a, hipStream_t s) {
+    if (a.causal)
+        return a.out_f32 ? launch_t<D, true, true, MX>(a, s) : launch_t<D, true, false, MX>(a, s);
+    return a.out_f32 ? launch_t<D, false, true, MX>(a, s) : launch_t<D, false, false, MX>(a, s);
+}
+
 template <int D>
 static hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
-    if (a.causal)
-        return a.out_f32 ? launch_t<D, true, true>(a, s) : launch_t<D, true, false>(a, s);
-    return a.out_f32 ? launch_t<D, false, true>(a, s) : launch_t<D, false, false>(a, s);
+    return a.mx ? launch_m<D, true>(a, s) : launch_m<D, false>(a, s);
 }
 
 hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t s) {

@@ -10,6 +10,7 @@
 namespace fa {
 
 constexpr int kQuantBlockRows = 128;   // rows per FP8 scale block
+constexpr int kMxNone = -1, kMxAlongD = 0, kMxAlongN = 1;   // PrepArgs::mx
 
 struct FwdArgs {
     const void* q;
@@ -21,8 +22,9 @@ struct FwdArgs {
     bool causal;
     float scale;        // softmax scale
     bool out_f32;
-    // FP8 only: byte offset of the float32 scale array inside q/k/v
+    // FP8 only: byte offset of the scale array inside q/k/v
     size_t scales_off;
+    bool mx = false;    // FP8: microscaled inputs (E8M0 scales per 32 elements)
 };
 
 // 16-bit forward (bf16 = true: bfloat16, else float16).
@@ -47,6 +49,7 @@ struct PrepArgs {
     size_t scales_off;
     int rope_style;     // 0 none, 1 interleaved pairs, 2 half pairs
     RopeFreqs rope;
+    int mx;             // kMxNone: fp32 block scales; microscaling along d or n
 };
 hipError_t launch_fp8_prep(const PrepArgs& a, hipStream_t s);
 

@@ -58,6 +58,7 @@ enum fa_dtype {
     FA_F16 = 0,
     FA_BF16 = 1,
     FA_FP8_E4M3 = 2,
+    FA_FP8_MX = 3,       /* e4m3 with microscaling (fa_mx_prep): q, k along d, v along N */
     FA_OUT_F32 = 0x100
 };
 
@@ -68,7 +69,8 @@ enum fa_dtype {
  *           dtype FA_FP8_E4M3, packed FP8 tensors written by fa_fp8_prep
  *           (e4m3 codes plus per-block float32 scales, see below). For FP8,
  *           q and k must have been prepared with the same sign vectors (or
- *           both without); v without signs.
+ *           both without); v without signs. With dtype FA_FP8_MX: q and k
+ *           from fa_mx_prep along d, v from fa_mx_prep along N.
  *  o        output [B][H][N][d]: input dtype (16-bit), bfloat16 (FP8), or
  *           float32 when FA_OUT_F32 is set. 16-byte aligned.
  *  lse      output [B][H][N] float32: natural-log log-sum-exp of each row of
@@ -78,10 +80,11 @@ enum fa_dtype {
  *  causal   nonzero: query i sees keys j <= i only.
  *  softmax_scale  finite and > 0 (usually 1/sqrt(d)); multiplies S before the
  *           softmax.
- *  dtype    FA_F16 | FA_BF16 | FA_FP8_E4M3, optionally | FA_OUT_F32.
+ *  dtype    FA_F16 | FA_BF16 | FA_FP8_E4M3 | FA_FP8_MX, optionally
+ *           | FA_OUT_F32.
  *  stream   hipStream_t or NULL.
  *
- * q, k, v must be 16-byte aligned. Returns FA_OK, FA_ERR_INVALID_ARG,
+ * q, k, v must be 16-byte aligned (256-byte for the FP8 dtypes). Returns FA_OK, FA_ERR_INVALID_ARG,
  * FA_ERR_UNSUPPORTED (d not in {64,128,256}, or N*d*2 > 2^31 - 2^16 - 1:
  * one head's K or V must be addressable with 31-bit offsets) or FA_ERR_HIP.
  */
@@ -232,6 +235,44 @@ enum fa_rope_style {
 int fa_fp8_prep_rope(const void* x, void* x8, const int8_t* signs,
                      int B, int H, int N, int d, int block_rows, int in_dtype,
                      int rope_style, float rope_base, int pos0, void* stream);
+
+/* Microscaling axis for fa_mx_prep. */
+enum fa_mx_axis {
+    FA_MX_ALONG_D = 0,   /* one scale per row and 32 columns (Q, K) */
+    FA_MX_ALONG_N = 1    /* one scale per column and 32 rows (V) */
+};
+
+/*
+ * fa_mx_prep - FP8 e4m3 quantisation with microscaling: a power-of-two
+ * scale per 32 elements (the finer-grained variant of the block
+ * quantisation of "FlashAttention-3: почему внимание стало быстрее", «Метод»
+ * item 3, in the OCP MX layout the gfx950 scaled matrix instructions read),
+ * after the optional random-sign Hadamard of fa_fp8_prep (Q and K only).
+ *
+ *  x        16-bit input [B][H][N][d], 16-byte aligned.
+ *  x8       output of fa_mx_packed_bytes(B,H,N,d) bytes, 256-byte aligned:
+ *             bytes [0, B*H*N*d)            e4m3 codes, [B][H][N][d]
+ *             at fa_fp8_scales_offset(...)  E8M0 scale bytes (2^(byte-127)):
+ *               FA_MX_ALONG_D: [B][H][N][d/32];
+ *               FA_MX_ALONG_N: [B][H][ceil(N/32)][32][d/32], the scale of
+ *               column c at [c % 32][c / 32] of its 32-row block.
+ *  signs    int8 [H][d] (Hadamard as in fa_fp8_prep) or NULL; must be NULL
+ *           for FA_MX_ALONG_N.
+ *  axis     FA_MX_ALONG_D (Q, K) or FA_MX_ALONG_N (V).
+ *  in_dtype FA_BF16 or FA_F16; d 64, 128 or 256.
+ *
+ * Per block of 32: e = floor(log2(max |x|)) - 8 clamped to [-127, 127]
+ * (-127 for an all-zero block), code = e4m3 round-to-nearest-even of
+ * x * 2^-e saturated to +-448, scale byte e + 127. fa_fwd with dtype
+ * FA_FP8_MX takes q and k prepared along d and v along N. Returns FA_OK,
+ * FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED or FA_ERR_HIP.
+ */
+int fa_mx_prep(const void* x, void* x8, const int8_t* signs, int B, int H, int N, int d,
+               int axis, int in_dtype, void* stream);
+
+/* Size in bytes of a packed microscaled tensor for [B][H][N][d] (either
+ * axis); 0 for invalid sizes. Pure host arithmetic. */
+size_t fa_mx_packed_bytes(int B, int H, int N, int d);
 
 /* Size in bytes of a packed FP8 tensor for [B][H][N][d]; 0 for invalid
  * sizes. Pure host arithmetic. */

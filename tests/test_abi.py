@@ -222,3 +222,38 @@ def prep_rope(**kw):
 ])
 def test_prep_rope_validation(L, kw, status):
     assert prep_rope(**kw) == status
+
+
+def mx(**kw):
+    a = dict(x=FAKE, x8=FAKE, signs=None, B=1, H=1, N=128, d=128, axis=fa.FA_MX_ALONG_D,
+             in_dtype=fa.FA_BF16)
+    a.update(kw)
+    return fa.mx_prep_raw(a["x"], a["x8"], a["signs"], a["B"], a["H"], a["N"], a["d"], a["axis"],
+                          a["in_dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(axis=2), fa.FA_ERR_INVALID_ARG),
+    (dict(axis=fa.FA_MX_ALONG_N, signs=FAKE), fa.FA_ERR_INVALID_ARG),   # no Hadamard for V
+    (dict(in_dtype=fa.FA_FP8_MX), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(x8=FAKE + 64), fa.FA_ERR_INVALID_ARG),
+    (dict(x=None), fa.FA_ERR_INVALID_ARG),
+    (dict(B=0), fa.FA_OK),
+])
+def test_mx_prep_validation(L, kw, status):
+    assert mx(**kw) == status
+
+
+def test_mx_sizes_and_fwd_dtype(L):
+    B, H, N, d = 2, 3, 100, 128
+    off = L.fa_fp8_scales_offset(B, H, N, d)
+    size = fa.mx_packed_bytes(B, H, N, d)
+    assert size % 256 == 0
+    assert size >= off + max(B * H * N * d // 32, B * H * 4 * d)
+    assert fa.mx_packed_bytes(1, 1, 1, 80) == 0
+    # the microscaled dtype is accepted by fa_fwd's validation (alignment 256)
+    assert fwd(dtype=fa.FA_FP8_MX, q=FAKE + 16) == fa.FA_ERR_INVALID_ARG
+    assert fwd(dtype=fa.FA_FP8_MX | 0x200) == fa.FA_ERR_INVALID_ARG
+    assert fwd(dtype=fa.FA_FP8_MX, B=0) == fa.FA_OK
