@@ -20,7 +20,10 @@ the same events and reported under `next_rows` (not part of `value`): the
 16-bit backward (dQ, dK, dV from the saved LSE) on the main shape, its work
 counted as 10*B*H*N^2*d (the five GEMMs of the gradient, halved for causal);
 the fused rotary + Hadamard + fp8 block quantisation of Q and K of the fp8
-workload (half pairing, GB/s of bytes read and written); and the
+workload (half pairing, GB/s of bytes read and written); the microscaled fp8
+variant on the fp8 workload (fa_mx_prep of Q, K along d with the Hadamard
+and V along the sequence, GB/s; the forward on its output, non-causal and
+causal, TFLOP/s against the dense fp8 peak); and the
 decode-shaped forward on its two workloads (B=8 H=16 sequences of
 16384 keys; B=16 with 64 query heads over 8 key/value heads and ragged key
 counts), in GB/s of the bytes it must move (K and V of every sequence's keys,
@@ -273,6 +276,27 @@ def build_next_legs(dev):
 
     legs.append(Leg("fp8_prep_rope_qk_b4h16n4k_d128", prep_rope, 0.0, rope_bytes))
     keep += [q8, k8, signs, pq, pk]
+    # microscaled fp8: prep of Q, K (along d, Hadamard) and V (along N), then
+    # the forward on the same workload
+    v8 = make_qkv(**c8)[2].to(dev)
+    mq, mk, mv = (torch.empty(fa.mx_packed_bytes(B8, H8, N8, d8), dtype=torch.uint8, device=dev)
+                  for _ in range(3))
+    mx_bytes = 3 * (nel * 2 + nel + nel // 32)
+
+    def prep_mx():
+        fa.mx_prep(q8, signs, "d", out=mq)
+        fa.mx_prep(k8, signs, "d", out=mk)
+        fa.mx_prep(v8, None, "n", out=mv)
+
+    legs.append(Leg("fp8_mx_prep_qkv_b4h16n4k_d128", prep_mx, 0.0, mx_bytes))
+    o8 = torch.empty((B8, H8, N8, d8), dtype=torch.bfloat16, device=dev)
+    lse8 = torch.empty((B8, H8, N8), dtype=torch.float32, device=dev)
+    for causal in (False, True):
+        legs.append(Leg("fp8_mx_fwd_b4h16n4k_d128" + ("_causal" if causal else ""),
+                        lambda causal=causal: fa.fwd_fp8(mq, mk, mv, B8, H8, N8, d8, causal, out=o8,
+                                                         lse=lse8, mx=True),
+                        attention_flops(B8, H8, N8, d8, causal)))
+    keep += [v8, mq, mk, mv, o8, lse8]
     for name, c in sorted(DECODE_CONFIGS.items()):
         B, H, Hkv, Nq, Nk, d = c["B"], c["H"], c["Hkv"], c["Nq"], c["Nk"], c["d"]
         qh, kh, vh, sl = make_decode(**c)
