@@ -23,7 +23,8 @@ the fused rotary + Hadamard + fp8 block quantisation of Q and K of the fp8
 workload (half pairing, GB/s of bytes read and written); the microscaled fp8
 variant on the fp8 workload (fa_mx_prep of Q, K along d with the Hadamard
 and V along the sequence, GB/s; the forward on its output, non-causal and
-causal, TFLOP/s against the dense fp8 peak); and the
+causal, TFLOP/s against the dense fp8 peak); the block-scaled fp8 forward,
+causal; and the
 decode-shaped forward on its two workloads (B=8 H=16 sequences of
 16384 keys; B=16 with 64 query heads over 8 key/value heads and ragged key
 counts), in GB/s of the bytes it must move (K and V of every sequence's keys,
@@ -297,6 +298,12 @@ def build_next_legs(dev):
                                                          lse=lse8, mx=True),
                         attention_flops(B8, H8, N8, d8, causal)))
     keep += [v8, mq, mk, mv, o8, lse8]
+    # block-scaled fp8, causal (the non-causal forward is in the step)
+    bq, bk, bv = (fa.fp8_prep(t, sg, 128) for t, sg in ((q8, signs), (k8, signs), (v8, None)))
+    legs.append(Leg("fp8_fwd_b4h16n4k_d128_causal",
+                    lambda: fa.fwd_fp8(bq, bk, bv, B8, H8, N8, d8, True, out=o8, lse=lse8),
+                    attention_flops(B8, H8, N8, d8, True)))
+    keep += [bq, bk, bv]
     for name, c in sorted(DECODE_CONFIGS.items()):
         B, H, Hkv, Nq, Nk, d = c["B"], c["H"], c["Hkv"], c["Nq"], c["Nk"], c["d"]
         qh, kh, vh, sl = make_decode(**c)

@@ -65,3 +65,31 @@ def check_lse(lse, lse_ref, where=""):
     err = float(np.max(np.abs(lse - lse_ref)))
     assert err <= LSE_TOL, f"LSE error {err:.3e} > {LSE_TOL} {where}"
     return err
+
+
+def fp8_p_rounding_bound(q, k, v, b, h, rows, causal, w=None, scale=None):
+    """Elementwise bound on |O_gpu - O_dq| for query rows `rows` of head
+    (b, h), where O_dq is exact attention of the dequantised inputs q, k, v
+    (float64 [B,H,N,d]) and the GPU differs from it only by rounding the
+    weights P' = 8 p_j w_j to e4m3 before the PV product (p_j relative to
+    the row maximum, the row sum taken from the unrounded p). An e4m3
+    rounding moves x by at most max(2^-4 x, 2^-10) (half a step of a normal,
+    half the subnormal spacing 2^-9), so
+        |dO_ic| <= sum_j max(2^-4 p_j, 2^-13 / w_j) |V_jc| / sum_j p_j.
+    w: per-key weight sv_j / sv_max of the block-scaled path (None: 1, the
+    microscaled path). Returns [len(rows), d]. Taking p against the true row
+    maximum only loosens the subnormal term (the GPU's p are never
+    smaller)."""
+    qh = np.asarray(q[b, h], dtype=np.float64)[rows]
+    kh = np.asarray(k[b, h], dtype=np.float64)
+    vh = np.abs(np.asarray(v[b, h], dtype=np.float64))
+    N, d = kh.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    s = scale * (qh @ kh.T)
+    if causal:
+        s = np.where(np.arange(N)[None, :] <= np.asarray(rows)[:, None], s, -np.inf)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    wj = np.ones(N) if w is None else np.asarray(w, dtype=np.float64)
+    err = np.maximum(2.0 ** -4 * p, np.where(p > 0, 2.0 ** -13 / wj[None, :], 0.0))
+    return (err @ vh) / p.sum(axis=1, keepdims=True)

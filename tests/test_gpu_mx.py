@@ -20,9 +20,9 @@ import torch
 import oracle
 import exact_attention_55_amd as fa
 from exact_attention_55_amd.inputs import CONFIGS, make_qkv, make_signs, to_f64
-from oracle.mx import fake_quant_attention_mx, mx_quantize
+from oracle.mx import fake_quant_attention_mx, mx_dequantize, mx_quantize
 
-from helpers import FP8_RMSE, check_lse, errors, sample_rows
+from helpers import FP8_RMSE, check_lse, errors, fp8_p_rounding_bound, half_ulp, sample_rows
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -167,3 +167,41 @@ def test_mx_outlier_workload():
     _, lse_fq = fake_quant_attention_mx(q64[:1, :1], k64[:1, :1], v64[:1, :1], signs[:1], False)
     rows = sample_rows(N, seed=3)
     check_lse(lse_mx[0, 0, rows], lse_fq[0, 0, rows])
+
+
+def test_mx_causal_workload():
+    """The fp8 outlier workload at full size with microscaling, causal, bf16
+    output: every row of two whole heads against exact causal attention (the
+    RMSE bound is over all elements; see the block-scaled causal test);
+    against the oracle's own MX-quantised inputs (one head): RMSE over all
+    rows, tile-boundary and random rows elementwise within the bound on the
+    e4m3 rounding of P' (fp8_p_rounding_bound), LSE within 1e-3."""
+    cfg = CONFIGS["fp8_b4h16n4k_d128"]
+    B, H, N, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
+    say("mx causal workload")
+    q, k, v = make_qkv(**cfg)
+    signs = make_signs(H, d, cfg["seed"])
+    q64, k64, v64 = to_f64(q), to_f64(k), to_f64(v)
+    o, lse = mx_run(q, k, v, signs, True, out_f32=False)
+    sq = []
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        o_ref, _ = oracle.attention(q64[b:b + 1, h:h + 1], k64[b:b + 1, h:h + 1], v64[b:b + 1, h:h + 1],
+                                    True)
+        sq.append((o[b, h] - o_ref[0, 0]) ** 2)
+    rmse = float(np.sqrt(np.mean(np.concatenate(sq))))
+    say(f"mx causal RMSE over two heads {rmse:.3e}")
+    assert rmse <= FP8_RMSE
+    qc, qe = mx_quantize(q64[:1, :1], "d", signs[:1])
+    kc, ke = mx_quantize(k64[:1, :1], "d", signs[:1])
+    vc, ve = mx_quantize(v64[:1, :1], "n")
+    qd, kd, vd = mx_dequantize(qc, qe, "d"), mx_dequantize(kc, ke, "d"), mx_dequantize(vc, ve, "n")
+    o_fq, lse_fq = oracle.attention(qd, kd, vd, True)
+    _, rmse_fq = errors(o[0, 0], o_fq[0, 0])
+    say(f"mx causal RMSE vs fake-quant over a head {rmse_fq:.3e}")
+    assert rmse_fq <= FP8_RMSE / 2, f"RMSE vs fake-quant {rmse_fq:.3e}"
+    rows = sample_rows(N, seed=11)
+    bound = fp8_p_rounding_bound(qd, kd, vd, 0, 0, rows, True)
+    bound += half_ulp(np.abs(o_fq[0, 0, rows]) + bound, "bf16") + 1e-6
+    err = np.abs(o[0, 0, rows] - o_fq[0, 0, rows])
+    assert np.all(err <= bound), f"worst excess {np.max(err - bound):.3e}"
+    check_lse(lse[0, 0, rows], lse_fq[0, 0, rows])
