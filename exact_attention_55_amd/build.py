@@ -59,8 +59,22 @@ def build(verbose=False):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    _check_undefined(tmp)
     os.replace(tmp, OUT)
     return OUT
+
+
+def _check_undefined(lib):
+    """A shared library links even when a kernel's host launch stub was never
+    emitted (the host pass drops it silently when it cannot compile
+    something in the kernel's device code); such a library only fails when
+    it is loaded. Refuse any undefined symbol of the library's own namespace."""
+    r = subprocess.run(["nm", "-D", "--undefined-only", lib], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"nm failed on {lib}:\n{r.stderr}")
+    own = [l.split()[-1] for l in r.stdout.splitlines() if l.split() and l.split()[-1].startswith("_ZN2fa")]
+    if own:
+        raise RuntimeError("undefined symbols of namespace fa in the built library:\n  " + "\n  ".join(own))
 
 
 if __name__ == "__main__":

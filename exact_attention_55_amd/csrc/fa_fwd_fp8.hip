@@ -213,6 +213,14 @@ struct Wave8 {
     // Exponentials against the reference maximum; a tile whose P' sum in
     // some lane exceeds kBig8 is redone with its exact maximum (moving m,
     // rescaling O and l). Then l takes the tile's unquantised row sum.
+    // The next tile's score MFMAs are issued before this branch; the 8-bit
+    // MFMA builtins are not convergent, so the compiler sinks them behind it
+    // (their results are first used there) and the score MFMAs run next to
+    // the PV MFMAs rather than among the exponentials. Keeping them in place
+    // (a use inside the redo branch) puts this tile's scores, needed by the
+    // redo, and the next tile's in registers together, which spills at
+    // d = 128 with two waves per SIMD and measured half the speed; the
+    // second wave of the SIMD overlaps its exponentials with them instead.
     __device__ __forceinline__ void settle(const f32x16 (&s)[NKB], uint32_t (&w)[NPV][8], float cj,
                                            float bj, float lscale, float (&ls)[2]) {
         if (wave_any(ls[0] + ls[1] > kBig8)) {
@@ -356,7 +364,10 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     constexpr int SCB = (KSB > 256 ? KSB : 256);
     static_assert(SBY % 4 == 0 || KSB + 4 <= SCB, "room for the dword-aligned start of 2-byte scale rows");
     static_assert(KSB == VSB, "one scale slot size for K and V");
-    __shared__ __attribute__((aligned(1024))) char smem[4 * TB + (MX ? 4 * SCB : 0)];
+    // Block-scaled path: the K and V block scales of a tile travel with its V
+    // tile into one of two BSB-byte slots (K floats, then V floats).
+    constexpr int BSB = 512;
+    __shared__ __attribute__((aligned(1024))) char smem[4 * TB + (MX ? 4 * SCB : 2 * BSB)];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -455,11 +466,31 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
         else if constexpr (SBY == 4) ts.v[0] = *reinterpret_cast<const uint32_t*>(q);
         else { const u32x2 x = *reinterpret_cast<const u32x2*>(q); ts.v[0] = x[0]; ts.v[SW - 1] = x[1]; }
     };
+    // Block-scaled path: 64 scale floats from the tile's block on (lane i:
+    // block + i, past the head's end zeros) by one dword LDS-DMA each for K
+    // and V; only the first is used. A global load here would make the
+    // compiler wait for all vector memory traffic, the tile copies included.
+    const i32x4 bks = make_rsrc(Ks, MX ? 0 : nsb * 4);
+    const i32x4 bvs = make_rsrc(Vs, MX ? 0 : nsb * 4);
+    auto load_bs = [&](int t, int s) {
+        if (wave_u != 0) return;
+        const int soff = (t * BC) / kQuantBlockRows * 4;
+        buffer_load_lds4(bks, scbase + s * BSB, 4 * lane, soff);
+        buffer_load_lds4(bvs, scbase + s * BSB + 256, 4 * lane, soff);
+    };
+    float tks = 1.f, tvs = 1.f;            // block scales of the tile whose softmax comes next
+    auto read_bs = [&](int s) {
+        if constexpr (!MX) {
+            tks = *reinterpret_cast<const float*>(smem + 4 * TB + s * BSB);
+            tvs = *reinterpret_cast<const float*>(smem + 4 * TB + s * BSB + 256);
+        }
+    };
     const int nkt_total = (N + BC - 1) / BC;
     const uint32_t sbase = lds_addr(smem);
     auto load_kv = [&](const i32x4& rs, int t, int slot) {
         if (t >= nkt_total) return;
         if constexpr (MX) load_sc(slot < 2 ? ksrs : vsrs, t, slot);
+        else if (slot >= 2) load_bs(t, slot - 2);
         const uint32_t dst = sbase + slot * TB + wave_u * NIW * 1024;
 #pragma unroll
         for (int j = 0; j < NIW; ++j) buffer_load_lds16(rs, dst + j * 1024, voff[j], t * TB);
@@ -467,15 +498,14 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     auto ktile = [&](int t) -> const char* { return smem + (t & 1) * TB; };
     auto vtile = [&](int t) -> const char* { return smem + (2 + (t & 1)) * TB; };
     // per-tile scale terms: score multiplier, P exponent offset, l weight
-    auto tile_scales = [&](int t, float& cj, float& bj, float& lscale) {
+    auto tile_scales = [&](float& cj, float& bj, float& lscale) {
         if constexpr (MX) {
             cj = c;
             bj = 3.0f;                                         // log2(kPScale)
             lscale = 1.0f / kPScale;
         } else {
-            const int sblk = (t * BC) / kQuantBlockRows;
-            const float wv = Vs[sblk] / svmax;                // (0, 1]
-            cj = cq * Ks[sblk];
+            const float wv = tvs / svmax;                     // (0, 1]
+            cj = cq * tks;
             bj = __builtin_amdgcn_logf(kPScale * wv);        // log2(8 w_j)
             lscale = 1.0f / (kPScale * wv);
         }
@@ -557,9 +587,10 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
         read_k(tk, 0);
         read_v(tv, 0);
     }
+    read_bs(0);
     if (nfull > 0) {
         float cj, bj, ls;
-        tile_scales(0, cj, bj, ls);
+        tile_scales(cj, bj, ls);
         W::scores(s, ktile(0), ka, qf, tk, qs);
         st.raise_max(W::tile_max(s, cj));    // first reference maximum: exact
         if constexpr (MX) read_k(tk, 1);
@@ -570,7 +601,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
         load_kv(krs, t + 2, t & 1);
         load_kv(vrs, t + 1, 2 + ((t + 1) & 1));
         float cj, bj, lscale;
-        tile_scales(t, cj, bj, lscale);
+        tile_scales(cj, bj, lscale);
         st.step(s, ktile(t + 1), ka, vtile(t), va, qf, cj, bj, lscale, tk, tv, qs);
         wait_vm_all();
         __syncthreads();
@@ -578,15 +609,17 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
             read_k(tk, t & 1);                 // tile t + 2
             read_v(tv, (t + 1) & 1);           // tile t + 1
         }
+        read_bs((t + 1) & 1);
     }
     if (nfull > 0) {                          // last full tile
         load_kv(vrs, t + 1, 2 + ((t + 1) & 1));
         float cj, bj, lscale;
-        tile_scales(t, cj, bj, lscale);
+        tile_scales(cj, bj, lscale);
         st.finish(s, vtile(t), va, cj, bj, lscale, tv);
         wait_vm_all();
         __syncthreads();
         if constexpr (MX) read_v(tv, (t + 1) & 1);   // the K scales of t + 1 are in tk already
+        read_bs((t + 1) & 1);
         ++t;
     }
     for (; t < nkt; ++t) {                    // ragged end / causal diagonal
@@ -595,7 +628,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
         const int k0 = t * BC;
         if (!CAUSAL || k0 <= q0 + QW - 1) {
             float cj, bj, lscale;
-            tile_scales(t, cj, bj, lscale);
+            tile_scales(cj, bj, lscale);
             W::scores(s, ktile(t), ka, qf, tk, qs);
             W::template mask<CAUSAL>(s, k0, q0, N, hi, l32);
             if (t == 0) st.raise_max(W::tile_max(s, cj));   // first reference maximum: exact
@@ -607,6 +640,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
             read_k(tk, (t + 1) & 1);
             read_v(tv, (t + 1) & 1);
         }
+        read_bs((t + 1) & 1);
     }
 
     // ---- epilogue: O = O_acc * sv_max / (8 l) (microscaled: O_acc / l, the
