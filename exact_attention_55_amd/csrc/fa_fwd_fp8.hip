@@ -404,6 +404,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
         for (int mm = 32; mm >= 1; mm /= 2) svmax = fmaxf(svmax, __shfl_xor(svmax, mm, 64));
         cq = Qs[min(q0, N - 1) / kQuantBlockRows] * c;
     }
+    const float rsvmax = 1.0f / svmax;
 
     // Tile copies: buffer loads straight into LDS (see fa_fwd16_kernel),
     // chunk swizzle lds_swz8; rows at or past N read as zeros.
@@ -504,10 +505,13 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
             bj = 3.0f;                                         // log2(kPScale)
             lscale = 1.0f / kPScale;
         } else {
-            const float wv = tvs / svmax;                     // (0, 1]
+            // no division in the loop: 1/sv_max is taken once, 1/(8 w_j) by
+            // the hardware reciprocal; P' and l use the same w_j, so the
+            // normalisation stays consistent to float32 rounding
+            const float wv = tvs * rsvmax;                    // (0, 1]
             cj = cq * tks;
             bj = __builtin_amdgcn_logf(kPScale * wv);        // log2(8 w_j)
-            lscale = 1.0f / (kPScale * wv);
+            lscale = __builtin_amdgcn_rcpf(kPScale * wv);
         }
     };
     // Q^T fragments: query q0 + l32, bytes [64*ch + 32*hi, +32) (microscaled:
