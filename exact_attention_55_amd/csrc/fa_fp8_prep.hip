@@ -287,35 +287,63 @@ fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t*
     }
 }
 
-// Microscaling along the sequence (V): one workgroup per (head, 32-row
-// block), one lane per column; the block's scale for column c is stored at
-// byte (c % 32) * (D / 32) + c / 32 of the block's D scale bytes, the order
-// in which a lane of the PV matrix instruction wants its column scales.
+// Microscaling along the sequence (V): each thread owns 8 adjacent columns
+// of one 32-row block and holds the block's 32 rows of them in registers
+// (16-byte row loads, so the threads of a block together read whole rows),
+// takes the 8 column maxima, then writes 8 code bytes per row; a workgroup
+// covers kPrepThreads / (D / 8) blocks, and rows past the head's end are
+// neither read nor written. The block's scale for column c is stored at byte
+// (c % 32) * (D / 32) + c / 32 of the block's D scale bytes, the order in
+// which a lane of the PV matrix instruction wants its column scales.
 template <typename T, int D>
-__global__ void __launch_bounds__(D)
+__global__ void __launch_bounds__(kPrepThreads)
 mx_prep_cols_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, uint8_t* __restrict__ scales,
-                    int N, int nkb)
+                    int N, int nkb, long long nblocks)
 {
-    const int c = threadIdx.x;
-    const int bh = blockIdx.x / nkb, kb = blockIdx.x % nkb;
-    const int r0 = kb * 32;
+    constexpr int CG = D / 8;                      // column groups of a block
+    constexpr int BPW = kPrepThreads / CG;         // blocks per workgroup
+    const int cg = threadIdx.x % CG;
+    const long long gb = (long long)blockIdx.x * BPW + threadIdx.x / CG;   // (head, block) index
+    if (gb >= nblocks) return;
+    const long long bh = gb / nkb;
+    const int r0 = (int)(gb - bh * nkb) * 32;
     const int nr = min(32, N - r0);
-    const size_t head = (size_t)bh * N * D;
-    float x[32];
-    float a = 0.f;
+    const size_t base = ((size_t)bh * N + r0) * D + 8 * cg;
+    typedef __attribute__((ext_vector_type(8))) T T8;
+    u32x4 raw[32];
+#pragma unroll
+    for (int r = 0; r < 32; ++r)
+        raw[r] = r < nr ? *reinterpret_cast<const u32x4*>(X + base + (size_t)r * D) : u32x4{0, 0, 0, 0};
+    float a[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = 0.f;
 #pragma unroll
     for (int r = 0; r < 32; ++r) {
-        x[r] = r < nr ? to_f(X[head + (size_t)(r0 + r) * D + c]) : 0.f;
-        a = fmaxf(a, fabsf(x[r]));
-    }
-    const int ex = mx_exponent(a);
+        const T8 x = __builtin_bit_cast(T8, raw[r]);
 #pragma unroll
-    for (int r = 0; r < 32; r += 2) {
-        const uint32_t w = e4m3x2(__builtin_ldexpf(x[r], -ex), __builtin_ldexpf(x[r + 1], -ex));
-        if (r < nr) X8[head + (size_t)(r0 + r) * D + c] = (uint8_t)(w & 0xff);
-        if (r + 1 < nr) X8[head + (size_t)(r0 + r + 1) * D + c] = (uint8_t)(w >> 8);
+        for (int e = 0; e < 8; ++e) a[e] = fmaxf(a[e], fabsf(to_f(x[e])));
     }
-    scales[((size_t)bh * nkb + kb) * D + (c % 32) * (D / 32) + c / 32] = (uint8_t)(ex + 127);
+    int ex[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ex[e] = mx_exponent(a[e]);
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+        if (r < nr) {
+            const T8 x = __builtin_bit_cast(T8, raw[r]);
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = __builtin_ldexpf(to_f(x[e]), -ex[e]);
+            const uint32_t w0 = e4m3x2(y[0], y[1]) | (e4m3x2(y[2], y[3]) << 16);
+            const uint32_t w1 = e4m3x2(y[4], y[5]) | (e4m3x2(y[6], y[7]) << 16);
+            *reinterpret_cast<u32x2*>(X8 + base + (size_t)r * D) = u32x2{w0, w1};
+        }
+    }
+    uint8_t* sc = scales + (size_t)gb * D;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int col = 8 * cg + e;
+        sc[(col % 32) * (D / 32) + col / 32] = (uint8_t)(ex[e] + 127);
+    }
 }
 
 __global__ void zero_u32_kernel(unsigned* p) { *p = 0u; }
@@ -341,8 +369,10 @@ static hipError_t prep_t(const PrepArgs& a, hipStream_t s) {
     const T* x = static_cast<const T*>(a.x);
     if (a.mx == kMxAlongN) {
         const int nkb = (a.N + 31) / 32;
-        hipLaunchKernelGGL((mx_prep_cols_kernel<T, D>), dim3((unsigned)((long long)a.B * a.H * nkb)),
-                           dim3(D), 0, s, x, a.x8, a.x8 + a.scales_off, a.N, nkb);
+        const long long nblocks = (long long)a.B * a.H * nkb;
+        constexpr int BPW = kPrepThreads / (D / 8);
+        hipLaunchKernelGGL((mx_prep_cols_kernel<T, D>), dim3((unsigned)((nblocks + BPW - 1) / BPW)),
+                           dim3(kPrepThreads), 0, s, x, a.x8, a.x8 + a.scales_off, a.N, nkb, nblocks);
         return hipGetLastError();
     }
     if (a.mx == kMxAlongD) {
