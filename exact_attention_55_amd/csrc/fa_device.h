@@ -69,6 +69,22 @@ __device__ __forceinline__ f32x16 mfma32(const f16x8& a, const f16x8& b, const f
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// o *= a on accumulators that live in the accumulation registers (AGPRs):
+// each element is read out, scaled and written back in one asm block. A
+// plain vector multiply there makes the compiler keep a VGPR copy of every
+// accumulator across the key loop (copied in at every iteration) because
+// VALU instructions cannot name AGPRs; with this form the accumulators stay
+// in AGPRs and only the rarely taken rescale moves them.
+__device__ __forceinline__ void scale_acc(f32x16& o, float a) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        float x = o[i], t;
+        asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                     : "+a"(x), "=&v"(t) : "v"(a));
+        o[i] = x;
+    }
+}
+
 // D(32x32 f32) += A(32x64) * B(64x32) with OCP e4m3 operands (32 bytes per
 // lane per operand) and unit block scales (E8M0 127 = 2^0).
 __device__ __forceinline__ f32x16 mfma32_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {

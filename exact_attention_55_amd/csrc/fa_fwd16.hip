@@ -103,7 +103,9 @@ template <> struct Cfg16<256> : CfgT<FA16_CFG_256> {};
 // Per-wave state and per-tile steps. A wave owns 32*QB query rows; a key
 // tile has BC keys. Swizzled LDS tiles: see lds_swz16 and the lane offsets ka
 // (K fragments) and va (transposing V reads) set up in the kernel.
-template <typename T, int D, int QB, int BC>
+// ACC: O lives in the accumulation registers (one wave per SIMD, where the
+// 512-register budget puts it there); its rare rescale then runs in place.
+template <typename T, int D, int QB, int BC, bool ACC>
 struct Wave16 {
     using X8 = typename Elt<T>::x8;
     using X2 = typename Elt<T>::x2;
@@ -216,7 +218,12 @@ struct Wave16 {
             l[qb] *= alpha;
             lx[qb] *= alpha;
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) o[qb][db] *= alpha;
+            for (int db = 0; db < NDB; ++db) {
+                if (ACC)
+                    scale_acc(o[qb][db], alpha);
+                else
+                    o[qb][db] *= alpha;
+            }
         }
     }
 
@@ -510,7 +517,7 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     using X8 = typename Elt<T>::x8;
     using X2 = typename Elt<T>::x2;
     constexpr int NW = Cfg16<D>::NW, QB = Cfg16<D>::QB, BC = Cfg16<D>::BC;
-    using W = Wave16<T, D, QB, BC>;
+    using W = Wave16<T, D, QB, BC, Cfg16<D>::WPE == 1>;
     constexpr int QW = 32 * QB;            // query rows per wave
     constexpr int BR = NW * QW;            // query rows per workgroup
     constexpr int NCH = W::NCH, NDB = W::NDB, NKB = W::NKB, RB = W::RB, NVA = W::NVA;

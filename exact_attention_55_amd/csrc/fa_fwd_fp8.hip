@@ -82,7 +82,9 @@ struct TileScales {
     __device__ __forceinline__ int vbyte(int db) const { return (v[db >> 2] >> (8 * (db & 3))) & 0xff; }
 };
 
-template <int D, int BC, bool MX>
+// ACC: O lives in the accumulation registers (one wave per SIMD); its rare
+// rescale then runs in place.
+template <int D, int BC, bool MX, bool ACC>
 struct Wave8 {
     static constexpr int RB = D;           // bytes per K / V row in LDS
     static constexpr int NCH = D / 64;     // k-steps of S^T = K Q^T
@@ -185,7 +187,12 @@ struct Wave8 {
         m = mnew;
         l *= alpha;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+        for (int db = 0; db < NDB; ++db) {
+            if (ACC)
+                scale_acc(o[db], alpha);
+            else
+                o[db] *= alpha;
+        }
     }
 
     // P' for score blocks 2t, 2t+1 -> PV operand t. Dword g of the operand
@@ -345,7 +352,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
                   int N, int num_qtiles, int num_blocks, int nsb, size_t scales_off, float c)
 {
     constexpr int NW = Cfg8<D>::NW, BC = Cfg8<D>::BC;
-    using W = Wave8<D, BC, MX>;
+    using W = Wave8<D, BC, MX, Cfg8<D>::WPE == 1>;
     using TS = typename W::TS;
     constexpr int SBY = D / 32;            // microscaling: scale bytes per row of Q or K
     static_assert(!MX || W::NPV == 1, "microscaled V scales are held for one PV k-step per tile");
