@@ -79,12 +79,20 @@ constexpr float kBig = 16384.0f;
 #define FA16_VPD 4
 #endif
 
-// Tile configuration per head dimension. NW waves per workgroup, each owning
-// 32*QB query rows; BC keys per K/V tile; WPE = waves per SIMD the register
-// budget is sized for (2: 256 registers per wave, so two waves share a SIMD
-// and one wave's softmax overlaps the other's MFMAs).
+// Tile configuration per head dimension (and, at d = 64, per mask). NW waves
+// per workgroup, each owning 32*QB query rows; BC keys per K/V tile; WPE =
+// waves per SIMD the register budget is sized for (2: 256 registers per
+// wave, so two waves share a SIMD and one wave's softmax overlaps the
+// other's MFMAs). At d = 64 the non-causal kernel gives each wave 64 query
+// rows (each K and V^T fragment read from LDS feeds two MFMAs, halving the
+// LDS bytes per flop) with 32-key tiles, which still fits two waves per
+// SIMD; causal keeps 32 rows per wave (its diagonal tiles cost more with
+// 256-row workgroups).
 #ifndef FA16_CFG_64
-#define FA16_CFG_64 4, 1, 64, 2
+#define FA16_CFG_64 4, 2, 32, 2
+#endif
+#ifndef FA16_CFG_64_CAUSAL
+#define FA16_CFG_64_CAUSAL 4, 1, 64, 2
 #endif
 #ifndef FA16_CFG_128
 #define FA16_CFG_128 4, 1, 64, 2
@@ -95,10 +103,11 @@ constexpr float kBig = 16384.0f;
 template <int NW_, int QB_, int BC_, int WPE_> struct CfgT {
     static constexpr int NW = NW_, QB = QB_, BC = BC_, WPE = WPE_;
 };
-template <int D> struct Cfg16;
-template <> struct Cfg16<64> : CfgT<FA16_CFG_64> {};
-template <> struct Cfg16<128> : CfgT<FA16_CFG_128> {};
-template <> struct Cfg16<256> : CfgT<FA16_CFG_256> {};
+template <int D, bool CAUSAL> struct Cfg16;
+template <> struct Cfg16<64, false> : CfgT<FA16_CFG_64> {};
+template <> struct Cfg16<64, true> : CfgT<FA16_CFG_64_CAUSAL> {};
+template <bool C> struct Cfg16<128, C> : CfgT<FA16_CFG_128> {};
+template <bool C> struct Cfg16<256, C> : CfgT<FA16_CFG_256> {};
 
 // Per-wave state and per-tile steps. A wave owns 32*QB query rows; a key
 // tile has BC keys. Swizzled LDS tiles: see lds_swz16 and the lane offsets ka
@@ -447,8 +456,9 @@ struct Wave16 {
         constexpr int NKF = NCH * NKB;      // K fragments = score MFMAs per tile
         constexpr int NVF = NPV * NDB;      // V^T fragments = PV MFMAs per tile
         constexpr int NPAIR = NKB * 8;      // exponential pairs per lane per tile
-        constexpr int KPD = FA16_KPD;       // K fragments read ahead of their MFMA
-        constexpr int VPD = FA16_VPD;       // V^T fragments read ahead of their MFMA
+        // K / V^T fragments read ahead of their MFMA (at most half a tile's)
+        constexpr int KPD = NKF >= 2 * FA16_KPD ? FA16_KPD : NKF / 2;
+        constexpr int VPD = NVF >= 2 * FA16_VPD ? FA16_VPD : NVF / 2;
         static_assert(NKF >= KPD + VPD && NVF > VPD, "tile too small for the read-ahead");
         X8 kf[NKB][NCH];
         f32x16 sn[QB][NKB];
@@ -509,15 +519,15 @@ struct Wave16 {
 };
 
 template <typename T, int D, bool CAUSAL, bool OUT_F32>
-__global__ void __launch_bounds__(Cfg16<D>::NW * 64, Cfg16<D>::WPE)
+__global__ void __launch_bounds__((Cfg16<D, CAUSAL>::NW * 64), (Cfg16<D, CAUSAL>::WPE))
 fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
                 void* __restrict__ Og, float* __restrict__ LSEg, int N, int num_qtiles,
                 int num_blocks, float c)
 {
     using X8 = typename Elt<T>::x8;
     using X2 = typename Elt<T>::x2;
-    constexpr int NW = Cfg16<D>::NW, QB = Cfg16<D>::QB, BC = Cfg16<D>::BC;
-    using W = Wave16<T, D, QB, BC, Cfg16<D>::WPE == 1>;
+    constexpr int NW = Cfg16<D, CAUSAL>::NW, QB = Cfg16<D, CAUSAL>::QB, BC = Cfg16<D, CAUSAL>::BC;
+    using W = Wave16<T, D, QB, BC, Cfg16<D, CAUSAL>::WPE == 1>;
     constexpr int QW = 32 * QB;            // query rows per wave
     constexpr int BR = NW * QW;            // query rows per workgroup
     constexpr int NCH = W::NCH, NDB = W::NDB, NKB = W::NKB, RB = W::RB, NVA = W::NVA;
@@ -741,13 +751,13 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
 
 template <typename T, int D, bool CAUSAL, bool OUT_F32>
 static hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
-    constexpr int BR = Cfg16<D>::NW * 32 * Cfg16<D>::QB;
+    constexpr int BR = Cfg16<D, CAUSAL>::NW * 32 * Cfg16<D, CAUSAL>::QB;
     const int num_qtiles = (a.N + BR - 1) / BR;
     const long long nblk = (long long)num_qtiles * a.B * a.H;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const float c = a.scale * kLog2e;
     hipLaunchKernelGGL((fa_fwd16_kernel<T, D, CAUSAL, OUT_F32>), dim3((unsigned)nblk),
-                       dim3(Cfg16<D>::NW * 64), 0, s, static_cast<const T*>(a.q),
+                       dim3(Cfg16<D, CAUSAL>::NW * 64), 0, s, static_cast<const T*>(a.q),
                        static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.o, a.lse, a.N,
                        num_qtiles, (int)nblk, c);
     return hipGetLastError();

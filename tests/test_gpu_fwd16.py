@@ -42,6 +42,7 @@ SMALL = [
     (1, 1, 256, 64, True, "fp16"),
     (2, 3, 300, 64, False, "bf16"),
     (2, 3, 300, 64, True, "bf16"),
+    (1, 2, 1000, 64, False, "fp16"),      # 64 rows per wave: 4 query tiles, ragged end
     (1, 2, 1000, 128, False, "bf16"),
     (1, 2, 1000, 128, True, "bf16"),
     (1, 2, 517, 128, True, "fp16"),
