@@ -111,14 +111,6 @@ struct Copier {
     }
 };
 
-// Workgroup -> (head, tile): consecutive workgroups land on different XCDs;
-// regroup so each XCD walks whole heads.
-__device__ __forceinline__ int xcd_block(int num_blocks) {
-    int bid = blockIdx.x;
-    if ((num_blocks & 7) == 0) bid = (bid & 7) * (num_blocks >> 3) + (bid >> 3);
-    return bid;
-}
-
 // 16-bit row of the head-major output for the transposed accumulator of a
 // lane (lane = row, register r of d-block db = column 32*db + 8*(r/4) +
 // 4*hi + r%4), scaled.
@@ -194,9 +186,9 @@ bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __res
     const int l32 = lane & 31, hi = lane >> 5;
     if (num_blocks < 0) smem[tid] = 0;     // keeps the LDS reads alive (tiles come by DMA)
 
-    const int bid = xcd_block(num_blocks);
-    const int bh = bid / num_qtiles;
-    int qt = bid - bh * num_qtiles;
+    // Workgroup -> (head, query tile) (see grid_tile); causal: heaviest first.
+    int bh, qt;
+    grid_tile(num_blocks, num_qtiles, CAUSAL, bh, qt);
     if (CAUSAL) qt = num_qtiles - 1 - qt;
     const size_t head = (size_t)bh * N * D;
     const int qtile0 = qt * BR, q0 = qtile0 + wave * QW;
@@ -216,6 +208,9 @@ bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __res
     auto ktile = [&](int t) -> const char* { return smem + (t & 1) * TB; };
     auto vtile = [&](int t) -> const char* { return smem + (2 + (t & 1)) * TB; };
 
+    // The first tile copies go out before the fragment loads, so the
+    // latencies overlap (the wait below covers both).
+    load_kv(0);
     // Q^T and dO^T fragments (B operands): lane = query, d = 16*ch + 8*hi .. +7
     X8 qf[NCH], of[NCH];
 #pragma unroll
@@ -236,7 +231,6 @@ bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __res
 
     const int kend = CAUSAL ? min(N, qtile0 + BR) : N;
     const int nkt = (kend + BC - 1) / BC;
-    load_kv(0);
     wait_vm_all();
     __syncthreads();
     for (int t = 0; t < nkt; ++t) {
@@ -348,9 +342,10 @@ bwd_dkv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __re
     const int l32 = lane & 31, hi = lane >> 5;
     if (num_blocks < 0) smem[tid] = 0;
 
-    const int bid = xcd_block(num_blocks);
-    const int bh = bid / num_ktiles;
-    const int kt = bid - bh * num_ktiles;
+    // Workgroup -> (head, key tile) (see grid_tile); causal: the first key
+    // tiles, which see the most queries, go first.
+    int bh, kt;
+    grid_tile(num_blocks, num_ktiles, CAUSAL, bh, kt);
     const size_t head = (size_t)bh * N * D;
     const int kblk0 = kt * BK, k0 = kblk0 + wave * KW;
     // lane -> key: permuted within the wave's 32 keys like the A-operand rows,
@@ -393,6 +388,18 @@ bwd_dkv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __re
         return a;
     };
 
+    // This wave's V rows k0 .. k0+31 into its LDS slot (rows >= N read 0)
+    // and the first Q/dO tile go out before the K fragment loads, so the
+    // latencies overlap (the wait below covers all of them).
+    const char* vw = smem + 4 * TB + 4 * CB + wave * VB;
+    {
+        Copier<D, KW, 1> vcp;
+        vcp.init(0, lane, sbase + 4 * TB + 4 * CB + wave_u * VB, 0);
+        const i32x4 vrs = make_rsrc(Vg + head + (size_t)k0 * D, max(N - k0, 0) * RB);
+        vcp.issue(vrs, 0, 0);
+    }
+    const int i0 = CAUSAL ? kblk0 / BQ : 0;
+    load_qo(i0);
     // K^T fragments (B operand of S): lane = key, d = 16*ch + 8*hi .. +7
     X8 kf[NCH];
 #pragma unroll
@@ -401,14 +408,6 @@ bwd_dkv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __re
         kf[ch] = key < N ? load16<X8>(Kg + head + (size_t)key * D + 16 * ch + 8 * hi) : z;
     }
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
-    // this wave's V rows k0 .. k0+31 into its LDS slot (rows >= N read 0)
-    const char* vw = smem + 4 * TB + 4 * CB + wave * VB;
-    {
-        Copier<D, KW, 1> vcp;
-        vcp.init(0, lane, sbase + 4 * TB + 4 * CB + wave_u * VB, 0);
-        const i32x4 vrs = make_rsrc(Vg + head + (size_t)k0 * D, max(N - k0, 0) * RB);
-        vcp.issue(vrs, 0, 0);
-    }
 
     TL tl;
     tl.init(lane);
@@ -416,8 +415,6 @@ bwd_dkv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __re
 #pragma unroll
     for (int db = 0; db < NDB; ++db) dk[db] = dv[db] = f32x16{};
 
-    const int i0 = CAUSAL ? kblk0 / BQ : 0;
-    load_qo(i0);
     wait_vm_all();
     __syncthreads();
     for (int i = i0; i < nqt; ++i) {

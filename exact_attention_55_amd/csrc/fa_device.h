@@ -247,6 +247,27 @@ __device__ __forceinline__ void buffer_load_lds16(i32x4 rsrc, uint32_t lds, uint
                  :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
 }
 
+// Workgroup -> (head, tile level) for a grid of heads x tiles workgroups.
+// Balanced (non-causal): consecutive workgroups land on different XCDs, so
+// they are regrouped to let each XCD walk whole heads (a head's K/V then stay
+// in that XCD's L2). Unbalanced (causal): workgroup i takes level i / heads
+// of head i % heads, so level 0 (the caller's heaviest tile) of every head is
+// dispatched before any lighter one; a head's tiles still share one XCD when
+// the head count is a multiple of 8.
+__device__ __forceinline__ void grid_tile(int num_blocks, int num_tiles, bool unbalanced, int& bh,
+                                          int& level) {
+    const int i = blockIdx.x;
+    if (unbalanced) {
+        const int heads = num_blocks / num_tiles;
+        level = i / heads;
+        bh = i - level * heads;
+        return;
+    }
+    const int bid = ((num_blocks & 7) == 0) ? (i & 7) * (num_blocks >> 3) + (i >> 3) : i;
+    bh = bid / num_tiles;
+    level = bid - bh * num_tiles;
+}
+
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // Phase boundary of the ping-pong schedule: nothing is scheduled across it,

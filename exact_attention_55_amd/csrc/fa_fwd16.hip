@@ -548,13 +548,10 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     // LDS reads from being treated as reads of uninitialised memory.
     if (num_blocks < 0) smem[tid] = 0;
 
-    // Workgroup -> (head, query tile). Consecutive workgroups land on
-    // different XCDs; regroup so each XCD walks whole heads (K/V of a head
-    // then stay in that XCD's L2). Causal: heaviest query tiles first.
-    int bid = blockIdx.x;
-    if ((num_blocks & 7) == 0) bid = (bid & 7) * (num_blocks >> 3) + (bid >> 3);
-    const int bh = bid / num_qtiles;
-    int qt = bid - bh * num_qtiles;
+    // Workgroup -> (head, query tile) (see grid_tile). Causal: the heaviest
+    // query tiles (last rows) of all heads go first.
+    int bh, qt;
+    grid_tile(num_blocks, num_qtiles, CAUSAL, bh, qt);
     if (CAUSAL) qt = num_qtiles - 1 - qt;
 
     const size_t head = (size_t)bh * N * D;
@@ -589,6 +586,11 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     auto load_v = [&](int t) { if (t < nkt_use) issue(vrs, t, 2 + (t & 1)); };
     auto ktile = [&](int t) -> const char* { return smem + (t & 1) * TB; };
 
+    // The first tile copies go out before Q's loads, so the two latencies
+    // overlap (the wait below covers both).
+    load_k(0);
+    load_v(0);
+    load_k(1);
     // Q^T fragments (B operand): lane holds query q0+32*qb+l32, d = 16*ch + 8*hi .. +7
     X8 qf[QB][NCH];
 #pragma unroll
@@ -602,10 +604,10 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
                 qf[qb][ch] = __builtin_bit_cast(X8, u32x4{0, 0, 0, 0});
         }
     }
-    // Q has landed before any tile copy is issued. (A wait the compiler can
-    // see: otherwise it keeps Q's loads pending on paths that skip the first
-    // use and re-waits inside the key loop, where vmcnt also counts the
-    // tile copies in flight.)
+    // Q (and the first tile copies) have landed before the key loop. (A wait
+    // the compiler can see: otherwise it keeps Q's loads pending on paths
+    // that skip the first use and re-waits inside the key loop, where vmcnt
+    // also counts the tile copies in flight.)
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
 
     // Key tiles [0, nfull) need no mask for any wave of the workgroup; tiles
@@ -656,9 +658,6 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     // Invariant at the top of step t: K_t, V_t and (if any) K_{t+1} are in
     // LDS. Step t fills the slots of K_{t-1}/K_t and V_{t-1} that every wave
     // finished with before the previous barrier.
-    load_k(0);
-    load_v(0);
-    load_k(1);
     wait_vm_all();
     __syncthreads();
     if (nfull > 0) {

@@ -384,10 +384,9 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     // compiler as stores); a store it cannot rule out keeps the reads alive.
     if (num_blocks < 0) smem[tid] = 0;
 
-    int bid = blockIdx.x;
-    if ((num_blocks & 7) == 0) bid = (bid & 7) * (num_blocks >> 3) + (bid >> 3);
-    const int bh = bid / num_qtiles;
-    int qt = bid - bh * num_qtiles;
+    // Workgroup -> (head, query tile) (see grid_tile); causal: heaviest first.
+    int bh, qt;
+    grid_tile(num_blocks, num_qtiles, CAUSAL, bh, qt);
     if (CAUSAL) qt = num_qtiles - 1 - qt;
 
     const size_t head = (size_t)bh * N * D;
@@ -521,6 +520,11 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
             lscale = __builtin_amdgcn_rcpf(kPScale * wv);
         }
     };
+    // The first tile copies go out before Q's loads, so the two latencies
+    // overlap (the wait below covers both).
+    load_kv(krs, 0, 0);
+    load_kv(vrs, 0, 2);
+    load_kv(krs, 1, 1);
     // Q^T fragments: query q0 + l32, bytes [64*ch + 32*hi, +32) (microscaled:
     // [64*ch + 16*hi, +16) and [64*ch + 32 + 16*hi, +16), the chunk order of
     // the K fragments); its MX scale byte 2*ch + hi of the row
@@ -555,8 +559,8 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
                            (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
         }
     }
-    // Q has landed before any tile copy is issued (a wait the compiler sees;
-    // see fa_fwd16_kernel).
+    // Q and the first tile copies have landed (a wait the compiler sees; see
+    // fa_fwd16_kernel).
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
 
     // Lane offsets into swizzled tiles.
@@ -589,9 +593,6 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     // next; the scales of a tile are requested with its copy and read after
     // the barrier that publishes it.
     TS tk, tv;
-    load_kv(krs, 0, 0);
-    load_kv(vrs, 0, 2);
-    load_kv(krs, 1, 1);
     wait_vm_all();
     __syncthreads();
     if constexpr (MX) {
