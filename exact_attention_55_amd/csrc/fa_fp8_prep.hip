@@ -148,15 +148,27 @@ fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t*
         }
     }
 
+    // All of the thread's row loads are issued before any is used, so they
+    // are in flight together (one at a time leaves each waiting a full
+    // memory latency).
+    // Rows past the end read the head's last row (always valid, N >= 1) and
+    // are zeroed, so the loads carry no branch.
+    u32x4 raw[NPASS];
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+        const int row = blk * kQuantBlockRows + p * RPP + rp;
+        raw[p] = *reinterpret_cast<const u32x4*>(X + head + (size_t)min(row, N - 1) * D + 8 * j);
+    }
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p)
+        if (blk * kQuantBlockRows + p * RPP + rp >= N) raw[p] = u32x4{0, 0, 0, 0};
     float v[NPASS][8];
     float amax = 0.f;
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
         const int row = blk * kQuantBlockRows + p * RPP + rp;
-        u32x4 raw = u32x4{0, 0, 0, 0};
-        if (row < N) raw = *reinterpret_cast<const u32x4*>(X + head + (size_t)row * D + 8 * j);
         typedef __attribute__((ext_vector_type(8))) T T8;
-        const T8 x = __builtin_bit_cast(T8, raw);
+        const T8 x = __builtin_bit_cast(T8, raw[p]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[p][e] = to_f(x[e]);
         if (ROPE != 0) {
