@@ -112,6 +112,47 @@ def test_fp8_small_vs_oracles(B, H, N, d, causal):
     assert rmse_fq <= FP8_RMSE / 2, f"RMSE vs fake-quant {rmse_fq:.3e}"
 
 
+JUMP_KEYS = [300, 301, 455]      # keys in later tiles, scaled by 8 (exact in bf16)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_late_score_jump(causal):
+    """Keys eight times longer than the rest, in tiles after the first, give
+    some queries scores far above the first tile's maximum: the quantised
+    P' = 8 p w_j would pass the e4m3 maximum there, so those tiles take the
+    exact-maximum redo (the reference maximum moves, O and l are rescaled).
+    Every row is held elementwise to exact attention of the oracle's own
+    quantised inputs within the bound on the e4m3 rounding of P'
+    (fp8_p_rounding_bound), and the LSE to it within 1e-3. (Against exact
+    attention of the unquantised inputs no fixed RMSE applies here: the e4m3
+    rounding of the long keys alone moves their logits by ~0.7.)"""
+    B, H, N, d = 1, 2, 600, 128
+    say(f"fp8 late score jump causal={causal}")
+    q, k, v = make_qkv(B, H, N, d, seed=57, dtype="bf16")
+    k = k.clone()
+    k[:, :, JUMP_KEYS] *= 8
+    signs = make_signs(H, d, 57)
+    q64, k64, v64 = to_f64(q), to_f64(k), to_f64(v)
+    o, lse = fp8_run(q, k, v, signs, 128, causal)
+    assert np.all(np.isfinite(o))
+    qc, qs = oracle.fp8_quantize(q64, signs, 128)
+    kc, ks = oracle.fp8_quantize(k64, signs, 128)
+    vc, vs = oracle.fp8_quantize(v64, None, 128)
+    qd, kd, vd = (oracle.fp8_dequantize(c, sc) for c, sc in ((qc, qs), (kc, ks), (vc, vs)))
+    o_fq, lse_fq = oracle.attention(qd, kd, vd, causal)
+    # the jump is real: some rows' largest logit lies many log2 units above
+    # every logit of the first key tile
+    s = np.einsum("bhid,bhjd->bhij", qd, kd) / np.sqrt(d)
+    assert np.max(lse_fq - s[..., :64].max(-1)) * np.log2(np.e) > 8
+    check_lse(lse, lse_fq)
+    rows = np.arange(N)
+    for h in range(H):
+        w = np.repeat(vs[0, h] / vs[0, h].max(), 128)[:N]
+        bound = fp8_p_rounding_bound(qd, kd, vd, 0, h, rows, causal, w) + 1e-5
+        err = np.abs(o[0, h] - o_fq[0, h])
+        assert np.all(err <= bound), f"head {h}: worst excess {np.max(err - bound):.3e}"
+
+
 def test_fp8_workload_outliers():
     """The outlier workload at full size: Hadamard + block scales stays within
     the RMSE bound and beats plain per-tensor FP8 (sampled rows)."""

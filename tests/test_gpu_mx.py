@@ -120,6 +120,38 @@ def test_mx_forward_vs_oracles(B, H, N, d, causal):
     assert rmse_fq <= FP8_RMSE / 2, f"RMSE vs fake-quant {rmse_fq:.3e}"
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_mx_late_score_jump(causal):
+    """As the block-scaled case: keys eight times longer than the rest in
+    tiles after the first push P' past the e4m3 maximum against the first
+    tile's maximum, so those tiles take the exact-maximum redo. Every row is
+    held elementwise to exact attention of the oracle's own MX-quantised
+    inputs within the bound on the e4m3 rounding of P' = 8 p, and the LSE
+    to it within 1e-3."""
+    B, H, N, d = 1, 2, 600, 128
+    say(f"mx late score jump causal={causal}")
+    q, k, v = make_qkv(B, H, N, d, seed=59, dtype="bf16")
+    k = k.clone()
+    k[:, :, [300, 301, 455]] *= 8
+    signs = make_signs(H, d, 59)
+    q64, k64, v64 = to_f64(q), to_f64(k), to_f64(v)
+    o, lse = mx_run(q, k, v, signs, causal)
+    assert np.all(np.isfinite(o))
+    qc, qe = mx_quantize(q64, "d", signs)
+    kc, ke = mx_quantize(k64, "d", signs)
+    vc, ve = mx_quantize(v64, "n", None)
+    qd, kd, vd = mx_dequantize(qc, qe, "d"), mx_dequantize(kc, ke, "d"), mx_dequantize(vc, ve, "n")
+    o_fq, lse_fq = oracle.attention(qd, kd, vd, causal)
+    s = np.einsum("bhid,bhjd->bhij", qd, kd) / np.sqrt(d)
+    assert np.max(lse_fq - s[..., :64].max(-1)) * np.log2(np.e) > 8
+    check_lse(lse, lse_fq)
+    rows = np.arange(N)
+    for h in range(H):
+        bound = fp8_p_rounding_bound(qd, kd, vd, 0, h, rows, causal) + 1e-5
+        err = np.abs(o[0, h] - o_fq[0, h])
+        assert np.all(err <= bound), f"head {h}: worst excess {np.max(err - bound):.3e}"
+
+
 @pytest.mark.parametrize("d", [64, 128, 256])
 def test_mx_single_key(d):
     """N = 1: the one quantised weight is exactly P' = 8, undone by the 2^-3
