@@ -18,7 +18,7 @@ import oracle
 import exact_attention_55_amd as fa
 from exact_attention_55_amd.inputs import CONFIGS, make_qkv, to_f64
 
-from helpers import check_lse, check_o, sample_rows
+from helpers import errors, check_lse, check_o, sample_rows
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -125,7 +125,10 @@ def test_full_size_sampled(name):
         o_ref, lse_ref = oracle.attention_rows(q64, k64, v64, b, h, rows, causal)
         o_s = o32[b, h, rows].cpu().numpy()
         check_o(o_s, o_ref, "f32", f"head {b},{h}")
-        check_lse(lse32[b, h, rows].cpu().numpy(), lse_ref, f"head {b},{h}")
+        lerr = check_lse(lse32[b, h, rows].cpu().numpy(), lse_ref, f"head {b},{h}")
+        mx, rmse = errors(o_s, o_ref)
+        say(f"{name} head {b},{h} ({len(rows)} rows, fp32 O): max-abs {mx:.2e} RMSE {rmse:.2e} "
+            f"LSE {lerr:.2e}")
         check_o(o16[b, h, rows].float().cpu().numpy(), o_ref, cfg["dtype"], f"head {b},{h} 16-bit")
         check_lse(lse16[b, h, rows].cpu().numpy(), lse_ref, f"head {b},{h} 16-bit")
 
