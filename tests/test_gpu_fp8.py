@@ -5,7 +5,8 @@ oracle (exact attention of the oracle's own dequantised inputs).
 
 Quantised codes: without the Hadamard every float32 step of the quantiser is
 reproduced exactly, so the codes must be bit-identical. With it, the GPU's
-float32 butterflies round in a different order than the float64 transform,
+float32 butterflies round in a different order than the float64 transform
+(and the kernel multiplies by the rounded 1/scale instead of dividing),
 which can move a value lying within a few float32 ulps of an e4m3 rounding
 boundary to the neighbouring code; those codes must still be one of the two
 neighbours of the exact value, and they must be rare.
