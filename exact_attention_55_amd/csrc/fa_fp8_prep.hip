@@ -122,16 +122,21 @@ __device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
 // MODE 3: microscaling along d: one power-of-two scale per 32 columns of a
 //         row (4 lanes), stored as the E8M0 byte e + 127 at
 //         scales[row of the tensor][column block] (see mx_exponent).
+// Threads per 128-row block: 512 at d = 256 (8 passes of 16 rows), so a
+// thread's rows in flight stay within the register budget; 256 otherwise.
+template <int D> constexpr int quant_threads() { return D == 256 ? 512 : kPrepThreads; }
+
 template <typename T, int D, bool HAD, int MODE, int ROPE>
-__global__ void __launch_bounds__(kPrepThreads)
+__global__ void __launch_bounds__(quant_threads<D>())
 fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t* __restrict__ signs,
                 float* __restrict__ scales, unsigned* __restrict__ gamax, int N, int H, int nblk,
                 RopeFreqs rf)
 {
+    constexpr int NT = quant_threads<D>();
     constexpr int LPR = D / 8;                 // lanes per row
-    constexpr int RPP = kPrepThreads / LPR;    // rows per pass
+    constexpr int RPP = NT / LPR;              // rows per pass
     constexpr int NPASS = kQuantBlockRows / RPP;
-    __shared__ float red[kPrepThreads / 64];
+    __shared__ float red[NT / 64];
 
     const int tid = threadIdx.x;
     const int j = tid % LPR, rp = tid / LPR;
@@ -278,7 +283,7 @@ fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t*
         __syncthreads();
         amax = red[0];
 #pragma unroll
-        for (int w = 1; w < kPrepThreads / 64; ++w) amax = fmaxf(amax, red[w]);
+        for (int w = 1; w < NT / 64; ++w) amax = fmaxf(amax, red[w]);
     }
     if (MODE == 1) {
         if (tid == 0) atomicMax(gamax, __float_as_uint(amax));
@@ -400,13 +405,13 @@ static hipError_t prep_t(const PrepArgs& a, hipStream_t s) {
     }
     if (a.mx == kMxAlongD) {
         hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 3, ROPE>), dim3((unsigned)grid),
-                           dim3(kPrepThreads), 0, s, x, a.x8, a.signs, scales, nullptr, a.N, a.H, nblk,
+                           dim3(quant_threads<D>()), 0, s, x, a.x8, a.signs, scales, nullptr, a.N, a.H, nblk,
                            a.rope);
         return hipGetLastError();
     }
     if (a.block_rows != 0) {
         hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 0, ROPE>), dim3((unsigned)grid),
-                           dim3(kPrepThreads), 0, s, x, a.x8, a.signs, scales, nullptr, a.N, a.H, nblk,
+                           dim3(quant_threads<D>()), 0, s, x, a.x8, a.signs, scales, nullptr, a.N, a.H, nblk,
                            a.rope);
         return hipGetLastError();
     }
@@ -414,9 +419,9 @@ static hipError_t prep_t(const PrepArgs& a, hipStream_t s) {
     // fill kernel reads it before overwriting every slot.
     unsigned* gamax = reinterpret_cast<unsigned*>(scales);
     hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(1), 0, s, gamax);
-    hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 1, ROPE>), dim3((unsigned)grid), dim3(kPrepThreads),
+    hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 1, ROPE>), dim3((unsigned)grid), dim3(quant_threads<D>()),
                        0, s, x, a.x8, a.signs, scales, gamax, a.N, a.H, nblk, a.rope);
-    hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 2, ROPE>), dim3((unsigned)grid), dim3(kPrepThreads),
+    hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 2, ROPE>), dim3((unsigned)grid), dim3(quant_threads<D>()),
                        0, s, x, a.x8, a.signs, scales, gamax, a.N, a.H, nblk, a.rope);
     hipLaunchKernelGGL(fill_scales_kernel, dim3(1), dim3(1024), 0, s, scales,
                        (const unsigned*)gamax, grid);
