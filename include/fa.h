@@ -193,9 +193,13 @@ size_t fa_decode_workspace_bytes(int B, int H, int Nq, int d, int num_splits);
  *
  * Per block: amax = max |x|, scale = amax / 448 in float32 (1 when amax is
  * 0), code = e4m3 round-to-nearest-even of x / scale, saturated to +-448.
- * d must be 64, 128 or 256. Per-tensor mode launches three kernels and uses
- * the scale slots as its reduction buffer; the tensor is only valid once the
- * stream reaches the end of the call. Returns FA_OK, FA_ERR_INVALID_ARG,
+ * Without signs x / scale is the IEEE float32 quotient; with them (rotated
+ * rows, whose float32 butterfly rounding already differs from an exact
+ * transform) it is x times the rounded 1 / scale, at most one float32 ulp
+ * from the quotient. d must be 64, 128 or 256. Per-tensor mode launches four
+ * kernels (clear, amax, quantise, fill the scale slots) and uses the scale
+ * slots as its reduction buffer; the tensor is only valid once the stream
+ * reaches the end of the call. Returns FA_OK, FA_ERR_INVALID_ARG,
  * FA_ERR_UNSUPPORTED or FA_ERR_HIP.
  */
 int fa_fp8_prep(const void* x, void* x8, const int8_t* signs,
