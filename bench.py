@@ -349,28 +349,38 @@ def leg_summary(L):
     return e
 
 
-def cpu_baseline(budget_s=12.0):
-    """The float64 oracle on whole heads of the main workload, until the budget
-    is spent (at least one head)."""
+def cpu_baseline():
+    """The float64 oracle on a bounded sample of one step of the timed
+    workload, on the same seeded inputs: the first half of the batch of every
+    leg, i.e. the bf16 forward, non-causal and causal, on 4 of the 8 sequences
+    of B=8 H=16 N=2048 d=128 (the oracle computes every score and masks; the
+    metric counts half for causal), and the fp8 leg as the fake-quant oracle
+    (random-sign Hadamard + per-128-row e4m3 quantisation of the outlier
+    inputs, then exact attention) on 2 of the 4 sequences of B=4 H=16 N=4096
+    d=128. Value: the sample's metric flops over the oracle's time."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
-    c = CONFIGS[MAIN]
-    q, k, v = make_qkv(1, 1, c["N"], c["d"], seed=c["seed"], dtype=c["dtype"])
-    q64, k64, v64 = (t.to(torch.float64).numpy() for t in (q, k, v))
-    heads, t0 = 0, time.perf_counter()
-    while True:
-        oracle.attention(q64, k64, v64, False)
-        heads += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or heads >= c["B"] * c["H"]:
-            break
-    fl = attention_flops(1, heads, c["N"], c["d"], False)
+    c, c8 = CONFIGS[MAIN], CONFIGS[FP8]
+    b, b8 = c["B"] // 2, c8["B"] // 2
+    q, k, v = (t[:b].to(torch.float64).numpy() for t in make_qkv(**c))
+    q8, k8, v8 = (t[:b8].to(torch.float64).numpy() for t in make_qkv(**c8))
+    signs = make_signs(c8["H"], c8["d"], c8["seed"])
+    fl = (attention_flops(b, c["H"], c["N"], c["d"], False)
+          + attention_flops(b, c["H"], c["N"], c["d"], True)
+          + attention_flops(b8, c8["H"], c8["N"], c8["d"], False))
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, False)
+    oracle.attention(q, k, v, True)
+    oracle.fake_quant_attention(q8, k8, v8, signs, 128, False)
+    el = time.perf_counter() - t0
     return {"value": fl / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{heads} of {c['B'] * c['H']} heads of B=8 H=16 N=2048 d=128 non-causal, "
+            "sample": f"first half of the batch of every leg of one step: bf16 {b} of 8 sequences "
+                      "x H=16, N=2048, d=128, non-causal and causal; fp8 fake-quant (Hadamard + "
+                      f"block e4m3) {b8} of 4 sequences x H=16, N=4096, d=128, outlier inputs; "
                       f"float64 numpy oracle, {el:.1f} s"}
 
 
