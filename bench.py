@@ -350,14 +350,13 @@ def leg_summary(L):
 
 
 def cpu_baseline():
-    """The float64 oracle on a bounded sample of one step of the timed
-    workload, on the same seeded inputs: the first half of the batch of every
-    leg, i.e. the bf16 forward, non-causal and causal, on 4 of the 8 sequences
-    of B=8 H=16 N=2048 d=128 (the oracle computes every score and masks; the
-    metric counts half for causal), and the fp8 leg as the fake-quant oracle
-    (random-sign Hadamard + per-128-row e4m3 quantisation of the outlier
-    inputs, then exact attention) on 2 of the 4 sequences of B=4 H=16 N=4096
-    d=128. Value: the sample's metric flops over the oracle's time."""
+    """The float64 oracle on one step of the timed workload (about 15 s on
+    16 host cores), on the same seeded inputs: the bf16 forward, non-causal
+    and causal, B=8 H=16 N=2048 d=128 (the oracle computes every score and
+    masks; the metric counts half for causal), and the fp8 leg as the
+    fake-quant oracle (random-sign Hadamard + per-128-row e4m3 quantisation of
+    the outlier inputs, then exact attention) at B=4 H=16 N=4096 d=128.
+    Value: the step's metric flops over the oracle's time."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -365,7 +364,7 @@ def cpu_baseline():
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
     c, c8 = CONFIGS[MAIN], CONFIGS[FP8]
-    b, b8 = c["B"] // 2, c8["B"] // 2
+    b, b8 = c["B"], c8["B"]
     q, k, v = (t[:b].to(torch.float64).numpy() for t in make_qkv(**c))
     q8, k8, v8 = (t[:b8].to(torch.float64).numpy() for t in make_qkv(**c8))
     signs = make_signs(c8["H"], c8["d"], c8["seed"])
@@ -378,10 +377,9 @@ def cpu_baseline():
     oracle.fake_quant_attention(q8, k8, v8, signs, 128, False)
     el = time.perf_counter() - t0
     return {"value": fl / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"first half of the batch of every leg of one step: bf16 {b} of 8 sequences "
-                      "x H=16, N=2048, d=128, non-causal and causal; fp8 fake-quant (Hadamard + "
-                      f"block e4m3) {b8} of 4 sequences x H=16, N=4096, d=128, outlier inputs; "
-                      f"float64 numpy oracle, {el:.1f} s"}
+            "sample": f"one step: bf16 B={b} H=16 N=2048 d=128 non-causal and causal; fp8 fake-quant "
+                      f"(Hadamard + block e4m3) B={b8} H=16 N=4096 d=128 outlier inputs; float64 numpy "
+                      f"oracle, {el:.1f} s"}
 
 
 def main():
