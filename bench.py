@@ -60,7 +60,7 @@ FP8 = "fp8_b4h16n4k_d128"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd16_b8h16n2k_d128_traffic.json")
 
 
-MAIN_SYMBOL = "_ZN2fa15fa_fwd16_kernelIDF16bLi128ELb0ELb0EEEvPKT_S3_S3_PvPfiiif"
+MAIN_SYMBOL = "_ZN2fa15fa_fwd16_kernelIDF16bLi128ELb0ELb0ELb0EEEvPKT_S3_S3_PvPfiiif"
 
 
 def _elf_sections(elf):

@@ -79,20 +79,20 @@ constexpr float kBig = 16384.0f;
 #define FA16_VPD 4
 #endif
 
-// Tile configuration per head dimension (and, at d = 64, per mask). NW waves
-// per workgroup, each owning 32*QB query rows; BC keys per K/V tile; WPE =
-// waves per SIMD the register budget is sized for (2: 256 registers per
-// wave, so two waves share a SIMD and one wave's softmax overlaps the
-// other's MFMAs). At d = 64 the non-causal kernel gives each wave 64 query
-// rows (each K and V^T fragment read from LDS feeds two MFMAs, halving the
-// LDS bytes per flop) with 32-key tiles, which still fits two waves per
-// SIMD; causal keeps 32 rows per wave (its diagonal tiles cost more with
-// 256-row workgroups).
+// Tile configuration per head dimension. NW waves per workgroup, each owning
+// 32*QB query rows; BC keys per K/V tile; WPE = waves per SIMD the register
+// budget is sized for (2: 256 registers per wave, so two waves share a SIMD
+// and one wave's softmax overlaps the other's MFMAs). At d = 64 a wide form
+// gives each wave 64 query rows (each K and V^T fragment read from LDS feeds
+// two MFMAs, halving the LDS bytes per flop) with 32-key tiles, which still
+// fits two waves per SIMD; it is launched when its grid fills the GPU twice
+// over (kWideMinBlocks workgroups), since 256-row workgroups leave a short
+// or small problem with too few of them.
 #ifndef FA16_CFG_64
-#define FA16_CFG_64 4, 2, 32, 2
+#define FA16_CFG_64 4, 1, 64, 2
 #endif
-#ifndef FA16_CFG_64_CAUSAL
-#define FA16_CFG_64_CAUSAL 4, 1, 64, 2
+#ifndef FA16_CFG_64_WIDE
+#define FA16_CFG_64_WIDE 4, 2, 32, 2
 #endif
 #ifndef FA16_CFG_128
 #define FA16_CFG_128 4, 1, 64, 2
@@ -100,18 +100,16 @@ constexpr float kBig = 16384.0f;
 #ifndef FA16_CFG_256
 #define FA16_CFG_256 4, 1, 64, 1
 #endif
+constexpr long long kWideMinBlocks = 1024;
 template <int NW_, int QB_, int BC_, int WPE_> struct CfgT {
     static constexpr int NW = NW_, QB = QB_, BC = BC_, WPE = WPE_;
 };
-template <int D, bool CAUSAL> struct Cfg16;
+template <int D, bool WIDE> struct Cfg16;
 template <> struct Cfg16<64, false> : CfgT<FA16_CFG_64> {};
-template <> struct Cfg16<64, true> : CfgT<FA16_CFG_64_CAUSAL> {};
-template <bool C> struct Cfg16<128, C> : CfgT<FA16_CFG_128> {};
-template <bool C> struct Cfg16<256, C> : CfgT<FA16_CFG_256> {};
+template <> struct Cfg16<64, true> : CfgT<FA16_CFG_64_WIDE> {};
+template <> struct Cfg16<128, false> : CfgT<FA16_CFG_128> {};
+template <> struct Cfg16<256, false> : CfgT<FA16_CFG_256> {};
 
-// Per-wave state and per-tile steps. A wave owns 32*QB query rows; a key
-// tile has BC keys. Swizzled LDS tiles: see lds_swz16 and the lane offsets ka
-// (K fragments) and va (transposing V reads) set up in the kernel.
 // ACC: O lives in the accumulation registers (one wave per SIMD, where the
 // 512-register budget puts it there); its rare rescale then runs in place.
 template <typename T, int D, int QB, int BC, bool ACC>
@@ -518,16 +516,16 @@ struct Wave16 {
     }
 };
 
-template <typename T, int D, bool CAUSAL, bool OUT_F32>
-__global__ void __launch_bounds__((Cfg16<D, CAUSAL>::NW * 64), (Cfg16<D, CAUSAL>::WPE))
+template <typename T, int D, bool CAUSAL, bool OUT_F32, bool WIDE>
+__global__ void __launch_bounds__((Cfg16<D, WIDE>::NW * 64), (Cfg16<D, WIDE>::WPE))
 fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
                 void* __restrict__ Og, float* __restrict__ LSEg, int N, int num_qtiles,
                 int num_blocks, float c)
 {
     using X8 = typename Elt<T>::x8;
     using X2 = typename Elt<T>::x2;
-    constexpr int NW = Cfg16<D, CAUSAL>::NW, QB = Cfg16<D, CAUSAL>::QB, BC = Cfg16<D, CAUSAL>::BC;
-    using W = Wave16<T, D, QB, BC, Cfg16<D, CAUSAL>::WPE == 1>;
+    constexpr int NW = Cfg16<D, WIDE>::NW, QB = Cfg16<D, WIDE>::QB, BC = Cfg16<D, WIDE>::BC;
+    using W = Wave16<T, D, QB, BC, Cfg16<D, WIDE>::WPE == 1>;
     constexpr int QW = 32 * QB;            // query rows per wave
     constexpr int BR = NW * QW;            // query rows per workgroup
     constexpr int NCH = W::NCH, NDB = W::NDB, NKB = W::NKB, RB = W::RB, NVA = W::NVA;
@@ -748,25 +746,35 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     }
 }
 
-template <typename T, int D, bool CAUSAL, bool OUT_F32>
+template <typename T, int D, bool CAUSAL, bool OUT_F32, bool WIDE>
 static hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
-    constexpr int BR = Cfg16<D, CAUSAL>::NW * 32 * Cfg16<D, CAUSAL>::QB;
+    constexpr int BR = Cfg16<D, WIDE>::NW * 32 * Cfg16<D, WIDE>::QB;
     const int num_qtiles = (a.N + BR - 1) / BR;
     const long long nblk = (long long)num_qtiles * a.B * a.H;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const float c = a.scale * kLog2e;
-    hipLaunchKernelGGL((fa_fwd16_kernel<T, D, CAUSAL, OUT_F32>), dim3((unsigned)nblk),
-                       dim3(Cfg16<D, CAUSAL>::NW * 64), 0, s, static_cast<const T*>(a.q),
+    hipLaunchKernelGGL((fa_fwd16_kernel<T, D, CAUSAL, OUT_F32, WIDE>), dim3((unsigned)nblk),
+                       dim3(Cfg16<D, WIDE>::NW * 64), 0, s, static_cast<const T*>(a.q),
                        static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.o, a.lse, a.N,
                        num_qtiles, (int)nblk, c);
     return hipGetLastError();
 }
 
+template <typename T, int D, bool CAUSAL, bool OUT_F32>
+static hipError_t launch_w(const FwdArgs& a, hipStream_t s) {
+    if constexpr (D == 64) {
+        constexpr int BRW = Cfg16<64, true>::NW * 32 * Cfg16<64, true>::QB;
+        if ((long long)a.B * a.H * ((a.N + BRW - 1) / BRW) >= kWideMinBlocks)
+            return launch_t<T, D, CAUSAL, OUT_F32, true>(a, s);
+    }
+    return launch_t<T, D, CAUSAL, OUT_F32, false>(a, s);
+}
+
 template <typename T, int D>
 static hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
     if (a.causal)
-        return a.out_f32 ? launch_t<T, D, true, true>(a, s) : launch_t<T, D, true, false>(a, s);
-    return a.out_f32 ? launch_t<T, D, false, true>(a, s) : launch_t<T, D, false, false>(a, s);
+        return a.out_f32 ? launch_w<T, D, true, true>(a, s) : launch_w<T, D, true, false>(a, s);
+    return a.out_f32 ? launch_w<T, D, false, true>(a, s) : launch_w<T, D, false, false>(a, s);
 }
 
 template <typename T>
