@@ -458,6 +458,9 @@ struct Wave16 {
         constexpr int KPD = NKF >= 2 * FA16_KPD ? FA16_KPD : NKF / 2;
         constexpr int VPD = NVF >= 2 * FA16_VPD ? FA16_VPD : NVF / 2;
         static_assert(NKF >= KPD + VPD && NVF > VPD, "tile too small for the read-ahead");
+        // The score phase reads the first KPD V^T fragments, the PV loop those
+        // from VPD on: every fragment is read only if KPD >= VPD.
+        static_assert(KPD >= VPD, "V^T fragments [KPD, VPD) would never be read");
         X8 kf[NKB][NCH];
         f32x16 sn[QB][NKB];
         X8 vf[NPV][NDB];

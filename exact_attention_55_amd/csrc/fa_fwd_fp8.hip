@@ -293,6 +293,9 @@ struct Wave8 {
         constexpr int KPD = NKF >= 4 ? 2 : 1;
         constexpr int VPD = (NKF - KPD) < 2 ? (NKF - KPD) : 2;
         static_assert(VPD >= 1 && VPD < NVF, "tile too small for the read-ahead");
+        // The score phase reads V^T fragments [0, min(KPD, VPD)), the PV loop
+        // those from VPD on: every fragment is read only if KPD >= VPD.
+        static_assert(KPD >= VPD, "V^T fragments [KPD, VPD) would never be read");
         i32x8 kf[NKB][NCH];
         f32x16 sn[NKB];
         i32x8 vf[NPV][NDB];
