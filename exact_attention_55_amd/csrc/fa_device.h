@@ -74,7 +74,11 @@ __device__ __forceinline__ f32x16 mfma32(const f16x8& a, const f16x8& b, const f
 // plain vector multiply there makes the compiler keep a VGPR copy of every
 // accumulator across the key loop (copied in at every iteration) because
 // VALU instructions cannot name AGPRs; with this form the accumulators stay
-// in AGPRs and only the rarely taken rescale moves them.
+// in AGPRs and only the rarely taken rescale moves them. The compiler does
+// not add wait states in front of an asm read of an MFMA result, so the
+// caller must run it well after the last MFMA that wrote o: the kernels call
+// it only after a tile's scores and exponentials, at least ~70 instructions
+// (several MFMAs of 32 cycles) past the last PV MFMA.
 __device__ __forceinline__ void scale_acc(f32x16& o, float a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {

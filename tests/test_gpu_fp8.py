@@ -116,8 +116,8 @@ def test_fp8_small_vs_oracles(B, H, N, d, causal):
 JUMP_KEYS = [300, 301, 455]      # keys in later tiles, scaled by 8 (exact in bf16)
 
 
-@pytest.mark.parametrize("causal", [False, True])
-def test_fp8_late_score_jump(causal):
+@pytest.mark.parametrize("causal,d", [(False, 128), (True, 128), (False, 256)])
+def test_fp8_late_score_jump(causal, d):
     """Keys eight times longer than the rest, in tiles after the first, give
     some queries scores far above the first tile's maximum: the quantised
     P' = 8 p w_j would pass the e4m3 maximum there, so those tiles take the
@@ -127,8 +127,8 @@ def test_fp8_late_score_jump(causal):
     (fp8_p_rounding_bound), and the LSE to it within 1e-3. (Against exact
     attention of the unquantised inputs no fixed RMSE applies here: the e4m3
     rounding of the long keys alone moves their logits by ~0.7.)"""
-    B, H, N, d = 1, 2, 600, 128
-    say(f"fp8 late score jump causal={causal}")
+    B, H, N = 1, 2, 600
+    say(f"fp8 late score jump causal={causal} d={d}")
     q, k, v = make_qkv(B, H, N, d, seed=57, dtype="bf16")
     k = k.clone()
     k[:, :, JUMP_KEYS] *= 8

@@ -72,10 +72,13 @@ def test_small_full_compare(B, H, N, d, causal, dt):
     check_lse(lse16, lse_ref)
 
 
-def test_scale_and_large_logits():
-    """Non-default scale and scores of tens of units: online max must track."""
-    say("large logits")
-    q, k, v = make_qkv(1, 2, 384, 64, seed=7, dtype="bf16")
+@pytest.mark.parametrize("d", [64, 256])
+def test_scale_and_large_logits(d):
+    """Non-default scale and scores of tens of units: online max must track.
+    Later tiles overflow the first tile's reference maximum, so O is
+    rescaled mid-row (at d = 256 in place in the accumulation registers)."""
+    say(f"large logits d={d}")
+    q, k, v = make_qkv(1, 2, 384, d, seed=7, dtype="bf16")
     q = (q.float() * 4).to(torch.bfloat16)
     for causal in (False, True):
         o_ref, lse_ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), causal, 0.5)
