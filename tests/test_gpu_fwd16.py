@@ -48,6 +48,8 @@ SMALL = [
     (1, 2, 517, 128, True, "fp16"),
     (1, 1, 257, 256, False, "bf16"),
     (1, 1, 700, 256, True, "bf16"),
+    (1, 2, 300, 256, True, "fp16"),
+    (2, 1, 300, 256, False, "fp16"),
     (1, 1, 1, 128, False, "bf16"),
     (1, 1, 1, 64, True, "bf16"),
     (3, 1, 33, 64, True, "fp16"),
