@@ -101,6 +101,13 @@ decode16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     const int k0 = min(L, s * chunk);
     const int k1 = min(L, k0 + chunk);
     const int nblk = (k1 - k0 + 31) / 32;
+    // A part of at most 64 keys feeds P to the PV MFMA as the rounded P~
+    // plus its rounding residue (two MFMAs per fragment): on a row that sees
+    // only a few keys, rounding P to bf16 (2^-9 relative) could otherwise
+    // move O by up to ~w(1-w) 2^-9 |v_a - v_b| (above 4e-3 for two keys of
+    // comparable weight whose values differ by ~8); over many keys it
+    // averages out.
+    const bool split_p = k1 - k0 <= 64;
 
     // Query row of this lane's score column: row r of the group is query
     // i = r % Nq of head hkv*g + r / Nq.
@@ -220,6 +227,21 @@ decode16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
             }
             pf[t] = X8{pp[0][0], pp[0][1], pp[1][0], pp[1][1], pp[2][0], pp[2][1], pp[3][0], pp[3][1]};
         }
+        X8 pr[2];                              // residue p - P~ (split parts only)
+        if (split_p) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                X2 pp[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float p0 = exp2_hw(fmaf(sc[8 * t + 2 * u], c, -mref));
+                    const float p1 = exp2_hw(fmaf(sc[8 * t + 2 * u + 1], c, -mref));
+                    pp[u] = pack2<T>(p0 - (float)pf[t][2 * u], p1 - (float)pf[t][2 * u + 1]);
+                    l = sum2(pp[u], l);
+                }
+                pr[t] = X8{pp[0][0], pp[0][1], pp[1][0], pp[1][1], pp[2][0], pp[2][1], pp[3][0], pp[3][1]};
+            }
+        }
         // O^T += V^T P^T: k-step t covers keys 16 t .. 16 t + 15 of the block.
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -230,6 +252,7 @@ decode16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
                 const u32x2 hi4 = lds_read_tr16(vp + vstep);
                 const X8 vf = __builtin_bit_cast(X8, u32x4{lo[0], lo[1], hi4[0], hi4[1]});
                 o[db] = mfma32(vf, pf[t], o[db]);
+                if (split_p) o[db] = mfma32(vf, pr[t], o[db]);
             }
         if (j + NST < nblk) {
             lds_reads_done();

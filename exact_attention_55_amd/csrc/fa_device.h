@@ -74,17 +74,28 @@ __device__ __forceinline__ f32x16 mfma32(const f16x8& a, const f16x8& b, const f
 // plain vector multiply there makes the compiler keep a VGPR copy of every
 // accumulator across the key loop (copied in at every iteration) because
 // VALU instructions cannot name AGPRs; with this form the accumulators stay
-// in AGPRs and only the rarely taken rescale moves them. The compiler does
-// not add wait states in front of an asm read of an MFMA result, so the
-// caller must run it well after the last MFMA that wrote o: the kernels call
-// it only after a tile's scores and exponentials, at least ~70 instructions
-// (several MFMAs of 32 cycles) past the last PV MFMA.
+// in AGPRs and only the rarely taken rescale moves them. The compiler adds no
+// wait states for an asm read of an MFMA result, so the first read carries
+// them itself: 21 (s_nop 7, 7, 4) cover the longest MFMA write -> VALU read
+// distance of gfx950 (a 16-pass 32x32 MFMA needs 18), whatever the caller
+// issued just before. Later reads come after it in program order. The last
+// write is followed by 3 more so that an MFMA reading o as its accumulator
+// input right after the call sees the written value.
 __device__ __forceinline__ void scale_acc(f32x16& o, float a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         float x = o[i], t;
-        asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                     : "+a"(x), "=&v"(t) : "v"(a));
+        if (i == 0)
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4\n\t"
+                         "v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                         : "+a"(x), "=&v"(t) : "v"(a));
+        else if (i == 15)
+            asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1\n\t"
+                         "s_nop 2"
+                         : "+a"(x), "=&v"(t) : "v"(a));
+        else
+            asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                         : "+a"(x), "=&v"(t) : "v"(a));
         o[i] = x;
     }
 }
@@ -221,12 +232,6 @@ template <int D> __device__ __forceinline__ int lds_swz8(int r) {
     return ((r & 7) << 1) | ((r >> 3) & 1);
 }
 
-// 16 bytes per lane from global memory straight into LDS: lane i's bytes
-// land at lds + 16*i (lds must be wave-uniform).
-__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
-    __builtin_amdgcn_global_load_lds(g, (FA_LDS void*)(lds), 16, 0, 0);
-}
-
 // Buffer resource over [base, base + bytes): raw (stride 0) byte-addressed
 // loads, range-checked against bytes. On gfx950 the check covers the whole
 // offset (VGPR offset + SGPR offset): a 16-byte read at or past the end
@@ -243,13 +248,24 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, int bytes) {
 // wave-uniform). Issued through inline asm so that the compiler does not
 // track it: otherwise it makes LDS reads wait for every outstanding copy,
 // because it cannot tell the tiles apart. Completion is awaited explicitly
-// (wait_vm_all) before the barrier that publishes the tile. Nothing else in
-// the kernels keeps a value in M0.
+// (wait_vm_all) before the barrier that publishes the tile. The LDS address
+// goes through M0, which the statement declares clobbered: M0 is reserved
+// (never given to an "s" operand), and the clobber keeps any value the
+// compiler holds in it from being assumed live across the copy (clang warns
+// that a reserved register is named; the warning is silenced here only).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void buffer_load_lds16(i32x4 rsrc, uint32_t lds, uint32_t voff,
                                                   uint32_t soff) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
+// 4 bytes per lane (lane i at lds + 4*i), otherwise as buffer_load_lds16.
+__device__ __forceinline__ void buffer_load_lds4(i32x4 rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 // Workgroup -> (head, tile level) for a grid of heads x tiles workgroups.
 // Balanced (non-causal): consecutive workgroups land on different XCDs, so
@@ -273,21 +289,6 @@ __device__ __forceinline__ void grid_tile(int num_blocks, int num_tiles, bool un
 }
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
-// Phase boundary of the ping-pong schedule: nothing is scheduled across it,
-// the wave's LDS reads have returned, then the workgroup barrier. The asm
-// memory clobber also keeps the compiler from moving LDS accesses across.
-__device__ __forceinline__ void phase_barrier() {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-}
-// Same, after this wave's global loads (direct-to-LDS copies included) landed.
-__device__ __forceinline__ void phase_barrier_vm() {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-}
 
 // s_waitcnt immediate (gfx9 encoding) for vmcnt(0), other counters ignored.
 constexpr int kVmcnt0 = 0x0f70;

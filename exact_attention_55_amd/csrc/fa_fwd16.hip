@@ -330,7 +330,43 @@ struct Wave16 {
         });
     }
 
-    // Softmax + PV of a tile whose scores are in s (no overlap).
+    // The rounding residue of P for the split form of the first key tile:
+    // plo = p - P~ (exact in fp32) rounded to the 16-bit type, so that P~ +
+    // plo carries p to about 16 significant bits; l takes its sum as well.
+    __device__ __forceinline__ void probs_lo(const f32x16 (&s)[QB][NKB], const X8 (&pf)[QB][NPV],
+                                             X8 (&plo)[QB][NPV], float c) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const float nm = -m[qb];
+            float ls = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    X2 pp[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float p0 = exp2_hw(fmaf(s[qb][kb][8 * h + 2 * j], c, nm));
+                        const float p1 = exp2_hw(fmaf(s[qb][kb][8 * h + 2 * j + 1], c, nm));
+                        pp[j] = pack2<T>(p0 - (float)pf[qb][2 * kb + h][2 * j],
+                                         p1 - (float)pf[qb][2 * kb + h][2 * j + 1]);
+                        ls = sum2(pp[j], ls);
+                    }
+                    plo[qb][2 * kb + h] = X8{pp[0][0], pp[0][1], pp[1][0], pp[1][1],
+                                             pp[2][0], pp[2][1], pp[3][0], pp[3][1]};
+                }
+            l[qb] += ls;
+        }
+    }
+
+    // Softmax + PV of a tile whose scores are in s (no overlap). SPLIT: P is
+    // fed to the PV MFMA as two 16-bit parts, P~ and the residue p - P~
+    // (twice the PV MFMAs), and l sums both. Used for the first key tile,
+    // the only one where a row can see few keys: rounding P to bf16 (2^-9
+    // relative) moves O by up to ~w(1-w) 2^-9 |v_a - v_b| on a row that two
+    // keys share with weights w, 1 - w, which exceeds 4e-3 for |v_a - v_b|
+    // near 8; once a row sees a few dozen keys the effect averages out.
+    template <bool SPLIT = false>
     __device__ __forceinline__ void finish(const f32x16 (&s)[QB][NKB], const uint32_t (&b0)[NVA],
                                            const uint32_t (&b1)[NVA], float c) {
         X8 pf[QB][NPV];
@@ -343,6 +379,11 @@ struct Wave16 {
         vfrags_async(vlo, vhi, b0, b1);
         __builtin_amdgcn_sched_barrier(0);
         pv_async(vlo, vhi, pf);
+        if constexpr (SPLIT) {
+            X8 plo[QB][NPV];
+            probs_lo(s, pf, plo, c);
+            pv_async(vlo, vhi, plo);
+        }
     }
 
     // Pipelined step, all in one wave's instruction stream: the score MFMAs
@@ -706,14 +747,17 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
         if (!CAUSAL || k0 <= q0 + QW - 1) {   // wave has a visible key in this tile
             W::scores(s, ktile(t), ka, qf);
             W::template mask<CAUSAL>(s, k0, q0, N, hi, l32);
+            uint32_t b0[NVA], b1[NVA];
+            vbases(sbase + (2 + (t & 1)) * TB, b0, b1);
             if (t == 0) {                      // first reference maximum: exact
                 float mt[QB];
                 W::tile_max(s, c, mt);
                 st.raise_max(mt);
+                // the first key tile masked: rows with fewer than BC keys
+                st.template finish<true>(s, b0, b1, c);
+            } else {
+                st.finish(s, b0, b1, c);
             }
-            uint32_t b0[NVA], b1[NVA];
-            vbases(sbase + (2 + (t & 1)) * TB, b0, b1);
-            st.finish(s, b0, b1, c);
         }
         wait_vm_all();
         __syncthreads();

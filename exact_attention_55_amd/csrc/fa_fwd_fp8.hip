@@ -340,14 +340,6 @@ struct Wave8 {
     }
 };
 
-// 4 bytes per lane from a buffer straight into LDS (lane i at lds + 4*i),
-// like buffer_load_lds16; used for the microscaled path's scale bytes, which
-// travel with their tile through the same wait and barrier.
-__device__ __forceinline__ void buffer_load_lds4(i32x4 rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
-}
-
 template <int D, bool CAUSAL, bool OUT_F32, bool MX>
 __global__ void __launch_bounds__(Cfg8<D>::NW * 64, Cfg8<D>::WPE)
 fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg,

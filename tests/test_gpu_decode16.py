@@ -92,6 +92,16 @@ def test_non_default_scale_and_split_invariance():
         run_case(2, 8, 4, 2, 3333, 128, True, "bf16", [3333, 2500], s, True, scale=0.3)
 
 
+def test_few_keys_bf16():
+    """Sequences of two or three keys (one part each, so the exact split of
+    P is taken), 64 sequences x 16 heads, bf16, every element with float32
+    O; and the same sequences under 4 splits (parts of 0 .. 1 keys)."""
+    lens = [2, 3] * 32
+    for splits in (1, 4):
+        say(f"decode few keys splits {splits}")
+        run_case(64, 16, 16, 1, 64, 128, False, "bf16", lens, splits, True, seed=23)
+
+
 @pytest.mark.parametrize("name", sorted(DECODE_CONFIGS))
 def test_full_workload(name):
     """The benchmark's decode workloads, full size, in its launch
