@@ -14,6 +14,7 @@ exact_attention_55_amd/libfa.so. Flags:
 
 import concurrent.futures
 import os
+import re
 import subprocess
 import sys
 
@@ -37,15 +38,64 @@ FLAGS = [
 
 def _compile(src, verbose):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + ["-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src),
+                             "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
-    if verbose and r.stderr.strip():
-        print(r.stderr, flush=True)
+    usage = _resource_usage(r.stderr)
+    with open(os.path.join(BUILD, os.path.splitext(src)[0] + ".resources.txt"), "w") as f:
+        for name, u in usage.items():
+            f.write(f"{name} {u}\n")
+    spilled = {n: u for n, u in usage.items()
+               if u.get("ScratchSize [bytes/lane]", 0) > _scratch_allowance(n)}
+    if spilled:
+        raise RuntimeError(f"kernels of {src} use scratch (register spills or stack):\n  " +
+                           "\n  ".join(f"{n}: {u}" for n, u in spilled.items()))
+    if verbose:
+        other = "\n".join(l for l in r.stderr.splitlines() if "kernel-resource-usage" not in l)
+        if other.strip():
+            print(other, flush=True)
     return obj
+
+
+# Kernels allowed a little scratch, with the reason (bytes per lane):
+#  * the one-wave-per-SIMD 16-bit forward at d = 256 (512 registers, all in
+#    use): a long-lived value or two saved in the prologue and reloaded in the
+#    epilogue, outside the key loop;
+#  * the rotary prep without the Hadamard at d = 256, half pairing.
+SCRATCH_ALLOWANCE = [
+    (re.compile(r"^_ZN2fa15fa_fwd16_kernelIDF16[b_]Li256E"), 32),
+    (re.compile(r"^_ZN2fa15fp8_prep_kernelIDF16[b_]Li256ELb0ELi2ELi2E"), 104),
+]
+
+
+def _scratch_allowance(name):
+    for pat, limit in SCRATCH_ALLOWANCE:
+        if pat.match(name):
+            return limit
+    return 0
+
+
+def _resource_usage(stderr):
+    """Per-kernel register and scratch figures from the compiler's
+    kernel-resource-usage remarks. A kernel that needs scratch (spilled
+    registers) is refused: every spill sits in the key loop's data path."""
+    usage, cur = {}, None
+    for line in stderr.splitlines():
+        if "remark:" not in line or "kernel-resource-usage" not in line:
+            continue
+        body = line.split("remark:", 1)[1].rsplit("[-Rpass", 1)[0].strip()
+        key, _, val = body.partition(":")
+        key, val = key.strip(), val.strip()
+        if key == "Function Name":
+            cur = val
+            usage[cur] = {}
+        elif cur is not None and val.lstrip("-").isdigit():
+            usage[cur][key] = int(val)
+    return usage
 
 
 def build(verbose=False):

@@ -330,60 +330,98 @@ struct Wave16 {
         });
     }
 
-    // The rounding residue of P for the split form of the first key tile:
-    // plo = p - P~ (exact in fp32) rounded to the 16-bit type, so that P~ +
-    // plo carries p to about 16 significant bits; l takes its sum as well.
-    __device__ __forceinline__ void probs_lo(const f32x16 (&s)[QB][NKB], const X8 (&pf)[QB][NPV],
-                                             X8 (&plo)[QB][NPV], float c) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            const float nm = -m[qb];
-            float ls = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    X2 pp[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float p0 = exp2_hw(fmaf(s[qb][kb][8 * h + 2 * j], c, nm));
-                        const float p1 = exp2_hw(fmaf(s[qb][kb][8 * h + 2 * j + 1], c, nm));
-                        pp[j] = pack2<T>(p0 - (float)pf[qb][2 * kb + h][2 * j],
-                                         p1 - (float)pf[qb][2 * kb + h][2 * j + 1]);
-                        ls = sum2(pp[j], ls);
-                    }
-                    plo[qb][2 * kb + h] = X8{pp[0][0], pp[0][1], pp[1][0], pp[1][1],
-                                             pp[2][0], pp[2][1], pp[3][0], pp[3][1]};
-                }
-            l[qb] += ls;
-        }
-    }
-
-    // Softmax + PV of a tile whose scores are in s (no overlap). SPLIT: P is
-    // fed to the PV MFMA as two 16-bit parts, P~ and the residue p - P~
-    // (twice the PV MFMAs), and l sums both. Used for the first key tile,
-    // the only one where a row can see few keys: rounding P to bf16 (2^-9
-    // relative) moves O by up to ~w(1-w) 2^-9 |v_a - v_b| on a row that two
-    // keys share with weights w, 1 - w, which exceeds 4e-3 for |v_a - v_b|
-    // near 8; once a row sees a few dozen keys the effect averages out.
-    template <bool SPLIT = false>
+    // Softmax + PV of a tile whose scores are in s (no overlap; masked
+    // tiles). P~, the exponentials rounded to the 16-bit type, or with RESID
+    // the rounding residue p - P~ (exact in fp32) instead, rounded to the
+    // 16-bit type; l sums it too, and the fp32 sum for the log-sum-exp is
+    // left alone. The kernel runs a tile once and, for the first key tile,
+    // again with RESID: P then reaches the PV product as P~ plus
+    // its residue (about 16 significant bits). The first key tile is the
+    // only one where a row can see few keys, and there rounding P to bf16
+    // (2^-9 relative) moves O by up to ~w(1-w) 2^-9 |v_a - v_b| on a row that
+    // two keys share with weights w, 1 - w: above 4e-3 for |v_a - v_b| near
+    // 8. Once a row sees a few dozen keys the effect averages out.
+    // RESID: 0 P~, 1 the residue, 2 chosen at run time by rm (0 or 1): one
+    // copy of the tile code for both passes, which the register budget of
+    // the one-wave-per-SIMD d = 256 kernel needs (two copies spill there).
+    template <int RESID = 0>
     __device__ __forceinline__ void finish(const f32x16 (&s)[QB][NKB], const uint32_t (&b0)[NVA],
-                                           const uint32_t (&b1)[NVA], float c) {
+                                           const uint32_t (&b1)[NVA], float c, float rm = 0.f) {
         X8 pf[QB][NPV];
         float ls[QB][2], lxs[QB][2];
         zero_sums(ls, lxs);
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) probs(s, pf, kb, c, ls, lxs);
-        settle(s, pf, c, ls, lxs);
-        u32x2 vlo[NPV][NDB], vhi[NPV][NDB];
-        vfrags_async(vlo, vhi, b0, b1);
-        __builtin_amdgcn_sched_barrier(0);
-        pv_async(vlo, vhi, pf);
-        if constexpr (SPLIT) {
-            X8 plo[QB][NPV];
-            probs_lo(s, pf, plo, c);
-            pv_async(vlo, vhi, plo);
+        for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const float nm = -m[qb];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    X2 pp[4];
+                    float xs = 0.f;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float p0 = exp2_hw(fmaf(s[qb][kb][8 * h + 2 * j], c, nm));
+                        float p1 = exp2_hw(fmaf(s[qb][kb][8 * h + 2 * j + 1], c, nm));
+                        if (XS) xs += p0 + p1;
+                        if constexpr (RESID == 1) {
+                            const X2 r = pack2<T>(p0, p1);
+                            p0 -= (float)r[0];
+                            p1 -= (float)r[1];
+                        } else if constexpr (RESID == 2) {
+                            const X2 r = pack2<T>(p0, p1);
+                            p0 = fmaf(-rm, (float)r[0], p0);
+                            p1 = fmaf(-rm, (float)r[1], p1);
+                        }
+                        pp[j] = pack2<T>(p0, p1);
+                    }
+                    ls[qb][h] = sum2(pp[3], sum2(pp[2], sum2(pp[1], sum2(pp[0], ls[qb][h]))));
+                    if (XS && RESID == 0) lxs[qb][h] += xs;
+                    if (XS && RESID == 2) lxs[qb][h] += xs * (1.f - rm);
+                    pf[qb][2 * kb + h] = X8{pp[0][0], pp[0][1], pp[1][0], pp[1][1],
+                                            pp[2][0], pp[2][1], pp[3][0], pp[3][1]};
+                }
+            }
         }
+        settle(s, pf, c, ls, lxs);
+        if constexpr (NPV * NDB > 16) {
+            // d = 256: the whole tile's V^T fragments would take 128 registers
+            pv_by_step(b0, b1, pf);
+        } else {
+            u32x2 vlo[NPV][NDB], vhi[NPV][NDB];
+            vfrags_async(vlo, vhi, b0, b1);
+            __builtin_amdgcn_sched_barrier(0);
+            pv_async(vlo, vhi, pf);
+        }
+    }
+
+    // O^T += V^T P^T for the tile, one k-step at a time: the step's V^T
+    // fragments are read, awaited and consumed before the next step's, so
+    // only NDB fragments are live (masked tiles at d = 256).
+    __device__ __forceinline__ void pv_by_step(const uint32_t (&b0)[NVA], const uint32_t (&b1)[NVA],
+                                               const X8 (&pf)[QB][NPV]) {
+        static_for<0, NPV>([&](auto tc) {
+            constexpr int t = decltype(tc)::value;
+            u32x2 vlo[NDB], vhi[NDB];
+            static_for<0, NDB>([&](auto dc) {
+                constexpr int db = decltype(dc)::value;
+                constexpr int off = NVA * 64 * (db / NVA) + 16 * t * RB;
+                vlo[db] = lds_tr16_async<off>(b0[db % NVA]);
+                vhi[db] = lds_tr16_async<off>(b1[db % NVA]);
+            });
+            lgkm_wait<0>();
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                lgkm_bind(vlo[db]);
+                lgkm_bind(vhi[db]);
+            }
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const X8 v = __builtin_bit_cast(X8, u32x4{vlo[db][0], vlo[db][1], vhi[db][0], vhi[db][1]});
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(v, pf[qb][t], o[qb][db]);
+            }
+        });
     }
 
     // Pipelined step, all in one wave's instruction stream: the score MFMAs
@@ -753,10 +791,15 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
                 float mt[QB];
                 W::tile_max(s, c, mt);
                 st.raise_max(mt);
-                // the first key tile masked: rows with fewer than BC keys
-                st.template finish<true>(s, b0, b1, c);
+            }
+            // the first key tile (rows with fewer than BC keys) is fed to the
+            // PV product as P~ plus its rounding residue (see Wave16::finish)
+            if constexpr (Cfg16<D, WIDE>::WPE == 1) {
+                const int npass = wave_uniform(t == 0 ? 2 : 1);
+                for (int pass = 0; pass < npass; ++pass) st.template finish<2>(s, b0, b1, c, (float)pass);
             } else {
                 st.finish(s, b0, b1, c);
+                if (t == 0) st.template finish<1>(s, b0, b1, c);
             }
         }
         wait_vm_all();
