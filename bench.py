@@ -2,33 +2,35 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-next]
 
-One step runs the whole hot path once, on inputs already resident in HBM:
-  1. bf16 forward, B=8 H=16 N=2048 d=128, non-causal   (16k tokens, hidden 2048)
-  2. bf16 forward, same shape, causal
-  3. fp8 path on B=4 H=16 N=4096 d=128 (0.1% outliers): fa_fp8_prep of Q and K
-     (random-sign Hadamard + 128-row block scales) and V (block scales), then
-     the fp8 forward.
-`value` is the metric work of the step (4*B*H*N^2*d per forward, halved for
-causal) divided by the step time. Every leg is also timed on its own with HIP
-events on the stream it runs on; `legs` reports each. `roofline` is for the
-dominant kernel, the non-causal bf16 forward, against the MI355X dense bf16
-MFMA peak. `cpu_baseline` times the float64 oracle on a bounded sample of the
-same workload (rank 0, N=1 only).
+One step runs the whole hot path once per workload, on inputs already
+resident in HBM, one launch per leg:
+  * bf16 forward on every 16-bit workload shape: B=2 H=16 N=8192 d=128 causal
+    and non-causal (the long-context d=128 regime), B=8 H=16 N=2048 d=128
+    non-causal and causal, B=4 H=32 N=4096 d=64 non-causal, B=2 H=8 N=16384
+    d=256 causal;
+  * the fp8 path on B=4 H=16 N=4096 d=128 (0.1 % outliers): fa_fp8_prep of Q
+    and K (random-sign Hadamard + 128-row block scales) and V (block scales),
+    then the fp8 forward.
+Each leg is timed with HIP events on the stream it is launched on.
 
-After the step, the rows built beyond the forward are timed on their own with
-the same events and reported under `next_rows` (not part of `value`): the
-16-bit backward (dQ, dK, dV from the saved LSE) on the main shape, its work
-counted as 10*B*H*N^2*d (the five GEMMs of the gradient, halved for causal);
-the fused rotary + Hadamard + fp8 block quantisation of Q and K of the fp8
-workload (half pairing, GB/s of bytes read and written); the microscaled fp8
-variant on the fp8 workload (fa_mx_prep of Q, K along d with the Hadamard
-and V along the sequence, GB/s; the forward on its output, non-causal and
-causal, TFLOP/s against the dense fp8 peak); the block-scaled fp8 forward,
-causal; and the
-decode-shaped forward on its two workloads (B=8 H=16 sequences of
-16384 keys; B=16 with 64 query heads over 8 key/value heads and ragged key
-counts), in GB/s of the bytes it must move (K and V of every sequence's keys,
-Q, O, LSE) against the HBM peak.
+Headlines, one per precision (work 4*B*H*N^2*d, halved for causal):
+  * value: bf16 forward TFLOP/s at B=2 H=16 N=8192 d=128, causal and
+    non-causal launches together (their work over their summed time);
+  * headlines.bf16_all: every bf16 leg of the step together;
+  * headlines.fp8: the fp8 forward leg, against the dense fp8 peak, and the
+    prep + forward pair end to end.
+`roofline` is the longest leg of the headline (the non-causal N=8192 launch)
+against the dense bf16 MFMA peak; `rooflines` has one entry per forward leg
+naming its kernel. Each carries the HBM bytes per launch measured by
+rocprofv3 counters when the committed summary was taken on the kernel's
+current machine code (else null). `cpu_baseline` times the float64 oracle on
+a bounded sample of the same workloads (rank 0, N=1 only).
+
+After the step, the rows built beyond the forward are timed on their own and
+reported under `next_rows` (not part of any headline): the 16-bit backward,
+the fused rotary + Hadamard + fp8 prep, the microscaled fp8 variant, the
+block-scaled fp8 forward causal and the decode-shaped forward (see
+build_next_legs).
 
 Prints ONE JSON line on stdout.
 """
@@ -36,8 +38,8 @@ Prints ONE JSON line on stdout.
 import argparse
 import hashlib
 import json
-import math
 import os
+import struct
 import sys
 import time
 
@@ -55,18 +57,31 @@ PEAK_BF16 = 2516.6   # TFLOP/s, MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 
 PEAK_FP8 = 5033.2    # TFLOP/s, dense fp8
 PEAK_HBM = 8000.0    # GB/s
 
-MAIN = "b8h16n2k_d128"
 FP8 = "fp8_b4h16n4k_d128"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd16_b8h16n2k_d128_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
-
-MAIN_SYMBOL = "_ZN2fa15fa_fwd16_kernelIDF16bLi128ELb0ELb0ELb0EEEvPKT_S3_S3_PvPfiiif"
+# Forward legs of the step: leg name -> (workload, kernel symbol in the code
+# object). The kernel is the one the library's launch picks for the shape.
+_F16 = "_ZN2fa15fa_fwd16_kernelIDF16bLi{d}ELb{c}ELb0ELb{w}EEEvPKT_S3_S3_PvPfiiif"
+FWD16_LEGS = {
+    "bf16_fwd_b2h16n8k_d128_causal": ("b2h16n8k_d128_causal", _F16.format(d=128, c=1, w=0)),
+    "bf16_fwd_b2h16n8k_d128": ("b2h16n8k_d128", _F16.format(d=128, c=0, w=0)),
+    "bf16_fwd_b8h16n2k_d128": ("b8h16n2k_d128", _F16.format(d=128, c=0, w=0)),
+    "bf16_fwd_b8h16n2k_d128_causal": ("b8h16n2k_d128_causal", _F16.format(d=128, c=1, w=0)),
+    "bf16_fwd_b4h32n4k_d64": ("b4h32n4k_d64", _F16.format(d=64, c=0, w=1)),
+    "bf16_fwd_b2h8n16k_d256_causal": ("b2h8n16k_d256_causal", _F16.format(d=256, c=1, w=0)),
+}
+FP8_FWD_LEG = "fp8_fwd_b4h16n4k_d128"
+FP8_PREP_LEG = "fp8_prep_qkv_b4h16n4k_d128"
+FP8_SYMBOL = "_ZN2fa17fa_fwd_fp8_kernelILi128ELb0ELb0ELb0EEEvPKhS2_S2_PvPfiiiimf"
+KERNEL_OF = {**{k: v[1] for k, v in FWD16_LEGS.items()}, FP8_FWD_LEG: FP8_SYMBOL}
+HEADLINE = ["bf16_fwd_b2h16n8k_d128_causal", "bf16_fwd_b2h16n8k_d128"]
+ROOF_LEG = "bf16_fwd_b2h16n8k_d128"
 
 
 def _elf_sections(elf):
     """(name, address, file offset, size) of every section of a little-endian
     ELF64 image, in section-index order."""
-    import struct
     shoff, = struct.unpack_from("<Q", elf, 0x28)
     shentsize, shnum, shstrndx = struct.unpack_from("<HHH", elf, 0x3A)
     raw = [struct.unpack_from("<IIQQQQ", elf, shoff + i * shentsize) for i in range(shnum)]
@@ -75,73 +90,105 @@ def _elf_sections(elf):
             for r in raw]
 
 
-def source_hash(symbol=MAIN_SYMBOL):
-    """SHA-256 of one kernel's machine code in the built library: the bytes of
-    its function and of its kernel descriptor (with the position-dependent
-    entry offset cleared), taken from the gfx950 code object inside the
-    .hip_fatbin section of libfa.so. It changes exactly when that kernel's
-    compiled code changes, not with comments, host code or other kernels."""
-    import struct
+def _gfx950_code_objects():
+    """The gfx950 code objects inside libfa.so: its .hip_fatbin section holds
+    one clang offload bundle per translation unit, each with one code object
+    per target."""
     path = os.path.join(ROOT, "exact_attention_55_amd", "libfa.so")
     with open(path, "rb") as f:
         elf = f.read()
     fat = [(o, n) for name, _, o, n in _elf_sections(elf) if name == ".hip_fatbin"]
     if not fat:
         raise RuntimeError(f"no .hip_fatbin section in {path}")
-    bundle = elf[fat[0][0]:fat[0][0] + fat[0][1]]
-    count, = struct.unpack_from("<Q", bundle, 24)          # clang offload bundle
-    pos, code = 32, None
-    for _ in range(count):
-        off, size, tlen = struct.unpack_from("<QQQ", bundle, pos)
-        triple = bundle[pos + 24:pos + 24 + tlen].decode()
-        pos += 24 + tlen
-        if triple.endswith("gfx950"):
-            code = bundle[off:off + size]
-    if code is None:
+    sec = elf[fat[0][0]:fat[0][0] + fat[0][1]]
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    out, start = [], sec.find(magic)
+    while start >= 0:
+        count, = struct.unpack_from("<Q", sec, start + 24)
+        pos = start + 32
+        for _ in range(count):
+            off, size, tlen = struct.unpack_from("<QQQ", sec, pos)
+            triple = sec[pos + 24:pos + 24 + tlen].decode()
+            pos += 24 + tlen
+            if triple.endswith("gfx950"):
+                out.append(sec[start + off:start + off + size])
+        start = sec.find(magic, start + 1)
+    if not out:
         raise RuntimeError("no gfx950 code object in the fat binary")
-    shdrs = _elf_sections(code)
-    secs = {name: (o, n) for name, _, o, n in shdrs}
-    symoff, symsize = secs[".symtab"]
-    stroff = secs[".strtab"][0]
-    h = hashlib.sha256()
-    found = 0
-    for j in range(symsize // 24):
-        st_name, _, _, shndx, value, size = struct.unpack_from("<IBBHQQ", code, symoff + j * 24)
-        name = code[stroff + st_name:code.index(b"\0", stroff + st_name)].decode()
-        if name not in (symbol, symbol + ".kd") or size == 0:
-            continue
-        _, addr, soff, _ = shdrs[shndx]
-        start = soff + value - addr                # file offset of the symbol
-        blob = bytearray(code[start:start + size])
-        if name.endswith(".kd"):
-            blob[16:24] = bytes(8)                 # kernel_code_entry_byte_offset
-        h.update(name.encode() + bytes(blob))
-        found += 1
-    if found != 2:
-        raise RuntimeError(f"kernel {symbol} not found in the code object")
-    return h.hexdigest()
+    return out
 
 
-def measured_traffic():
-    """HBM bytes per launch of the dominant kernel from the committed counter
-    summary (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or
-    None when the kernels changed since the counters were taken."""
+def source_hash(symbol):
+    """SHA-256 of one kernel's machine code in the built library: the bytes of
+    its function and of its kernel descriptor (with the position-dependent
+    entry offset cleared). It changes exactly when that kernel's compiled
+    code changes, not with comments, host code or other kernels."""
+    for code in _gfx950_code_objects():
+        shdrs = _elf_sections(code)
+        secs = {name: (o, n) for name, _, o, n in shdrs}
+        symoff, symsize = secs[".symtab"]
+        stroff = secs[".strtab"][0]
+        h = hashlib.sha256()
+        found = 0
+        for j in range(symsize // 24):
+            st_name, _, _, shndx, value, size = struct.unpack_from("<IBBHQQ", code, symoff + j * 24)
+            name = code[stroff + st_name:code.index(b"\0", stroff + st_name)].decode()
+            if name not in (symbol, symbol + ".kd") or size == 0:
+                continue
+            _, addr, soff, _ = shdrs[shndx]
+            start = soff + value - addr                # file offset of the symbol
+            blob = bytearray(code[start:start + size])
+            if name.endswith(".kd"):
+                blob[16:24] = bytes(8)                 # kernel_code_entry_byte_offset
+            h.update(name.encode() + bytes(blob))
+            found += 1
+        if found == 2:
+            return h.hexdigest()
+    raise RuntimeError(f"kernel {symbol} not found in the code objects")
+
+
+def measured_traffic(leg):
+    """HBM bytes per launch of a forward leg's kernel from the committed
+    counter summary (FETCH_SIZE + WRITE_SIZE, calibrated against a plain
+    copy), or None when that kernel's machine code changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+            t = json.load(f)["legs"][leg]
+    except (OSError, ValueError, KeyError):
         return None
-    if t.get("code_sha256") != source_hash():
+    if t.get("code_sha256") != source_hash(KERNEL_OF[leg]):
         return None
     return t.get("hbm_bytes_per_launch")
 
 
+def algorithmic_bytes(leg):
+    """Bytes a forward must move per launch: Q, K, V in, O out, LSE out (and
+    the fp8 scales)."""
+    if leg == FP8_FWD_LEG:
+        c = CONFIGS[FP8]
+        nel = c["B"] * c["H"] * c["N"] * c["d"]
+        rows = c["B"] * c["H"] * c["N"]
+        return 3 * nel + 2 * nel + 4 * rows + 3 * 4 * c["B"] * c["H"] * (c["N"] // 128)
+    c = CONFIGS[FWD16_LEGS[leg][0]]
+    nel = c["B"] * c["H"] * c["N"] * c["d"]
+    return 4 * nel * 2 + 4 * c["B"] * c["H"] * c["N"]
+
+
+def traffic_commands():
+    cmds = []
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        for leg in KERNEL_OF:
+            cmds.append(f"rocprofv3 --pmc {c} -d <out>/pmc_{c} -o {leg} -f csv -- python3 bench.py "
+                        f"--only {leg} --steps 3 --warmup 1 --no-cpu --no-next")
+        cmds.append(f"rocprofv3 --pmc {c} -d <out>/pmc_{c} -o copy -f csv -- python3 bench.py --copy-calib")
+    return cmds + ["python3 bench.py --traffic-summary <out>"]
+
+
 def traffic_summary(run_dir):
-    """Build the HBM-traffic summary of the dominant kernel from four
-    rocprofv3 counter runs under run_dir (pmc_FETCH_SIZE/{main,copy} and
-    pmc_WRITE_SIZE/{main,copy}, see TRAFFIC_COMMANDS) and write it to
-    TRAFFIC_FILE. FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by
-    what the same counter reads for a plain 1 GiB device copy."""
+    """Write TRAFFIC_FILE from the counter runs under run_dir (see
+    traffic_commands): per forward leg, FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch of its kernel) each scaled by what the same counter reads for a
+    plain 1 GiB device copy."""
     import csv
 
     def per_dispatch(path, name_part):
@@ -152,43 +199,32 @@ def traffic_summary(run_dir):
                     vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
         return vals
 
-    out = {}
+    scale = {}
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
-        main = per_dispatch(os.path.join(run_dir, f"pmc_{c}", "main_counter_collection.csv"),
-                            "fa_fwd16_kernel")
         copy = per_dispatch(os.path.join(run_dir, f"pmc_{c}", "copy_counter_collection.csv"), "")
         copy_kib = sorted(copy.values())[-2]          # median of the three 1 GiB copies
-        ideal_kib = (1 << 30) / 1024.0                # each copy reads and writes 1 GiB
-        out[c] = {"kib_per_dispatch": float(np.mean(list(main.values()))), "dispatches": len(main),
-                  "copy_kib": copy_kib, "scale": ideal_kib / copy_kib}
-    c = CONFIGS[MAIN]
-    B, H, N, d = c["B"], c["H"], c["N"], c["d"]
-    algorithmic = 4 * B * H * N * d * 2 + B * H * N * 4          # Q, K, V in, O out (bf16), LSE
-    fetch = out["FETCH_SIZE"]["kib_per_dispatch"] * 1024 * out["FETCH_SIZE"]["scale"]
-    write = out["WRITE_SIZE"]["kib_per_dispatch"] * 1024 * out["WRITE_SIZE"]["scale"]
-    summary = {
-        "kernel": "fa_fwd16_kernel<bf16, d=128, non-causal, bf16 out>",
-        "workload": "B=8 H=16 N=2048 d=128 bf16 non-causal forward (bench.py main leg)",
-        "commands": TRAFFIC_COMMANDS + [f"python3 bench.py --traffic-summary <out>"],
-        "counters": out,
-        "hbm_fetch_bytes_per_launch": fetch,
-        "hbm_write_bytes_per_launch": write,
-        "hbm_bytes_per_launch": fetch + write,
-        "algorithmic_bytes_per_launch": algorithmic,
-        "traffic_over_algorithmic": (fetch + write) / algorithmic,
-        "code_sha256": source_hash(),
-    }
+        scale[c] = {"copy_kib": copy_kib, "scale": (1 << 30) / 1024.0 / copy_kib}
+    legs = {}
+    for leg, sym in KERNEL_OF.items():
+        part = "fa_fwd_fp8_kernel" if leg == FP8_FWD_LEG else "fa_fwd16_kernel"
+        e = {"kernel_symbol": sym}
+        try:
+            for c in ("FETCH_SIZE", "WRITE_SIZE"):
+                v = per_dispatch(os.path.join(run_dir, f"pmc_{c}", f"{leg}_counter_collection.csv"), part)
+                kib = float(np.mean(list(v.values())))
+                e[c] = {"kib_per_dispatch": kib, "dispatches": len(v),
+                        "bytes_per_launch": kib * 1024 * scale[c]["scale"]}
+        except (OSError, ValueError):
+            continue
+        e["hbm_bytes_per_launch"] = e["FETCH_SIZE"]["bytes_per_launch"] + e["WRITE_SIZE"]["bytes_per_launch"]
+        e["algorithmic_bytes_per_launch"] = algorithmic_bytes(leg)
+        e["traffic_over_algorithmic"] = e["hbm_bytes_per_launch"] / e["algorithmic_bytes_per_launch"]
+        e["code_sha256"] = source_hash(sym)
+        legs[leg] = e
+    summary = {"commands": traffic_commands(), "copy_calibration": scale, "legs": legs}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(summary, f, indent=1)
     print(json.dumps(summary, indent=1))
-
-
-TRAFFIC_COMMANDS = [
-    "rocprofv3 --pmc FETCH_SIZE -d <out>/pmc_FETCH_SIZE -o main -f csv -- python3 bench.py --only-main --steps 3 --warmup 1 --no-cpu",
-    "rocprofv3 --pmc FETCH_SIZE -d <out>/pmc_FETCH_SIZE -o copy -f csv -- python3 bench.py --copy-calib",
-    "rocprofv3 --pmc WRITE_SIZE -d <out>/pmc_WRITE_SIZE -o main -f csv -- python3 bench.py --only-main --steps 3 --warmup 1 --no-cpu",
-    "rocprofv3 --pmc WRITE_SIZE -d <out>/pmc_WRITE_SIZE -o copy -f csv -- python3 bench.py --copy-calib",
-]
 
 
 def log(msg):
@@ -196,8 +232,8 @@ def log(msg):
 
 
 class Leg:
-    def __init__(self, name, fn, flops=0.0, bytes_=0.0):
-        self.name, self.fn, self.flops, self.bytes = name, fn, flops, bytes_
+    def __init__(self, name, fn, flops=0.0, bytes_=0.0, peak=PEAK_BF16):
+        self.name, self.fn, self.flops, self.bytes, self.peak = name, fn, flops, bytes_, peak
         self.times = []
 
     def run(self, timed):
@@ -212,17 +248,22 @@ class Leg:
         return None
 
 
-def build_legs(dev):
-    legs = []
-    c = CONFIGS[MAIN]
-    q, k, v = (t.to(dev) for t in make_qkv(**c))
-    o = torch.empty_like(q)
-    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-    B, H, N, d = c["B"], c["H"], c["N"], c["d"]
-    fl = attention_flops(B, H, N, d, False)
-    legs.append(Leg("bf16_fwd_b8h16n2k_d128", lambda: fa.fwd(q, k, v, False, out=o, lse=lse), fl))
-    legs.append(Leg("bf16_fwd_b8h16n2k_d128_causal",
-                    lambda: fa.fwd(q, k, v, True, out=o, lse=lse), fl / 2))
+def build_legs(dev, only=None):
+    """The step's legs (all, or the names in `only`) and the tensors they use."""
+    legs, keep = [], []
+    for name, (cfg, _) in FWD16_LEGS.items():
+        if only and name not in only:
+            continue
+        c = CONFIGS[cfg]
+        q, k, v = (t.to(dev) for t in make_qkv(**c))
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        fl = attention_flops(c["B"], c["H"], c["N"], c["d"], c["causal"])
+        legs.append(Leg(name, lambda q=q, k=k, v=v, o=o, lse=lse, causal=c["causal"]:
+                        fa.fwd(q, k, v, causal, out=o, lse=lse), fl))
+        keep += [q, k, v, o, lse]
+    if only and FP8_PREP_LEG not in only and FP8_FWD_LEG not in only:
+        return legs, keep
     c8 = CONFIGS[FP8]
     B8, H8, N8, d8 = c8["B"], c8["H"], c8["N"], c8["d"]
     q8, k8, v8 = (t.to(dev) for t in make_qkv(**c8))
@@ -238,18 +279,30 @@ def build_legs(dev):
         fa.fp8_prep(k8, signs, 128, out=pk)
         fa.fp8_prep(v8, None, 128, out=pv)
 
-    legs.append(Leg("fp8_prep_qkv_b4h16n4k_d128", prep, 0.0, prep_bytes))
-    legs.append(Leg("fp8_fwd_b4h16n4k_d128",
-                    lambda: fa.fwd_fp8(pq, pk, pv, B8, H8, N8, d8, False, out=o8, lse=lse8),
-                    attention_flops(B8, H8, N8, d8, False)))
-    keep = (q, k, v, o, lse, q8, k8, v8, signs, pq, pk, pv, o8, lse8)
+    prep()                      # the forward leg alone still reads prepared inputs
+    if not only or FP8_PREP_LEG in only:
+        legs.append(Leg(FP8_PREP_LEG, prep, 0.0, prep_bytes))
+    if not only or FP8_FWD_LEG in only:
+        legs.append(Leg(FP8_FWD_LEG,
+                        lambda: fa.fwd_fp8(pq, pk, pv, B8, H8, N8, d8, False, out=o8, lse=lse8),
+                        attention_flops(B8, H8, N8, d8, False), peak=PEAK_FP8))
+    keep += [q8, k8, v8, signs, pq, pk, pv, o8, lse8]
     return legs, keep
 
 
 def build_next_legs(dev):
-    """Legs of the rows beyond the forward; timed apart from the step."""
+    """Legs of the rows beyond the forward; timed apart from the step:
+    the 16-bit backward (dQ, dK, dV from the saved LSE) on B=8 H=16 N=2048
+    d=128, work 10*B*H*N^2*d (the five GEMMs of the gradient, halved for
+    causal); the fused rotary + Hadamard + fp8 block quantisation of Q and K
+    of the fp8 workload (half pairing, GB/s of bytes read and written); the
+    microscaled fp8 variant (fa_mx_prep of Q, K along d with the Hadamard and
+    V along the sequence, GB/s; the forward on its output, non-causal and
+    causal); the block-scaled fp8 forward, causal; and the decode-shaped
+    forward on its two workloads, in GB/s of the bytes it must move (K and V
+    of every sequence's keys, Q, O, LSE)."""
     legs = []
-    c = CONFIGS[MAIN]
+    c = CONFIGS["b8h16n2k_d128"]
     B, H, N, d = c["B"], c["H"], c["N"], c["d"]
     q, k, v = (t.to(dev) for t in make_qkv(**c))
     do = make_dout(B, H, N, d, c["seed"] + 500, c["dtype"]).to(dev)
@@ -265,7 +318,7 @@ def build_next_legs(dev):
             q, k, v, o, lse, do, causal, grads=grads, delta=delta), fl))
     c8 = CONFIGS[FP8]
     B8, H8, N8, d8 = c8["B"], c8["H"], c8["N"], c8["d"]
-    q8, k8, _ = (t.to(dev) for t in make_qkv(**c8))
+    q8, k8, v8 = (t.to(dev) for t in make_qkv(**c8))
     signs = torch.from_numpy(make_signs(H8, d8, c8["seed"])).to(dev)
     pq, pk = (fa.fp8_alloc_packed(B8, H8, N8, d8, dev) for _ in range(2))
     nel = B8 * H8 * N8 * d8
@@ -276,10 +329,7 @@ def build_next_legs(dev):
         fa.fp8_prep(k8, signs, 128, out=pk, rope=("half", 10000.0, 0))
 
     legs.append(Leg("fp8_prep_rope_qk_b4h16n4k_d128", prep_rope, 0.0, rope_bytes))
-    keep += [q8, k8, signs, pq, pk]
-    # microscaled fp8: prep of Q, K (along d, Hadamard) and V (along N), then
-    # the forward on the same workload
-    v8 = make_qkv(**c8)[2].to(dev)
+    keep += [q8, k8, v8, signs, pq, pk]
     mq, mk, mv = (torch.empty(fa.mx_packed_bytes(B8, H8, N8, d8), dtype=torch.uint8, device=dev)
                   for _ in range(3))
     mx_bytes = 3 * (nel * 2 + nel + nel // 32)
@@ -290,19 +340,19 @@ def build_next_legs(dev):
         fa.mx_prep(v8, None, "n", out=mv)
 
     legs.append(Leg("fp8_mx_prep_qkv_b4h16n4k_d128", prep_mx, 0.0, mx_bytes))
+    prep_mx()
     o8 = torch.empty((B8, H8, N8, d8), dtype=torch.bfloat16, device=dev)
     lse8 = torch.empty((B8, H8, N8), dtype=torch.float32, device=dev)
     for causal in (False, True):
         legs.append(Leg("fp8_mx_fwd_b4h16n4k_d128" + ("_causal" if causal else ""),
                         lambda causal=causal: fa.fwd_fp8(mq, mk, mv, B8, H8, N8, d8, causal, out=o8,
                                                          lse=lse8, mx=True),
-                        attention_flops(B8, H8, N8, d8, causal)))
-    keep += [v8, mq, mk, mv, o8, lse8]
-    # block-scaled fp8, causal (the non-causal forward is in the step)
+                        attention_flops(B8, H8, N8, d8, causal), peak=PEAK_FP8))
+    keep += [mq, mk, mv, o8, lse8]
     bq, bk, bv = (fa.fp8_prep(t, sg, 128) for t, sg in ((q8, signs), (k8, signs), (v8, None)))
     legs.append(Leg("fp8_fwd_b4h16n4k_d128_causal",
                     lambda: fa.fwd_fp8(bq, bk, bv, B8, H8, N8, d8, True, out=o8, lse=lse8),
-                    attention_flops(B8, H8, N8, d8, True)))
+                    attention_flops(B8, H8, N8, d8, True), peak=PEAK_FP8))
     keep += [bq, bk, bv]
     for name, c in sorted(DECODE_CONFIGS.items()):
         B, H, Hkv, Nq, Nk, d = c["B"], c["H"], c["Hkv"], c["Nq"], c["Nk"], c["d"]
@@ -325,61 +375,80 @@ def build_next_legs(dev):
 
 
 def time_legs(legs, steps, warmup):
+    """Warm up, then time `steps` rounds of every leg; returns the wall time."""
     for _ in range(warmup):
         for L in legs:
             L.run(False)
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
     events = [[L.run(True) for L in legs] for _ in range(steps)]
     torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     for step in events:
         for L, (a, b) in zip(legs, step):
             L.times.append(a.elapsed_time(b) * 1e-3)
+    return wall
 
 
 def leg_summary(L):
     t = float(np.mean(L.times))
     e = {"ms": t * 1e3, "ms_min": float(np.min(L.times)) * 1e3}
     if L.flops:
-        peak = PEAK_FP8 if L.name.startswith("fp8") else PEAK_BF16
         e["tflops"] = L.flops / t / 1e12
-        e["frac_of_peak"] = e["tflops"] / peak
+        e["frac_of_peak"] = e["tflops"] / L.peak
     if L.bytes:
         e["gbps"] = L.bytes / t / 1e9
         e["frac_of_hbm"] = e["gbps"] / PEAK_HBM
     return e
 
 
+def roofline(L):
+    t = float(np.mean(L.times))
+    achieved = L.flops / t / 1e12
+    return {"bound": "mfma", "achieved": achieved, "peak": L.peak, "unit": "TFLOP/s",
+            "frac": achieved / L.peak, "traffic": measured_traffic(L.name),
+            "kernel": KERNEL_OF[L.name], "leg": L.name, "launch_ms": t * 1e3}
+
+
+def headline(legs):
+    fl = sum(L.flops for L in legs)
+    t = sum(float(np.mean(L.times)) for L in legs)
+    peak = legs[0].peak
+    return {"tflops": fl / t / 1e12, "frac_of_peak": fl / t / 1e12 / peak, "peak": peak,
+            "legs": [L.name for L in legs], "ms": t * 1e3}
+
+
 def cpu_baseline():
-    """The float64 oracle on one step of the timed workload (about 15 s on
-    16 host cores), on the same seeded inputs: the bf16 forward, non-causal
-    and causal, B=8 H=16 N=2048 d=128 (the oracle computes every score and
-    masks; the metric counts half for causal), and the fp8 leg as the
-    fake-quant oracle (random-sign Hadamard + per-128-row e4m3 quantisation of
-    the outlier inputs, then exact attention) at B=4 H=16 N=4096 d=128.
-    Value: the step's metric flops over the oracle's time."""
+    """The float64 oracle on a bounded sample of the step's workloads (about
+    15-25 s on 16 host cores), on the same seeded inputs: batch 0 (16 heads)
+    of B=2 H=16 N=8192 d=128, causal and non-causal (the oracle computes every
+    score and masks; the metric counts half for causal), and the fp8 leg as
+    the fake-quant oracle (random-sign Hadamard + per-128-row e4m3
+    quantisation of the outlier inputs, then exact attention) on batch 0 of
+    B=4 H=16 N=4096 d=128. Value: the sample's metric flops over the oracle's
+    time."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
-    c, c8 = CONFIGS[MAIN], CONFIGS[FP8]
-    b, b8 = c["B"], c8["B"]
-    q, k, v = (t[:b].to(torch.float64).numpy() for t in make_qkv(**c))
-    q8, k8, v8 = (t[:b8].to(torch.float64).numpy() for t in make_qkv(**c8))
+    c, c8 = CONFIGS["b2h16n8k_d128"], CONFIGS[FP8]
+    q, k, v = (t[:1].to(torch.float64).numpy() for t in make_qkv(**c))
+    q8, k8, v8 = (t[:1].to(torch.float64).numpy() for t in make_qkv(**c8))
     signs = make_signs(c8["H"], c8["d"], c8["seed"])
-    fl = (attention_flops(b, c["H"], c["N"], c["d"], False)
-          + attention_flops(b, c["H"], c["N"], c["d"], True)
-          + attention_flops(b8, c8["H"], c8["N"], c8["d"], False))
+    fl = (attention_flops(1, c["H"], c["N"], c["d"], False)
+          + attention_flops(1, c["H"], c["N"], c["d"], True)
+          + attention_flops(1, c8["H"], c8["N"], c8["d"], False))
     t0 = time.perf_counter()
     oracle.attention(q, k, v, False)
     oracle.attention(q, k, v, True)
     oracle.fake_quant_attention(q8, k8, v8, signs, 128, False)
     el = time.perf_counter() - t0
     return {"value": fl / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"one step: bf16 B={b} H=16 N=2048 d=128 non-causal and causal; fp8 fake-quant "
-                      f"(Hadamard + block e4m3) B={b8} H=16 N=4096 d=128 outlier inputs; float64 numpy "
-                      f"oracle, {el:.1f} s"}
+            "sample": f"bf16 B=1 (of 2) H=16 N=8192 d=128 non-causal and causal; fp8 fake-quant "
+                      f"(Hadamard + block e4m3) B=1 (of 4) H=16 N=4096 d=128 outlier inputs; "
+                      f"float64 numpy oracle, {el:.1f} s"}
 
 
 def main():
@@ -392,14 +461,14 @@ def main():
                     help="skip the rows beyond the forward (backward, rotary prep, decode)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device copy three times (HBM counter calibration)")
-    ap.add_argument("--only-main", action="store_true",
-                    help="only launch the bf16 non-causal forward (for counter runs)")
-    ap.add_argument("--source-hash", action="store_true", help="print the kernel source hash")
+    ap.add_argument("--only", action="append", metavar="LEG",
+                    help="only launch these step legs (for counter runs)")
+    ap.add_argument("--source-hash", metavar="LEG", help="print a forward leg's kernel code hash")
     ap.add_argument("--traffic-summary", metavar="DIR",
                     help="write the HBM-traffic summary from the counter runs under DIR (no GPU)")
     args = ap.parse_args()
     if args.source_hash:
-        print(source_hash())
+        print(source_hash(KERNEL_OF[args.source_hash]))
         return
     if args.traffic_summary:
         traffic_summary(args.traffic_summary)
@@ -423,59 +492,54 @@ def main():
         return
     fa.lib()
     log("building inputs")
-    legs, _keep = build_legs(dev)
-    if args.only_main:
-        legs = legs[:1]
-    for _ in range(args.warmup):
-        for L in legs:
-            L.run(False)
-    torch.cuda.synchronize()
-    log(f"warmup done; timing {args.steps} steps")
-    events = []
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        events.append([L.run(True) for L in legs])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    for step in events:
-        for L, (a, b) in zip(legs, step):
-            L.times.append(a.elapsed_time(b) * 1e-3)
-    total_flops = sum(L.flops for L in legs)
-    step_s = wall / args.steps
-    legs_out = {L.name: leg_summary(L) for L in legs}
-    dom = legs[0]
-    t_dom = float(np.mean(dom.times))
-    achieved = dom.flops / t_dom / 1e12
-    roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16, "unit": "TFLOP/s",
-            "frac": achieved / PEAK_BF16, "traffic": measured_traffic(),
-            "kernel": "fa_fwd16_kernel<bf16,128,noncausal>", "launch_ms": t_dom * 1e3}
+    legs, _keep = build_legs(dev, args.only)
+    if not legs:
+        sys.exit(f"no step leg named {args.only}")
+    log(f"timing {args.steps} steps of {len(legs)} legs")
+    wall = time_legs(legs, args.steps, args.warmup)
+    by = {L.name: L for L in legs}
     out = {
-        "metric": "attention fwd TFLOP/s (4*B*H*N^2*d, /2 causal), bf16 and fp8",
-        "value": total_flops / step_s / 1e12,
+        "metric": "attention fwd TFLOP/s (4*B*H*N^2*d, /2 causal), % of MFMA peak",
+        "value": None,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": step_s * 1e3,
+        "ms_per_step": wall / args.steps * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16+fp8",
+        "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "bf16 fwd B=8 H=16 N=2048 d=128 (non-causal + causal) + fp8 "
-                               "prep/fwd B=4 H=16 N=4096 d=128 (0.1% outliers)",
-                   "global_batch": 8, "seq_len": 2048, "head_dim": 128, "heads": 16,
+        "config": {"workload": "bf16 fwd B=2 H=16 N=8192 d=128, causal + non-causal launches",
+                   "global_batch": 2, "seq_len": 8192, "head_dim": 128, "heads": 16,
                    "parallelism": "single-gpu"},
-        "legs": legs_out,
-        "roofline": roof,
+        "legs": {L.name: leg_summary(L) for L in legs},
     }
-    if not args.only_main and not args.no_next:
+    if all(n in by for n in HEADLINE):
+        h = headline([by[n] for n in HEADLINE])
+        out["value"] = h["tflops"]
+        out["frac_of_peak"] = h["frac_of_peak"]
+        heads = {"bf16_d128_n8k": h}
+        bf = [L for L in legs if L.name in FWD16_LEGS]
+        heads["bf16_all"] = headline(bf)
+        if FP8_FWD_LEG in by:
+            f = headline([by[FP8_FWD_LEG]])
+            if FP8_PREP_LEG in by:
+                tp = float(np.mean(by[FP8_PREP_LEG].times))
+                f["with_prep_tflops"] = by[FP8_FWD_LEG].flops / (f["ms"] * 1e-3 + tp) / 1e12
+            heads["fp8"] = f
+        out["headlines"] = heads
+    fwd_legs = [L for L in legs if L.name in KERNEL_OF]
+    if ROOF_LEG in by:
+        out["roofline"] = roofline(by[ROOF_LEG])
+    out["rooflines"] = {L.name: roofline(L) for L in fwd_legs}
+    if not args.only and not args.no_next:
         log("timing the rows beyond the forward")
         nlegs, _nkeep = build_next_legs(dev)
         time_legs(nlegs, args.steps, args.warmup)
         out["next_rows"] = {L.name: leg_summary(L) for L in nlegs}
-    if not args.no_cpu:
+    if not args.only and not args.no_cpu:
         log("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

@@ -30,6 +30,9 @@ CONFIGS = {
     "b8h16n2k_d128_causal": dict(B=8, H=16, N=2048, d=128, causal=True, dtype="bf16", seed=1),
     "b4h32n4k_d64": dict(B=4, H=32, N=4096, d=64, causal=False, dtype="bf16", seed=2),
     "b2h16n8k_d128_causal": dict(B=2, H=16, N=8192, d=128, causal=True, dtype="bf16", seed=5),
+    # the same shape and inputs without the mask (the long-context d = 128
+    # regime, non-causal)
+    "b2h16n8k_d128": dict(B=2, H=16, N=8192, d=128, causal=False, dtype="bf16", seed=5),
     "b2h8n16k_d256_causal": dict(B=2, H=8, N=16384, d=256, causal=True, dtype="bf16", seed=3),
     "fp8_b4h16n4k_d128": dict(B=4, H=16, N=4096, d=128, causal=False, dtype="bf16", seed=4,
                               outliers=True),
