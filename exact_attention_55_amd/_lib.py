@@ -12,7 +12,8 @@ import os
 
 import torch
 
-FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_TOO_LARGE = 0, 1, 2, 3, 4
+FA_NOALLOC_SCRATCH_BYTES = 16 << 20
 FA_F16, FA_BF16, FA_FP8_E4M3, FA_FP8_MX = 0, 1, 2, 3
 FA_MX_ALONG_D, FA_MX_ALONG_N = 0, 1
 FA_OUT_F32 = 0x100
@@ -50,6 +51,8 @@ def lib():
     L.fa_fwd_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                 i, i, i, i, i, i, i, f, i, i, vp]
     L.fa_fwd_decode.restype = i
+    L.fa_fwd_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp]
+    L.fa_fwd_decode_noalloc.restype = i
     L.fa_decode_splits.argtypes = [i, i, i, i, i, i]
     L.fa_decode_splits.restype = i
     L.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i]
@@ -106,6 +109,15 @@ def decode_raw(q, k, v, o, lse, seqlens_k, workspace, workspace_bytes, B, H, H_k
     return lib().fa_fwd_decode(q, k, v, o, lse, seqlens_k, workspace, workspace_bytes, B, H, H_kv,
                                Nq, Nk, d, int(causal), float(softmax_scale), int(num_splits),
                                int(dtype), stream)
+
+
+def decode_noalloc_raw(q, k, v, o, lse, seqlens_k, B, H, H_kv, Nq, Nk, d, causal, softmax_scale,
+                       num_splits, dtype, stream=None):
+    """Direct call of the allocation-free decode entry point; returns the
+    status code."""
+    return lib().fa_fwd_decode_noalloc(q, k, v, o, lse, seqlens_k, B, H, H_kv, Nq, Nk, d,
+                                       int(causal), float(softmax_scale), int(num_splits),
+                                       int(dtype), stream)
 
 
 def decode_splits(B, H, H_kv, Nq, Nk, d):

@@ -49,6 +49,7 @@ const char* fa_status_string(int status) {
         case FA_ERR_INVALID_ARG: return "invalid argument";
         case FA_ERR_UNSUPPORTED: return "unsupported configuration";
         case FA_ERR_HIP: return "HIP runtime error";
+        case FA_ERR_TOO_LARGE: return "request exceeds the fixed scratch of an allocation-free entry point";
     }
     return "unknown status";
 }
@@ -131,10 +132,18 @@ size_t fa_decode_workspace_bytes(int B, int H, int Nq, int d, int num_splits) {
     return fa::decode_workspace_bytes((long long)B * H * Nq, num_splits, d);
 }
 
-int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
-                  const int* seqlens_k, void* workspace, size_t workspace_bytes, int B, int H,
-                  int H_kv, int Nq, int Nk, int d, int causal, float softmax_scale, int num_splits,
-                  int dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the two decode entry points. Returns FA_OK with
+// *empty set for a valid empty problem (nothing to launch). With
+// caller_ws the caller's workspace must hold the split partials.
+int decode_args(const void* q, const void* k, const void* v, void* o, float* lse,
+                const int* seqlens_k, void* workspace, size_t workspace_bytes, bool caller_ws,
+                int B, int H, int H_kv, int Nq, int Nk, int d, int causal, float softmax_scale,
+                int num_splits, int dtype, void* stream, fa::DecodeArgs& a, bool* empty) {
+    *empty = false;
     const int base = dtype & 0xff;
     const int flags = dtype & ~0xff;
     if ((flags & ~FA_OUT_F32) != 0) return FA_ERR_INVALID_ARG;
@@ -145,7 +154,10 @@ int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* l
     if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_INVALID_ARG;
     if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
     if ((long long)Nk * d * 2 > kMaxHeadBytes) return FA_ERR_UNSUPPORTED;
-    if (B == 0 || H == 0 || Nq == 0) return FA_OK;
+    if (B == 0 || H == 0 || Nq == 0) {
+        *empty = true;
+        return FA_OK;
+    }
     // the query rows sharing one key/value head are addressed with 31-bit offsets
     if ((long long)(H / H_kv) * Nq * d * 2 > kMaxHeadBytes) return FA_ERR_UNSUPPORTED;
     const long long rgroups = ((long long)(H / H_kv) * Nq + 31) / 32;
@@ -154,12 +166,10 @@ int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* l
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
         !aligned(lse, 4) || !aligned(seqlens_k, 4))
         return FA_ERR_INVALID_ARG;
-    if (num_splits > 1) {
+    if (caller_ws && num_splits > 1) {
         const size_t need = fa::decode_workspace_bytes((long long)B * H * Nq, num_splits, d);
         if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return FA_ERR_INVALID_ARG;
     }
-
-    fa::DecodeArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
     a.seqlens = seqlens_k;
     a.workspace = workspace;
@@ -168,9 +178,48 @@ int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* l
     a.scale = softmax_scale;
     a.out_f32 = (flags & FA_OUT_F32) != 0;
     a.splits = num_splits;
+    (void)stream;
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int* seqlens_k, void* workspace, size_t workspace_bytes, int B, int H,
+                  int H_kv, int Nq, int Nk, int d, int causal, float softmax_scale, int num_splits,
+                  int dtype, void* stream) {
+    fa::DecodeArgs a;
+    bool empty;
+    const int st = decode_args(q, k, v, o, lse, seqlens_k, workspace, workspace_bytes, true, B, H,
+                               H_kv, Nq, Nk, d, causal, softmax_scale, num_splits, dtype, stream, a,
+                               &empty);
+    if (st != FA_OK || empty) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    return from_hip(fa::launch_decode16(a, base == FA_BF16, s));
+    return from_hip(fa::launch_decode16(a, (dtype & 0xff) == FA_BF16, s));
+}
+
+int fa_fwd_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                          const int* seqlens_k, int B, int H, int H_kv, int Nq, int Nk, int d,
+                          int causal, float softmax_scale, int num_splits, int dtype, void* stream) {
+    fa::DecodeArgs a;
+    bool empty;
+    const int st = decode_args(q, k, v, o, lse, seqlens_k, nullptr, 0, false, B, H, H_kv, Nq, Nk,
+                               d, causal, softmax_scale, num_splits, dtype, stream, a, &empty);
+    if (st != FA_OK || empty) return st;
+    if (num_splits > 1 &&
+        fa::decode_workspace_bytes((long long)B * H * Nq, num_splits, d) > FA_NOALLOC_SCRATCH_BYTES)
+        return FA_ERR_TOO_LARGE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (num_splits > 1) {
+        void* p = nullptr;
+        if (fa::decode_scratch(s, &p) != hipSuccess) return FA_ERR_HIP;
+        a.workspace = p;
+    }
+    return from_hip(fa::launch_decode16(a, (dtype & 0xff) == FA_BF16, s));
 }
 
 int fa_fp8_prep_rope(const void* x, void* x8, const int8_t* signs, int B, int H, int N, int d,

@@ -24,10 +24,13 @@
 // Output: with one split the wave writes O and LSE; otherwise it writes a
 // partial (O_s normalised by its own sum, LSE_s) and decode_merge_kernel
 // combines them: LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.
+#include "fa.h"
 #include "fa_device.h"
 #include "fa_internal.h"
 
 #include <math.h>
+
+#include <mutex>
 
 namespace fa {
 namespace {
@@ -399,6 +402,45 @@ int decode_default_splits(int B, int H, int Hkv, int Nq, int Nk, int d) {
 
 hipError_t launch_decode16(const DecodeArgs& a, bool bf16, hipStream_t st) {
     return bf16 ? launch_ty<__bf16>(a, st) : launch_ty<_Float16>(a, st);
+}
+
+// Split partials of fa_fwd_decode_noalloc, for callers that cannot allocate:
+// a fixed array in device memory, one per GPU the library runs on, held
+// until the process ends. Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in for the symbol): its device
+// address is looked up once per device and kept.
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(hipStream_t s, void** ptr) {
+    int dev = 0;
+    hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        // with that device current
+        int cur = 0;
+        e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_addr[dev] = p;
+    }
+    *ptr = g_scratch_addr[dev];
+    return hipSuccess;
 }
 
 }  // namespace fa

@@ -95,5 +95,9 @@ size_t decode_workspace_bytes(long long rows, int splits, int d);
 int decode_default_splits(int B, int H, int Hkv, int Nq, int Nk, int d);
 // Decode-shaped 16-bit forward (bf16 = true: bfloat16, else float16).
 hipError_t launch_decode16(const DecodeArgs& a, bool bf16, hipStream_t s);
+// Device address of the fixed decode scratch (FA_NOALLOC_SCRATCH_BYTES) on
+// the device of stream s (the current device for a null stream), looked up
+// once per device.
+hipError_t decode_scratch(hipStream_t s, void** ptr);
 
 }  // namespace fa

@@ -48,8 +48,13 @@ enum fa_status {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size or scale   */
     FA_ERR_UNSUPPORTED = 2,   /* valid request the library has no kernel for */
-    FA_ERR_HIP = 3            /* the HIP runtime rejected a launch            */
+    FA_ERR_HIP = 3,           /* the HIP runtime rejected a launch            */
+    FA_ERR_TOO_LARGE = 4      /* request exceeds the fixed scratch of an
+                                 allocation-free entry point                  */
 };
+
+/* Bytes of the fixed per-device scratch array of fa_fwd_decode_noalloc. */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 /* Element types. FA_OUT_F32 may be OR-ed into fa_fwd's dtype: O is then
  * written as float32 instead of the default (the input type for 16-bit
@@ -164,6 +169,31 @@ int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* l
                   const int* seqlens_k, void* workspace, size_t workspace_bytes,
                   int B, int H, int H_kv, int Nq, int Nk, int d, int causal,
                   float softmax_scale, int num_splits, int dtype, void* stream);
+
+/*
+ * fa_fwd_decode_noalloc - fa_fwd_decode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, kernels and results as
+ * fa_fwd_decode, without the workspace: the split partials go to a fixed
+ * array of FA_NOALLOC_SCRATCH_BYTES (16 MiB) in device memory, one per GPU
+ * the library runs on, held until the process ends. The call makes no
+ * hipMalloc or hipFree and calls no allocating library routine; the first
+ * call on a device looks up that device's array address once (the device of
+ * `stream`, or the current device for NULL).
+ *
+ * A request whose partials need more than FA_NOALLOC_SCRATCH_BYTES
+ * (fa_decode_workspace_bytes(B, H, Nq, d, num_splits) > the limit) returns
+ * FA_ERR_TOO_LARGE before any HIP call; num_splits == 1 uses no scratch.
+ * Nothing in the array needs clearing between calls: the merge reads only
+ * partials the same call's split kernel wrote. Every call on one GPU shares
+ * its array, so calls that overlap on one GPU (on different streams, or
+ * from different threads) race and give wrong results: serialise them.
+ * Returns the statuses of fa_fwd_decode and FA_ERR_TOO_LARGE.
+ */
+int fa_fwd_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                          const int* seqlens_k, int B, int H, int H_kv, int Nq, int Nk, int d,
+                          int causal, float softmax_scale, int num_splits, int dtype,
+                          void* stream);
 
 /* Suggested num_splits for fa_fwd_decode (enough parts to fill the GPU, each
  * at least 256 keys). Returns 1 for invalid or empty shapes. */

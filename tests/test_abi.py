@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for code in (0, 1, 2, 3):
+    for code in (0, 1, 2, 3, 4):
         assert fa.status_string(code) != "unknown status"
     assert L.fa_status_string(99).decode() == "unknown status"
 
