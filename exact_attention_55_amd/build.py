@@ -23,8 +23,12 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libfa.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["fa_api.hip", "fa_fwd16.hip", "fa_fwd_fp8.hip", "fa_fp8_prep.hip", "fa_bwd16.hip",
-           "fa_decode16.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd16.hip", "fa_fwd16_pipe.hip", "fa_fwd_fp8.hip", "fa_fp8_prep.hip",
+           "fa_bwd16.hip", "fa_decode16.hip"]
+# Per-source flags. fa_fwd16_pipe.hip: the compiler's MFMA builtins write
+# vector registers (the score tiles feed the exponentials directly), while
+# the file's P V MFMAs keep O in the accumulation registers through asm.
+EXTRA_FLAGS = {"fa_fwd16_pipe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -38,8 +42,8 @@ FLAGS = [
 
 def _compile(src, verbose):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src),
-                             "-o", obj]
+    cmd = [HIPCC] + FLAGS + EXTRA_FLAGS.get(src, []) + [
+        "-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

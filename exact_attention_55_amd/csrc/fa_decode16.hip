@@ -106,8 +106,8 @@ decode16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     const int nblk = (k1 - k0 + 31) / 32;
     // A part of at most 64 keys feeds P to the PV MFMA as the rounded P~
     // plus its rounding residue (two MFMAs per fragment): on a row that sees
-    // only a few keys, rounding P to bf16 (2^-9 relative) could otherwise
-    // move O by up to ~w(1-w) 2^-9 |v_a - v_b| (above 4e-3 for two keys of
+    // only a few keys, rounding P to bf16 (2^-8 relative) could otherwise
+    // move O by up to ~w(1-w) 2^-8 |v_a - v_b| (above 4e-3 for two keys of
     // comparable weight whose values differ by ~8); over many keys it
     // averages out.
     const bool split_p = k1 - k0 <= 64;

@@ -43,7 +43,7 @@
 //    ones) normalises O, which makes O an exact convex combination of V rows
 //    even when one key dominates. For fp16 it also gives the log-sum-exp
 //    (relative error at most fp16's rounding of P, 2^-11: within the LSE
-//    tolerance). bf16's rounding (2^-9) is not, so bf16 keeps a second,
+//    tolerance). bf16's rounding (2^-8) is not, so bf16 keeps a second,
 //    fp32 sum for the log-sum-exp: two more adds per pair of exponentials
 //    (2.5-5.5 % of the kernel time; FA16_XSUM=1 forces it for fp16 too).
 //  * Schedule ("FlashAttention-3: ...", "Overlapping GEMM and Softmax"): two
@@ -338,7 +338,7 @@ struct Wave16 {
     // again with RESID: P then reaches the PV product as P~ plus
     // its residue (about 16 significant bits). The first key tile is the
     // only one where a row can see few keys, and there rounding P to bf16
-    // (2^-9 relative) moves O by up to ~w(1-w) 2^-9 |v_a - v_b| on a row that
+    // (2^-8 relative) moves O by up to ~w(1-w) 2^-8 |v_a - v_b| on a row that
     // two keys share with weights w, 1 - w: above 4e-3 for |v_a - v_b| near
     // 8. Once a row sees a few dozen keys the effect averages out.
     // RESID: 0 P~, 1 the residue, 2 chosen at run time by rm (0 or 1): one
@@ -525,11 +525,13 @@ struct Wave16 {
     //   one score MFMA of the next tile, and an even share of this tile's
     //   exponentials, which run in the MFMA's shadow;
     //   the overflow check (a branch, rarely taken);
-    //   NPVM chunks, each: the reads of the V^T fragment VPD ahead, one PV
-    //   MFMA, and a share of the copy of the next scores into s.
-    __device__ __forceinline__ void step(f32x16 (&s)[QB][NKB], const char* kn, const int (&ka)[NKA],
-                                         const char* vl, const int (&va)[NVA], int vstep,
-                                         const X8 (&qf)[QB][NCH], float c) {
+    //   NPVM chunks, each: the reads of the V^T fragment VPD ahead and one PV
+    //   MFMA.
+    // The next tile's scores go to sn: the caller alternates two register
+    // sets, so nothing is copied.
+    __device__ __forceinline__ void step(const f32x16 (&s)[QB][NKB], f32x16 (&sn)[QB][NKB], const char* kn,
+                                         const int (&ka)[NKA], const char* vl, const int (&va)[NVA],
+                                         int vstep, const X8 (&qf)[QB][NCH], float c) {
         constexpr int NKF = NCH * NKB;      // K fragments = score MFMAs per tile
         constexpr int NVF = NPV * NDB;      // V^T fragments = PV MFMAs per tile
         constexpr int NPAIR = NKB * 8;      // exponential pairs per lane per tile
@@ -541,7 +543,6 @@ struct Wave16 {
         // from VPD on: every fragment is read only if KPD >= VPD.
         static_assert(KPD >= VPD, "V^T fragments [KPD, VPD) would never be read");
         X8 kf[NKB][NCH];
-        f32x16 sn[QB][NKB];
         X8 vf[NPV][NDB];
         X2 pp[QB][NKB][2][4];
         float ls[QB][2], lxs[QB][2];
@@ -592,7 +593,6 @@ struct Wave16 {
             const int t = j / NDB, db = j % NDB;
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(vf[t][db], pf[qb][t], o[qb][db]);
-            if (j < QB * NKB) s[j / NKB][j % NKB] = sn[j / NKB][j % NKB];
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -749,24 +749,45 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     }
     int t = 0;
     // Pipelined full tiles: the scores of tile t+1 are computed while the
-    // softmax of tile t runs.
-    for (; t + 1 < nfull; ++t) {
+    // softmax of tile t runs; two tiles per trip, the scores alternating
+    // between s and s2.
+    f32x16 s2[QB][NKB];
+    auto full_step = [&](const f32x16 (&sc)[QB][NKB], f32x16 (&sn)[QB][NKB]) {
         load_k(t + 2);
         load_v(t + 1);
 #if FA16_SCHED
-        st.step(s, ktile(t + 1), ka, smem + (2 + (t & 1)) * TB, vai, vsi, qf, c);
+        st.step(sc, sn, ktile(t + 1), ka, smem + (2 + (t & 1)) * TB, vai, vsi, qf, c);
 #else
         uint32_t b0[NVA], b1[NVA];
         vbases(sbase + (2 + (t & 1)) * TB, b0, b1);
-        f32x16 sn[QB][NKB];
-        st.overlap(s, sn, ktile(t + 1), ka, b0, b1, qf, c);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) s[qb][kb] = sn[qb][kb];
+        st.overlap(sc, sn, ktile(t + 1), ka, b0, b1, qf, c);
 #endif
         wait_vm_all();
         __syncthreads();
+        ++t;
+    };
+    auto copy_back = [&]() {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) s[qb][kb] = s2[qb][kb];
+    };
+    if constexpr (Cfg16<D, WIDE>::WPE == 1) {
+        // one wave per SIMD (d = 256): the accumulation registers hold O and
+        // the scores, with no room for a second set; copied each tile
+        for (; t + 1 < nfull;) {
+            full_step(s, s2);
+            copy_back();
+        }
+    } else {
+        for (; t + 2 < nfull;) {
+            full_step(s, s2);
+            full_step(s2, s);
+        }
+        if (t + 1 < nfull) {                  // an odd number of them: the scores end in s2
+            full_step(s, s2);
+            copy_back();
+        }
     }
     if (nfull > 0) {                          // last full tile: no next scores
         load_v(t + 1);
@@ -877,7 +898,18 @@ static hipError_t launch_ty(const FwdArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
+// d = 128 goes to the 64-rows-per-wave pipelined kernel (fa_fwd16_pipe.hip)
+// when its grid of 256-row workgroups (one per CU) fills the GPU at least
+// kPipeMinBlocks / 256 times over; smaller problems keep the 128-row
+// workgroups of this file's kernel (two per CU), which spread them further.
+#ifndef FA16_PIPE
+#define FA16_PIPE 1
+#endif
+constexpr long long kPipeMinBlocks = 256;
+
 hipError_t launch_fwd16(const FwdArgs& a, bool bf16, hipStream_t s) {
+    if (FA16_PIPE && a.d == 128 && (long long)a.B * a.H * ((a.N + 255) / 256) >= kPipeMinBlocks)
+        return launch_fwd16_pipe(a, bf16, s);
     return bf16 ? launch_ty<__bf16>(a, s) : launch_ty<_Float16>(a, s);
 }
 

@@ -280,13 +280,13 @@ struct Wave8 {
     // kn), the LDS reads of the fragment KPD ahead (in the last chunks the
     // first VPD V^T fragments of this tile) and an even share of this tile's
     // exponential groups; the overflow check; per PV MFMA of this tile, the
-    // reads of the V^T fragment VPD ahead and a share of the copy of the next
-    // scores into s.
+    // reads of the V^T fragment VPD ahead. The next tile's scores go to sn
+    // (the caller alternates two register sets, so nothing is copied).
     // tsn: scales of the next tile's score MFMAs; ts: this tile's PV scales.
-    __device__ __forceinline__ void step(f32x16 (&s)[NKB], const char* kn, const int (&ka)[NKA][2],
-                                         const char* vl, const int (&va)[NVA], const i32x8 (&qf)[NCH],
-                                         float cj, float bj, float lscale, const TS& tsn, const TS& ts,
-                                         const int (&qs)[NCH]) {
+    __device__ __forceinline__ void step(const f32x16 (&s)[NKB], f32x16 (&sn)[NKB], const char* kn,
+                                         const int (&ka)[NKA][2], const char* vl, const int (&va)[NVA],
+                                         const i32x8 (&qf)[NCH], float cj, float bj, float lscale,
+                                         const TS& tsn, const TS& ts, const int (&qs)[NCH]) {
         constexpr int NKF = NCH * NKB;      // K fragments = score MFMAs per tile
         constexpr int NVF = NPV * NDB;      // V^T fragments = PV MFMAs per tile
         constexpr int NG = 8 * NPV;         // exponential groups (4 each) per lane
@@ -297,7 +297,6 @@ struct Wave8 {
         // those from VPD on: every fragment is read only if KPD >= VPD.
         static_assert(KPD >= VPD, "V^T fragments [KPD, VPD) would never be read");
         i32x8 kf[NKB][NCH];
-        f32x16 sn[NKB];
         i32x8 vf[NPV][NDB];
         uint32_t w[NPV][8];
         float ls[2] = {0.f, 0.f};
@@ -333,8 +332,6 @@ struct Wave8 {
             if (v < NVF) vf[v / NDB][v % NDB] = vfrag(vl, va, v / NDB, v % NDB);
             const int t = j / NDB, db = j % NDB;
             o[db] = mm(vf[t][db], pf[t], o[db], ts.vbyte(db), kPScaleE8M0);
-#pragma unroll
-            for (int kb = j * NKB / NVF; kb < (j + 1) * NKB / NVF; ++kb) s[kb] = sn[kb];
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -604,12 +601,15 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
         __syncthreads();                     // all waves done reading K_0's slot
     }
     int t = 0;
-    for (; t + 1 < nfull; ++t) {
+    // Pipelined full tiles, two per trip: the scores alternate between s and
+    // s2, so no step copies them.
+    f32x16 s2[NKB];
+    auto full_step = [&](const f32x16 (&sc)[NKB], f32x16 (&sn)[NKB]) {
         load_kv(krs, t + 2, t & 1);
         load_kv(vrs, t + 1, 2 + ((t + 1) & 1));
         float cj, bj, lscale;
         tile_scales(cj, bj, lscale);
-        st.step(s, ktile(t + 1), ka, vtile(t), va, qf, cj, bj, lscale, tk, tv, qs);
+        st.step(sc, sn, ktile(t + 1), ka, vtile(t), va, qf, cj, bj, lscale, tk, tv, qs);
         wait_vm_all();
         __syncthreads();
         if constexpr (MX) {
@@ -617,6 +617,16 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
             read_v(tv, (t + 1) & 1);           // tile t + 1
         }
         read_bs((t + 1) & 1);
+        ++t;
+    };
+    for (; t + 2 < nfull; ) {
+        full_step(s, s2);
+        full_step(s2, s);
+    }
+    if (t + 1 < nfull) {                     // an odd number of them: the scores end in s2
+        full_step(s, s2);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) s[kb] = s2[kb];
     }
     if (nfull > 0) {                          // last full tile
         load_kv(vrs, t + 1, 2 + ((t + 1) & 1));

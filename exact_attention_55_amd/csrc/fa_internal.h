@@ -29,6 +29,9 @@ struct FwdArgs {
 
 // 16-bit forward (bf16 = true: bfloat16, else float16).
 hipError_t launch_fwd16(const FwdArgs& a, bool bf16, hipStream_t s);
+// 16-bit forward at d = 128 with 64 query rows per wave and the in-wave
+// three-stage pipeline (fa_fwd16_pipe.hip).
+hipError_t launch_fwd16_pipe(const FwdArgs& a, bool bf16, hipStream_t s);
 // FP8 e4m3 forward on packed tensors.
 hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t s);
 

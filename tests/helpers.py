@@ -93,3 +93,26 @@ def fp8_p_rounding_bound(q, k, v, b, h, rows, causal, w=None, scale=None):
     wj = np.ones(N) if w is None else np.asarray(w, dtype=np.float64)
     err = np.maximum(2.0 ** -4 * p, np.where(p > 0, 2.0 ** -13 / wj[None, :], 0.0))
     return (err @ vh) / p.sum(axis=1, keepdims=True)
+
+
+def p16_rounding_bound(q, k, v, b, h, causal, scale, dtype="bf16"):
+    """Elementwise bound on |O_gpu - O_ref| for every row of head (b, h) when
+    the GPU rounds each weight p_j to a 16-bit float (relative error <= u,
+    the unit roundoff: 2^-8 for bf16, 8 significant bits; 2^-11 for fp16) and normalises by the sum of the rounded
+    weights. With w_j = p_j / sum p and r_j = p_j (1 + e_j),
+        O - O_ref = sum_j w_j e_j (v_j - O_ref) / (1 + sum_j w_j e_j),
+    so |dO_c| <= u / (1 - u) * sum_j w_j |v_jc - O_ref_c|. Returns [N, d]
+    (float64), plus 1e-5 * max|v| for the fp32 accumulation."""
+    u = {"bf16": 2.0 ** -8, "fp16": 2.0 ** -11}[dtype]
+    qh = np.asarray(q[b, h], dtype=np.float64)
+    kh = np.asarray(k[b, h], dtype=np.float64)
+    vh = np.asarray(v[b, h], dtype=np.float64)
+    N = qh.shape[0]
+    s = scale * (qh @ kh.T)
+    if causal:
+        s = np.where(np.arange(N)[None, :] <= np.arange(N)[:, None], s, -np.inf)
+    w = np.exp(s - s.max(axis=1, keepdims=True))
+    w /= w.sum(axis=1, keepdims=True)
+    o = w @ vh
+    dev = np.einsum("ij,ijc->ic", w, np.abs(vh[None, :, :] - o[:, None, :]))
+    return u / (1.0 - u) * dev + 1e-5 * np.max(np.abs(vh))

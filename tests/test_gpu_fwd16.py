@@ -18,7 +18,7 @@ import oracle
 import exact_attention_55_amd as fa
 from exact_attention_55_amd.inputs import CONFIGS, make_qkv, to_f64
 
-from helpers import errors, check_lse, check_o, sample_rows
+from helpers import errors, check_lse, check_o, p16_rounding_bound, sample_rows
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -199,6 +199,75 @@ def test_few_keys_bf16(N, causal, d):
     mx, rmse = check_o(o, o_ref, "f32", "(fp32 out)")
     say(f"few keys N={N} causal={causal} d={d}: max-abs {mx:.2e} RMSE {rmse:.2e}")
     check_lse(lse, lse_ref)
+
+
+# d = 128 shapes whose grid of 256-row workgroups is large enough for the
+# launch to pick the 64-rows-per-wave pipelined kernel (B*H*ceil(N/256) >= 256)
+PIPE = [
+    # B, H, N, causal, dtype
+    (4, 64, 300, False, "bf16"),          # ragged query and key tiles
+    (4, 64, 300, True, "bf16"),
+    (2, 128, 700, True, "fp16"),
+    (2, 128, 513, False, "fp16"),
+    (1, 256, 64, False, "bf16"),          # one full tile: no steady-state step
+    (1, 256, 128, False, "bf16"),         # two full tiles
+    (1, 256, 1, False, "bf16"),           # no full tile
+    (1, 256, 257, True, "bf16"),
+]
+
+
+@pytest.mark.parametrize("B,H,N,causal,dt", PIPE)
+def test_pipe_d128_full_compare(B, H, N, causal, dt):
+    """The pipelined d = 128 kernel, every element against the oracle, fp32
+    and 16-bit outputs."""
+    say(f"pipe d=128 B={B} H={H} N={N} causal={causal} {dt}")
+    q, k, v = make_qkv(B, H, N, 128, seed=200 + N, dtype=dt)
+    o_ref, lse_ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), causal)
+    o32, lse = run(q, k, v, causal, True)
+    mx, rmse = check_o(o32, o_ref, "f32", "(fp32 out)")
+    check_lse(lse, lse_ref)
+    say(f"pipe d=128 B={B} H={H} N={N} causal={causal} {dt}: max-abs {mx:.2e} RMSE {rmse:.2e}")
+    o16, lse16 = run(q, k, v, causal, False)
+    check_o(o16, o_ref, dt, "(16-bit out)")
+    check_lse(lse16, lse_ref)
+
+
+@pytest.mark.parametrize("dt", ["fp16", "bf16"])
+def test_pipe_d128_large_logits_and_constant_v(dt):
+    """Scores of tens of units through the pipelined kernel: later blocks pass
+    the first block's reference maximum, so O is rescaled in place in the
+    accumulation registers mid-row; and constant V comes back exactly.
+
+    Such scores leave most rows to one to three keys, at any position. In
+    fp16 every element meets the 4e-3 bound. In bf16, rounding a weight to
+    2^-8 on a row two keys share moves O by up to ~2^-10 |v_a - v_b| (~4.7e-3
+    on these inputs even with the exact row maximum, computed on the CPU), so
+    each element is held to the bound derived from that rounding
+    (helpers.p16_rounding_bound) and the RMSE to the usual 5e-4."""
+    say(f"pipe d=128 large logits {dt}")
+    q, k, v = make_qkv(1, 256, 384, 128, seed=17, dtype=dt)
+    q = (q.float() * 4).to(q.dtype)
+    q64, k64, v64 = to_f64(q), to_f64(k), to_f64(v)
+    for causal in (False, True):
+        o_ref, lse_ref = oracle.attention(q64, k64, v64, causal, 0.5)
+        o, lse = run(q, k, v, causal, True, scale=0.5)
+        check_lse(lse, lse_ref)
+        if dt == "fp16":
+            check_o(o, o_ref, "f32")
+            continue
+        mx, rmse = errors(o, o_ref)
+        assert rmse <= 5e-4, f"RMSE {rmse:.3e}"
+        worst = 0.0
+        for h in range(q.shape[1]):
+            bound = p16_rounding_bound(q64, k64, v64, 0, h, causal, 0.5)
+            err = np.abs(o[0, h] - o_ref[0, h])
+            assert np.all(err <= bound), f"head {h}: {np.max(err - bound):.3e} past the rounding bound"
+            worst = max(worst, float(np.max(err / bound)))
+        say(f"pipe large logits bf16 causal={causal}: max-abs {mx:.2e} RMSE {rmse:.2e}, "
+            f"worst error / bound {worst:.2f}")
+    vc = torch.full_like(q, 0.7109375)
+    o, _ = run(q, k, vc, False, True, scale=0.5)
+    assert np.max(np.abs(o - 0.7109375)) <= 2e-6
 
 
 def test_many_heads_grid():
