@@ -277,7 +277,7 @@ def build_legs(dev, only=None):
     def prep():
         fa.fp8_prep(q8, signs, 128, out=pq)
         fa.fp8_prep(k8, signs, 128, out=pk)
-        fa.fp8_prep(v8, None, 128, out=pv)
+        fa.fp8_prep(v8, None, 128, out=pv, pow2_scale=True)
 
     prep()                      # the forward leg alone still reads prepared inputs
     if not only or FP8_PREP_LEG in only:
@@ -349,7 +349,8 @@ def build_next_legs(dev):
                                                          lse=lse8, mx=True),
                         attention_flops(B8, H8, N8, d8, causal), peak=PEAK_FP8))
     keep += [mq, mk, mv, o8, lse8]
-    bq, bk, bv = (fa.fp8_prep(t, sg, 128) for t, sg in ((q8, signs), (k8, signs), (v8, None)))
+    bq, bk = (fa.fp8_prep(t, signs, 128) for t in (q8, k8))
+    bv = fa.fp8_prep(v8, None, 128, pow2_scale=True)
     legs.append(Leg("fp8_fwd_b4h16n4k_d128_causal",
                     lambda: fa.fwd_fp8(bq, bk, bv, B8, H8, N8, d8, True, out=o8, lse=lse8),
                     attention_flops(B8, H8, N8, d8, True), peak=PEAK_FP8))

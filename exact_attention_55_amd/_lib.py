@@ -17,6 +17,7 @@ FA_NOALLOC_SCRATCH_BYTES = 16 << 20
 FA_F16, FA_BF16, FA_FP8_E4M3, FA_FP8_MX = 0, 1, 2, 3
 FA_MX_ALONG_D, FA_MX_ALONG_N = 0, 1
 FA_OUT_F32 = 0x100
+FA_SCALE_POW2 = 0x200
 FA_ROPE_NONE, FA_ROPE_INTERLEAVED, FA_ROPE_HALF = 0, 1, 2
 ROPE_STYLES = {"interleaved": FA_ROPE_INTERLEAVED, "half": FA_ROPE_HALF}
 
@@ -300,14 +301,15 @@ def fp8_scales_view(packed, B, H, N, d):
     return packed[off: off + 4 * B * H * nb].view(torch.float32).view(B, H, nb)
 
 
-def fp8_prep(x, signs=None, block_rows=128, out=None, rope=None):
+def fp8_prep(x, signs=None, block_rows=128, out=None, rope=None, pow2_scale=False):
     """Random-sign Hadamard (when signs is given) + fp8 e4m3 block quantisation.
 
     x: 16-bit [B,H,N,d] device tensor; signs: int8 [H,d] device tensor of +-1
     or None; block_rows: 128, or 0 for one scale per tensor; rope: None, or
     (style, base, pos0) with style "interleaved" or "half" to apply the
-    rotary embedding first, in the same pass. Returns the packed uint8 tensor
-    (codes then float32 scales) that fwd_fp8 consumes.
+    rotary embedding first, in the same pass; pow2_scale: round the scales up
+    to powers of two (the form fwd_fp8 applies exactly for V). Returns the
+    packed uint8 tensor (codes then float32 scales) that fwd_fp8 consumes.
     """
     B, H, N, d = x.shape
     if out is None:
@@ -319,14 +321,15 @@ def fp8_prep(x, signs=None, block_rows=128, out=None, rope=None):
         _check_device(x, out, signs)
     else:
         _check_device(x, out)
+    code = _dtype_code(x) | (FA_SCALE_POW2 if pow2_scale else 0)
     if rope is None:
         st = fp8_prep_raw(_ptr(x), _ptr(out), _ptr(signs), B, H, N, d, block_rows,
-                          _dtype_code(x), _stream(x.device))
+                          code, _stream(x.device))
     else:
         style, base, pos0 = rope
         _check(style in ROPE_STYLES, f"rope style must be one of {sorted(ROPE_STYLES)}")
         st = fp8_prep_rope_raw(_ptr(x), _ptr(out), _ptr(signs), B, H, N, d, block_rows,
-                               _dtype_code(x), ROPE_STYLES[style], base, pos0, _stream(x.device))
+                               code, ROPE_STYLES[style], base, pos0, _stream(x.device))
     if st != FA_OK:
         raise FaError(st, "fa_fp8_prep")
     return out

@@ -225,6 +225,8 @@ int fa_fwd_decode_noalloc(const void* q, const void* k, const void* v, void* o, 
 int fa_fp8_prep_rope(const void* x, void* x8, const int8_t* signs, int B, int H, int N, int d,
                      int block_rows, int in_dtype, int rope_style, float rope_base, int pos0,
                      void* stream) {
+    const int pow2 = (in_dtype & FA_SCALE_POW2) != 0;
+    in_dtype &= ~FA_SCALE_POW2;
     if (in_dtype != FA_BF16 && in_dtype != FA_F16) return FA_ERR_INVALID_ARG;
     if (!sizes_ok(B, H, N, d)) return FA_ERR_INVALID_ARG;
     if (rope_style != FA_ROPE_NONE && rope_style != FA_ROPE_INTERLEAVED && rope_style != FA_ROPE_HALF)
@@ -248,6 +250,7 @@ int fa_fp8_prep_rope(const void* x, void* x8, const int8_t* signs, int B, int H,
     a.scales_off = fa_fp8_scales_offset(B, H, N, d);
     a.rope_style = rope_style;
     a.mx = fa::kMxNone;
+    a.pow2 = pow2;
     a.rope.pos0 = pos0;
     for (int i = 0; i < 128; ++i)
         a.rope.w[i] = i < d / 2 ? (float)pow((double)rope_base, -2.0 * i / d) : 0.0f;

@@ -126,11 +126,22 @@ __device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
 // thread's rows in flight stay within the register budget; 256 otherwise.
 template <int D> constexpr int quant_threads() { return D == 256 ? 512 : kPrepThreads; }
 
+// Scale of a block with largest magnitude amax: amax / 448 in float32 (1 for
+// an all-zero block), with pow2 rounded up to the next power of two (exact:
+// frexp splits s = m 2^e with m in [0.5, 1); s is already one when m = 0.5).
+// Block scales that are powers of two let the fp8 forward apply V's scales
+// exactly inside the PV product.
+__device__ __forceinline__ float block_scale(float amax, int pow2) {
+    const float s = amax > 0.f ? amax / kE4M3Max : 1.0f;
+    if (!pow2 || __builtin_amdgcn_frexp_mantf(s) == 0.5f) return s;
+    return __builtin_amdgcn_ldexpf(1.0f, __builtin_amdgcn_frexp_expf(s));
+}
+
 template <typename T, int D, bool HAD, int MODE, int ROPE>
 __global__ void __launch_bounds__(quant_threads<D>())
 fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t* __restrict__ signs,
                 float* __restrict__ scales, unsigned* __restrict__ gamax, int N, int H, int nblk,
-                RopeFreqs rf)
+                RopeFreqs rf, int pow2)
 {
     constexpr int NT = quant_threads<D>();
     constexpr int LPR = D / 8;                 // lanes per row
@@ -291,7 +302,7 @@ fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t*
     }
     if (MODE == 2) amax = __uint_as_float(*gamax);
 
-    const float scale = amax > 0.f ? amax / kE4M3Max : 1.0f;
+    const float scale = block_scale(amax, pow2);
     if (MODE == 0 && tid == 0) scales[blockIdx.x] = scale;
     // x / scale. Without the Hadamard this is the IEEE division, so the codes
     // equal those of the same float32 steps exactly. With it, the values
@@ -378,12 +389,9 @@ __global__ void zero_u32_kernel(unsigned* p) { *p = 0u; }
 
 // One workgroup: read the tensor-wide amax first, then fill every slot.
 __global__ void __launch_bounds__(1024) fill_scales_kernel(float* scales, const unsigned* gamax,
-                                                           long long n) {
+                                                           long long n, int pow2) {
     __shared__ float sc;
-    if (threadIdx.x == 0) {
-        const float amax = __uint_as_float(*gamax);
-        sc = amax > 0.f ? amax / kE4M3Max : 1.0f;
-    }
+    if (threadIdx.x == 0) sc = block_scale(__uint_as_float(*gamax), pow2);
     __syncthreads();
     const float s = sc;
     for (long long i = threadIdx.x; i < n; i += blockDim.x) scales[i] = s;
@@ -406,13 +414,13 @@ static hipError_t prep_t(const PrepArgs& a, hipStream_t s) {
     if (a.mx == kMxAlongD) {
         hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 3, ROPE>), dim3((unsigned)grid),
                            dim3(quant_threads<D>()), 0, s, x, a.x8, a.signs, scales, nullptr, a.N, a.H, nblk,
-                           a.rope);
+                           a.rope, a.pow2);
         return hipGetLastError();
     }
     if (a.block_rows != 0) {
         hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 0, ROPE>), dim3((unsigned)grid),
                            dim3(quant_threads<D>()), 0, s, x, a.x8, a.signs, scales, nullptr, a.N, a.H, nblk,
-                           a.rope);
+                           a.rope, a.pow2);
         return hipGetLastError();
     }
     // Per-tensor: the first scale slot serves as the amax accumulator; the
@@ -420,11 +428,11 @@ static hipError_t prep_t(const PrepArgs& a, hipStream_t s) {
     unsigned* gamax = reinterpret_cast<unsigned*>(scales);
     hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(1), 0, s, gamax);
     hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 1, ROPE>), dim3((unsigned)grid), dim3(quant_threads<D>()),
-                       0, s, x, a.x8, a.signs, scales, gamax, a.N, a.H, nblk, a.rope);
+                       0, s, x, a.x8, a.signs, scales, gamax, a.N, a.H, nblk, a.rope, a.pow2);
     hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 2, ROPE>), dim3((unsigned)grid), dim3(quant_threads<D>()),
-                       0, s, x, a.x8, a.signs, scales, gamax, a.N, a.H, nblk, a.rope);
+                       0, s, x, a.x8, a.signs, scales, gamax, a.N, a.H, nblk, a.rope, a.pow2);
     hipLaunchKernelGGL(fill_scales_kernel, dim3(1), dim3(1024), 0, s, scales,
-                       (const unsigned*)gamax, grid);
+                       (const unsigned*)gamax, grid, a.pow2);
     return hipGetLastError();
 }
 

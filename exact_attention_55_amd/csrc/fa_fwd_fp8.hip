@@ -17,14 +17,22 @@
 //  * logits: s = acc * sq_i * sk_j * softmax_scale; in the base-2 domain the
 //    product c_j = sq_i * sk_j * softmax_scale * log2(e) is one scalar per
 //    tile, folded into the fma that feeds exp2;
-//  * P is quantised to e4m3 for the PV MFMA as P' = p * 8 * w_j with
-//    w_j = sv_j / sv_max (sv_max = largest V block scale of the head): the
-//    factor is folded into the exponent, p' = exp2(s*c - m + log2(8 w_j)), so
-//    the V block scale costs no extra VALU work. A tile whose P' sum in some
-//    lane exceeds kBig8 = 384 is redone with its exact maximum, so every P'
-//    is <= 384 < 448 (e4m3 maximum); at the reference maximum a lane's 32
-//    values sum to at most 256, and p >= 2^-9 stays normal;
-//  * the row sum l accumulates the unquantised p (rowsum(P') / (8 w_j));
+//  * P is quantised to e4m3 for the PV MFMA. The V block scale enters as
+//    w_j = sv_j / sv_max (sv_max = largest V block scale of the head), split
+//    as w_j = 2^e_j * f_j / 2 with f_j in [1, 2): the power of two rides in
+//    the PV MFMA's scale byte for V (exact), and P' = 8 p f_j, with the
+//    factor folded into the exponent, p' = exp2(s*c - m + log2(8 f_j)), so
+//    the V block scale costs no extra VALU work. V prepared with
+//    power-of-two block scales (fa_fp8_prep with FA_SCALE_POW2) has f_j = 1:
+//    P' = 8 p, and a row dominated by the key at the reference maximum
+//    (p = 1) takes that key's weight exactly. Other f_j leave every P' with
+//    its e4m3 rounding of 2^-4 relative, including that dominant one. (Folding
+//    all of w_j into P' would also push blocks with small V scales into
+//    e4m3's subnormal range.) A
+//    tile whose P' sum in some lane exceeds kBig8 = 448 (the e4m3 maximum)
+//    is redone with its exact maximum, so every P' is <= 448; at the exact
+//    maximum every P' is below 16, and P' >= 8 p keeps p >= 2^-9 normal;
+//  * the row sum l accumulates the unquantised p (rowsum(P') / (8 f_j));
 //  * epilogue: O = O_acc * sv_max / (8 l).
 // Microscaled inputs (fa_mx_prep: one power-of-two E8M0 scale per 32
 // elements, along d for Q and K, along the sequence for V) take the scaled
@@ -41,7 +49,7 @@ namespace fa {
 
 constexpr float kPScale = 8.0f;     // P multiplier before e4m3 rounding
 constexpr int kPScaleE8M0 = 124;    // 2^-3: the microscaled PV MFMA undoes kPScale
-constexpr float kBig8 = 384.0f;     // per-lane tile sum of P' that forces the exact-maximum path
+constexpr float kBig8 = 448.0f;     // per-lane tile sum of P' that forces the exact-maximum path
 
 #ifndef FA8_CFG_64
 #define FA8_CFG_64 4, 64, 2
@@ -76,6 +84,9 @@ template <int NKB, int SW>
 struct TileScales {
     uint32_t k[NKB][SW];
     uint32_t v[SW];
+    // block-scaled path: E8M0 byte of the power-of-two part of the tile's V
+    // block scale relative to the head's largest (see tile_scales)
+    int vblk = 127;
     __device__ __forceinline__ int kbyte(int kb, int ch) const {
         return (k[kb][ch >> 1] >> (16 * (ch & 1))) & 0xff;
     }
@@ -101,6 +112,14 @@ struct Wave8 {
                                                 int sb) {
         if constexpr (MX) return mfma32_fp8s(a, b, c, sa, sb);
         else return mfma32_fp8(a, b, c);
+    }
+    // P V MFMA of d-block db: microscaled, the V bytes of the block and 2^-3
+    // for P'; block-scaled, the power-of-two part of the tile's V scale
+    // (exact) and unit P'.
+    static __device__ __forceinline__ f32x16 mm_pv(const i32x8& a, const i32x8& b, const f32x16& c,
+                                                   const TS& ts, int db) {
+        if constexpr (MX) return mfma32_fp8s(a, b, c, ts.vbyte(db), kPScaleE8M0);
+        else return mfma32_fp8s(a, b, c, ts.vblk, 127);
     }
 
     f32x16 o[NDB];
@@ -272,7 +291,7 @@ struct Wave8 {
 #pragma unroll
         for (int t = 0; t < NPV; ++t)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) o[db] = mm(vf[t][db], pf[t], o[db], ts.vbyte(db), kPScaleE8M0);
+            for (int db = 0; db < NDB; ++db) o[db] = mm_pv(vf[t][db], pf[t], o[db], ts, db);
     }
 
     // Pipelined step as one instruction stream in program order (every chunk
@@ -331,7 +350,7 @@ struct Wave8 {
             const int v = j + VPD;
             if (v < NVF) vf[v / NDB][v % NDB] = vfrag(vl, va, v / NDB, v % NDB);
             const int t = j / NDB, db = j % NDB;
-            o[db] = mm(vf[t][db], pf[t], o[db], ts.vbyte(db), kPScaleE8M0);
+            o[db] = mm_pv(vf[t][db], pf[t], o[db], ts, db);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -496,20 +515,29 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     };
     auto ktile = [&](int t) -> const char* { return smem + (t & 1) * TB; };
     auto vtile = [&](int t) -> const char* { return smem + (2 + (t & 1)) * TB; };
-    // per-tile scale terms: score multiplier, P exponent offset, l weight
-    auto tile_scales = [&](float& cj, float& bj, float& lscale) {
+    // per-tile scale terms: score multiplier, P exponent offset, l weight;
+    // block-scaled path also the V scale byte of the PV MFMAs (into vt)
+    auto tile_scales = [&](float& cj, float& bj, float& lscale, TS& vt) {
         if constexpr (MX) {
             cj = c;
             bj = 3.0f;                                         // log2(kPScale)
             lscale = 1.0f / kPScale;
         } else {
-            // no division in the loop: 1/sv_max is taken once, 1/(8 w_j) by
-            // the hardware reciprocal; P' and l use the same w_j, so the
-            // normalisation stays consistent to float32 rounding
-            const float wv = tvs * rsvmax;                    // (0, 1]
+            // w = sv_j / sv_max in (0, 1] is split as 2^(e-1) * f with f in
+            // [1, 2): the power of two goes to the PV MFMA's V scale byte
+            // (exact), only f into P' = 8 p f. Folding all of w into P'
+            // would push the weights of blocks with small V scales into
+            // e4m3's subnormal range, where they round coarsely. P' and l
+            // share f, so the normalisation stays consistent. w is held at
+            // >= 2^-126 so the byte stays in range (a block that much
+            // weaker than the head's strongest is weighted 2^-126 instead).
+            const float wv = fmaxf(tvs * rsvmax, 0x1p-126f);
+            const int ex = __builtin_amdgcn_frexp_expf(wv);                 // >= -125
+            const float f = 2.0f * __builtin_amdgcn_frexp_mantf(wv);       // [1, 2)
             cj = cq * tks;
-            bj = __builtin_amdgcn_logf(kPScale * wv);        // log2(8 w_j)
-            lscale = __builtin_amdgcn_rcpf(kPScale * wv);
+            bj = __builtin_amdgcn_logf(kPScale * f);          // log2(8 f)
+            lscale = __builtin_amdgcn_rcpf(kPScale * f);
+            vt.vblk = 126 + ex;                                // 2^(ex - 1)
         }
     };
     // The first tile copies go out before Q's loads, so the two latencies
@@ -594,7 +622,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     read_bs(0);
     if (nfull > 0) {
         float cj, bj, ls;
-        tile_scales(cj, bj, ls);
+        tile_scales(cj, bj, ls, tv);
         W::scores(s, ktile(0), ka, qf, tk, qs);
         st.raise_max(W::tile_max(s, cj));    // first reference maximum: exact
         if constexpr (MX) read_k(tk, 1);
@@ -608,7 +636,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
         load_kv(krs, t + 2, t & 1);
         load_kv(vrs, t + 1, 2 + ((t + 1) & 1));
         float cj, bj, lscale;
-        tile_scales(cj, bj, lscale);
+        tile_scales(cj, bj, lscale, tv);
         st.step(sc, sn, ktile(t + 1), ka, vtile(t), va, qf, cj, bj, lscale, tk, tv, qs);
         wait_vm_all();
         __syncthreads();
@@ -631,7 +659,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     if (nfull > 0) {                          // last full tile
         load_kv(vrs, t + 1, 2 + ((t + 1) & 1));
         float cj, bj, lscale;
-        tile_scales(cj, bj, lscale);
+        tile_scales(cj, bj, lscale, tv);
         st.finish(s, vtile(t), va, cj, bj, lscale, tv);
         wait_vm_all();
         __syncthreads();
@@ -645,7 +673,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
         const int k0 = t * BC;
         if (!CAUSAL || k0 <= q0 + QW - 1) {
             float cj, bj, lscale;
-            tile_scales(cj, bj, lscale);
+            tile_scales(cj, bj, lscale, tv);
             W::scores(s, ktile(t), ka, qf, tk, qs);
             W::template mask<CAUSAL>(s, k0, q0, N, hi, l32);
             if (t == 0) st.raise_max(W::tile_max(s, cj));   // first reference maximum: exact

@@ -53,6 +53,7 @@ struct PrepArgs {
     int rope_style;     // 0 none, 1 interleaved pairs, 2 half pairs
     RopeFreqs rope;
     int mx;             // kMxNone: fp32 block scales; microscaling along d or n
+    int pow2 = 0;       // fp32 block scales rounded up to powers of two
 };
 hipError_t launch_fp8_prep(const PrepArgs& a, hipStream_t s);
 

@@ -58,13 +58,15 @@ enum fa_status {
 
 /* Element types. FA_OUT_F32 may be OR-ed into fa_fwd's dtype: O is then
  * written as float32 instead of the default (the input type for 16-bit
- * inputs, bfloat16 for FP8 inputs). */
+ * inputs, bfloat16 for FP8 inputs). FA_SCALE_POW2 may be OR-ed into
+ * fa_fp8_prep's in_dtype: block scales are rounded up to powers of two. */
 enum fa_dtype {
     FA_F16 = 0,
     FA_BF16 = 1,
     FA_FP8_E4M3 = 2,
     FA_FP8_MX = 3,       /* e4m3 with microscaling (fa_mx_prep): q, k along d, v along N */
-    FA_OUT_F32 = 0x100
+    FA_OUT_F32 = 0x100,
+    FA_SCALE_POW2 = 0x200
 };
 
 /*
@@ -219,10 +221,16 @@ size_t fa_decode_workspace_bytes(int B, int H, int Nq, int d, int num_splits);
  *           block may be shorter); 0: one scale for the whole tensor (the
  *           plain per-tensor baseline; the same scale is stored in every
  *           slot).
- *  in_dtype FA_BF16 or FA_F16.
+ *  in_dtype FA_BF16 or FA_F16, optionally | FA_SCALE_POW2.
  *
  * Per block: amax = max |x|, scale = amax / 448 in float32 (1 when amax is
- * 0), code = e4m3 round-to-nearest-even of x / scale, saturated to +-448.
+ * 0); with FA_SCALE_POW2 that scale is rounded up to the next power of two
+ * (same relative precision on the e4m3 grid, the largest code then lies in
+ * [224, 448]). code = e4m3 round-to-nearest-even of x / scale, saturated to
+ * +-448. Prepare V with FA_SCALE_POW2: the fp8 forward then applies V's
+ * block scales exactly in the PV product, with P rounded to e4m3 as 8 p;
+ * other V scales cost it the extra rounding of 8 p f, f in [1, 2) the
+ * significand of the scale's ratio to the head's largest.
  * Without signs x / scale is the IEEE float32 quotient; with them (rotated
  * rows, whose float32 butterfly rounding already differs from an exact
  * transform) it is x times the rounded 1 / scale, at most one float32 ulp

@@ -40,7 +40,7 @@ from .attention import attention, attention_rows, softmax_probs  # noqa: F401
 from .online import attention_online  # noqa: F401
 from .hadamard import fwht, random_sign_hadamard  # noqa: F401
 from .fp8 import e4m3_round, e4m3_encode, e4m3_decode, E4M3_MAX  # noqa: F401
-from .quant import fp8_quantize, fp8_dequantize, fake_quant_attention  # noqa: F401
+from .quant import fp8_quantize, fp8_dequantize, fake_quant_attention, pow2_ceil_f32  # noqa: F401
 from .backward import attention_backward, attention_delta  # noqa: F401
 from .decode import attention_decode, visible_keys  # noqa: F401
 from .rope import rope, rope_angles, rope_cos_sin, rope_frequencies  # noqa: F401

@@ -15,8 +15,13 @@ Readings (the pages give no block shape, scale rule or rounding):
   block of a head may be shorter;
 * per-tensor mode (block_rows == 0) uses one scale for the whole [B,H,N,d]
   tensor;
-* scale = amax / 448 in float32 (not rounded to a power of two); an all-zero
-  block gets scale 1;
+* scale = amax / 448 in float32; an all-zero block gets scale 1;
+* optionally (pow2, the form used for V) that scale is rounded up to the
+  next power of two, 2^ceil(log2(amax / 448)). e4m3 is a floating-point
+  grid, so a power-of-two scale loses no relative precision on normal values
+  (the largest code then lies in [224, 448]); what it buys is that ratios
+  of block scales are powers of two, which a matrix product applies exactly
+  through an E8M0 scale byte;
 * code = e4m3 round-to-nearest-even, saturating, of x / scale;
 * dequantised value = decode(code) * scale.
 
@@ -48,7 +53,16 @@ def _rotated_f32(x, signs, rope=None):
     return x.astype(np.float32)
 
 
-def fp8_quantize(x, signs=None, block_rows=128, rope=None):
+def pow2_ceil_f32(s):
+    """Smallest power of two >= s for float32 s > 0 (exact, subnormals
+    included), as float32."""
+    s = np.asarray(s, dtype=np.float32)
+    m, e = np.frexp(s)                          # s = m 2^e, m in [0.5, 1)
+    up = np.ldexp(np.float32(1.0), e).astype(np.float32)
+    return np.where(m == 0.5, s, up).astype(np.float32)
+
+
+def fp8_quantize(x, signs=None, block_rows=128, rope=None, pow2=False):
     """Quantise x [B, H, N, d] to e4m3 codes with float32 scales.
 
     signs: [H, d] of +-1 to apply the random-sign Hadamard first (Q and K), or
@@ -56,6 +70,7 @@ def fp8_quantize(x, signs=None, block_rows=128, rope=None):
     block_rows: rows per block (128), or 0 for one scale per tensor.
     rope: None, or (style, base, pos0) to apply the rotary embedding first
     (the fused rotary + Hadamard + quantisation step).
+    pow2: round each scale up to a power of two (pow2_ceil_f32).
     Returns (codes uint8 [B,H,N,d], scales float32 [B,H,ceil(N/block_rows)];
     per-tensor mode returns the same scale in every slot of a
     [B,H,ceil(N/128)] array so both modes have one layout).
@@ -68,13 +83,14 @@ def fp8_quantize(x, signs=None, block_rows=128, rope=None):
     if block_rows == 0:
         amax = np.max(np.abs(y)) if y.size else np.float32(0)
         s = np.float32(amax) / np.float32(E4M3_MAX) if amax > 0 else np.float32(1.0)
-        scales[...] = s
+        scales[...] = pow2_ceil_f32(s) if pow2 else s
     else:
         for j in range(nb):
             blk = np.abs(y[:, :, j * br:(j + 1) * br, :])
             amax = np.max(blk, axis=(2, 3)).astype(np.float32)
             s = amax / np.float32(E4M3_MAX)                       # float32 division
-            scales[:, :, j] = np.where(amax > 0, s, np.float32(1.0))
+            s = np.where(amax > 0, s, np.float32(1.0))
+            scales[:, :, j] = pow2_ceil_f32(s) if pow2 else s
     row_scale = np.repeat(scales, br, axis=2)[:, :, :N]           # [B,H,N]
     q = (y / row_scale[..., None]).astype(np.float32)             # float32 division
     codes = e4m3_encode(q.astype(np.float64))
@@ -90,7 +106,7 @@ def fp8_dequantize(codes, scales, block_rows=128):
 
 
 def fake_quant_attention(q, k, v, signs=None, block_rows=128, causal=False,
-                         scale=None, rope=None):
+                         scale=None, rope=None, v_pow2=True):
     """Exact float64 attention on the dequantised fp8 inputs.
 
     Q and K are rotated by the same random-sign Hadamard (when signs is given)
@@ -100,7 +116,8 @@ def fake_quant_attention(q, k, v, signs=None, block_rows=128, causal=False,
     reference for the fp8 kernel's log-sum-exp (which never sees the rounding
     of P) and a diagnostic for its output. With rope = (style, base, pos0)
     Q and K get the rotary embedding before the rotation and quantisation.
-    Returns (O, LSE, (qc, qs), (kc, ks), (vc, vs)).
+    v_pow2: V's block scales are powers of two (the form the fp8 forward
+    applies exactly). Returns (O, LSE, (qc, qs), (kc, ks), (vc, vs)).
     """
     from .attention import attention
     d = np.asarray(q).shape[-1]
@@ -108,7 +125,7 @@ def fake_quant_attention(q, k, v, signs=None, block_rows=128, causal=False,
         scale = 1.0 / np.sqrt(d)
     qc, qs = fp8_quantize(q, signs, block_rows, rope)
     kc, ks = fp8_quantize(k, signs, block_rows, rope)
-    vc, vs = fp8_quantize(v, None, block_rows)
+    vc, vs = fp8_quantize(v, None, block_rows, pow2=v_pow2)
     o, lse = attention(fp8_dequantize(qc, qs, block_rows),
                        fp8_dequantize(kc, ks, block_rows),
                        fp8_dequantize(vc, vs, block_rows), causal, scale)

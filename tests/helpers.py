@@ -67,18 +67,29 @@ def check_lse(lse, lse_ref, where=""):
     return err
 
 
+def fp8_p_factor(vs, N, block_rows=128):
+    """Per-key factor f_j in [1, 2) by which the block-scaled fp8 forward
+    multiplies 8 p_j before rounding P' to e4m3: the significand part of
+    w_j = sv_j / sv_max (vs: one head's V block scales), w_j = 2^(e_j - 1) f_j,
+    whose power of two the PV product applies exactly. [N] float64."""
+    w = np.maximum(np.asarray(vs, dtype=np.float64) / np.max(vs), 2.0 ** -126)
+    m, _ = np.frexp(w)
+    return np.repeat(2.0 * m, block_rows)[:N]
+
+
 def fp8_p_rounding_bound(q, k, v, b, h, rows, causal, w=None, scale=None):
     """Elementwise bound on |O_gpu - O_dq| for query rows `rows` of head
     (b, h), where O_dq is exact attention of the dequantised inputs q, k, v
     (float64 [B,H,N,d]) and the GPU differs from it only by rounding the
     weights P' = 8 p_j w_j to e4m3 before the PV product (p_j relative to
-    the row maximum, the row sum taken from the unrounded p). An e4m3
-    rounding moves x by at most max(2^-4 x, 2^-10) (half a step of a normal,
-    half the subnormal spacing 2^-9), so
+    the row maximum, the row sum taken from the unrounded p, the factor w_j
+    undone exactly afterwards). An e4m3 rounding moves x by at most
+    max(2^-4 x, 2^-10) (half a step of a normal, half the subnormal spacing
+    2^-9), so
         |dO_ic| <= sum_j max(2^-4 p_j, 2^-13 / w_j) |V_jc| / sum_j p_j.
-    w: per-key weight sv_j / sv_max of the block-scaled path (None: 1, the
-    microscaled path). Returns [len(rows), d]. Taking p against the true row
-    maximum only loosens the subnormal term (the GPU's p are never
+    w: per-key factor of P' (the block-scaled path: fp8_p_factor; None: 1,
+    the microscaled path). Returns [len(rows), d]. Taking p against the true
+    row maximum only loosens the subnormal term (the GPU's p are never
     smaller)."""
     qh = np.asarray(q[b, h], dtype=np.float64)[rows]
     kh = np.asarray(k[b, h], dtype=np.float64)

@@ -1,7 +1,10 @@
 """CPU check of fp8_p_rounding_bound (the elementwise bound the fp8 GPU
-tests use on rows with few keys): a float64 emulation of P' = 8 p w rounded
+tests use on rows with few keys): a float64 emulation of P' = 8 p f rounded
 to e4m3 with the oracle's e4m3 rounding stays within it, and the bound is
-not vacuous (the emulated error reaches a fair part of it)."""
+not vacuous (the emulated error reaches a fair part of it). Also pins the
+split of the V block weight w_j = sv_j / sv_max into an exact power of two
+and f_j in [1, 2) (fp8_p_factor), and that power-of-two V scales (f = 1)
+are what brings the emulated error down on the outlier inputs."""
 
 import numpy as np
 import pytest
@@ -9,12 +12,13 @@ import pytest
 import oracle
 from exact_attention_55_amd.inputs import make_qkv, make_signs, to_f64
 
-from helpers import fp8_p_rounding_bound
+from helpers import fp8_p_factor, fp8_p_rounding_bound
 
 
 def emulate(qd, kd, vd, rows, causal, w):
-    """O with P' = 8 p w rounded to e4m3 (p against the row maximum), the V
-    factor 1/w undone after the product and the row sum from the unrounded p."""
+    """O with P' = 8 p w rounded to e4m3 (p against the row maximum), the
+    factor w undone exactly after the product and the row sum from the
+    unrounded p."""
     q = qd[0, 0][rows]
     k, v = kd[0, 0], vd[0, 0]
     N, d = k.shape
@@ -37,7 +41,7 @@ def test_bound_covers_emulated_rounding(causal, blocks):
     kc, ks = oracle.fp8_quantize(k64, signs, 128)
     vc, vs = oracle.fp8_quantize(v64, None, 128)
     qd, kd, vd = (oracle.fp8_dequantize(c, sc) for c, sc in ((qc, qs), (kc, ks), (vc, vs)))
-    w = np.repeat(vs[0, 0] / vs[0, 0].max(), 128)[:N] if blocks else np.ones(N)
+    w = fp8_p_factor(vs[0, 0], N) if blocks else np.ones(N)
     rows = np.arange(N)
     o_fq, _ = oracle.attention(qd, kd, vd, causal)
     o_em = emulate(qd, kd, vd, rows, causal, w)
@@ -45,6 +49,79 @@ def test_bound_covers_emulated_rounding(causal, blocks):
     bound = fp8_p_rounding_bound(qd, kd, vd, 0, 0, rows, causal, None if not blocks else w)
     assert np.all(err <= bound * (1 + 1e-9) + 1e-12)
     assert np.max(err / np.maximum(bound, 1e-30)) > 0.05
+
+
+def test_p_factor_split():
+    """w_j = 2^(e_j - 1) f_j with f_j in [1, 2) and e_j an integer, blockwise;
+    the largest block has f = 1 (w = 1)."""
+    vs = np.array([3.0, 0.75, 1.5, 0.1, 2.0 ** -140])
+    f = fp8_p_factor(vs, 5 * 128 - 7)
+    assert f.shape == (5 * 128 - 7,)
+    fb = f[::128]
+    w = np.maximum(vs / vs.max(), 2.0 ** -126)
+    e = np.log2(w / fb) + 1
+    assert np.all((fb >= 1) & (fb < 2))
+    np.testing.assert_array_equal(e, np.round(e))
+    assert fb[0] == 1.0 and fb[1] == 1.0 and fb[2] == 1.0
+    assert fb[3] == 0.1 / 3 * 32
+    assert np.all(f[:128] == f[0]) and np.all(f[-121:] == fb[-1])
+
+
+def emulate_tiles(qd, kd, vd, rows, f, tile=64):
+    """Non-causal O as the block-scaled fp8 forward forms it, tile by tile:
+    p against a reference maximum taken from the first key tile, raised to
+    the tile's own maximum (O and l rescaled) only when the tile's P' sum
+    passes the e4m3 maximum 448; P' = 8 p f rounded to e4m3, the factor f
+    undone exactly after the product, l from the unrounded p."""
+    q = qd[0, 0][rows]
+    k, v = kd[0, 0], vd[0, 0]
+    N, d = k.shape
+    s = (q @ k.T) / np.sqrt(d)
+    m = s[:, :tile].max(axis=1)
+    acc = np.zeros((len(rows), d))
+    l = np.zeros(len(rows))
+    for t0 in range(0, N, tile):
+        st, ft = s[:, t0:t0 + tile], f[t0:t0 + tile]
+        big = (8.0 * np.exp(st - m[:, None]) * ft).sum(axis=1) > 448.0
+        mn = np.where(big, np.maximum(m, st.max(axis=1)), m)
+        alpha = np.exp(m - mn)
+        acc *= alpha[:, None]
+        l *= alpha
+        m = mn
+        p = np.exp(st - m[:, None])
+        acc += oracle.e4m3_round(8.0 * p * ft) @ (v[t0:t0 + tile] / ft[:, None])
+        l += p.sum(axis=1)
+    return acc / (8.0 * l[:, None])
+
+
+def test_pow2_v_scales_beat_arbitrary_ones():
+    """On the outlier inputs at the workload's head size, the tile-wise
+    emulation with V's block scales rounded to powers of two (P' = 8 p) is
+    much closer to its fake-quant attention than with amax / 448 scales
+    (P' = 8 p f, f in [1, 2): rows dominated by one key lose that key's
+    exactness), and splitting the weight (f in P', power of two exact) is no
+    worse than folding all of w into P'."""
+    N, d = 4096, 128
+    q, k, v = make_qkv(1, 1, N, d, seed=4, dtype="bf16", outliers=True)
+    q64, k64, v64 = to_f64(q), to_f64(k), to_f64(v)
+    signs = make_signs(1, d, 4)
+    qc, qs = oracle.fp8_quantize(q64, signs, 128)
+    kc, ks = oracle.fp8_quantize(k64, signs, 128)
+    qd, kd = oracle.fp8_dequantize(qc, qs), oracle.fp8_dequantize(kc, ks)
+    rows = np.arange(0, N, 4)
+    err = {}
+    for p2 in (True, False):
+        vc, vs = oracle.fp8_quantize(v64, None, 128, pow2=p2)
+        vd = oracle.fp8_dequantize(vc, vs)
+        o_fq, _ = oracle.attention_rows(qd, kd, vd, 0, 0, rows, False)
+        f = fp8_p_factor(vs[0, 0], N)
+        assert np.all(f == 1.0) == p2
+        err["pow2" if p2 else "split"] = np.sqrt(np.mean((emulate_tiles(qd, kd, vd, rows, f) - o_fq) ** 2))
+        if not p2:
+            w = np.repeat(vs[0, 0] / vs[0, 0].max(), 128)[:N]
+            err["fold"] = np.sqrt(np.mean((emulate_tiles(qd, kd, vd, rows, w) - o_fq) ** 2))
+    assert err["pow2"] < 0.6 * err["split"], err
+    assert err["split"] <= 1.02 * err["fold"], err
 
 
 def _bf16(x):

@@ -5,8 +5,9 @@ Codec: against hand-derived points of the OCP E4M3 encoding
 float8_e4m3fn (a library routine that rounds to nearest even but does not
 saturate, so inputs are clamped to +-448 first).
 
-Quantiser and fake-quant attention: per-block scale = amax / 448, error within
-half an e4m3 step, exactness on inputs that already lie on the grid, and the
+Quantiser and fake-quant attention: per-block scale = amax / 448 (or that
+rounded up to a power of two, checked against an independent 4-bit rounding),
+error within half an e4m3 step, exactness on inputs that already lie on the grid, and the
 qualitative claim of "FlashAttention-3: Fast & Accurate Attention with
 Asynchrony & Low-Precision", section "Incoherent Processing for FP8 Accuracy":
 on inputs with 0.1% large outliers the random-sign Hadamard with block scales
@@ -97,6 +98,48 @@ def test_zero_block_and_per_tensor():
     assert scales[0, 1, 0] == np.float32(3.0) / np.float32(448)
     c2, s2 = oracle.fp8_quantize(x, None, 0)
     assert np.all(s2 == s2.flat[0]) and s2.flat[0] == np.float32(3.0) / np.float32(448)
+
+
+def test_pow2_ceil():
+    """Smallest power of two at or above s, on powers of two, their float32
+    neighbours and float32 subnormals."""
+    f = oracle.pow2_ceil_f32
+    one_up = np.nextafter(np.float32(1), np.float32(2))
+    assert f(np.float32(1.0)) == 1.0 and f(one_up) == 2.0
+    assert f(np.nextafter(np.float32(1), np.float32(0))) == 1.0
+    assert f(np.float32(0.75)) == 1.0 and f(np.float32(3 / 448)) == np.float32(2.0 ** -7)
+    sub = np.float32(3 * 2.0 ** -140)
+    assert f(sub) == np.float32(2.0 ** -138)
+    assert f(np.float32(2.0 ** -149)) == np.float32(2.0 ** -149)
+
+
+def test_pow2_scales_round_like_a_4bit_float():
+    """With power-of-two block scales x / scale is exact, so each
+    dequantised value is x rounded to 4 significant bits (round half to
+    even) where x / scale >= 2^-6, and to multiples of 2^-9 scale below: an
+    independent rounding of x written from that definition. Scales: powers
+    of two with amax / 448 <= scale < 2 amax / 448; an all-zero block gets 1."""
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((1, 2, 300, 64)) * np.exp2(rng.integers(-12, 12, (1, 2, 300, 1))))
+    x = x.astype(np.float32).astype(np.float64)
+    x[0, 1, 256:] = 0.0
+    codes, scales = oracle.fp8_quantize(x, None, 128, pow2=True)
+    m, _ = np.frexp(scales)
+    assert np.all(m == 0.5)
+    for j in range(3):
+        amax = np.max(np.abs(x[:, :, j * 128:(j + 1) * 128].astype(np.float32)), axis=(2, 3))
+        q = amax / np.float32(448)
+        live = amax > 0
+        assert np.all(scales[:, :, j][live] >= q[live]) and np.all(scales[:, :, j][live] < 2 * q[live])
+        assert np.all(scales[:, :, j][~live] == 1.0)
+    rs = np.repeat(scales, 128, axis=2)[:, :, :300, None].astype(np.float64)
+    y = x / rs
+    e = np.floor(np.log2(np.maximum(np.abs(y), 2.0 ** -6)))
+    step = np.exp2(np.maximum(e, -6) - 3)
+    ref = np.round(y / step) * step * rs
+    np.testing.assert_array_equal(oracle.fp8_dequantize(codes, scales, 128), ref)
+    c0, s0 = oracle.fp8_quantize(x, None, 0, pow2=True)
+    assert np.all(s0 == s0.flat[0]) and np.frexp(s0.flat[0])[0] == 0.5
 
 
 def test_grid_inputs_quantise_exactly():
