@@ -300,7 +300,8 @@ def build_next_legs(dev):
     V along the sequence, GB/s; the forward on its output, non-causal and
     causal); the block-scaled fp8 forward, causal; and the decode-shaped
     forward on its two workloads, in GB/s of the bytes it must move (K and V
-    of every sequence's keys, Q, O, LSE)."""
+    of every sequence's keys, Q, O, LSE); and, as an ablation, the pipelined
+    16-bit kernel on the headline workload."""
     legs = []
     c = CONFIGS["b8h16n2k_d128"]
     B, H, N, d = c["B"], c["H"], c["N"], c["d"]
@@ -316,6 +317,18 @@ def build_next_legs(dev):
         name = "bf16_bwd_b8h16n2k_d128" + ("_causal" if causal else "")
         legs.append(Leg(name, lambda o=o, lse=lse, causal=causal: fa.bwd(
             q, k, v, o, lse, do, causal, grads=grads, delta=delta), fl))
+    # the 64-rows-per-wave pipelined kernel (FA_FWD_PIPELINED) on the 16-bit
+    # headline workload, beside the default kernel the step times
+    for cfg in ("b2h16n8k_d128", "b2h16n8k_d128_causal"):
+        cp = CONFIGS[cfg]
+        qp, kp, vp = (t.to(dev) for t in make_qkv(**cp))
+        op = torch.empty_like(qp)
+        lp = torch.empty(qp.shape[:3], dtype=torch.float32, device=dev)
+        keep += [qp, kp, vp, op, lp]
+        legs.append(Leg("bf16_fwd_" + cfg + "_pipelined",
+                        lambda qp=qp, kp=kp, vp=vp, op=op, lp=lp, causal=cp["causal"]:
+                        fa.fwd(qp, kp, vp, causal, out=op, lse=lp, pipelined=True),
+                        attention_flops(cp["B"], cp["H"], cp["N"], cp["d"], cp["causal"])))
     c8 = CONFIGS[FP8]
     B8, H8, N8, d8 = c8["B"], c8["H"], c8["N"], c8["d"]
     q8, k8, v8 = (t.to(dev) for t in make_qkv(**c8))

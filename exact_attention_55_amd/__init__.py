@@ -12,7 +12,7 @@ arithmetic of its own.
 from ._lib import (  # noqa: F401
     FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_TOO_LARGE,
     FA_NOALLOC_SCRATCH_BYTES, decode_noalloc_raw,
-    FA_F16, FA_BF16, FA_FP8_E4M3, FA_OUT_F32, FA_SCALE_POW2,
+    FA_F16, FA_BF16, FA_FP8_E4M3, FA_OUT_F32, FA_SCALE_POW2, FA_FWD_PIPELINED,
     FaError, lib, lib_path, fwd, fwd_raw, bwd, bwd_raw, fwd_fp8, fp8_prep, fp8_prep_raw, fp8_packed_bytes,
     fp8_alloc_packed, fp8_scales_view, fp8_codes_view, status_string,
     fwd_decode, decode_raw, decode_splits, decode_workspace_bytes,

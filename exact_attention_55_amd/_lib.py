@@ -18,6 +18,7 @@ FA_F16, FA_BF16, FA_FP8_E4M3, FA_FP8_MX = 0, 1, 2, 3
 FA_MX_ALONG_D, FA_MX_ALONG_N = 0, 1
 FA_OUT_F32 = 0x100
 FA_SCALE_POW2 = 0x200
+FA_FWD_PIPELINED = 0x400
 FA_ROPE_NONE, FA_ROPE_INTERLEAVED, FA_ROPE_HALF = 0, 1, 2
 ROPE_STYLES = {"interleaved": FA_ROPE_INTERLEAVED, "half": FA_ROPE_HALF}
 
@@ -172,11 +173,13 @@ def _dtype_code(t):
     raise FaError(FA_ERR_UNSUPPORTED, f"dtype {t.dtype}")
 
 
-def fwd(q, k, v, causal=False, softmax_scale=None, out=None, lse=None, out_f32=False):
+def fwd(q, k, v, causal=False, softmax_scale=None, out=None, lse=None, out_f32=False,
+        pipelined=False):
     """Attention forward on 16-bit [B,H,N,d] device tensors.
 
     Returns (o, lse): o has q's dtype (float32 with out_f32=True), lse is
-    float32 [B,H,N].
+    float32 [B,H,N]. pipelined: at d = 128, run the 64-rows-per-wave kernel
+    with the in-wave pipeline instead of the default one.
     """
     B, H, N, d = q.shape
     if softmax_scale is None:
@@ -189,6 +192,8 @@ def fwd(q, k, v, causal=False, softmax_scale=None, out=None, lse=None, out_f32=F
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if out_f32:
         code |= FA_OUT_F32
+    if pipelined:
+        code |= FA_FWD_PIPELINED
     _check(q.dim() == 4 and k.shape == q.shape and v.shape == q.shape, "q, k, v shapes differ")
     _check(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v dtypes differ")
     _check(out.shape == q.shape and out.dtype == odt, "bad output tensor")

@@ -58,7 +58,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
            int d, int causal, float softmax_scale, int dtype, void* stream) {
     const int base = dtype & 0xff;
     const int flags = dtype & ~0xff;
-    if ((flags & ~FA_OUT_F32) != 0) return FA_ERR_INVALID_ARG;
+    if ((flags & ~(FA_OUT_F32 | FA_FWD_PIPELINED)) != 0) return FA_ERR_INVALID_ARG;
     if (base != FA_F16 && base != FA_BF16 && base != FA_FP8_E4M3 && base != FA_FP8_MX)
         return FA_ERR_INVALID_ARG;
     if (!sizes_ok(B, H, N, d)) return FA_ERR_INVALID_ARG;
@@ -83,6 +83,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     a.out_f32 = (flags & FA_OUT_F32) != 0;
     a.scales_off = fa_fp8_scales_offset(B, H, N, d);
     a.mx = base == FA_FP8_MX;
+    a.pipelined = (flags & FA_FWD_PIPELINED) != 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();   // do not report an earlier, unrelated error
     if (fp8) return from_hip(fa::launch_fwd_fp8(a, s));

@@ -898,18 +898,13 @@ static hipError_t launch_ty(const FwdArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-// d = 128 goes to the 64-rows-per-wave pipelined kernel (fa_fwd16_pipe.hip)
-// when its grid of 256-row workgroups (one per CU) fills the GPU at least
-// kPipeMinBlocks / 256 times over; smaller problems keep the 128-row
-// workgroups of this file's kernel (two per CU), which spread them further.
-#ifndef FA16_PIPE
-#define FA16_PIPE 1
-#endif
-constexpr long long kPipeMinBlocks = 256;
-
+// d = 128 with FA_FWD_PIPELINED goes to the 64-rows-per-wave pipelined
+// kernel (fa_fwd16_pipe.hip, one wave per SIMD). It halves the LDS fragment
+// reads per MFMA but a single wave issues the softmax alone; on MI355X it
+// measured slower than this file's kernel (two waves per SIMD) on most
+// shapes, so it is a selectable variant rather than the default.
 hipError_t launch_fwd16(const FwdArgs& a, bool bf16, hipStream_t s) {
-    if (FA16_PIPE && a.d == 128 && (long long)a.B * a.H * ((a.N + 255) / 256) >= kPipeMinBlocks)
-        return launch_fwd16_pipe(a, bf16, s);
+    if (a.pipelined && a.d == 128) return launch_fwd16_pipe(a, bf16, s);
     return bf16 ? launch_ty<__bf16>(a, s) : launch_ty<_Float16>(a, s);
 }
 

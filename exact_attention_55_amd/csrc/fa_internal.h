@@ -25,6 +25,7 @@ struct FwdArgs {
     // FP8 only: byte offset of the scale array inside q/k/v
     size_t scales_off;
     bool mx = false;    // FP8: microscaled inputs (E8M0 scales per 32 elements)
+    bool pipelined = false;   // 16-bit, d = 128: the 64-rows-per-wave pipelined kernel
 };
 
 // 16-bit forward (bf16 = true: bfloat16, else float16).

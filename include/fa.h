@@ -58,7 +58,11 @@ enum fa_status {
 
 /* Element types. FA_OUT_F32 may be OR-ed into fa_fwd's dtype: O is then
  * written as float32 instead of the default (the input type for 16-bit
- * inputs, bfloat16 for FP8 inputs). FA_SCALE_POW2 may be OR-ed into
+ * inputs, bfloat16 for FP8 inputs). FA_FWD_PIPELINED may be OR-ed into
+ * fa_fwd's dtype: 16-bit inputs at d = 128 run the 64-rows-per-wave kernel
+ * that overlaps the next block's score MFMAs, this block's exponentials and
+ * the previous block's PV MFMAs inside one wave (same results up to
+ * rounding; ignored for other inputs). FA_SCALE_POW2 may be OR-ed into
  * fa_fp8_prep's in_dtype: block scales are rounded up to powers of two. */
 enum fa_dtype {
     FA_F16 = 0,
@@ -66,7 +70,8 @@ enum fa_dtype {
     FA_FP8_E4M3 = 2,
     FA_FP8_MX = 3,       /* e4m3 with microscaling (fa_mx_prep): q, k along d, v along N */
     FA_OUT_F32 = 0x100,
-    FA_SCALE_POW2 = 0x200
+    FA_SCALE_POW2 = 0x200,
+    FA_FWD_PIPELINED = 0x400
 };
 
 /*
@@ -88,7 +93,7 @@ enum fa_dtype {
  *  softmax_scale  finite and > 0 (usually 1/sqrt(d)); multiplies S before the
  *           softmax.
  *  dtype    FA_F16 | FA_BF16 | FA_FP8_E4M3 | FA_FP8_MX, optionally
- *           | FA_OUT_F32.
+ *           | FA_OUT_F32 and (16-bit inputs) | FA_FWD_PIPELINED.
  *  stream   hipStream_t or NULL.
  *
  * q, k, v must be 16-byte aligned (256-byte for the FP8 dtypes). Returns FA_OK, FA_ERR_INVALID_ARG,

@@ -63,6 +63,7 @@ def fwd(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=7), fa.FA_ERR_INVALID_ARG),
     (dict(dtype=fa.FA_BF16 | 0x200), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=fa.FA_BF16 | fa.FA_FWD_PIPELINED | 0x800), fa.FA_ERR_INVALID_ARG),
     (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(d=32), fa.FA_ERR_UNSUPPORTED),
     # one head's K/V past 2^31 - 2^16 - 1 bytes (31-bit buffer offsets)
@@ -97,6 +98,9 @@ def prep(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(in_dtype=fa.FA_FP8_E4M3), fa.FA_ERR_INVALID_ARG),
+    (dict(in_dtype=fa.FA_FP8_E4M3 | fa.FA_SCALE_POW2), fa.FA_ERR_INVALID_ARG),
+    (dict(in_dtype=fa.FA_BF16 | fa.FA_SCALE_POW2, block_rows=64), fa.FA_ERR_UNSUPPORTED),
+    (dict(in_dtype=fa.FA_BF16 | fa.FA_OUT_F32), fa.FA_ERR_INVALID_ARG),
     (dict(block_rows=64), fa.FA_ERR_UNSUPPORTED),
     (dict(d=80), fa.FA_ERR_UNSUPPORTED),
     (dict(N=-5), fa.FA_ERR_INVALID_ARG),
@@ -236,6 +240,7 @@ def mx(**kw):
     (dict(axis=2), fa.FA_ERR_INVALID_ARG),
     (dict(axis=fa.FA_MX_ALONG_N, signs=FAKE), fa.FA_ERR_INVALID_ARG),   # no Hadamard for V
     (dict(in_dtype=fa.FA_FP8_MX), fa.FA_ERR_INVALID_ARG),
+    (dict(in_dtype=fa.FA_BF16 | fa.FA_SCALE_POW2), fa.FA_ERR_INVALID_ARG),   # E8M0 scales already
     (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(N=-1), fa.FA_ERR_INVALID_ARG),
     (dict(x8=FAKE + 64), fa.FA_ERR_INVALID_ARG),

@@ -29,9 +29,10 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run(q, k, v, causal, out_f32, scale=None):
+def run(q, k, v, causal, out_f32, scale=None, pipelined=False):
     qd, kd, vd = (t.to(DEV) for t in (q, k, v))
-    o, lse = fa.fwd(qd, kd, vd, causal=causal, softmax_scale=scale, out_f32=out_f32)
+    o, lse = fa.fwd(qd, kd, vd, causal=causal, softmax_scale=scale, out_f32=out_f32,
+                    pipelined=pipelined)
     torch.cuda.synchronize()
     return o.float().cpu().numpy(), lse.cpu().numpy()
 
@@ -201,8 +202,7 @@ def test_few_keys_bf16(N, causal, d):
     check_lse(lse, lse_ref)
 
 
-# d = 128 shapes whose grid of 256-row workgroups is large enough for the
-# launch to pick the 64-rows-per-wave pipelined kernel (B*H*ceil(N/256) >= 256)
+# d = 128 shapes for the 64-rows-per-wave pipelined kernel (FA_FWD_PIPELINED)
 PIPE = [
     # B, H, N, causal, dtype
     (4, 64, 300, False, "bf16"),          # ragged query and key tiles
@@ -223,11 +223,11 @@ def test_pipe_d128_full_compare(B, H, N, causal, dt):
     say(f"pipe d=128 B={B} H={H} N={N} causal={causal} {dt}")
     q, k, v = make_qkv(B, H, N, 128, seed=200 + N, dtype=dt)
     o_ref, lse_ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), causal)
-    o32, lse = run(q, k, v, causal, True)
+    o32, lse = run(q, k, v, causal, True, pipelined=True)
     mx, rmse = check_o(o32, o_ref, "f32", "(fp32 out)")
     check_lse(lse, lse_ref)
     say(f"pipe d=128 B={B} H={H} N={N} causal={causal} {dt}: max-abs {mx:.2e} RMSE {rmse:.2e}")
-    o16, lse16 = run(q, k, v, causal, False)
+    o16, lse16 = run(q, k, v, causal, False, pipelined=True)
     check_o(o16, o_ref, dt, "(16-bit out)")
     check_lse(lse16, lse_ref)
 
@@ -250,7 +250,7 @@ def test_pipe_d128_large_logits_and_constant_v(dt):
     q64, k64, v64 = to_f64(q), to_f64(k), to_f64(v)
     for causal in (False, True):
         o_ref, lse_ref = oracle.attention(q64, k64, v64, causal, 0.5)
-        o, lse = run(q, k, v, causal, True, scale=0.5)
+        o, lse = run(q, k, v, causal, True, scale=0.5, pipelined=True)
         check_lse(lse, lse_ref)
         if dt == "fp16":
             check_o(o, o_ref, "f32")
@@ -266,7 +266,7 @@ def test_pipe_d128_large_logits_and_constant_v(dt):
         say(f"pipe large logits bf16 causal={causal}: max-abs {mx:.2e} RMSE {rmse:.2e}, "
             f"worst error / bound {worst:.2f}")
     vc = torch.full_like(q, 0.7109375)
-    o, _ = run(q, k, vc, False, True, scale=0.5)
+    o, _ = run(q, k, vc, False, True, scale=0.5, pipelined=True)
     assert np.max(np.abs(o - 0.7109375)) <= 2e-6
 
 
