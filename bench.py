@@ -300,7 +300,8 @@ def build_next_legs(dev):
     V along the sequence, GB/s; the forward on its output, non-causal and
     causal); the block-scaled fp8 forward, causal; and the decode-shaped
     forward on its two workloads, in GB/s of the bytes it must move (K and V
-    of every sequence's keys, Q, O, LSE); and, as an ablation, the pipelined
+    of every sequence's keys, Q, O, LSE); the backward at d = 256 on the
+    B=2 H=8 N=16384 causal workload; and, as an ablation, the pipelined
     16-bit kernel on the headline workload."""
     legs = []
     c = CONFIGS["b8h16n2k_d128"]
@@ -329,6 +330,17 @@ def build_next_legs(dev):
                         lambda qp=qp, kp=kp, vp=vp, op=op, lp=lp, causal=cp["causal"]:
                         fa.fwd(qp, kp, vp, causal, out=op, lse=lp, pipelined=True),
                         attention_flops(cp["B"], cp["H"], cp["N"], cp["d"], cp["causal"])))
+    # the backward at d = 256 on the long-sequence d = 256 forward workload
+    c4 = CONFIGS["b2h8n16k_d256_causal"]
+    q4, k4, v4 = (t.to(dev) for t in make_qkv(**c4))
+    do4 = make_dout(c4["B"], c4["H"], c4["N"], c4["d"], c4["seed"] + 500, c4["dtype"]).to(dev)
+    o4, l4 = fa.fwd(q4, k4, v4, True)
+    g4 = tuple(torch.empty_like(q4) for _ in range(3))
+    dl4 = torch.empty((2,) + tuple(q4.shape[:3]), dtype=torch.float32, device=dev)
+    keep += [q4, k4, v4, do4, o4, l4, g4, dl4]
+    legs.append(Leg("bf16_bwd_b2h8n16k_d256_causal", lambda: fa.bwd(
+        q4, k4, v4, o4, l4, do4, True, grads=g4, delta=dl4),
+        2.5 * attention_flops(c4["B"], c4["H"], c4["N"], c4["d"], True)))
     c8 = CONFIGS[FP8]
     B8, H8, N8, d8 = c8["B"], c8["H"], c8["N"], c8["d"]
     q8, k8, v8 = (t.to(dev) for t in make_qkv(**c8))

@@ -25,10 +25,12 @@ OUT = os.path.join(HERE, "libfa.so")
 BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["fa_api.hip", "fa_fwd16.hip", "fa_fwd16_pipe.hip", "fa_fwd_fp8.hip", "fa_fp8_prep.hip",
            "fa_bwd16.hip", "fa_decode16.hip"]
-# Per-source flags. fa_fwd16_pipe.hip: the compiler's MFMA builtins write
-# vector registers (the score tiles feed the exponentials directly), while
-# the file's P V MFMAs keep O in the accumulation registers through asm.
-EXTRA_FLAGS = {"fa_fwd16_pipe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source flags. fa_fwd16_pipe.hip and fa_bwd16.hip: the compiler's MFMA
+# builtins write vector registers (score tiles feed the exponentials
+# directly), while the long-lived accumulators (O of the pipelined forward,
+# the gradients at d = 256) stay in the accumulation registers through asm.
+EXTRA_FLAGS = {"fa_fwd16_pipe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "fa_bwd16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

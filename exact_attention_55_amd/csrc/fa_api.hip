@@ -99,7 +99,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
     if (base != FA_F16 && base != FA_BF16) return FA_ERR_INVALID_ARG;
     if (!sizes_ok(B, H, N, d)) return FA_ERR_INVALID_ARG;
     if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return FA_ERR_INVALID_ARG;
-    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
     if ((long long)B * H > 0x7fffffffLL / 2) return FA_ERR_UNSUPPORTED;
     if ((long long)N * d * 2 > kMaxHeadBytes) return FA_ERR_UNSUPPORTED;
     if (B == 0 || H == 0 || N == 0) return FA_OK;

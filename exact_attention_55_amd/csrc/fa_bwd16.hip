@@ -27,6 +27,14 @@
 // Tiles go global -> LDS by buffer loads (see fa_fwd16.hip); the LDS
 // swizzle, the row permutation of the A operand (krow_perm) and the lane
 // layouts are those of the forward.
+// At d = 256 both gradient kernels run one wave per SIMD and keep their
+// gradient accumulators (dQ^T: 128 registers; dK^T and dV^T: 256) in the
+// accumulation registers for the whole kernel, through asm MFMAs
+// (mfma_acc); the score and dP MFMAs are compiler builtins that write vector
+// registers (this file is built with the VGPR form of the MFMA forced), so
+// the exponentials read them directly. Inputs of an asm MFMA written by
+// vector instructions (dS, P) pass through a two-wait-state barrier first,
+// and the epilogue waits out the last MFMA's latency before reading.
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -86,6 +94,32 @@ struct Tile {
         return __builtin_bit_cast(X8, u32x4{lo[0], lo[1], hi4[0], hi4[1]});
     }
 };
+
+// Waves per SIMD: two at d <= 128; one at d = 256, where the two d x 32
+// gradient accumulators of the key-parallel kernel alone take 256 of a
+// lane's 512 registers (the compiler keeps them in the accumulation
+// registers) and the query-parallel kernel holds Q^T and dO^T fragments of
+// 256 columns.
+template <int D> constexpr int bwd_occupancy() { return D == 256 ? 1 : 2; }
+// Fragments of a d-long operand loaded per batch before their MFMAs: the
+// whole operand at d <= 128, a quarter of it at d = 256 (bounds the live
+// registers).
+template <int D> constexpr int bwd_batch() { return D == 256 ? D / 64 : D / 16; }
+
+// acc += A B for a gradient accumulator: asm into the accumulation registers
+// at d = 256 (see the file header), the builtin elsewhere.
+template <int D, typename X8>
+__device__ __forceinline__ void grad_mfma(f32x16& acc, const X8& a, const X8& b) {
+    if constexpr (D == 256) mfma_acc(acc, a, b);
+    else acc = mfma32(a, b, acc);
+}
+template <int D, int N>
+__device__ __forceinline__ void grad_settle(f32x16 (&acc)[N]) {
+    if constexpr (D == 256) {
+#pragma unroll
+        for (int i = 0; i + 3 < N; i += 4) acc_settle(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
+    }
+}
 
 // Global -> LDS tile copies for a [rows, D] tile of one head (see fa_fwd16).
 template <int D, int TROWS, int NW>
@@ -166,18 +200,21 @@ __global__ void __launch_bounds__(256) bwd_delta_kernel(const T* __restrict__ O,
 }
 
 // ---------------------------------------------------------------------------
-// dQ: one workgroup = 4 waves x 32 query rows; key tiles of 64.
+// dQ: one workgroup = 4 waves x 32 query rows; key tiles of 64 (32 at
+// d = 256, so that the score and dP tiles fit beside the fragments).
 template <typename T, int D, bool CAUSAL, bool OUT_F32>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256, bwd_occupancy<D>())
 bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
               const T* __restrict__ dOg, const float* __restrict__ LSEg, const float* __restrict__ Dg,
               void* __restrict__ dQg, int N, int num_qtiles, int num_blocks, float c, float scale)
 {
     using X8 = typename Bw<T>::x8;
     using TL = Tile<T, D>;
-    constexpr int NW = 4, QW = 32, BR = NW * QW, BC = 64;
+    constexpr int NW = 4, QW = 32, BR = NW * QW, BC = D == 256 ? 32 : 64;
     constexpr int NCH = TL::NCH, NDB = TL::NDB, RB = TL::RB;
     constexpr int NKB = BC / 32, NPV = BC / 16;
+    constexpr int KB = bwd_batch<D>();       // K / V fragments per batch
+    constexpr int TB4 = NDB < 4 ? NDB : 4;   // K^T fragments per batch
     using CP = Copier<D, BC, NW>;
     constexpr int TB = CP::TB;
     __shared__ __attribute__((aligned(1024))) char smem[4 * TB];   // K: slots 0,1; V: 2,3
@@ -236,37 +273,41 @@ bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __res
     for (int t = 0; t < nkt; ++t) {
         load_kv(t + 1);
         const int k0 = t * BC;
-        if (!CAUSAL || k0 <= q0 + QW - 1) {
+        // A wave whose rows see none of the tile's keys skips it, except at
+        // d = 256: there a branch around the accumulating asm MFMAs splits
+        // the accumulators' register live ranges (copies every tile), so the
+        // wave runs the tile fully masked instead (at most three tiles).
+        if (D == 256 || !CAUSAL || k0 <= q0 + QW - 1) {
             // S^T = K Q^T and dP^T = V dO^T (lane = query, registers = keys)
             f32x16 s[NKB], dp[NKB];
-            {
-                X8 kf[NKB][NCH];
 #pragma unroll
-                for (int ch = 0; ch < NCH; ++ch)
+            for (int kb = 0; kb < NKB; ++kb) s[kb] = dp[kb] = f32x16{};
 #pragma unroll
-                    for (int kb = 0; kb < NKB; ++kb) kf[kb][ch] = tl.kfrag(ktile(t), ch, kb);
+            for (int c0 = 0; c0 < NCH; c0 += KB) {
+                X8 kf[NKB][KB];
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+                for (int ch = 0; ch < KB; ++ch)
 #pragma unroll
-                for (int ch = 0; ch < NCH; ++ch)
+                    for (int kb = 0; kb < NKB; ++kb) kf[kb][ch] = tl.kfrag(ktile(t), c0 + ch, kb);
 #pragma unroll
-                    for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma32(kf[kb][ch], qf[ch], s[kb]);
+                for (int ch = 0; ch < KB; ++ch)
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma32(kf[kb][ch], qf[c0 + ch], s[kb]);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
-            {
-                X8 vf[NKB][NCH];
 #pragma unroll
-                for (int ch = 0; ch < NCH; ++ch)
+            for (int c0 = 0; c0 < NCH; c0 += KB) {
+                X8 vf[NKB][KB];
 #pragma unroll
-                    for (int kb = 0; kb < NKB; ++kb) vf[kb][ch] = tl.kfrag(vtile(t), ch, kb);
+                for (int ch = 0; ch < KB; ++ch)
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) dp[kb] = f32x16{};
+                    for (int kb = 0; kb < NKB; ++kb) vf[kb][ch] = tl.kfrag(vtile(t), c0 + ch, kb);
 #pragma unroll
-                for (int ch = 0; ch < NCH; ++ch)
+                for (int ch = 0; ch < KB; ++ch)
 #pragma unroll
-                    for (int kb = 0; kb < NKB; ++kb) dp[kb] = mfma32(vf[kb][ch], of[ch], dp[kb]);
+                    for (int kb = 0; kb < NKB; ++kb) dp[kb] = mfma32(vf[kb][ch], of[c0 + ch], dp[kb]);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
             // dS^T = P^T (dP^T - D), P^T = exp2(c S^T - lse2); masked keys give 0
             const bool masked = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0);
             X8 dsf[NPV];
@@ -293,20 +334,27 @@ bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __res
                     dsf[2 * kb + h] = X8{w[0][0], w[0][1], w[1][0], w[1][1],
                                          w[2][0], w[2][1], w[3][0], w[3][1]};
                 }
+            if constexpr (D == 256) {
+#pragma unroll
+                for (int tt = 0; tt < NPV; ++tt) asm volatile("s_nop 1" : "+v"(dsf[tt]));
+            }
             __builtin_amdgcn_sched_barrier(0);
             // dQ^T += K^T dS^T
 #pragma unroll
-            for (int tt = 0; tt < NPV; ++tt) {
-                X8 kt[NDB];
+            for (int tt = 0; tt < NPV; ++tt)
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) kt[db] = tl.tfrag(ktile(t), tt, db);
+                for (int d0 = 0; d0 < NDB; d0 += TB4) {
+                    X8 kt[TB4];
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) acc[db] = mfma32(kt[db], dsf[tt], acc[db]);
-            }
+                    for (int db = 0; db < TB4; ++db) kt[db] = tl.tfrag(ktile(t), tt, d0 + db);
+#pragma unroll
+                    for (int db = 0; db < TB4; ++db) grad_mfma<D>(acc[d0 + db], kt[db], dsf[tt]);
+                }
         }
         wait_vm_all();
         __syncthreads();
     }
+    grad_settle<D>(acc);
     if (row < N) store_rowT<T, D, OUT_F32>(dQg, head + (size_t)row * D, acc, scale, hi);
 }
 
@@ -318,7 +366,7 @@ bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __res
 // accumulator from -D (read from LDS into the accumulator registers), so
 // P = exp2(c * S') and dS = P * dP' need no per-row registers.
 template <typename T, int D, bool CAUSAL, bool OUT_F32>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256, bwd_occupancy<D>())
 bwd_dkv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
                const T* __restrict__ dOg, const float* __restrict__ Cg, void* __restrict__ dKg,
                void* __restrict__ dVg, int N, long long rows, int num_ktiles, int num_blocks,
@@ -329,6 +377,9 @@ bwd_dkv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __re
     constexpr int NW = 4, KW = 32, BK = NW * KW, BQ = 32;
     constexpr int NCH = TL::NCH, NDB = TL::NDB, RB = TL::RB;
     constexpr int NPV = BQ / 16;
+    // fragments per batch (d = 256: 2, the d x 32 accumulators leave few registers)
+    constexpr int KB = D == 256 ? 2 : NCH / 2;
+    constexpr int TB4 = D == 256 ? 2 : NDB;  // transposed fragments per batch
     using CP = Copier<D, BQ, NW>;
     constexpr int TB = CP::TB;
     constexpr int CB = 1024;                 // bytes per row-constant slot
@@ -420,30 +471,31 @@ bwd_dkv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __re
     for (int i = i0; i < nqt; ++i) {
         load_qo(i + 1);
         const int q0 = i * BQ;
-        if (!CAUSAL || q0 + BQ - 1 >= k0) {        // this wave has a visible pair
+        // this wave has a visible pair (d = 256: always run, see bwd_dq_kernel)
+        if (D == 256 || !CAUSAL || q0 + BQ - 1 >= k0) {
             // S' = Q K^T + Lr and dP' = dO V^T - D (lane = key, registers =
             // queries); operands in half batches to bound the live registers
             f32x16 s = acc_init(i, 0, 1.0f);
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                X8 qa[NCH / 2];
+            for (int c0 = 0; c0 < NCH; c0 += KB) {
+                X8 qa[KB];
 #pragma unroll
-                for (int ch = 0; ch < NCH / 2; ++ch) qa[ch] = tl.kfrag(qtile(i), half * NCH / 2 + ch, 0);
+                for (int ch = 0; ch < KB; ++ch) qa[ch] = tl.kfrag(qtile(i), c0 + ch, 0);
 #pragma unroll
-                for (int ch = 0; ch < NCH / 2; ++ch) s = mfma32(qa[ch], kf[half * NCH / 2 + ch], s);
+                for (int ch = 0; ch < KB; ++ch) s = mfma32(qa[ch], kf[c0 + ch], s);
                 __builtin_amdgcn_sched_barrier(0);
             }
             f32x16 dp = acc_init(i, 1, -1.0f);
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                X8 oa[NCH / 2];
+            for (int c0 = 0; c0 < NCH; c0 += KB) {
+                X8 oa[KB];
 #pragma unroll
-                for (int ch = 0; ch < NCH / 2; ++ch) oa[ch] = tl.kfrag(otile(i), half * NCH / 2 + ch, 0);
-                X8 vb[NCH / 2];
+                for (int ch = 0; ch < KB; ++ch) oa[ch] = tl.kfrag(otile(i), c0 + ch, 0);
+                X8 vb[KB];
 #pragma unroll
-                for (int ch = 0; ch < NCH / 2; ++ch) vb[ch] = tl.kfrag(vw, half * NCH / 2 + ch, 0);
+                for (int ch = 0; ch < KB; ++ch) vb[ch] = tl.kfrag(vw, c0 + ch, 0);
 #pragma unroll
-                for (int ch = 0; ch < NCH / 2; ++ch) dp = mfma32(oa[ch], vb[ch], dp);
+                for (int ch = 0; ch < KB; ++ch) dp = mfma32(oa[ch], vb[ch], dp);
                 __builtin_amdgcn_sched_barrier(0);
             }
             const bool masked = (q0 + BQ > N) || (CAUSAL && q0 < k0 + KW - 1);
@@ -471,31 +523,36 @@ bwd_dkv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __re
                 pf[h] = X8{wp[0][0], wp[0][1], wp[1][0], wp[1][1], wp[2][0], wp[2][1], wp[3][0], wp[3][1]};
                 dsf[h] = X8{wd[0][0], wd[0][1], wd[1][0], wd[1][1], wd[2][0], wd[2][1], wd[3][0], wd[3][1]};
             }
+            if constexpr (D == 256) asm volatile("s_nop 1" : "+v"(pf[0]), "+v"(pf[1]), "+v"(dsf[0]), "+v"(dsf[1]));
             __builtin_amdgcn_sched_barrier(0);
             // dV^T += dO^T P,  dK^T += Q^T dS
 #pragma unroll
-            for (int tt = 0; tt < NPV; ++tt) {
-                {
-                    X8 ot[NDB];
+            for (int tt = 0; tt < NPV; ++tt)
 #pragma unroll
-                    for (int db = 0; db < NDB; ++db) ot[db] = tl.tfrag(otile(i), tt, db);
+                for (int d0 = 0; d0 < NDB; d0 += TB4) {
+                    {
+                        X8 ot[TB4];
 #pragma unroll
-                    for (int db = 0; db < NDB; ++db) dv[db] = mfma32(ot[db], pf[tt], dv[db]);
+                        for (int db = 0; db < TB4; ++db) ot[db] = tl.tfrag(otile(i), tt, d0 + db);
+#pragma unroll
+                        for (int db = 0; db < TB4; ++db) grad_mfma<D>(dv[d0 + db], ot[db], pf[tt]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    {
+                        X8 qt[TB4];
+#pragma unroll
+                        for (int db = 0; db < TB4; ++db) qt[db] = tl.tfrag(qtile(i), tt, d0 + db);
+#pragma unroll
+                        for (int db = 0; db < TB4; ++db) grad_mfma<D>(dk[d0 + db], qt[db], dsf[tt]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                __builtin_amdgcn_sched_barrier(0);
-                {
-                    X8 qt[NDB];
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) qt[db] = tl.tfrag(qtile(i), tt, db);
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) dk[db] = mfma32(qt[db], dsf[tt], dk[db]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
         }
         wait_vm_all();
         __syncthreads();
     }
+    grad_settle<D>(dk);
+    grad_settle<D>(dv);
     if (key < N) {
         store_rowT<T, D, OUT_F32>(dKg, head + (size_t)key * D, dk, scale, hi);
         store_rowT<T, D, OUT_F32>(dVg, head + (size_t)key * D, dv, 1.0f, hi);
@@ -543,6 +600,7 @@ hipError_t launch_ty(const BwdArgs& a, hipStream_t s) {
     switch (a.d) {
         case 64: return launch_d<T, 64>(a, s);
         case 128: return launch_d<T, 128>(a, s);
+        case 256: return launch_d<T, 256>(a, s);
     }
     return hipErrorInvalidValue;
 }

@@ -68,6 +68,23 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 __device__ __forceinline__ f32x16 mfma32(const f16x8& a, const f16x8& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
+// acc += A B with acc bound to the accumulation registers (AGPRs) through
+// inline asm, for kernels that keep large accumulators there for their whole
+// life (one wave per SIMD). The compiler does not treat these as MFMAs: the
+// caller makes sure their vector inputs were written at least two wait
+// states before (or by loads the compiler waits for), and that vector
+// instructions read acc only after the MFMA's result latency.
+__device__ __forceinline__ void mfma_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_acc(f32x16& acc, const f16x8& a, const f16x8& b) {
+    asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Waits out the result latency of the asm MFMAs that last wrote the given
+// accumulators before vector instructions read them.
+__device__ __forceinline__ void acc_settle(f32x16& a0, f32x16& a1, f32x16& a2, f32x16& a3) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+a"(a0), "+a"(a1), "+a"(a2), "+a"(a3));
+}
 
 // o *= a on accumulators that live in the accumulation registers (AGPRs):
 // each element is read out, scaled and written back in one asm block. A

@@ -57,14 +57,8 @@ constexpr float kBigP = 16384.0f;   // per-lane sum of p that forces the exact-m
 #define FA16P_NPF 3                  // fragments read ahead of their first MFMA
 #endif
 
-// O^T += V^T P^T with O held in the accumulation registers (see the file
-// header): the compiler does not treat these as MFMAs.
-__device__ __forceinline__ void mfma_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_acc(f32x16& acc, const f16x8& a, const f16x8& b) {
-    asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
+// O^T += V^T P^T with O held in the accumulation registers (mfma_acc, see
+// the file header): the compiler does not treat these as MFMAs.
 
 template <typename T, int D>
 struct PipeWave {

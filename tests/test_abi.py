@@ -134,7 +134,8 @@ def bwd(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=fa.FA_FP8_E4M3), fa.FA_ERR_INVALID_ARG),
     (dict(dtype=fa.FA_BF16 | 0x400), fa.FA_ERR_INVALID_ARG),
-    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=1 << 23, d=256), fa.FA_ERR_UNSUPPORTED),
     (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(N=8388352, d=128), fa.FA_ERR_UNSUPPORTED),
     (dict(N=-1), fa.FA_ERR_INVALID_ARG),

@@ -113,6 +113,14 @@ SMALL = [
     (1, 2, 300, 128, True, "fp16"),
     (1, 1, 513, 128, True, "bf16"),
     (1, 1, 640, 64, False, "bf16"),
+    # d = 256: one wave per SIMD, gradients in the accumulation registers;
+    # key tiles of 32 in the query-parallel kernel
+    (1, 1, 1, 256, False, "bf16"),
+    (1, 2, 65, 256, True, "bf16"),
+    (1, 1, 200, 256, False, "fp16"),
+    (2, 1, 257, 256, True, "bf16"),
+    (1, 1, 513, 256, True, "fp16"),
+    (1, 2, 300, 256, False, "bf16"),
 ]
 
 
@@ -165,3 +173,27 @@ def test_full_workload_sampled_heads():
             m = bounds(q64, k64, v64, do64, causal, 1.0 / math.sqrt(d), "bf16")
             for name, g, gr, mm in zip(("dq", "dk", "dv"), (dq, dk, dv), ref, m):
                 check_grad(g[sl].cpu().numpy(), gr, mm, "bf16", "f32", f"{name} head ({b},{h})")
+
+
+def test_d256_sampled_heads():
+    """d = 256 at B=2 H=8 N=4096 (the head shape of the long-sequence d = 256
+    forward workload, a quarter of its length), causal and not, in the
+    launch configuration of the full call; two heads checked element by
+    element."""
+    B, H, N, d = 2, 8, 4096, 256
+    q, k, v = make_qkv(B, H, N, d, seed=2, dtype="bf16")
+    do = make_dout(B, H, N, d, 78, "bf16")
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    for causal in (False, True):
+        say(f"bwd B=2 H=8 N=4096 d=256 causal={causal}")
+        o, lse = fa.fwd(qd, kd, vd, causal=causal)
+        dq, dk, dv = fa.bwd(qd, kd, vd, o, lse, dod, causal=causal, out_f32=True)
+        torch.cuda.synchronize()
+        for b, h in ((0, 0), (1, 7)):
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            q64, k64, v64, do64 = (to_f64(t[sl]) for t in (q, k, v, do))
+            ref = oracle.attention_backward(q64, k64, v64, do64, causal)
+            m = bounds(q64, k64, v64, do64, causal, 1.0 / math.sqrt(d), "bf16")
+            for name, g, gr, mm in zip(("dq", "dk", "dv"), (dq, dk, dv), ref, m):
+                w, r = check_grad(g[sl].cpu().numpy(), gr, mm, "bf16", "f32", f"{name} head ({b},{h})")
+                say(f"  {name} head ({b},{h}): worst/bound {w:.2f} nRMSE {r:.2e}")
