@@ -227,6 +227,112 @@ def traffic_summary(run_dir):
     print(json.dumps(summary, indent=1))
 
 
+# Ablations of the 16-bit forward: variant -> (build.py -D flags or None for
+# the default library, leg-name suffix). Each is measured on the two d = 128
+# workloads below with two SQ counter passes.
+ABLATIONS = {
+    "default": (None, ""),
+    "pingpong": (["-DFA16_PINGPONG=1"], ""),
+    "no_setprio": (["-DFA16_PRIO=0"], ""),
+    "compiler_schedule": (["-DFA16_SCHED=0"], ""),
+    "read_ahead_2": (["-DFA16_KPD=2", "-DFA16_VPD=2"], ""),
+    "eight_waves": (["-DFA16_CFG_128=8,1,64,2"], ""),
+    "pipelined_64_rows": (None, "_pipelined"),
+}
+ABLATION_LEGS = ["bf16_fwd_b8h16n2k_d128", "bf16_fwd_b2h16n8k_d128_causal"]
+COUNTER_PASSES = [
+    "SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA "
+    "SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE",
+    "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_MISC SQ_WAIT_INST_LDS SQ_LDS_IDX_ACTIVE "
+    "SQ_WAIT_ANY SQ_INSTS_SALU SQ_ACTIVE_INST_ANY GRBM_GUI_ACTIVE",
+]
+ABLATION_FILE = os.path.join(ROOT, "profiles", "ablation_fwd16_d128.md")
+
+
+def ablation_commands():
+    """Build and counter commands of the ablation table (from the repository
+    root; <out> a scratch directory)."""
+    cmds = []
+    for name, (flags, suffix) in ABLATIONS.items():
+        lib = ""
+        if flags:
+            cmds.append(f"python3 -m exact_attention_55_amd.build --variant {name} " + " ".join(flags))
+            lib = f"FA_LIB=exact_attention_55_amd/variants/libfa_{name}.so "
+        only = " ".join(f"--only {leg}{suffix}" for leg in ABLATION_LEGS)
+        for i, ctr in enumerate(COUNTER_PASSES):
+            cmds.append(f"{lib}rocprofv3 --pmc {ctr} -d <out>/{name}_p{i + 1} -o run -f csv -- "
+                        f"python3 bench.py {only} --steps 3 --warmup 1 --no-cpu --no-next")
+    return cmds + ["python3 bench.py --counter-summary <out>"]
+
+
+def counter_summary(run_dir):
+    """Write ABLATION_FILE from the counter runs under run_dir (see
+    ablation_commands): per variant and workload, the mean per dispatch of
+    each counter over the forward kernel's dispatches, and the derived
+    figures."""
+    import csv
+    rows = []
+    for name, (_, suffix) in ABLATIONS.items():
+        per = {}
+        for i in range(len(COUNTER_PASSES)):
+            path = os.path.join(run_dir, f"{name}_p{i + 1}", "run_counter_collection.csv")
+            disp = {}
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    k = r["Kernel_Name"]
+                    if "fa_fwd16" not in k:
+                        continue
+                    if "Li128E" in k:                        # mangled name
+                        causal = k.split("Li128E", 1)[1].startswith("Lb1")
+                    else:                                     # demangled: <T, 128, causal, ...>
+                        causal = k.split("<", 1)[1].split(",")[2].strip() == "true"
+                    key = (causal, r["Dispatch_Id"])
+                    d = disp.setdefault(key, {})
+                    d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            for (causal, _), d in disp.items():
+                acc = per.setdefault(causal, {})
+                for c, v in d.items():
+                    acc.setdefault(c, []).append(v)
+        for causal, acc in sorted(per.items()):
+            m = {c: float(np.mean(v)) for c, v in acc.items()}
+            leg = ABLATION_LEGS[1 if causal else 0]
+            cyc = m["GRBM_GUI_ACTIVE"] / 8                # per XCD
+            waves = m["SQ_WAVES"]
+            rows.append((name, leg + suffix, {
+                "cycles": cyc,
+                "mfma_busy": m["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * cyc),
+                "valu_active": m["SQ_ACTIVE_INST_VALU"] / m["SQ_WAVE_CYCLES"],
+                "wait_any": m["SQ_WAIT_ANY"] / m["SQ_WAVE_CYCLES"],
+                "wait_lds": m["SQ_WAIT_INST_LDS"] / m["SQ_WAVE_CYCLES"],
+                "valu_per_wave": m["SQ_INSTS_VALU"] / waves,
+                "mfma_per_wave": m["SQ_INSTS_MFMA"] / waves,
+                "lds_per_wave": m["SQ_INSTS_LDS"] / waves,
+                "bank_conflicts": m["SQ_LDS_BANK_CONFLICT"],
+            }))
+    lines = ["# Ablations of the 16-bit forward at d = 128 (SQ counters)", "",
+             "Each variant is a compile-time switch of `csrc/fa_fwd16.hip` built with",
+             "`python3 -m exact_attention_55_amd.build --variant NAME -D...` and loaded through",
+             "`FA_LIB`; `pipelined_64_rows` is the default library with `FA_FWD_PIPELINED`.",
+             "Commands (repository root, TMPDIR=/tmp, <out> a scratch directory):", ""]
+    lines += ["    " + c for c in ablation_commands()]
+    lines += ["", "Mean per dispatch over the kernel's dispatches (3 timed + 1 warm-up). cycles: "
+              "GRBM_GUI_ACTIVE / 8 (one XCD); MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x "
+              "cycles); VALU active and waits are fractions of SQ_WAVE_CYCLES; instruction counts "
+              "per wave.", "",
+              "| variant | workload | cycles | MFMA busy | VALU active | wait any | wait LDS | "
+              "VALU / wave | MFMA / wave | LDS / wave | bank conflicts |",
+              "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for name, leg, v in rows:
+        lines.append(f"| {name} | {leg} | {v['cycles']:.3g} | {100 * v['mfma_busy']:.1f} % | "
+                     f"{100 * v['valu_active']:.1f} % | {100 * v['wait_any']:.1f} % | "
+                     f"{100 * v['wait_lds']:.1f} % | {v['valu_per_wave']:.0f} | "
+                     f"{v['mfma_per_wave']:.0f} | {v['lds_per_wave']:.0f} | {v['bank_conflicts']:.0f} |")
+    text = "\n".join(lines) + "\n"
+    with open(ABLATION_FILE, "w") as f:
+        f.write(text)
+    print(text)
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -249,18 +355,25 @@ class Leg:
 
 
 def build_legs(dev, only=None):
-    """The step's legs (all, or the names in `only`) and the tensors they use."""
+    """The step's legs (all, or the names in `only`) and the tensors they use.
+    With `only`, a 16-bit forward leg's name plus "_pipelined" selects the
+    same leg run by the 64-rows-per-wave pipelined kernel (an ablation)."""
     legs, keep = [], []
-    for name, (cfg, _) in FWD16_LEGS.items():
-        if only and name not in only:
+    names = [(n, False) for n in FWD16_LEGS]
+    if only:
+        names += [(n, True) for n in FWD16_LEGS if n + "_pipelined" in only]
+    for name, piped in names:
+        cfg = FWD16_LEGS[name][0]
+        if only and not piped and name not in only:
             continue
         c = CONFIGS[cfg]
         q, k, v = (t.to(dev) for t in make_qkv(**c))
         o = torch.empty_like(q)
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
         fl = attention_flops(c["B"], c["H"], c["N"], c["d"], c["causal"])
-        legs.append(Leg(name, lambda q=q, k=k, v=v, o=o, lse=lse, causal=c["causal"]:
-                        fa.fwd(q, k, v, causal, out=o, lse=lse), fl))
+        legs.append(Leg(name + ("_pipelined" if piped else ""),
+                        lambda q=q, k=k, v=v, o=o, lse=lse, causal=c["causal"], piped=piped:
+                        fa.fwd(q, k, v, causal, out=o, lse=lse, pipelined=piped), fl))
         keep += [q, k, v, o, lse]
     if only and FP8_PREP_LEG not in only and FP8_FWD_LEG not in only:
         return legs, keep
@@ -492,7 +605,17 @@ def main():
     ap.add_argument("--source-hash", metavar="LEG", help="print a forward leg's kernel code hash")
     ap.add_argument("--traffic-summary", metavar="DIR",
                     help="write the HBM-traffic summary from the counter runs under DIR (no GPU)")
+    ap.add_argument("--counter-summary", metavar="DIR",
+                    help="write the ablation counter table from the runs under DIR (no GPU)")
+    ap.add_argument("--ablation-commands", action="store_true",
+                    help="print the commands of the ablation counter runs")
     args = ap.parse_args()
+    if args.ablation_commands:
+        print("\n".join(ablation_commands()))
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
+        return
     if args.source_hash:
         print(source_hash(KERNEL_OF[args.source_hash]))
         return

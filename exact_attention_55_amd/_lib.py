@@ -33,11 +33,13 @@ class FaError(RuntimeError):
 
 
 def lib_path():
-    return os.path.join(_HERE, "libfa.so")
+    """The library this process loads: libfa.so beside this file, or the
+    build FA_LIB names (an ablation variant from build.py --variant)."""
+    return os.environ.get("FA_LIB") or os.path.join(_HERE, "libfa.so")
 
 
 def lib():
-    """Load libfa.so once; raise if it has not been built."""
+    """Load the library once; raise if it has not been built."""
     global _LIB
     if _LIB is not None:
         return _LIB

@@ -1,6 +1,12 @@
 """Build libfa.so in-tree with hipcc for gfx950.
 
     python -m exact_attention_55_amd.build [-v]
+    python -m exact_attention_55_amd.build --variant NAME -DMACRO=VALUE ...
+
+The second form builds a variant of the library with the given macros (the
+kernels' compile-time switches: FA16_PINGPONG, FA16_PRIO, FA16_SCHED,
+FA16_CFG_128, ...) into exact_attention_55_amd/variants/libfa_NAME.so, for
+ablations: setting FA_LIB to that path makes the binding load it instead.
 
 Each translation unit under csrc/ is compiled in parallel, then linked into
 exact_attention_55_amd/libfa.so. Flags:
@@ -42,9 +48,9 @@ FLAGS = [
 ]
 
 
-def _compile(src, verbose):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + EXTRA_FLAGS.get(src, []) + [
+def _compile(src, verbose, defines=(), objdir=BUILD):
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC] + FLAGS + EXTRA_FLAGS.get(src, []) + list(defines) + [
         "-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -52,7 +58,7 @@ def _compile(src, verbose):
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
     usage = _resource_usage(r.stderr)
-    with open(os.path.join(BUILD, os.path.splitext(src)[0] + ".resources.txt"), "w") as f:
+    with open(os.path.join(objdir, os.path.splitext(src)[0] + ".resources.txt"), "w") as f:
         for name, u in usage.items():
             f.write(f"{name} {u}\n")
     spilled = {n: u for n, u in usage.items()
@@ -104,11 +110,20 @@ def _resource_usage(stderr):
     return usage
 
 
-def build(verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose=False, variant=None, defines=()):
+    """Compile and link the library; with variant, the ablation build of that
+    name with the given -D flags (see the module docstring)."""
+    objdir, out = BUILD, OUT
+    if variant is not None:
+        if not re.fullmatch(r"[A-Za-z0-9_]+", variant):
+            raise ValueError(f"variant name {variant!r}: letters, digits and _ only")
+        objdir = os.path.join(BUILD, "variant_" + variant)
+        out = os.path.join(HERE, "variants", f"libfa_{variant}.so")
+        os.makedirs(os.path.dirname(out), exist_ok=True)
+    os.makedirs(objdir, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = OUT + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, defines, objdir), SOURCES))
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -116,8 +131,8 @@ def build(verbose=False):
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     _check_undefined(tmp)
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
 
 
 def _check_undefined(lib):
@@ -134,4 +149,9 @@ def _check_undefined(lib):
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    args = sys.argv[1:]
+    name = None
+    if "--variant" in args:
+        name = args[args.index("--variant") + 1]
+    defs = [a for a in args if a.startswith("-D")]
+    print(build(verbose="-v" in args, variant=name, defines=defs))

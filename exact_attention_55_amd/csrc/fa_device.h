@@ -313,4 +313,15 @@ constexpr int kVmcnt0 = 0x0f70;
 // Wait until this wave's global loads (including direct-to-LDS ones) landed.
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Workgroup barrier after this wave's global->LDS copies, except the newest
+// VM of them, have landed. Nothing is scheduled across it and memory
+// accesses are not moved across it.
+template <int VM>
+__device__ __forceinline__ void sync_tiles() {
+    static_assert(VM >= 0 && VM <= 63, "vmcnt is a 6-bit field");
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(VM) : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 }  // namespace fa

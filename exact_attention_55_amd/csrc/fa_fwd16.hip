@@ -78,6 +78,15 @@ constexpr float kBig = 16384.0f;
 #ifndef FA16_VPD
 #define FA16_VPD 4
 #endif
+// 1: two wave groups per workgroup in ping-pong (see the full-tile loop of
+// fa_fwd16_kernel); the d = 128 configuration then has 8 waves.
+#ifndef FA16_PINGPONG
+#define FA16_PINGPONG 0
+#endif
+// 0: the score phase of a step runs at normal wave priority.
+#ifndef FA16_PRIO
+#define FA16_PRIO 1
+#endif
 
 // Tile configuration per head dimension. NW waves per workgroup, each owning
 // 32*QB query rows; BC keys per K/V tile; WPE = waves per SIMD the register
@@ -95,7 +104,11 @@ constexpr float kBig = 16384.0f;
 #define FA16_CFG_64_WIDE 4, 2, 32, 2
 #endif
 #ifndef FA16_CFG_128
+#if FA16_PINGPONG
+#define FA16_CFG_128 8, 1, 64, 2
+#else
 #define FA16_CFG_128 4, 1, 64, 2
+#endif
 #endif
 #ifndef FA16_CFG_256
 #define FA16_CFG_256 4, 1, 64, 1
@@ -451,7 +464,7 @@ struct Wave16 {
         // The MFMA + exponential phase runs at raised wave priority: of the
         // two waves sharing a SIMD, the one in this phase issues first and the
         // other (in its PV phase) fills the matrix core around it.
-        __builtin_amdgcn_s_setprio(1);
+        if (FA16_PRIO) __builtin_amdgcn_s_setprio(1);
         qk(sn, kf, qf, 0, NCH / 2);
 #pragma unroll
         for (int kb = 0; kb < NKB / 2; ++kb) probs(s, pf, kb, c, ls, lxs);
@@ -475,7 +488,7 @@ struct Wave16 {
             __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_setprio(0);
+        if (FA16_PRIO) __builtin_amdgcn_s_setprio(0);
         settle(s, pf, c, ls, lxs);
         u32x2 vlo[NPV][NDB], vhi[NPV][NDB];
         vfrags_async(vlo, vhi, b0, b1);
@@ -551,7 +564,7 @@ struct Wave16 {
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) sn[qb][kb] = f32x16{};
-        __builtin_amdgcn_s_setprio(1);
+        if (FA16_PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int f = 0; f < KPD; ++f) kf[f % NKB][f / NKB] = kfrag(kn, ka, f / NKB, f % NKB);
         __builtin_amdgcn_sched_barrier(0);
@@ -572,7 +585,7 @@ struct Wave16 {
                 prob_pair(s, pp, q / 8, (q / 4) % 2, q % 4, c, ls, lxs);
             __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_s_setprio(0);
+        if (FA16_PRIO) __builtin_amdgcn_s_setprio(0);
         X8 pf[QB][NPV];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -585,6 +598,73 @@ struct Wave16 {
                         X8{w[0][0], w[0][1], w[1][0], w[1][1], w[2][0], w[2][1], w[3][0], w[3][1]};
                 }
         settle(s, pf, c, ls, lxs);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < NVF; ++j) {
+            const int v = j + VPD;
+            if (v < NVF) vf[v / NDB][v % NDB] = vfrag(vl, va, vstep, v / NDB, v % NDB);
+            const int t = j / NDB, db = j % NDB;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(vf[t][db], pf[qb][t], o[qb][db]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // The two halves of step() for the ping-pong schedule, which puts a
+    // workgroup barrier between them: phase_a runs the score MFMAs of the
+    // next tile with this tile's exponentials and the overflow check (P into
+    // pf, which stays live across the barrier); phase_b the PV MFMAs.
+    __device__ __forceinline__ void phase_a(const f32x16 (&s)[QB][NKB], f32x16 (&sn)[QB][NKB],
+                                            const char* kn, const int (&ka)[NKA],
+                                            const X8 (&qf)[QB][NCH], float c, X8 (&pf)[QB][NPV]) {
+        constexpr int NKF = NCH * NKB;
+        constexpr int NPAIR = NKB * 8;
+        constexpr int KPD = NKF >= 2 * FA16_KPD ? FA16_KPD : NKF / 2;
+        X8 kf[NKB][NCH];
+        X2 pp[QB][NKB][2][4];
+        float ls[QB][2], lxs[QB][2];
+        zero_sums(ls, lxs);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) sn[qb][kb] = f32x16{};
+        if (FA16_PRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int f = 0; f < KPD; ++f) kf[f % NKB][f / NKB] = kfrag(kn, ka, f / NKB, f % NKB);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NKF; ++i) {
+            const int f = i + KPD;
+            if (f < NKF) kf[f % NKB][f / NKB] = kfrag(kn, ka, f / NKB, f % NKB);
+            const int ch = i / NKB, kb = i % NKB;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) sn[qb][kb] = mfma32(kf[kb][ch], qf[qb][ch], sn[qb][kb]);
+#pragma unroll
+            for (int q = i * NPAIR / NKF; q < (i + 1) * NPAIR / NKF; ++q)
+                prob_pair(s, pp, q / 8, (q / 4) % 2, q % 4, c, ls, lxs);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (FA16_PRIO) __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const X2 (&w)[4] = pp[qb][kb][h];
+                    pf[qb][2 * kb + h] =
+                        X8{w[0][0], w[0][1], w[1][0], w[1][1], w[2][0], w[2][1], w[3][0], w[3][1]};
+                }
+        settle(s, pf, c, ls, lxs);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __device__ __forceinline__ void phase_b(const char* vl, const int (&va)[NVA], int vstep,
+                                            const X8 (&pf)[QB][NPV]) {
+        constexpr int NVF = NPV * NDB;
+        constexpr int VPD = NVF >= 2 * FA16_VPD ? FA16_VPD : NVF / 2;
+        X8 vf[NPV][NDB];
+#pragma unroll
+        for (int v = 0; v < VPD; ++v) vf[v / NDB][v % NDB] = vfrag(vl, va, vstep, v / NDB, v % NDB);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < NVF; ++j) {
@@ -772,7 +852,68 @@ fa_fwd16_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) s[qb][kb] = s2[qb][kb];
     };
-    if constexpr (Cfg16<D, WIDE>::WPE == 1) {
+    // Ping-pong ("FlashAttention-3", "Overlapping GEMM and Softmax"): waves
+    // 0-3 and 4-7 of an 8-wave workgroup (the two waves of each SIMD) run
+    // the same step, phase_a (score MFMAs of t+1, exponentials of t) and
+    // phase_b (PV MFMAs of t), each ending in a workgroup barrier, but
+    // waves 4-7 start one barrier late and waves 0-3 end one barrier
+    // early. So while one wave of a SIMD runs its exponentials, the other
+    // runs MFMAs. Only waves 0-3 copy tiles: K t+2 at the start of their
+    // phase_a(t) (into the slot of K t, last read by waves 4-7 in their
+    // phase_a(t-1), one barrier earlier), V t+1 at the start of their
+    // phase_b(t) (the slot of V t-1, last read by waves 4-7 in their
+    // phase_b(t-1)); each copy has landed at the barrier after the next
+    // half, before its first reader.
+    constexpr bool PP = FA16_PINGPONG && FA16_SCHED && NW == 8 && Cfg16<D, WIDE>::WPE == 2;
+    if constexpr (PP) {
+        constexpr int NL = NW / 2;                    // copying waves
+        constexpr int NIWL = TB / 1024 / NL;
+        const bool g0 = wave_u < NL;
+        uint32_t loff[NIWL];
+#pragma unroll
+        for (int j = 0; j < NIWL; ++j) {
+            const int p = ((wave & (NL - 1)) * NIWL + j) * 1024 + 16 * lane;
+            const int row = p / RB;
+            loff[j] = row * RB + ((p % RB / 16) ^ lds_swz16<D>(row)) * 16;
+        }
+        // copy tile tt into slot, by waves 0-3; true if issued
+        auto pcopy = [&](const i32x4& rs, int tt, int slot) -> bool {
+            if (tt >= nkt_use) return false;
+            if (g0) {
+                const uint32_t dst = sbase + slot * TB + (wave_u & (NL - 1)) * NIWL * 1024;
+#pragma unroll
+                for (int j = 0; j < NIWL; ++j) buffer_load_lds16(rs, dst + j * 1024, loff[j], tt * TB);
+            }
+            return true;
+        };
+        auto sync_after = [&](bool issued) {
+            if (issued) sync_tiles<NIWL>(); else sync_tiles<0>();
+        };
+        X8 pf[QB][W::NPV];
+        // Slots by the parity P of t, known at compile time (steps come in
+        // pairs from t = 0), so tile addresses are immediate offsets.
+        auto pp_step = [&](const f32x16 (&sc)[QB][NKB], f32x16 (&sn)[QB][NKB], auto pc) {
+            constexpr int P = decltype(pc)::value;
+            const bool kc = pcopy(krs, t + 2, P);
+            st.phase_a(sc, sn, smem + ((P + 1) & 1) * TB, ka, qf, c, pf);
+            sync_after(kc);
+            const bool vc = pcopy(vrs, t + 1, 2 + ((P + 1) & 1));
+            st.phase_b(smem + (2 + P) * TB, vai, vsi, pf);
+            sync_after(vc);
+            ++t;
+        };
+        if (!g0) sync_tiles<0>();                     // waves 4-7 start one barrier late
+        for (; t + 2 < nfull;) {
+            pp_step(s, s2, std::integral_constant<int, 0>{});
+            pp_step(s2, s, std::integral_constant<int, 1>{});
+        }
+        if (t + 1 < nfull) {
+            pp_step(s, s2, std::integral_constant<int, 0>{});
+            copy_back();
+        }
+        if (g0) sync_tiles<0>();                      // waves 0-3 end one barrier early
+        sync_tiles<0>();
+    } else if constexpr (Cfg16<D, WIDE>::WPE == 1) {
         // one wave per SIMD (d = 256): the accumulation registers hold O and
         // the scores, with no room for a second set; copied each tile
         for (; t + 1 < nfull;) {

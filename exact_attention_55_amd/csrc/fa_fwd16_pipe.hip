@@ -422,16 +422,6 @@ struct PipeWave {
     }
 };
 
-// Workgroup barrier after this wave's global->LDS copies, except the newest
-// VM of them, have landed. Nothing is scheduled across it and memory
-// accesses are not moved across it.
-template <int VM>
-__device__ __forceinline__ void sync_tiles() {
-    static_assert(VM >= 0 && VM <= 63, "vmcnt is a 6-bit field");
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(VM) : "memory");
-    __builtin_amdgcn_sched_barrier(0);
-}
 
 template <typename T, int D, bool CAUSAL, bool OUT_F32>
 __global__ void __launch_bounds__(256, 1)
