@@ -51,6 +51,9 @@ constexpr float kPScale = 8.0f;     // P multiplier before e4m3 rounding
 constexpr int kPScaleE8M0 = 124;    // 2^-3: the microscaled PV MFMA undoes kPScale
 constexpr float kBig8 = 448.0f;     // per-lane tile sum of P' that forces the exact-maximum path
 
+#ifndef FA8_PRIO                   // 0: the score phase runs at normal wave priority
+#define FA8_PRIO 1
+#endif
 #ifndef FA8_CFG_64
 #define FA8_CFG_64 4, 64, 2
 #endif
@@ -69,8 +72,11 @@ template <> struct Cfg8<64> : Cfg8T<FA8_CFG_64> {};
 template <> struct Cfg8<128> : Cfg8T<FA8_CFG_128> {};
 template <> struct Cfg8<256> : Cfg8T<FA8_CFG_256> {};
 
+// Four floats -> four e4m3 bytes. The first conversion writes the low half
+// of a register whose high half the second overwrites, so it starts from
+// any value (a's bits: no register has to be zeroed first).
 __device__ __forceinline__ uint32_t cvt4_e4m3(float a, float b, float c, float d) {
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
     return (uint32_t)w;
 }
@@ -321,7 +327,7 @@ struct Wave8 {
         float ls[2] = {0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) sn[kb] = f32x16{};
-        __builtin_amdgcn_s_setprio(1);
+        if (FA8_PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int f = 0; f < KPD; ++f) kf[f % NKB][f / NKB] = kfrag(kn, ka, f / NKB, f % NKB);
         __builtin_amdgcn_sched_barrier(0);
@@ -340,7 +346,7 @@ struct Wave8 {
             for (int q = i * NG / NKF; q < (i + 1) * NG / NKF; ++q) prob_group(s, w, q, cj, bj, ls);
             __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_s_setprio(0);
+        if (FA8_PRIO) __builtin_amdgcn_s_setprio(0);
         settle(s, w, cj, bj, lscale, ls);
         i32x8 pf[NPV];
         pack_p(w, pf);
