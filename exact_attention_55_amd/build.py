@@ -76,11 +76,9 @@ def _compile(src, verbose, defines=(), objdir=BUILD):
 # Kernels allowed a little scratch, with the reason (bytes per lane):
 #  * the one-wave-per-SIMD 16-bit forward at d = 256 (512 registers, all in
 #    use): a long-lived value or two saved in the prologue and reloaded in the
-#    epilogue, outside the key loop;
-#  * the rotary prep without the Hadamard at d = 256, half pairing.
+#    epilogue, outside the key loop.
 SCRATCH_ALLOWANCE = [
     (re.compile(r"^_ZN2fa15fa_fwd16_kernelIDF16[b_]Li256E"), 32),
-    (re.compile(r"^_ZN2fa15fp8_prep_kernelIDF16[b_]Li256ELb0ELi2ELi2E"), 104),
 ]
 
 

@@ -25,9 +25,13 @@
 // pair (a, b) of the row at position p = pos0 + row turns into
 // (a c - b s, a s + b c), c and s the float32 cosine and sine of the float32
 // product p * w_i; the frequencies w_i = base^(-2i/d) are rounded to float32
-// on the host and passed by value. Interleaved pairs sit inside a lane; for
-// the half pairing the partner of element e of lane j is element e of lane
-// j ^ (d/16).
+// on the host and passed by value. Interleaved pairs sit inside a lane. For
+// the half pairing a lane holds columns 4j .. 4j+3 and d/2 + 4j .. +3 (two
+// 8-byte loads) instead of 8j .. 8j+7, so both members of a pair are in
+// the lane too. The Hadamard stages are the same code in either layout:
+// the in-lane butterfly across elements e, e+4 then works on column bit
+// log2(d)-1 instead of bit 2, and since the Sylvester matrix is a Kronecker
+// product over the column bits, the order of the stages does not matter.
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -60,7 +64,7 @@ __device__ __forceinline__ float lane_xor(float x) {
 // sin and cos of a float32 angle t, |t| < 2^25. Reduction t = k (pi/2) + r
 // in double precision with pi/2 split into two doubles (the error of r is far
 // below a float32 ulp even for k near 2^24), then the Taylor series of sin
-// and cos on |r| <= pi/4 in float32 (truncation below 1e-11), and the
+// and cos on |r| <= pi/4 in float32 (truncation below 2e-9), and the
 // quadrant k mod 4 selects and signs the pair.
 __device__ __forceinline__ void sincos_f32(float t, float* sn, float* cs) {
     constexpr double kPio2Hi = 1.5707963267948966;          // nearest double to pi/2
@@ -71,16 +75,16 @@ __device__ __forceinline__ void sincos_f32(float t, float* sn, float* cs) {
     const double rd = __builtin_fma(-k, kPio2Lo, __builtin_fma(-k, kPio2Hi, td));
     const float r = (float)rd;
     const float r2 = r * r;
-    // sin r = r (1 - r^2/3! + r^4/5! - ... - r^10/11!)
-    float ps = -1.0f / 39916800.0f;
-    ps = fmaf(ps, r2, 1.0f / 362880.0f);
+    // sin r = r (1 - r^2/3! + r^4/5! - r^6/7! + r^8/9!); the next term,
+    // r^11/11!, is below 2e-9 on |r| <= pi/4
+    float ps = 1.0f / 362880.0f;
     ps = fmaf(ps, r2, -1.0f / 5040.0f);
     ps = fmaf(ps, r2, 1.0f / 120.0f);
     ps = fmaf(ps, r2, -1.0f / 6.0f);
     const float s0 = fmaf(r * r2, ps, r);
-    // cos r = 1 - r^2/2! + r^4/4! - ... + r^12/12!
-    float pc = 1.0f / 479001600.0f;
-    pc = fmaf(pc, r2, -1.0f / 3628800.0f);
+    // cos r = 1 - r^2/2! + r^4/4! - ... - r^10/10!; the next term, r^12/12!,
+    // is below 2e-10 on |r| <= pi/4
+    float pc = -1.0f / 3628800.0f;
     pc = fmaf(pc, r2, 1.0f / 40320.0f);
     pc = fmaf(pc, r2, -1.0f / 720.0f);
     pc = fmaf(pc, r2, 1.0f / 24.0f);
@@ -122,9 +126,16 @@ __device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
 // MODE 3: microscaling along d: one power-of-two scale per 32 columns of a
 //         row (4 lanes), stored as the E8M0 byte e + 127 at
 //         scales[row of the tensor][column block] (see mx_exponent).
-// Threads per 128-row block: 512 at d = 256 (8 passes of 16 rows), so a
-// thread's rows in flight stay within the register budget; 256 otherwise.
-template <int D> constexpr int quant_threads() { return D == 256 ? 512 : kPrepThreads; }
+// Threads per 128-row block: 512 at d = 256 (8 passes of 16 rows) and with
+// the rotary step (4 passes of 32 rows at d = 128), so a thread's rows in
+// flight and the sine / cosine temporaries stay within a register budget
+// that leaves several waves per SIMD to hide memory latency; 256 otherwise.
+#ifndef FA_PREP_WIDE                // 1: 512 threads at d = 128 without the rotary step too
+#define FA_PREP_WIDE 0
+#endif
+template <int D, int ROPE = 0> constexpr int quant_threads() {
+    return (D == 256 || (D == 128 && (ROPE != 0 || FA_PREP_WIDE))) ? 512 : kPrepThreads;
+}
 
 // Scale of a block with largest magnitude amax: amax / 448 in float32 (1 for
 // an all-zero block), with pow2 rounded up to the next power of two (exact:
@@ -138,27 +149,32 @@ __device__ __forceinline__ float block_scale(float amax, int pow2) {
 }
 
 template <typename T, int D, bool HAD, int MODE, int ROPE>
-__global__ void __launch_bounds__(quant_threads<D>())
+__global__ void __launch_bounds__((quant_threads<D, ROPE>()))
 fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t* __restrict__ signs,
                 float* __restrict__ scales, unsigned* __restrict__ gamax, int N, int H, int nblk,
                 RopeFreqs rf, int pow2)
 {
-    constexpr int NT = quant_threads<D>();
+    constexpr int NT = quant_threads<D, ROPE>();
     constexpr int LPR = D / 8;                 // lanes per row
     constexpr int RPP = NT / LPR;              // rows per pass
     constexpr int NPASS = kQuantBlockRows / RPP;
     __shared__ float red[NT / 64];
 
+    // SPLIT: elements 0..3 of lane j are columns 4j.., elements 4..7 columns
+    // d/2 + 4j.. (the half pairing); otherwise columns 8j .. 8j+7.
+    constexpr bool SPLIT = ROPE == 2;
+    static_assert(!(SPLIT && MODE == 3), "microscaling takes contiguous columns");
     const int tid = threadIdx.x;
     const int j = tid % LPR, rp = tid / LPR;
+    const int c0 = SPLIT ? 4 * j : 8 * j, c1 = SPLIT ? D / 2 + 4 * j : 8 * j + 4;
     const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
     const int h = bh % H;
     const size_t head = (size_t)bh * N * D;
 
     float sg[8];
     if (HAD) {
-        const uint32_t* sp = reinterpret_cast<const uint32_t*>(signs + (size_t)h * D + 8 * j);
-        const uint32_t w0 = sp[0], w1 = sp[1];
+        const uint32_t w0 = *reinterpret_cast<const uint32_t*>(signs + (size_t)h * D + c0);
+        const uint32_t w1 = *reinterpret_cast<const uint32_t*>(signs + (size_t)h * D + c1);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             sg[e] = (float)(int8_t)((w0 >> (8 * e)) & 0xff);
@@ -175,7 +191,14 @@ fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t*
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
         const int row = blk * kQuantBlockRows + p * RPP + rp;
-        raw[p] = *reinterpret_cast<const u32x4*>(X + head + (size_t)min(row, N - 1) * D + 8 * j);
+        const T* xr = X + head + (size_t)min(row, N - 1) * D;
+        if constexpr (SPLIT) {
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(xr + c0);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(xr + c1);
+            raw[p] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        } else {
+            raw[p] = *reinterpret_cast<const u32x4*>(xr + c0);
+        }
     }
 #pragma unroll
     for (int p = 0; p < NPASS; ++p)
@@ -201,26 +224,14 @@ fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t*
                     v[p][2 * k + 1] = a * sn + b * cs;
                 }
             } else {
-                // Lanes j and j ^ (LPR/2) need the same 8 angles: each takes
-                // the cosine and sine of 4 of them and trades with the other.
-                const bool second = j >= LPR / 2;
-                const int i0 = (8 * j) % (D / 2);
-                float cs[8], sn[8];
+                // pairs (4j + k, d/2 + 4j + k) are elements k, k + 4
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    const int e = second ? 4 + k : k;
-                    sincos_f32(pos * rf.w[i0 + e], &sn[e], &cs[e]);
-                }
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int mine = second ? 4 + k : k, theirs = second ? k : 4 + k;
-                    cs[theirs] = lane_xor<LPR / 2>(cs[mine]);
-                    sn[theirs] = lane_xor<LPR / 2>(sn[mine]);
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float other = lane_xor<LPR / 2>(v[p][e]);
-                    v[p][e] = second ? v[p][e] * cs[e] + other * sn[e] : v[p][e] * cs[e] - other * sn[e];
+                    float sn, cs;
+                    sincos_f32(pos * rf.w[4 * j + k], &sn, &cs);
+                    const float a = v[p][k], b = v[p][k + 4];
+                    v[p][k] = a * cs - b * sn;
+                    v[p][k + 4] = a * sn + b * cs;
                 }
             }
         }
@@ -321,7 +332,13 @@ fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t*
                                 (e4m3x2(qs(v[p][2]), qs(v[p][3])) << 16);
             const uint32_t w1 = e4m3x2(qs(v[p][4]), qs(v[p][5])) |
                                 (e4m3x2(qs(v[p][6]), qs(v[p][7])) << 16);
-            *reinterpret_cast<u32x2*>(X8 + head + (size_t)row * D + 8 * j) = u32x2{w0, w1};
+            uint8_t* xr = X8 + head + (size_t)row * D;
+            if constexpr (SPLIT) {
+                *reinterpret_cast<uint32_t*>(xr + c0) = w0;
+                *reinterpret_cast<uint32_t*>(xr + c1) = w1;
+            } else {
+                *reinterpret_cast<u32x2*>(xr + c0) = u32x2{w0, w1};
+            }
         }
     }
 }
@@ -412,14 +429,15 @@ static hipError_t prep_t(const PrepArgs& a, hipStream_t s) {
         return hipGetLastError();
     }
     if (a.mx == kMxAlongD) {
-        hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 3, ROPE>), dim3((unsigned)grid),
-                           dim3(quant_threads<D>()), 0, s, x, a.x8, a.signs, scales, nullptr, a.N, a.H, nblk,
+        if constexpr (ROPE != 0) return hipErrorInvalidValue;     // fa_mx_prep has no rotary step
+        hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 3, 0>), dim3((unsigned)grid),
+                           dim3(quant_threads<D, 0>()), 0, s, x, a.x8, a.signs, scales, nullptr, a.N, a.H, nblk,
                            a.rope, a.pow2);
         return hipGetLastError();
     }
     if (a.block_rows != 0) {
         hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 0, ROPE>), dim3((unsigned)grid),
-                           dim3(quant_threads<D>()), 0, s, x, a.x8, a.signs, scales, nullptr, a.N, a.H, nblk,
+                           dim3(quant_threads<D, ROPE>()), 0, s, x, a.x8, a.signs, scales, nullptr, a.N, a.H, nblk,
                            a.rope, a.pow2);
         return hipGetLastError();
     }
@@ -427,9 +445,9 @@ static hipError_t prep_t(const PrepArgs& a, hipStream_t s) {
     // fill kernel reads it before overwriting every slot.
     unsigned* gamax = reinterpret_cast<unsigned*>(scales);
     hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(1), 0, s, gamax);
-    hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 1, ROPE>), dim3((unsigned)grid), dim3(quant_threads<D>()),
+    hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 1, ROPE>), dim3((unsigned)grid), dim3(quant_threads<D, ROPE>()),
                        0, s, x, a.x8, a.signs, scales, gamax, a.N, a.H, nblk, a.rope, a.pow2);
-    hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 2, ROPE>), dim3((unsigned)grid), dim3(quant_threads<D>()),
+    hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 2, ROPE>), dim3((unsigned)grid), dim3(quant_threads<D, ROPE>()),
                        0, s, x, a.x8, a.signs, scales, gamax, a.N, a.H, nblk, a.rope, a.pow2);
     hipLaunchKernelGGL(fill_scales_kernel, dim3(1), dim3(1024), 0, s, scales,
                        (const unsigned*)gamax, grid, a.pow2);
