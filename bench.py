@@ -227,6 +227,90 @@ def traffic_summary(run_dir):
     print(json.dumps(summary, indent=1))
 
 
+TRACE_FILE = os.path.join(ROOT, "profiles", "bench_kernel_trace.md")
+
+
+def trace_commands():
+    """The kernel-trace run of the whole bench (from the repository root;
+    <out> a scratch directory)."""
+    return ["rocprofv3 --kernel-trace --stats -d <out>/trace_all -o run -f csv -- python3 bench.py "
+            "--steps 5 --warmup 2 --no-cpu",
+            "python3 bench.py --trace-summary <out>"]
+
+
+def _short_kernel_name(n):
+    """Kernel name with its template arguments, from the mangled symbol (the
+    demangler leaves the bf16 ones mangled) or the demangled form."""
+    import re
+    import subprocess
+    m = re.match(r"_ZN2fa(?:12_GLOBAL__N_1)?(\d+)", n)
+    if m:
+        k = int(m.group(1))
+        rest = n[m.end():]
+        name, rest = rest[:k], rest[k:]
+        if rest.startswith("I") and "EEv" in rest:
+            toks = re.findall(r"(DF16b)|(DF16_)|Li(\d+)E|Lb([01])E", rest[1:rest.index("EEv") + 1])
+            args = ["bf16" if a else "fp16" if b else c if c else ("true" if d == "1" else "false")
+                    for a, b, c, d in toks]
+            return f"{name}<{','.join(args)}>"
+        return name
+    try:
+        n = subprocess.run(["c++filt", n], capture_output=True, text=True).stdout.strip() or n
+    except OSError:
+        pass
+    n = n.replace("fa::(anonymous namespace)::", "").replace("fa::", "").replace("void ", "")
+    return n.split("(")[0].replace("__bf16", "bf16").replace(" ", "")
+
+
+def trace_summary(run_dir, warmup=2, steps=5):
+    """Write TRACE_FILE from the run of trace_commands under run_dir. Per
+    forward leg: its kernel's dispatches in the timed steps. Every step runs
+    the legs in order, one dispatch of its kernel each, so the dispatches of
+    a kernel that several legs share go to those legs in turn."""
+    import csv
+    base = os.path.join(run_dir, "trace_all")
+    with open(os.path.join(base, "run_kernel_trace.csv")) as f:
+        trace = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    lines = ["# Kernel trace of bench.py", "",
+             "Commands (repository root, TMPDIR=/tmp, <out> a scratch directory):", ""]
+    lines += ["    " + c for c in trace_commands()]
+    lines += ["", f"## Forward legs of the step ({steps} timed steps after {warmup} warm-up ones)", "",
+              "| leg | kernel | dispatches | avg us | min us | max us | TFLOP/s at avg | of peak |",
+              "|---|---|---|---|---|---|---|---|"]
+    order = list(KERNEL_OF)
+    for leg, sym in KERNEL_OF.items():
+        short = _short_kernel_name(sym)
+        sharing = [l for l in order if _short_kernel_name(KERNEL_OF[l]) == short]
+        disp = [r for r in trace if r["Kernel_Name"] == sym or _short_kernel_name(r["Kernel_Name"]) == short]
+        disp = disp[: (warmup + steps) * len(sharing)]
+        mine = disp[sharing.index(leg)::len(sharing)][warmup:]
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in mine]
+        if not d:
+            continue
+        if leg == FP8_FWD_LEG:
+            c, peak = CONFIGS[FP8], PEAK_FP8
+        else:
+            c, peak = CONFIGS[FWD16_LEGS[leg][0]], PEAK_BF16
+        fl = attention_flops(c["B"], c["H"], c["N"], c["d"], c["causal"])
+        avg = float(np.mean(d))
+        lines.append(f"| {leg} | {short} | {len(d)} | {avg:.1f} | {min(d):.1f} | {max(d):.1f} | "
+                     f"{fl / avg / 1e6:.0f} | {fl / avg / 1e6 / peak:.3f} |")
+    with open(os.path.join(base, "run_kernel_stats.csv")) as f:
+        rows = list(csv.DictReader(f))
+    tot = sum(float(r["TotalDurationNs"]) for r in rows)
+    lines += ["", "## All kernels of the run (step legs, then the rows beyond the forward)", "",
+              "A kernel several legs share is averaged over all of them here.", "",
+              "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {_short_kernel_name(r['Name'])} | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['TotalDurationNs']) / tot * 100:.1f} |")
+    text = "\n".join(lines) + "\n"
+    with open(TRACE_FILE, "w") as f:
+        f.write(text)
+    print(text)
+
+
 # Ablations of the 16-bit forward: variant -> (build.py -D flags or None for
 # the default library, leg-name suffix). Each is measured on the two d = 128
 # workloads below with two SQ counter passes.
@@ -238,8 +322,17 @@ ABLATIONS = {
     "read_ahead_2": (["-DFA16_KPD=2", "-DFA16_VPD=2"], ""),
     "eight_waves": (["-DFA16_CFG_128=8,1,64,2"], ""),
     "pipelined_64_rows": (None, "_pipelined"),
+    "fp8_default": (None, "fp8"),          # the fp8 forward's counters, for reference
 }
 ABLATION_LEGS = ["bf16_fwd_b8h16n2k_d128", "bf16_fwd_b2h16n8k_d128_causal"]
+
+
+def _ablation_legs(suffix):
+    """The legs of one ablation run, in the order build_legs runs them."""
+    if suffix == "fp8":
+        return [FP8_FWD_LEG]
+    order = list(FWD16_LEGS)
+    return [leg + suffix for leg in sorted(ABLATION_LEGS, key=order.index)]
 COUNTER_PASSES = [
     "SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA "
     "SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE",
@@ -258,7 +351,7 @@ def ablation_commands():
         if flags:
             cmds.append(f"python3 -m exact_attention_55_amd.build --variant {name} " + " ".join(flags))
             lib = f"FA_LIB=exact_attention_55_amd/variants/libfa_{name}.so "
-        only = " ".join(f"--only {leg}{suffix}" for leg in ABLATION_LEGS)
+        only = " ".join(f"--only {leg}" for leg in _ablation_legs(suffix))
         for i, ctr in enumerate(COUNTER_PASSES):
             cmds.append(f"{lib}rocprofv3 --pmc {ctr} -d <out>/{name}_p{i + 1} -o run -f csv -- "
                         f"python3 bench.py {only} --steps 3 --warmup 1 --no-cpu --no-next")
@@ -273,32 +366,29 @@ def counter_summary(run_dir):
     import csv
     rows = []
     for name, (_, suffix) in ABLATIONS.items():
+        legs = _ablation_legs(suffix)
         per = {}
         for i in range(len(COUNTER_PASSES)):
             path = os.path.join(run_dir, f"{name}_p{i + 1}", "run_counter_collection.csv")
             disp = {}
             with open(path) as f:
                 for r in csv.DictReader(f):
-                    k = r["Kernel_Name"]
-                    if "fa_fwd16" not in k:
+                    if "fa_fwd" not in r["Kernel_Name"]:
                         continue
-                    if "Li128E" in k:                        # mangled name
-                        causal = k.split("Li128E", 1)[1].startswith("Lb1")
-                    else:                                     # demangled: <T, 128, causal, ...>
-                        causal = k.split("<", 1)[1].split(",")[2].strip() == "true"
-                    key = (causal, r["Dispatch_Id"])
-                    d = disp.setdefault(key, {})
+                    d = disp.setdefault(int(r["Dispatch_Id"]), {})
                     d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
-            for (causal, _), d in disp.items():
-                acc = per.setdefault(causal, {})
-                for c, v in d.items():
+            # every step runs the legs in order, one forward dispatch each
+            for k, did in enumerate(sorted(disp)):
+                acc = per.setdefault(legs[k % len(legs)], {})
+                for c, v in disp[did].items():
                     acc.setdefault(c, []).append(v)
-        for causal, acc in sorted(per.items()):
-            m = {c: float(np.mean(v)) for c, v in acc.items()}
-            leg = ABLATION_LEGS[1 if causal else 0]
+        for leg in legs:
+            if leg not in per:
+                continue
+            m = {c: float(np.mean(v)) for c, v in per[leg].items()}
             cyc = m["GRBM_GUI_ACTIVE"] / 8                # per XCD
             waves = m["SQ_WAVES"]
-            rows.append((name, leg + suffix, {
+            rows.append((name, leg, {
                 "cycles": cyc,
                 "mfma_busy": m["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * cyc),
                 "valu_active": m["SQ_ACTIVE_INST_VALU"] / m["SQ_WAVE_CYCLES"],
@@ -605,11 +695,26 @@ def main():
     ap.add_argument("--source-hash", metavar="LEG", help="print a forward leg's kernel code hash")
     ap.add_argument("--traffic-summary", metavar="DIR",
                     help="write the HBM-traffic summary from the counter runs under DIR (no GPU)")
+    ap.add_argument("--traffic-commands", action="store_true",
+                    help="print the commands of the HBM-traffic counter runs")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="write the kernel-trace summary from the runs under DIR (no GPU)")
+    ap.add_argument("--trace-commands", action="store_true",
+                    help="print the commands of the kernel-trace runs")
     ap.add_argument("--counter-summary", metavar="DIR",
                     help="write the ablation counter table from the runs under DIR (no GPU)")
     ap.add_argument("--ablation-commands", action="store_true",
                     help="print the commands of the ablation counter runs")
     args = ap.parse_args()
+    if args.traffic_commands:
+        print("\n".join(traffic_commands()))
+        return
+    if args.trace_commands:
+        print("\n".join(trace_commands()))
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
     if args.ablation_commands:
         print("\n".join(ablation_commands()))
         return
