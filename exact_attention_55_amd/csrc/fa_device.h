@@ -306,6 +306,9 @@ __device__ __forceinline__ void grid_tile(int num_blocks, int num_tiles, bool un
 }
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ float uniform_f(float x) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
 
 // s_waitcnt immediate (gfx9 encoding) for vmcnt(0), other counters ignored.
 constexpr int kVmcnt0 = 0x0f70;

@@ -54,6 +54,9 @@ constexpr float kBig8 = 448.0f;     // per-lane tile sum of P' that forces the e
 #ifndef FA8_PRIO                   // 0: the score phase runs at normal wave priority
 #define FA8_PRIO 1
 #endif
+#ifndef FA8_KEEP                   // 0: the compiler may sink the next tile's score MFMAs behind the overflow check
+#define FA8_KEEP 1
+#endif
 #ifndef FA8_CFG_64
 #define FA8_CFG_64 4, 64, 2
 #endif
@@ -245,14 +248,9 @@ struct Wave8 {
     // Exponentials against the reference maximum; a tile whose P' sum in
     // some lane exceeds kBig8 is redone with its exact maximum (moving m,
     // rescaling O and l). Then l takes the tile's unquantised row sum.
-    // The next tile's score MFMAs are issued before this branch; the 8-bit
-    // MFMA builtins are not convergent, so the compiler sinks them behind it
-    // (their results are first used there) and the score MFMAs run next to
-    // the PV MFMAs rather than among the exponentials. Keeping them in place
-    // (a use inside the redo branch) puts this tile's scores, needed by the
-    // redo, and the next tile's in registers together, which spills at
-    // d = 128 with two waves per SIMD and measured half the speed; the
-    // second wave of the SIMD overlaps its exponentials with them instead.
+    // The redo reads this tile's scores, so they stay in registers until
+    // here, next to the next tile's (step pins those MFMAs before this
+    // branch).
     __device__ __forceinline__ void settle(const f32x16 (&s)[NKB], uint32_t (&w)[NPV][8], float cj,
                                            float bj, float lscale, float (&ls)[2]) {
         if (wave_any(ls[0] + ls[1] > kBig8)) {
@@ -347,6 +345,19 @@ struct Wave8 {
             __builtin_amdgcn_sched_barrier(0);
         }
         if (FA8_PRIO) __builtin_amdgcn_s_setprio(0);
+        // An empty use of each of the next tile's score tiles before the
+        // overflow branch: without it the compiler sinks their MFMAs (whose
+        // results are first read in the next step) behind the branch, where
+        // they run back to back with the PV MFMAs instead of among the
+        // exponentials. By this point the last of them is a chunk of
+        // exponentials old, so the use costs no wait states. Not at d = 64:
+        // the scores held together there cost the microscaled kernel its
+        // third wave per SIMD (measured 8-11 % slower), and the block-scaled
+        // one gains nothing.
+        if (FA8_KEEP && D > 64) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) asm volatile("" ::"v"(sn[kb][0]));
+        }
         settle(s, w, cj, bj, lscale, ls);
         i32x8 pf[NPV];
         pack_p(w, pf);
@@ -505,8 +516,8 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     float tks = 1.f, tvs = 1.f;            // block scales of the tile whose softmax comes next
     auto read_bs = [&](int s) {
         if constexpr (!MX) {
-            tks = *reinterpret_cast<const float*>(smem + 4 * TB + s * BSB);
-            tvs = *reinterpret_cast<const float*>(smem + 4 * TB + s * BSB + 256);
+            tks = uniform_f(*reinterpret_cast<const float*>(smem + 4 * TB + s * BSB));
+            tvs = uniform_f(*reinterpret_cast<const float*>(smem + 4 * TB + s * BSB + 256));
         }
     };
     const int nkt_total = (N + BC - 1) / BC;
@@ -540,10 +551,10 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
             const float wv = fmaxf(tvs * rsvmax, 0x1p-126f);
             const int ex = __builtin_amdgcn_frexp_expf(wv);                 // >= -125
             const float f = 2.0f * __builtin_amdgcn_frexp_mantf(wv);       // [1, 2)
-            cj = cq * tks;
-            bj = __builtin_amdgcn_logf(kPScale * f);          // log2(8 f)
-            lscale = __builtin_amdgcn_rcpf(kPScale * f);
-            vt.vblk = 126 + ex;                                // 2^(ex - 1)
+            cj = uniform_f(cq * tks);
+            bj = uniform_f(__builtin_amdgcn_logf(kPScale * f));          // log2(8 f)
+            lscale = uniform_f(__builtin_amdgcn_rcpf(kPScale * f));
+            vt.vblk = wave_uniform(126 + ex);                            // 2^(ex - 1)
         }
     };
     // The first tile copies go out before Q's loads, so the two latencies
