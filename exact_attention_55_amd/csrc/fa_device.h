@@ -315,6 +315,13 @@ constexpr int kVmcnt0 = 0x0f70;
 
 // Wait until this wave's global loads (including direct-to-LDS ones) landed.
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N of this wave's global loads are still in flight (they
+// complete in issue order for this count).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit field");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Workgroup barrier after this wave's global->LDS copies, except the newest
 // VM of them, have landed. Nothing is scheduled across it and memory

@@ -57,6 +57,9 @@ constexpr float kBig8 = 448.0f;     // per-lane tile sum of P' that forces the e
 #ifndef FA8_KEEP                   // 0: the compiler may sink the next tile's score MFMAs behind the overflow check
 #define FA8_KEEP 1
 #endif
+#ifndef FA8_RING                   // K and V tiles in LDS per workgroup (ring depth), 2 or 4
+#define FA8_RING 2
+#endif
 #ifndef FA8_CFG_64
 #define FA8_CFG_64 4, 64, 2
 #endif
@@ -116,19 +119,56 @@ struct Wave8 {
     static_assert(NKB == 2 * NPV, "one PV MFMA per two score blocks");
     using TS = TileScales<NKB, (D + 127) / 128>;
 
-    // MFMA with the tile's scales (microscaled) or unit scales.
-    static __device__ __forceinline__ f32x16 mm(const i32x8& a, const i32x8& b, const f32x16& c, int sa,
-                                                int sb) {
+    // Score MFMA with the tile's scales (microscaled) or unit scales.
+    __device__ __forceinline__ f32x16 mm(const i32x8& a, const i32x8& b, const f32x16& c, int sa,
+                                         int sb) const {
         if constexpr (MX) return mfma32_fp8s(a, b, c, sa, sb);
-        else return mfma32_fp8(a, b, c);
+        else return mfma32_fp8s(a, b, c, usc, usc);
     }
     // P V MFMA of d-block db: microscaled, the V bytes of the block and 2^-3
     // for P'; block-scaled, the power-of-two part of the tile's V scale
     // (exact) and unit P'.
-    static __device__ __forceinline__ f32x16 mm_pv(const i32x8& a, const i32x8& b, const f32x16& c,
-                                                   const TS& ts, int db) {
-        if constexpr (MX) return mfma32_fp8s(a, b, c, ts.vbyte(db), kPScaleE8M0);
-        else return mfma32_fp8s(a, b, c, ts.vblk, 127);
+    // Scale operands are the one MFMA input the compiler lets a later
+    // instruction overwrite too early: the matrix unit reads them when the
+    // MFMA starts, which for the last of a run of back-to-back MFMAs is well
+    // after its issue, and an LDS load landing in such a register right after
+    // the PV block was seen to corrupt O (run to run). The PV scales are
+    // therefore held in registers of their own (pvs) from just before their
+    // block until the next PV block begins (a whole score phase later) or,
+    // after finish(), until a read of the last PV result shows the block
+    // done; the microscaled score MFMAs keep theirs the same way.
+    // Constant scale operands (unit 2^0; 2^-3 for the microscaled P') live in
+    // registers of their own for the same reason (usc, psc).
+    static constexpr int NPS = MX ? NDB : 1;
+    int pvs[NPS];
+    int usc, psc;
+    __device__ __forceinline__ void hold_pv_scales() {
+#pragma unroll
+        for (int i = 0; i < NPS; ++i) asm volatile("" ::"v"(pvs[i]));
+        asm volatile("" ::"v"(usc), "v"(psc));
+    }
+    // (Re)load pvs for the tile with scales ts, after the previous block's
+    // are released.
+    __device__ __forceinline__ void set_pv_scales(const TS& ts) {
+        hold_pv_scales();
+#pragma unroll
+        for (int i = 0; i < NPS; ++i) {
+            pvs[i] = MX ? ts.vbyte(i) : ts.vblk;
+            asm volatile("" : "+v"(pvs[i]));
+        }
+    }
+    // P V MFMA of d-block db: microscaled, the V bytes of the block and 2^-3
+    // for P'; block-scaled, the power-of-two part of the tile's V scale
+    // (exact) and unit P'. Scales from pvs (set_pv_scales).
+    __device__ __forceinline__ f32x16 mm_pv(const i32x8& a, const i32x8& b, const f32x16& c, int db) {
+        return mfma32_fp8s(a, b, c, pvs[MX ? db : 0], psc);
+    }
+    // After a PV block with nothing of the kind behind it: a read of its last
+    // result waits for the block, then pvs may go.
+    __device__ __forceinline__ void settle_pv_block() {
+        const int r = __builtin_amdgcn_readfirstlane(__float_as_int(o[NDB - 1][0]));
+        asm volatile("" ::"s"(r));
+        hold_pv_scales();
     }
 
     f32x16 o[NDB];
@@ -139,6 +179,14 @@ struct Wave8 {
         l = 0.f;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+#pragma unroll
+        for (int i = 0; i < NPS; ++i) {
+            pvs[i] = 127;
+            asm volatile("" : "+v"(pvs[i]));
+        }
+        usc = 127;
+        psc = MX ? kPScaleE8M0 : 127;
+        asm volatile("" : "+v"(usc), "+v"(psc));
     }
 
     // K fragment (ch, kb): row perm(l32) + 32*kb, 16-byte logical chunks
@@ -156,18 +204,37 @@ struct Wave8 {
                      (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
     }
 
-    static __device__ __forceinline__ void qk(f32x16 (&s)[NKB], const i32x8 (&kf)[NKB][NCH],
-                                              const i32x8 (&qf)[NCH], int c0, int c1, const TS& ts,
-                                              const int (&qs)[NCH]) {
+    // All score MFMAs of a tile back to back (first and ragged tiles); the
+    // microscaled K scale operands stay held until a read of the last score
+    // shows the MFMAs done (see pvs).
+    __device__ __forceinline__ void qk(f32x16 (&s)[NKB], const i32x8 (&kf)[NKB][NCH],
+                                       const i32x8 (&qf)[NCH], const TS& ts, const int (&qs)[NCH]) {
+        int ks[NCH][NKB];
 #pragma unroll
-        for (int ch = c0; ch < c1; ++ch)
+        for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) s[kb] = mm(kf[kb][ch], qf[ch], s[kb], ts.kbyte(kb, ch), qs[ch]);
+            for (int kb = 0; kb < NKB; ++kb) {
+                ks[ch][kb] = MX ? ts.kbyte(kb, ch) : 127;
+                if (MX) asm volatile("" : "+v"(ks[ch][kb]));
+            }
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) s[kb] = mm(kf[kb][ch], qf[ch], s[kb], ks[ch][kb], qs[ch]);
+        if constexpr (MX) {
+            const int r = __builtin_amdgcn_readfirstlane(__float_as_int(s[NKB - 1][0]));
+            asm volatile("" ::"s"(r));
+#pragma unroll
+            for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) asm volatile("" ::"v"(ks[ch][kb]));
+#pragma unroll
+            for (int ch = 0; ch < NCH; ++ch) asm volatile("" ::"v"(qs[ch]));
+        }
     }
 
-    static __device__ __forceinline__ void scores(f32x16 (&s)[NKB], const char* kl,
-                                                  const int (&ka)[NKA][2], const i32x8 (&qf)[NCH],
-                                                  const TS& ts, const int (&qs)[NCH]) {
+    __device__ __forceinline__ void scores(f32x16 (&s)[NKB], const char* kl, const int (&ka)[NKA][2],
+                                           const i32x8 (&qf)[NCH], const TS& ts, const int (&qs)[NCH]) {
         i32x8 kf[NKB][NCH];
 #pragma unroll
         for (int ch = 0; ch < NCH; ++ch)
@@ -176,7 +243,7 @@ struct Wave8 {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
-        qk(s, kf, qf, 0, NCH, ts, qs);
+        qk(s, kf, qf, ts, qs);
     }
 
     template <bool CAUSAL>
@@ -292,10 +359,12 @@ struct Wave8 {
         for (int t = 0; t < NPV; ++t)
 #pragma unroll
             for (int db = 0; db < NDB; ++db) vf[t][db] = vfrag(vl, va, t, db);
+        set_pv_scales(ts);
 #pragma unroll
         for (int t = 0; t < NPV; ++t)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) o[db] = mm_pv(vf[t][db], pf[t], o[db], ts, db);
+            for (int db = 0; db < NDB; ++db) o[db] = mm_pv(vf[t][db], pf[t], o[db], db);
+        settle_pv_block();
     }
 
     // Pipelined step as one instruction stream in program order (every chunk
@@ -323,6 +392,14 @@ struct Wave8 {
         i32x8 vf[NPV][NDB];
         uint32_t w[NPV][8];
         float ls[2] = {0.f, 0.f};
+        // microscaled score MFMAs: their K scale operands, held until the PV
+        // block (see pvs)
+        int ks[NKF];
+#pragma unroll
+        for (int i = 0; i < NKF; ++i) {
+            ks[i] = MX ? tsn.kbyte(i % NKB, i / NKB) : 127;
+            if (MX) asm volatile("" : "+v"(ks[i]));
+        }
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) sn[kb] = f32x16{};
         if (FA8_PRIO) __builtin_amdgcn_s_setprio(1);
@@ -339,7 +416,7 @@ struct Wave8 {
                 vf[v / NDB][v % NDB] = vfrag(vl, va, v / NDB, v % NDB);
             }
             const int ch = i / NKB, kb = i % NKB;
-            sn[kb] = mm(kf[kb][ch], qf[ch], sn[kb], tsn.kbyte(kb, ch), qs[ch]);
+            sn[kb] = mm(kf[kb][ch], qf[ch], sn[kb], ks[i], qs[ch]);
 #pragma unroll
             for (int q = i * NG / NKF; q < (i + 1) * NG / NKF; ++q) prob_group(s, w, q, cj, bj, ls);
             __builtin_amdgcn_sched_barrier(0);
@@ -361,13 +438,18 @@ struct Wave8 {
         settle(s, w, cj, bj, lscale, ls);
         i32x8 pf[NPV];
         pack_p(w, pf);
+        if (MX) {
+#pragma unroll
+            for (int i = 0; i < NKF; ++i) asm volatile("" ::"v"(ks[i]));
+        }
+        set_pv_scales(ts);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < NVF; ++j) {
             const int v = j + VPD;
             if (v < NVF) vf[v / NDB][v % NDB] = vfrag(vl, va, v / NDB, v % NDB);
             const int t = j / NDB, db = j % NDB;
-            o[db] = mm_pv(vf[t][db], pf[t], o[db], ts, db);
+            o[db] = mm_pv(vf[t][db], pf[t], o[db], db);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -391,18 +473,23 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     static_assert(TB % (1024 * NW) == 0, "tile must split into 1 KB loads per wave");
     static_assert(kQuantBlockRows % BC == 0 && kQuantBlockRows % QW == 0, "scale blocks");
 
-    // LDS: K tiles in slots 0, 1 and V tiles in slots 2, 3 (tile t uses t & 1);
-    // microscaled path: then the tiles' scale bytes, K in slots 0, 1 and V
-    // in slots 2, 3 of SCB bytes each.
+    // LDS: a ring of R slots for K tiles (tile t in slot t & (R - 1)), then
+    // one for V tiles; microscaled path: then the tiles' scale bytes, R slots
+    // for K and R for V, of SCB bytes each. Copies run R - 1 tiles ahead of
+    // use. The key loop runs R tiles per trip, so every slot is a
+    // compile-time offset there.
+    constexpr int R = FA8_RING;
+    static_assert(R == 2 || R == 4, "ring depth");
+    auto ring = [](int t) { return t & (R - 1); };
     constexpr int KSB = BC * (D / 32);     // K scale bytes of a tile (one row per key)
     constexpr int VSB = (BC / 32) * D;     // V scale bytes of a tile (32-key blocks)
     constexpr int SCB = (KSB > 256 ? KSB : 256);
     static_assert(SBY % 4 == 0 || KSB + 4 <= SCB, "room for the dword-aligned start of 2-byte scale rows");
     static_assert(KSB == VSB, "one scale slot size for K and V");
     // Block-scaled path: the K and V block scales of a tile travel with its V
-    // tile into one of two BSB-byte slots (K floats, then V floats).
+    // tile into one of R BSB-byte slots (K floats, then V floats).
     constexpr int BSB = 512;
-    __shared__ __attribute__((aligned(1024))) char smem[4 * TB + (MX ? 4 * SCB : 2 * BSB)];
+    __shared__ __attribute__((aligned(1024))) char smem[2 * R * TB + (MX ? 2 * R * SCB : R * BSB)];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -471,7 +558,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     const int kdelta = (int)(kso & 3);
     const i32x4 ksrs = make_rsrc(Kg + scales_off + kso - kdelta, MX ? (kdelta + N * SBY + 3) & ~3 : 0);
     const i32x4 vsrs = make_rsrc(Vg + scales_off + (size_t)bh * nkb32 * D, MX ? (int)(nkb32 * D) : 0);
-    const uint32_t scbase = lds_addr(smem) + 4 * TB;
+    const uint32_t scbase = lds_addr(smem) + 2 * R * TB;
     auto load_sc = [&](const i32x4& rs, int t, int slot) {
         if (wave_u != 0) return;
         // 256 bytes per instruction; with KSB < 256 the upper lanes copy the
@@ -483,7 +570,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     constexpr int SW = (SBY + 3) / 4;
     // scale words of the lane for the tile in K slot ks / V slot vs
     auto read_k = [&](TS& ts, int ks) {
-        const char* p = smem + 4 * TB + ks * SCB + kdelta;
+        const char* p = smem + 2 * R * TB + ks * SCB + kdelta;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             const char* q = p + (32 * kb + krow0) * SBY;
@@ -496,7 +583,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
         }
     };
     auto read_v = [&](TS& ts, int vs) {
-        const char* q = smem + 4 * TB + (2 + vs) * SCB + hi * D + l32 * SBY;
+        const char* q = smem + 2 * R * TB + (R + vs) * SCB + hi * D + l32 * SBY;
         if constexpr (SBY == 2) ts.v[0] = *reinterpret_cast<const uint16_t*>(q);
         else if constexpr (SBY == 4) ts.v[0] = *reinterpret_cast<const uint32_t*>(q);
         else { const u32x2 x = *reinterpret_cast<const u32x2*>(q); ts.v[0] = x[0]; ts.v[SW - 1] = x[1]; }
@@ -516,22 +603,24 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     float tks = 1.f, tvs = 1.f;            // block scales of the tile whose softmax comes next
     auto read_bs = [&](int s) {
         if constexpr (!MX) {
-            tks = uniform_f(*reinterpret_cast<const float*>(smem + 4 * TB + s * BSB));
-            tvs = uniform_f(*reinterpret_cast<const float*>(smem + 4 * TB + s * BSB + 256));
+            tks = uniform_f(*reinterpret_cast<const float*>(smem + 2 * R * TB + s * BSB));
+            tvs = uniform_f(*reinterpret_cast<const float*>(smem + 2 * R * TB + s * BSB + 256));
         }
     };
     const int nkt_total = (N + BC - 1) / BC;
     const uint32_t sbase = lds_addr(smem);
-    auto load_kv = [&](const i32x4& rs, int t, int slot) {
+    // copy of K (V = false) or V tile t into its ring slot
+    auto load_kv = [&](const i32x4& rs, int t, bool V) {
         if (t >= nkt_total) return;
-        if constexpr (MX) load_sc(slot < 2 ? ksrs : vsrs, t, slot);
-        else if (slot >= 2) load_bs(t, slot - 2);
+        const int slot = (V ? R : 0) + ring(t);
+        if constexpr (MX) load_sc(V ? vsrs : ksrs, t, slot);
+        else if (V) load_bs(t, ring(t));
         const uint32_t dst = sbase + slot * TB + wave_u * NIW * 1024;
 #pragma unroll
         for (int j = 0; j < NIW; ++j) buffer_load_lds16(rs, dst + j * 1024, voff[j], t * TB);
     };
-    auto ktile = [&](int t) -> const char* { return smem + (t & 1) * TB; };
-    auto vtile = [&](int t) -> const char* { return smem + (2 + (t & 1)) * TB; };
+    auto ktile = [&](int t) -> const char* { return smem + ring(t) * TB; };
+    auto vtile = [&](int t) -> const char* { return smem + (R + ring(t)) * TB; };
     // per-tile scale terms: score multiplier, P exponent offset, l weight;
     // block-scaled path also the V scale byte of the PV MFMAs (into vt)
     auto tile_scales = [&](float& cj, float& bj, float& lscale, TS& vt) {
@@ -559,9 +648,13 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     };
     // The first tile copies go out before Q's loads, so the two latencies
     // overlap (the wait below covers both).
-    load_kv(krs, 0, 0);
-    load_kv(vrs, 0, 2);
-    load_kv(krs, 1, 1);
+    load_kv(krs, 0, false);
+    load_kv(vrs, 0, true);
+#pragma unroll
+    for (int i = 1; i < R; ++i) {
+        load_kv(krs, i, false);
+        if (i < R - 1) load_kv(vrs, i, true);
+    }
     // Q^T fragments: query q0 + l32, bytes [64*ch + 32*hi, +32) (microscaled:
     // [64*ch + 16*hi, +16) and [64*ch + 32 + 16*hi, +16), the chunk order of
     // the K fragments); its MX scale byte 2*ch + hi of the row
@@ -640,7 +733,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     if (nfull > 0) {
         float cj, bj, ls;
         tile_scales(cj, bj, ls, tv);
-        W::scores(s, ktile(0), ka, qf, tk, qs);
+        st.scores(s, ktile(0), ka, qf, tk, qs);
         st.raise_max(W::tile_max(s, cj));    // first reference maximum: exact
         if constexpr (MX) read_k(tk, 1);
         __syncthreads();                     // all waves done reading K_0's slot
@@ -649,49 +742,74 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     // Pipelined full tiles, two per trip: the scores alternate between s and
     // s2, so no step copies them.
     f32x16 s2[NKB];
+    // Block-scaled path: the two key tiles of a 128-row scale block share
+    // their scale terms, so the even tile computes them and the odd one
+    // keeps them (and its scale floats are not read). The key loop runs
+    // tiles in pairs, so the parity is known at compile time there.
+    constexpr bool PAIR = !MX && 2 * BC == kQuantBlockRows;
+    float pcj = 0.f, pbj = 0.f, pls = 0.f;
     auto full_step = [&](const f32x16 (&sc)[NKB], f32x16 (&sn)[NKB]) {
-        load_kv(krs, t + 2, t & 1);
-        load_kv(vrs, t + 1, 2 + ((t + 1) & 1));
-        float cj, bj, lscale;
-        tile_scales(cj, bj, lscale, tv);
-        st.step(sc, sn, ktile(t + 1), ka, vtile(t), va, qf, cj, bj, lscale, tk, tv, qs);
-        wait_vm_all();
+        load_kv(krs, t + R, false);
+        load_kv(vrs, t + R - 1, true);
+        if (!PAIR || (t & 1) == 0) tile_scales(pcj, pbj, pls, tv);
+        st.step(sc, sn, ktile(t + 1), ka, vtile(t), va, qf, pcj, pbj, pls, tk, tv, qs);
+        // K of t + 2 and V of t + 1 have landed. They were copied R - 2
+        // steps ago; the copies of the steps since may stay in flight
+        // (2 NIW tile copies per wave and step; wave 0, which also copies
+        // scales, then waits for some of its newer copies too).
+        if (R == 2) wait_vm_all();
+        else wait_vm<(R - 2) * 2 * NIW>();
         __syncthreads();
         if constexpr (MX) {
-            read_k(tk, t & 1);                 // tile t + 2
-            read_v(tv, (t + 1) & 1);           // tile t + 1
+            read_k(tk, ring(t + 2));           // tile t + 2
+            read_v(tv, ring(t + 1));           // tile t + 1
         }
-        read_bs((t + 1) & 1);
+        if (!PAIR || (t & 1) == 1) read_bs(ring(t + 1));
         ++t;
     };
-    for (; t + 2 < nfull; ) {
-        full_step(s, s2);
-        full_step(s2, s);
+    for (; t + R < nfull; ) {
+#pragma unroll
+        for (int u = 0; u < R; u += 2) {
+            full_step(s, s2);
+            full_step(s2, s);
+        }
     }
-    if (t + 1 < nfull) {                     // an odd number of them: the scores end in s2
-        full_step(s, s2);
+    // fewer than R full steps left; after an odd number of them the scores
+    // are in s2
+    bool odd = false;
+#pragma unroll
+    for (int u = 0; u < R - 1; ++u) {
+        if (t + 1 < nfull) {
+            if (u % 2 == 0) full_step(s, s2);
+            else full_step(s2, s);
+            odd = !odd;
+        }
+    }
+    if (odd) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) s[kb] = s2[kb];
     }
     if (nfull > 0) {                          // last full tile
-        load_kv(vrs, t + 1, 2 + ((t + 1) & 1));
+        if (R == 2) load_kv(vrs, t + 1, true);     // (with R = 4 already copied)
         float cj, bj, lscale;
         tile_scales(cj, bj, lscale, tv);
         st.finish(s, vtile(t), va, cj, bj, lscale, tv);
         wait_vm_all();
         __syncthreads();
-        if constexpr (MX) read_v(tv, (t + 1) & 1);   // the K scales of t + 1 are in tk already
-        read_bs((t + 1) & 1);
+        if constexpr (MX) read_v(tv, ring(t + 1));   // the K scales of t + 1 are in tk already
+        read_bs(ring(t + 1));
         ++t;
     }
     for (; t < nkt; ++t) {                    // ragged end / causal diagonal
-        load_kv(krs, t + 1, (t + 1) & 1);
-        load_kv(vrs, t + 1, 2 + ((t + 1) & 1));
+        // one tile ahead (with R = 4 possibly a second copy of a tile already
+        // there: the same bytes into a slot no wave reads in this iteration)
+        load_kv(krs, t + 1, false);
+        load_kv(vrs, t + 1, true);
         const int k0 = t * BC;
         if (!CAUSAL || k0 <= q0 + QW - 1) {
             float cj, bj, lscale;
             tile_scales(cj, bj, lscale, tv);
-            W::scores(s, ktile(t), ka, qf, tk, qs);
+            st.scores(s, ktile(t), ka, qf, tk, qs);
             W::template mask<CAUSAL>(s, k0, q0, N, hi, l32);
             if (t == 0) st.raise_max(W::tile_max(s, cj));   // first reference maximum: exact
             st.finish(s, vtile(t), va, cj, bj, lscale, tv);
@@ -699,10 +817,10 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
         wait_vm_all();
         __syncthreads();
         if constexpr (MX) {
-            read_k(tk, (t + 1) & 1);
-            read_v(tv, (t + 1) & 1);
+            read_k(tk, ring(t + 1));
+            read_v(tv, ring(t + 1));
         }
-        read_bs((t + 1) & 1);
+        read_bs(ring(t + 1));
     }
 
     // ---- epilogue: O = O_acc * sv_max / (8 l) (microscaled: O_acc / l, the
