@@ -7,8 +7,11 @@
 // внимание стало быстрее", section "Метод", item 3 (block quantisation, one
 // scale per block).
 //
-// One workgroup per (head, 128-row block). A row of d elements is spread over
-// d/8 lanes, 8 contiguous elements per lane (one 16-byte load). The Sylvester
+// One workgroup per (head, 128-row block); with the rotary step, per 128-row
+// block of up to four consecutive heads, whose rows share their cosines and
+// sines (computed once, while the first head's loads are in flight). A row
+// of d elements is spread over d/8 lanes, 8 contiguous elements per lane (one
+// 16-byte load). The Sylvester
 // Walsh-Hadamard butterflies of span 1, 2, 4 run inside a lane, spans 8 .. d/2
 // across lanes (xor-partner exchange). The block is held in registers until
 // its amax is known, so the input is read once and the codes written once.
@@ -148,7 +151,9 @@ __device__ __forceinline__ float block_scale(float amax, int pow2) {
     return __builtin_amdgcn_ldexpf(1.0f, __builtin_amdgcn_frexp_expf(s));
 }
 
-template <typename T, int D, bool HAD, int MODE, int ROPE>
+// HB heads per workgroup (rotary step: the same 128-row block of HB
+// consecutive heads, which share every row's cosines and sines).
+template <typename T, int D, bool HAD, int MODE, int ROPE, int HB = 1>
 __global__ void __launch_bounds__((quant_threads<D, ROPE>()))
 fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t* __restrict__ signs,
                 float* __restrict__ scales, unsigned* __restrict__ gamax, int N, int H, int nblk,
@@ -158,7 +163,10 @@ fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t*
     constexpr int LPR = D / 8;                 // lanes per row
     constexpr int RPP = NT / LPR;              // rows per pass
     constexpr int NPASS = kQuantBlockRows / RPP;
-    __shared__ float red[NT / 64];
+    static_assert(HB == 1 || ROPE != 0, "several heads per workgroup only share rotary terms");
+    // one reduction buffer per head of the workgroup (a buffer is not
+    // written again before every wave has read it)
+    __shared__ float red[HB][NT / 64];
 
     // SPLIT: elements 0..3 of lane j are columns 4j.., elements 4..7 columns
     // d/2 + 4j.. (the half pairing); otherwise columns 8j .. 8j+7.
@@ -167,180 +175,197 @@ fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t*
     const int tid = threadIdx.x;
     const int j = tid % LPR, rp = tid / LPR;
     const int c0 = SPLIT ? 4 * j : 8 * j, c1 = SPLIT ? D / 2 + 4 * j : 8 * j + 4;
-    const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
-    const int h = bh % H;
-    const size_t head = (size_t)bh * N * D;
+    const int blk = blockIdx.x % nblk;
+    // rotary terms of the thread's rows, computed once for the HB heads
+    float rsn[ROPE != 0 ? NPASS : 1][4], rcs[ROPE != 0 ? NPASS : 1][4];
+    bool rope_ready = false;
+#pragma unroll 1
+    for (int hh = 0; hh < HB; ++hh) {
+        const int bh = (blockIdx.x / nblk) * HB + hh;
+        const int gslot = bh * nblk + blk;            // scale slot of this (head, block)
+        const int h = bh % H;
+        const size_t head = (size_t)bh * N * D;
 
-    float sg[8];
-    if (HAD) {
-        const uint32_t w0 = *reinterpret_cast<const uint32_t*>(signs + (size_t)h * D + c0);
-        const uint32_t w1 = *reinterpret_cast<const uint32_t*>(signs + (size_t)h * D + c1);
+        float sg[8];
+        if (HAD) {
+            const uint32_t w0 = *reinterpret_cast<const uint32_t*>(signs + (size_t)h * D + c0);
+            const uint32_t w1 = *reinterpret_cast<const uint32_t*>(signs + (size_t)h * D + c1);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            sg[e] = (float)(int8_t)((w0 >> (8 * e)) & 0xff);
-            sg[e + 4] = (float)(int8_t)((w1 >> (8 * e)) & 0xff);
-        }
-    }
-
-    // All of the thread's row loads are issued before any is used, so they
-    // are in flight together (one at a time leaves each waiting a full
-    // memory latency).
-    // Rows past the end read the head's last row (always valid, N >= 1) and
-    // are zeroed, so the loads carry no branch.
-    u32x4 raw[NPASS];
-#pragma unroll
-    for (int p = 0; p < NPASS; ++p) {
-        const int row = blk * kQuantBlockRows + p * RPP + rp;
-        const T* xr = X + head + (size_t)min(row, N - 1) * D;
-        if constexpr (SPLIT) {
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(xr + c0);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(xr + c1);
-            raw[p] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-        } else {
-            raw[p] = *reinterpret_cast<const u32x4*>(xr + c0);
-        }
-    }
-#pragma unroll
-    for (int p = 0; p < NPASS; ++p)
-        if (blk * kQuantBlockRows + p * RPP + rp >= N) raw[p] = u32x4{0, 0, 0, 0};
-    float v[NPASS][8];
-    float amax = 0.f;
-#pragma unroll
-    for (int p = 0; p < NPASS; ++p) {
-        const int row = blk * kQuantBlockRows + p * RPP + rp;
-        typedef __attribute__((ext_vector_type(8))) T T8;
-        const T8 x = __builtin_bit_cast(T8, raw[p]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[p][e] = to_f(x[e]);
-        if (ROPE != 0) {
-            const float pos = (float)(rf.pos0 + row);
-            if (ROPE == 1) {
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    float sn, cs;
-                    sincos_f32(pos * rf.w[4 * j + k], &sn, &cs);
-                    const float a = v[p][2 * k], b = v[p][2 * k + 1];
-                    v[p][2 * k] = a * cs - b * sn;
-                    v[p][2 * k + 1] = a * sn + b * cs;
-                }
-            } else {
-                // pairs (4j + k, d/2 + 4j + k) are elements k, k + 4
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    float sn, cs;
-                    sincos_f32(pos * rf.w[4 * j + k], &sn, &cs);
-                    const float a = v[p][k], b = v[p][k + 4];
-                    v[p][k] = a * cs - b * sn;
-                    v[p][k + 4] = a * sn + b * cs;
-                }
+            for (int e = 0; e < 4; ++e) {
+                sg[e] = (float)(int8_t)((w0 >> (8 * e)) & 0xff);
+                sg[e + 4] = (float)(int8_t)((w1 >> (8 * e)) & 0xff);
             }
         }
-        if (HAD) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[p][e] *= sg[e];
-            // in-lane butterflies, spans 1, 2, 4
-#pragma unroll
-            for (int span = 1; span < 8; span *= 2)
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if ((e & span) == 0) {
-                        const float a = v[p][e], b = v[p][e + span];
-                        v[p][e] = a + b;
-                        v[p][e + span] = a - b;
-                    }
-            // cross-lane butterflies, spans 8 .. D/2 (partner lane j ^ m)
-            static_for<0, 5>([&](auto mc) {
-                constexpr int m = 1 << decltype(mc)::value;
-                if constexpr (m < LPR) {
-                    const bool upper = (j & m) != 0;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float other = lane_xor<m>(v[p][e]);
-                        v[p][e] = upper ? (other - v[p][e]) : (v[p][e] + other);
-                    }
-                }
-            });
-            const float rs = 1.0f / __builtin_sqrtf((float)D);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[p][e] *= rs;
-        }
-        if (row < N) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[p][e]));
-        }
-    }
 
-    if (MODE == 3) {
+        // All of the thread's row loads are issued before any is used, so they
+        // are in flight together (one at a time leaves each waiting a full
+        // memory latency).
+        // Rows past the end read the head's last row (always valid, N >= 1) and
+        // are zeroed, so the loads carry no branch.
+        u32x4 raw[NPASS];
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
             const int row = blk * kQuantBlockRows + p * RPP + rp;
-            float la = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) la = fmaxf(la, fabsf(v[p][e]));
-            la = fmaxf(la, lane_xor<1>(la));
-            la = fmaxf(la, lane_xor<2>(la));
-            const int ex = mx_exponent(la);
-            if (row < N) {
-                uint32_t w[2];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const float* x = &v[p][4 * h];
-                    w[h] = e4m3x2(__builtin_ldexpf(x[0], -ex), __builtin_ldexpf(x[1], -ex)) |
-                           (e4m3x2(__builtin_ldexpf(x[2], -ex), __builtin_ldexpf(x[3], -ex)) << 16);
-                }
-                *reinterpret_cast<u32x2*>(X8 + head + (size_t)row * D + 8 * j) = u32x2{w[0], w[1]};
-                if ((j & 3) == 0)
-                    reinterpret_cast<uint8_t*>(scales)[((size_t)bh * N + row) * (D / 32) + j / 4] =
-                        (uint8_t)(ex + 127);
-            }
-        }
-        return;
-    }
-
-    if (MODE != 2) {
-        // workgroup amax
-#pragma unroll
-        for (int m = 32; m >= 1; m /= 2) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
-        if ((tid & 63) == 0) red[tid >> 6] = amax;
-        __syncthreads();
-        amax = red[0];
-#pragma unroll
-        for (int w = 1; w < NT / 64; ++w) amax = fmaxf(amax, red[w]);
-    }
-    if (MODE == 1) {
-        if (tid == 0) atomicMax(gamax, __float_as_uint(amax));
-        return;
-    }
-    if (MODE == 2) amax = __uint_as_float(*gamax);
-
-    const float scale = block_scale(amax, pow2);
-    if (MODE == 0 && tid == 0) scales[blockIdx.x] = scale;
-    // x / scale. Without the Hadamard this is the IEEE division, so the codes
-    // equal those of the same float32 steps exactly. With it, the values
-    // already carry float32 butterfly rounding (a code next to an e4m3
-    // rounding boundary may land on the neighbouring one either way), and a
-    // multiply by the rounded reciprocal, at most one float32 ulp away, adds
-    // only more of the same; it replaces ~10 instructions per element in a
-    // kernel that is VALU-bound with the transform.
-    const float inv = 1.0f / scale;
-    auto qs = [&](float x) { return HAD ? x * inv : x / scale; };
-#pragma unroll
-    for (int p = 0; p < NPASS; ++p) {
-        const int row = blk * kQuantBlockRows + p * RPP + rp;
-        if (row < N) {
-            const uint32_t w0 = e4m3x2(qs(v[p][0]), qs(v[p][1])) |
-                                (e4m3x2(qs(v[p][2]), qs(v[p][3])) << 16);
-            const uint32_t w1 = e4m3x2(qs(v[p][4]), qs(v[p][5])) |
-                                (e4m3x2(qs(v[p][6]), qs(v[p][7])) << 16);
-            uint8_t* xr = X8 + head + (size_t)row * D;
+            const T* xr = X + head + (size_t)min(row, N - 1) * D;
             if constexpr (SPLIT) {
-                *reinterpret_cast<uint32_t*>(xr + c0) = w0;
-                *reinterpret_cast<uint32_t*>(xr + c1) = w1;
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(xr + c0);
+                const u32x2 hi = *reinterpret_cast<const u32x2*>(xr + c1);
+                raw[p] = u32x4{lo[0], lo[1], hi[0], hi[1]};
             } else {
-                *reinterpret_cast<u32x2*>(xr + c0) = u32x2{w0, w1};
+                raw[p] = *reinterpret_cast<const u32x4*>(xr + c0);
             }
         }
-    }
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p)
+            if (blk * kQuantBlockRows + p * RPP + rp >= N) raw[p] = u32x4{0, 0, 0, 0};
+        // while the loads are in flight: the rotary terms (first head only)
+        if (ROPE != 0 && !rope_ready) {
+#pragma unroll
+            for (int p = 0; p < NPASS; ++p) {
+                const float pos = (float)(rf.pos0 + blk * kQuantBlockRows + p * RPP + rp);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    sincos_f32(pos * rf.w[4 * j + k], &rsn[p][k], &rcs[p][k]);
+                }
+            }
+            rope_ready = true;
+        }
+        float v[NPASS][8];
+        float amax = 0.f;
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+            const int row = blk * kQuantBlockRows + p * RPP + rp;
+            typedef __attribute__((ext_vector_type(8))) T T8;
+            const T8 x = __builtin_bit_cast(T8, raw[p]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[p][e] = to_f(x[e]);
+            if (ROPE != 0) {
+                if (ROPE == 1) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const float sn = rsn[p][k], cs = rcs[p][k];
+                        const float a = v[p][2 * k], b = v[p][2 * k + 1];
+                        v[p][2 * k] = a * cs - b * sn;
+                        v[p][2 * k + 1] = a * sn + b * cs;
+                    }
+                } else {
+                    // pairs (4j + k, d/2 + 4j + k) are elements k, k + 4
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const float sn = rsn[p][k], cs = rcs[p][k];
+                        const float a = v[p][k], b = v[p][k + 4];
+                        v[p][k] = a * cs - b * sn;
+                        v[p][k + 4] = a * sn + b * cs;
+                    }
+                }
+            }
+            if (HAD) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[p][e] *= sg[e];
+                // in-lane butterflies, spans 1, 2, 4
+#pragma unroll
+                for (int span = 1; span < 8; span *= 2)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if ((e & span) == 0) {
+                            const float a = v[p][e], b = v[p][e + span];
+                            v[p][e] = a + b;
+                            v[p][e + span] = a - b;
+                        }
+                // cross-lane butterflies, spans 8 .. D/2 (partner lane j ^ m)
+                static_for<0, 5>([&](auto mc) {
+                    constexpr int m = 1 << decltype(mc)::value;
+                    if constexpr (m < LPR) {
+                        const bool upper = (j & m) != 0;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float other = lane_xor<m>(v[p][e]);
+                            v[p][e] = upper ? (other - v[p][e]) : (v[p][e] + other);
+                        }
+                    }
+                });
+                const float rs = 1.0f / __builtin_sqrtf((float)D);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[p][e] *= rs;
+            }
+            if (row < N) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[p][e]));
+            }
+        }
+
+        if (MODE == 3) {
+#pragma unroll
+            for (int p = 0; p < NPASS; ++p) {
+                const int row = blk * kQuantBlockRows + p * RPP + rp;
+                float la = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) la = fmaxf(la, fabsf(v[p][e]));
+                la = fmaxf(la, lane_xor<1>(la));
+                la = fmaxf(la, lane_xor<2>(la));
+                const int ex = mx_exponent(la);
+                if (row < N) {
+                    uint32_t w[2];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const float* x = &v[p][4 * h];
+                        w[h] = e4m3x2(__builtin_ldexpf(x[0], -ex), __builtin_ldexpf(x[1], -ex)) |
+                               (e4m3x2(__builtin_ldexpf(x[2], -ex), __builtin_ldexpf(x[3], -ex)) << 16);
+                    }
+                    *reinterpret_cast<u32x2*>(X8 + head + (size_t)row * D + 8 * j) = u32x2{w[0], w[1]};
+                    if ((j & 3) == 0)
+                        reinterpret_cast<uint8_t*>(scales)[((size_t)bh * N + row) * (D / 32) + j / 4] =
+                            (uint8_t)(ex + 127);
+                }
+            }
+            return;
+        }
+
+        if (MODE != 2) {
+            // workgroup amax
+#pragma unroll
+            for (int m = 32; m >= 1; m /= 2) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+            if ((tid & 63) == 0) red[hh][tid >> 6] = amax;
+            __syncthreads();
+            amax = red[hh][0];
+#pragma unroll
+            for (int w = 1; w < NT / 64; ++w) amax = fmaxf(amax, red[hh][w]);
+        }
+        if (MODE == 1) {
+            if (tid == 0) atomicMax(gamax, __float_as_uint(amax));
+            continue;
+        }
+        if (MODE == 2) amax = __uint_as_float(*gamax);
+
+        const float scale = block_scale(amax, pow2);
+        if (MODE == 0 && tid == 0) scales[gslot] = scale;
+        // x / scale. Without the Hadamard this is the IEEE division, so the codes
+        // equal those of the same float32 steps exactly. With it, the values
+        // already carry float32 butterfly rounding (a code next to an e4m3
+        // rounding boundary may land on the neighbouring one either way), and a
+        // multiply by the rounded reciprocal, at most one float32 ulp away, adds
+        // only more of the same; it replaces ~10 instructions per element in a
+        // kernel that is VALU-bound with the transform.
+        const float inv = 1.0f / scale;
+        auto qs = [&](float x) { return HAD ? x * inv : x / scale; };
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+            const int row = blk * kQuantBlockRows + p * RPP + rp;
+            if (row < N) {
+                const uint32_t w0 = e4m3x2(qs(v[p][0]), qs(v[p][1])) |
+                                    (e4m3x2(qs(v[p][2]), qs(v[p][3])) << 16);
+                const uint32_t w1 = e4m3x2(qs(v[p][4]), qs(v[p][5])) |
+                                    (e4m3x2(qs(v[p][6]), qs(v[p][7])) << 16);
+                uint8_t* xr = X8 + head + (size_t)row * D;
+                if constexpr (SPLIT) {
+                    *reinterpret_cast<uint32_t*>(xr + c0) = w0;
+                    *reinterpret_cast<uint32_t*>(xr + c1) = w1;
+                } else {
+                    *reinterpret_cast<u32x2*>(xr + c0) = u32x2{w0, w1};
+                }
+            }
+        }
+    }   // heads of the workgroup
 }
 
 // Microscaling along the sequence (V): each thread owns 8 adjacent columns
@@ -436,9 +461,24 @@ static hipError_t prep_t(const PrepArgs& a, hipStream_t s) {
         return hipGetLastError();
     }
     if (a.block_rows != 0) {
-        hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 0, ROPE>), dim3((unsigned)grid),
-                           dim3(quant_threads<D, ROPE>()), 0, s, x, a.x8, a.signs, scales, nullptr, a.N, a.H, nblk,
-                           a.rope, a.pow2);
+        // The rotary step: four (else two) heads per workgroup share the
+        // cosines and sines of its rows (heads of a workgroup are consecutive
+        // in [B][H] order, so B*H must divide evenly). Measured on
+        // B=4 H=16 N=4096 d=128: 1.53x the plain prep's time with one head
+        // per workgroup, 1.30x with two, 1.23x with four.
+        const long long heads = (long long)a.B * a.H;
+        if (ROPE != 0 && heads % 4 == 0)
+            hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 0, ROPE, ROPE != 0 ? 4 : 1>), dim3((unsigned)(grid / 4)),
+                               dim3(quant_threads<D, ROPE>()), 0, s, x, a.x8, a.signs, scales, nullptr, a.N,
+                               a.H, nblk, a.rope, a.pow2);
+        else if (ROPE != 0 && heads % 2 == 0)
+            hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 0, ROPE, ROPE != 0 ? 2 : 1>), dim3((unsigned)(grid / 2)),
+                               dim3(quant_threads<D, ROPE>()), 0, s, x, a.x8, a.signs, scales, nullptr, a.N,
+                               a.H, nblk, a.rope, a.pow2);
+        else
+            hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 0, ROPE>), dim3((unsigned)grid),
+                               dim3(quant_threads<D, ROPE>()), 0, s, x, a.x8, a.signs, scales, nullptr, a.N,
+                               a.H, nblk, a.rope, a.pow2);
         return hipGetLastError();
     }
     // Per-tensor: the first scale slot serves as the amax accumulator; the

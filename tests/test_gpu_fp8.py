@@ -310,6 +310,22 @@ def test_prep_rope_matches_oracle(d, style, had):
     compare_codes(codes, scales, rc, rs, exact=False)
 
 
+@pytest.mark.parametrize("B,H", [(4, 3), (2, 3), (1, 3)])
+@pytest.mark.parametrize("style", ["interleaved", "half"])
+def test_prep_rope_heads_per_workgroup(B, H, style):
+    """The rotary prep runs four, two or one heads per workgroup (B*H
+    divisible by 4, by 2, or neither); with H = 3 the groups of four and two
+    cross batch boundaries, so every head still takes its own signs."""
+    say(f"prep rope heads per workgroup B={B} H={H} {style}")
+    N, d = 300, 128
+    x, _, _ = make_qkv(B, H, N, d, seed=53 + B, dtype="bf16", outliers=True)
+    signs = make_signs(H, d, 53)
+    rope = (style, 10000.0, 5)
+    _, codes, scales = gpu_prep(x, signs, 128, rope)
+    rc, rs = oracle.fp8_quantize(to_f64(x), signs, 128, rope)
+    compare_codes(codes, scales, rc, rs, exact=False)
+
+
 @pytest.mark.parametrize("style", ["interleaved", "half"])
 def test_prep_rope_large_positions_and_tensor_scale(style):
     """Positions near 2^24 (large angles) and the per-tensor scale."""
