@@ -322,7 +322,9 @@ ABLATIONS = {
     "read_ahead_2": (["-DFA16_KPD=2", "-DFA16_VPD=2"], ""),
     "eight_waves": (["-DFA16_CFG_128=8,1,64,2"], ""),
     "pipelined_64_rows": (None, "_pipelined"),
-    "fp8_default": (None, "fp8"),          # the fp8 forward's counters, for reference
+    "fp8_default": (None, "fp8"),          # the fp8 forward's counters
+    "fp8_unpinned_scores": (["-DFA8_KEEP=0"], "fp8"),
+    "fp8_ring_4": (["-DFA8_RING=4"], "fp8"),
 }
 ABLATION_LEGS = ["bf16_fwd_b8h16n2k_d128", "bf16_fwd_b2h16n8k_d128_causal"]
 
@@ -399,8 +401,9 @@ def counter_summary(run_dir):
                 "lds_per_wave": m["SQ_INSTS_LDS"] / waves,
                 "bank_conflicts": m["SQ_LDS_BANK_CONFLICT"],
             }))
-    lines = ["# Ablations of the 16-bit forward at d = 128 (SQ counters)", "",
-             "Each variant is a compile-time switch of `csrc/fa_fwd16.hip` built with",
+    lines = ["# Ablations of the 16-bit and fp8 forwards at d = 128 (SQ counters)", "",
+             "Each variant is a compile-time switch of `csrc/fa_fwd16.hip` (FA16_*) or",
+             "`csrc/fa_fwd_fp8.hip` (FA8_*) built with",
              "`python3 -m exact_attention_55_amd.build --variant NAME -D...` and loaded through",
              "`FA_LIB`; `pipelined_64_rows` is the default library with `FA_FWD_PIPELINED`.",
              "Commands (repository root, TMPDIR=/tmp, <out> a scratch directory):", ""]

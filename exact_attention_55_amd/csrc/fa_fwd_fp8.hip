@@ -478,7 +478,8 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     // for K and R for V, of SCB bytes each. Copies run R - 1 tiles ahead of
     // use. The key loop runs R tiles per trip, so every slot is a
     // compile-time offset there.
-    constexpr int R = FA8_RING;
+    // (d = 256 keeps 2: with 4 the microscaled kernel runs out of registers)
+    constexpr int R = D == 256 ? 2 : FA8_RING;
     static_assert(R == 2 || R == 4, "ring depth");
     auto ring = [](int t) { return t & (R - 1); };
     constexpr int KSB = BC * (D / 32);     // K scale bytes of a tile (one row per key)
