@@ -463,15 +463,17 @@ static hipError_t prep_t(const PrepArgs& a, hipStream_t s) {
     if (a.block_rows != 0) {
         // The rotary step: four (else two) heads per workgroup share the
         // cosines and sines of its rows (heads of a workgroup are consecutive
-        // in [B][H] order, so B*H must divide evenly). Measured on
-        // B=4 H=16 N=4096 d=128: 1.53x the plain prep's time with one head
-        // per workgroup, 1.30x with two, 1.23x with four.
+        // in [B][H] order, so B*H must divide evenly), as long as that leaves
+        // at least 512 workgroups (fewer starve the memory system: small
+        // shapes keep one head each). Measured on B=4 H=16 N=4096 d=128:
+        // 1.53x the plain prep's time with one head per workgroup, 1.30x
+        // with two, 1.23x with four.
         const long long heads = (long long)a.B * a.H;
-        if (ROPE != 0 && heads % 4 == 0)
+        if (ROPE != 0 && heads % 4 == 0 && grid / 4 >= 512)
             hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 0, ROPE, ROPE != 0 ? 4 : 1>), dim3((unsigned)(grid / 4)),
                                dim3(quant_threads<D, ROPE>()), 0, s, x, a.x8, a.signs, scales, nullptr, a.N,
                                a.H, nblk, a.rope, a.pow2);
-        else if (ROPE != 0 && heads % 2 == 0)
+        else if (ROPE != 0 && heads % 2 == 0 && grid / 2 >= 512)
             hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 0, ROPE, ROPE != 0 ? 2 : 1>), dim3((unsigned)(grid / 2)),
                                dim3(quant_threads<D, ROPE>()), 0, s, x, a.x8, a.signs, scales, nullptr, a.N,
                                a.H, nblk, a.rope, a.pow2);

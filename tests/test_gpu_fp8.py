@@ -314,16 +314,24 @@ def test_prep_rope_matches_oracle(d, style, had):
 @pytest.mark.parametrize("style", ["interleaved", "half"])
 def test_prep_rope_heads_per_workgroup(B, H, style):
     """The rotary prep runs four, two or one heads per workgroup (B*H
-    divisible by 4, by 2, or neither); with H = 3 the groups of four and two
-    cross batch boundaries, so every head still takes its own signs."""
+    divisible by 4, by 2, or neither, with at least 512 workgroups left);
+    with H = 3 the groups of four and two cross batch boundaries, so every
+    head must still take its own signs and scale slots. N gives 171 blocks
+    per head (the last one ragged); the oracle checks sampled (head, block)
+    pairs, each quantised from its own rows at its own positions."""
     say(f"prep rope heads per workgroup B={B} H={H} {style}")
-    N, d = 300, 128
+    N, d, pos0 = 21800, 128, 5
     x, _, _ = make_qkv(B, H, N, d, seed=53 + B, dtype="bf16", outliers=True)
     signs = make_signs(H, d, 53)
-    rope = (style, 10000.0, 5)
-    _, codes, scales = gpu_prep(x, signs, 128, rope)
-    rc, rs = oracle.fp8_quantize(to_f64(x), signs, 128, rope)
-    compare_codes(codes, scales, rc, rs, exact=False)
+    _, codes, scales = gpu_prep(x, signs, 128, (style, 10000.0, pos0))
+    x64 = to_f64(x)
+    nblk = (N + 127) // 128
+    for b, h in sorted({(0, 0), (B - 1, H - 1), (B // 2, 1)}):
+        for blk in (0, nblk // 2, nblk - 1):
+            r0, r1 = 128 * blk, min(N, 128 * blk + 128)
+            rc, rs = oracle.fp8_quantize(x64[b:b + 1, h:h + 1, r0:r1], signs[h:h + 1], 128,
+                                         (style, 10000.0, pos0 + r0))
+            compare_codes(codes[b, h, r0:r1], scales[b, h, blk:blk + 1], rc[0, 0], rs[0, 0], exact=False)
 
 
 @pytest.mark.parametrize("style", ["interleaved", "half"])
