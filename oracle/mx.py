@@ -19,7 +19,11 @@ Readings (listed in the design notes):
 * element code = e4m3 round-to-nearest-even of x / X, saturated to +-448
   (x / X lies in [256, 512) for the largest element of a block, so the top
   of that range clamps);
-* the value is decode(code) * X; the stored scale byte is e + 127.
+* the value is decode(code) * X; the stored scale byte is e + 127;
+* optionally (along d only, prescale = p) the rotated float32 values are
+  multiplied by p in float32 before the block maximum, so the codes and
+  exponents represent x * p (the form in which Q carries
+  softmax_scale * log2(e) for the fp8 forward).
 The rotated values are formed in float64 and rounded once to float32 before
 the block maximum (the GPU's precision, as for the per-128-row quantiser);
 x / X is exact in float32 because X is a power of two.
@@ -43,19 +47,25 @@ def _block_exponents(amax):
     return np.clip(e, -127, 127).astype(np.int32)
 
 
-def mx_quantize(x, axis, signs=None):
+def mx_quantize(x, axis, signs=None, prescale=None):
     """MX e4m3 quantisation of x [B, H, N, d].
 
     axis: "d" (blocks of 32 columns of a row: Q, K) or "n" (blocks of 32
     rows of a column: V). signs: [H, d] of +-1 to apply the random-sign
-    Hadamard along d first (Q and K), or None.
+    Hadamard along d first (Q and K), or None. prescale: None, or a float32
+    factor applied to the rotated values (axis "d" only).
     Returns (codes uint8 [B,H,N,d], exponents int32: [B,H,N,d/32] for "d",
     [B,H,ceil(N/32),d] for "n").
     """
     x = np.asarray(x, dtype=np.float64)
     if signs is not None:
         x = random_sign_hadamard(x, signs)
-    y = x.astype(np.float32).astype(np.float64)
+    y = x.astype(np.float32)
+    if prescale is not None:
+        if axis != "d":
+            raise ValueError("prescale is defined along d only")
+        y = (y * np.float32(prescale)).astype(np.float32)
+    y = y.astype(np.float64)
     B, H, N, d = y.shape
     if axis == "d":
         if d % MX_BLOCK:
@@ -88,13 +98,19 @@ def mx_dequantize(codes, exps, axis):
     return v * rows
 
 
-def fake_quant_attention_mx(q, k, v, signs=None, causal=False, scale=None):
+def fake_quant_attention_mx(q, k, v, signs=None, causal=False, scale=None, prescaled=False):
     """Exact float64 attention of the MX-dequantised inputs (Q, K along d
     after the optional random-sign Hadamard; V along the sequence).
-    Returns (O, LSE)."""
+    prescaled: Q quantised as x * float32(scale * log2(e)); the dequantised
+    logits are then base-2 exponents and the attention takes the softmax
+    scale ln(2). Returns (O, LSE)."""
     from .attention import attention
-    qc, qe = mx_quantize(q, "d", signs)
+    d = np.asarray(q).shape[-1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    pq = np.float32(scale * np.log2(np.e)) if prescaled else None
+    qc, qe = mx_quantize(q, "d", signs, prescale=pq)
     kc, ke = mx_quantize(k, "d", signs)
     vc, ve = mx_quantize(v, "n", None)
     return attention(mx_dequantize(qc, qe, "d"), mx_dequantize(kc, ke, "d"),
-                     mx_dequantize(vc, ve, "n"), causal, scale)
+                     mx_dequantize(vc, ve, "n"), causal, np.log(2.0) if prescaled else scale)

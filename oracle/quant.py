@@ -24,6 +24,11 @@ Readings (the pages give no block shape, scale rule or rounding):
   through an E8M0 scale byte;
 * code = e4m3 round-to-nearest-even, saturating, of x / scale;
 * dequantised value = decode(code) * scale.
+* optionally (prescale = p, the form the fp8 forward reads without a
+  multiply per score when p = softmax_scale * log2(e)) the rotated float32
+  values are multiplied by p in float32 before the block maximum, so the
+  codes and scales represent x * p; with p a power of two this only moves
+  every scale by p.
 
 Precision of the integer decision: the rotated value is formed in float64
 (the definition) and then rounded once to float32, the precision the GPU works
@@ -41,16 +46,19 @@ from .hadamard import random_sign_hadamard
 from .rope import rope as rotary
 
 
-def _rotated_f32(x, signs, rope=None):
+def _rotated_f32(x, signs, rope=None, prescale=None):
     """The values that get quantised: x, optionally after the rotary
     embedding (rope = (style, base, pos0)), then x M when signs are given,
-    rounded once to float32."""
+    rounded once to float32; with prescale, then times prescale in float32."""
     x = np.asarray(x, dtype=np.float64)
     if rope is not None:
         x = rotary(x, *rope)
     if signs is not None:
         x = random_sign_hadamard(x, signs)
-    return x.astype(np.float32)
+    y = x.astype(np.float32)
+    if prescale is not None:
+        y = (y * np.float32(prescale)).astype(np.float32)
+    return y
 
 
 def pow2_ceil_f32(s):
@@ -62,7 +70,7 @@ def pow2_ceil_f32(s):
     return np.where(m == 0.5, s, up).astype(np.float32)
 
 
-def fp8_quantize(x, signs=None, block_rows=128, rope=None, pow2=False):
+def fp8_quantize(x, signs=None, block_rows=128, rope=None, pow2=False, prescale=None):
     """Quantise x [B, H, N, d] to e4m3 codes with float32 scales.
 
     signs: [H, d] of +-1 to apply the random-sign Hadamard first (Q and K), or
@@ -71,11 +79,13 @@ def fp8_quantize(x, signs=None, block_rows=128, rope=None, pow2=False):
     rope: None, or (style, base, pos0) to apply the rotary embedding first
     (the fused rotary + Hadamard + quantisation step).
     pow2: round each scale up to a power of two (pow2_ceil_f32).
+    prescale: None, or a float32 factor applied to the rotated values before
+    the block maximum (the result then represents x * prescale).
     Returns (codes uint8 [B,H,N,d], scales float32 [B,H,ceil(N/block_rows)];
     per-tensor mode returns the same scale in every slot of a
     [B,H,ceil(N/128)] array so both modes have one layout).
     """
-    y = _rotated_f32(x, signs, rope)
+    y = _rotated_f32(x, signs, rope, prescale)
     B, H, N, d = y.shape
     br = block_rows if block_rows > 0 else 128
     nb = (N + br - 1) // br
@@ -106,7 +116,7 @@ def fp8_dequantize(codes, scales, block_rows=128):
 
 
 def fake_quant_attention(q, k, v, signs=None, block_rows=128, causal=False,
-                         scale=None, rope=None, v_pow2=True):
+                         scale=None, rope=None, v_pow2=True, prescaled=False):
     """Exact float64 attention on the dequantised fp8 inputs.
 
     Q and K are rotated by the same random-sign Hadamard (when signs is given)
@@ -117,16 +127,23 @@ def fake_quant_attention(q, k, v, signs=None, block_rows=128, causal=False,
     of P) and a diagnostic for its output. With rope = (style, base, pos0)
     Q and K get the rotary embedding before the rotation and quantisation.
     v_pow2: V's block scales are powers of two (the form the fp8 forward
-    applies exactly). Returns (O, LSE, (qc, qs), (kc, ks), (vc, vs)).
+    applies exactly).
+    prescaled: Q is quantised as x * p, p = float32(scale * log2(e)), and Q
+    and K with power-of-two scales, so the dequantised logits Q K^T are
+    already base-2 exponents; the attention of the dequantised tensors then
+    takes the softmax scale ln(2) (exp(ln2 * t) = 2^t).
+    Returns (O, LSE, (qc, qs), (kc, ks), (vc, vs)).
     """
     from .attention import attention
     d = np.asarray(q).shape[-1]
     if scale is None:
         scale = 1.0 / np.sqrt(d)
-    qc, qs = fp8_quantize(q, signs, block_rows, rope)
-    kc, ks = fp8_quantize(k, signs, block_rows, rope)
+    pq = np.float32(scale * np.log2(np.e)) if prescaled else None
+    qc, qs = fp8_quantize(q, signs, block_rows, rope, pow2=prescaled, prescale=pq)
+    kc, ks = fp8_quantize(k, signs, block_rows, rope, pow2=prescaled)
     vc, vs = fp8_quantize(v, None, block_rows, pow2=v_pow2)
     o, lse = attention(fp8_dequantize(qc, qs, block_rows),
                        fp8_dequantize(kc, ks, block_rows),
-                       fp8_dequantize(vc, vs, block_rows), causal, scale)
+                       fp8_dequantize(vc, vs, block_rows), causal,
+                       np.log(2.0) if prescaled else scale)
     return o, lse, (qc, qs), (kc, ks), (vc, vs)
