@@ -9,8 +9,9 @@ resident in HBM, one launch per leg:
     non-causal and causal, B=4 H=32 N=4096 d=64 non-causal, B=2 H=8 N=16384
     d=256 causal;
   * the fp8 path on B=4 H=16 N=4096 d=128 (0.1 % outliers): fa_fp8_prep of Q
-    and K (random-sign Hadamard + 128-row block scales) and V (block scales),
-    then the fp8 forward.
+    and K (random-sign Hadamard + 128-row power-of-two block scales, Q
+    prescaled by softmax_scale * log2(e)) and V (power-of-two block scales),
+    then the fp8 forward in its multiply-free form (FA_FP8_QSCALED).
 Each leg is timed with HIP events on the stream it is launched on.
 
 Headlines, one per precision (work 4*B*H*N^2*d, halved for causal):
@@ -29,8 +30,9 @@ a bounded sample of the same workloads (rank 0, N=1 only).
 After the step, the rows built beyond the forward are timed on their own and
 reported under `next_rows` (not part of any headline): the 16-bit backward,
 the fused rotary + Hadamard + fp8 prep, the microscaled fp8 variant, the
-block-scaled fp8 forward causal and the decode-shaped forward (see
-build_next_legs).
+block-scaled fp8 forward causal, the fp8 forward on inputs prepared without
+the prescale (amax / 448 scales for Q and K) and the decode-shaped forward
+(see build_next_legs).
 
 Prints ONE JSON line on stdout.
 """
@@ -73,7 +75,7 @@ FWD16_LEGS = {
 }
 FP8_FWD_LEG = "fp8_fwd_b4h16n4k_d128"
 FP8_PREP_LEG = "fp8_prep_qkv_b4h16n4k_d128"
-FP8_SYMBOL = "_ZN2fa17fa_fwd_fp8_kernelILi128ELb0ELb0ELb0EEEvPKhS2_S2_PvPfiiiimf"
+FP8_SYMBOL = "_ZN2fa17fa_fwd_fp8_kernelILi128ELb0ELb0ELb0ELb1EEEvPKhS2_S2_PvPfiiiimf"
 KERNEL_OF = {**{k: v[1] for k, v in FWD16_LEGS.items()}, FP8_FWD_LEG: FP8_SYMBOL}
 HEADLINE = ["bf16_fwd_b2h16n8k_d128_causal", "bf16_fwd_b2h16n8k_d128"]
 ROOF_LEG = "bf16_fwd_b2h16n8k_d128"
@@ -480,9 +482,11 @@ def build_legs(dev, only=None):
     nel = B8 * H8 * N8 * d8
     prep_bytes = 3 * (nel * 2 + nel + B8 * H8 * (N8 // 128) * 4)
 
+    prescale = fa.qk_prescale(1.0 / d8 ** 0.5)
+
     def prep():
-        fa.fp8_prep(q8, signs, 128, out=pq)
-        fa.fp8_prep(k8, signs, 128, out=pk)
+        fa.fp8_prep(q8, signs, 128, out=pq, prescale=prescale)
+        fa.fp8_prep(k8, signs, 128, out=pk, pow2_scale=True)
         fa.fp8_prep(v8, None, 128, out=pv, pow2_scale=True)
 
     prep()                      # the forward leg alone still reads prepared inputs
@@ -490,7 +494,8 @@ def build_legs(dev, only=None):
         legs.append(Leg(FP8_PREP_LEG, prep, 0.0, prep_bytes))
     if not only or FP8_FWD_LEG in only:
         legs.append(Leg(FP8_FWD_LEG,
-                        lambda: fa.fwd_fp8(pq, pk, pv, B8, H8, N8, d8, False, out=o8, lse=lse8),
+                        lambda: fa.fwd_fp8(pq, pk, pv, B8, H8, N8, d8, False, out=o8, lse=lse8,
+                                           qscaled=True),
                         attention_flops(B8, H8, N8, d8, False), peak=PEAK_FP8))
     keep += [q8, k8, v8, signs, pq, pk, pv, o8, lse8]
     return legs, keep
@@ -502,9 +507,11 @@ def build_next_legs(dev):
     d=128, work 10*B*H*N^2*d (the five GEMMs of the gradient, halved for
     causal); the fused rotary + Hadamard + fp8 block quantisation of Q and K
     of the fp8 workload (half pairing, GB/s of bytes read and written); the
-    microscaled fp8 variant (fa_mx_prep of Q, K along d with the Hadamard and
-    V along the sequence, GB/s; the forward on its output, non-causal and
-    causal); the block-scaled fp8 forward, causal; and the decode-shaped
+    microscaled fp8 variant (fa_mx_prep of Q, K along d with the Hadamard, Q
+    prescaled, and V along the sequence, GB/s; the forward on its output,
+    non-causal and causal); the block-scaled fp8 forward, causal; the fp8
+    forward on inputs prepared without the prescale (amax / 448 scales for Q
+    and K, one multiply-add per score); and the decode-shaped
     forward on its two workloads, in GB/s of the bytes it must move (K and V
     of every sequence's keys, Q, O, LSE); the backward at d = 256 on the
     B=2 H=8 N=16384 causal workload; and, as an ablation, the pipelined
@@ -565,8 +572,10 @@ def build_next_legs(dev):
                   for _ in range(3))
     mx_bytes = 3 * (nel * 2 + nel + nel // 32)
 
+    prescale = fa.qk_prescale(1.0 / d8 ** 0.5)
+
     def prep_mx():
-        fa.mx_prep(q8, signs, "d", out=mq)
+        fa.mx_prep(q8, signs, "d", out=mq, prescale=prescale)
         fa.mx_prep(k8, signs, "d", out=mk)
         fa.mx_prep(v8, None, "n", out=mv)
 
@@ -577,15 +586,21 @@ def build_next_legs(dev):
     for causal in (False, True):
         legs.append(Leg("fp8_mx_fwd_b4h16n4k_d128" + ("_causal" if causal else ""),
                         lambda causal=causal: fa.fwd_fp8(mq, mk, mv, B8, H8, N8, d8, causal, out=o8,
-                                                         lse=lse8, mx=True),
+                                                         lse=lse8, mx=True, qscaled=True),
                         attention_flops(B8, H8, N8, d8, causal), peak=PEAK_FP8))
     keep += [mq, mk, mv, o8, lse8]
-    bq, bk = (fa.fp8_prep(t, signs, 128) for t in (q8, k8))
+    bq = fa.fp8_prep(q8, signs, 128, prescale=prescale)
+    bk = fa.fp8_prep(k8, signs, 128, pow2_scale=True)
     bv = fa.fp8_prep(v8, None, 128, pow2_scale=True)
     legs.append(Leg("fp8_fwd_b4h16n4k_d128_causal",
-                    lambda: fa.fwd_fp8(bq, bk, bv, B8, H8, N8, d8, True, out=o8, lse=lse8),
+                    lambda: fa.fwd_fp8(bq, bk, bv, B8, H8, N8, d8, True, out=o8, lse=lse8,
+                                       qscaled=True),
                     attention_flops(B8, H8, N8, d8, True), peak=PEAK_FP8))
-    keep += [bq, bk, bv]
+    uq, uk = (fa.fp8_prep(t, signs, 128) for t in (q8, k8))
+    legs.append(Leg("fp8_fwd_b4h16n4k_d128_unscaled",
+                    lambda: fa.fwd_fp8(uq, uk, bv, B8, H8, N8, d8, False, out=o8, lse=lse8),
+                    attention_flops(B8, H8, N8, d8, False), peak=PEAK_FP8))
+    keep += [bq, bk, bv, uq, uk]
     for name, c in sorted(DECODE_CONFIGS.items()):
         B, H, Hkv, Nq, Nk, d = c["B"], c["H"], c["Hkv"], c["Nq"], c["Nk"], c["d"]
         qh, kh, vh, sl = make_decode(**c)
@@ -656,9 +671,9 @@ def cpu_baseline():
     of B=2 H=16 N=8192 d=128, causal and non-causal (the oracle computes every
     score and masks; the metric counts half for causal), and the fp8 leg as
     the fake-quant oracle (random-sign Hadamard + per-128-row e4m3
-    quantisation of the outlier inputs, then exact attention) on batch 0 of
-    B=4 H=16 N=4096 d=128. Value: the sample's metric flops over the oracle's
-    time."""
+    quantisation of the outlier inputs with Q prescaled and power-of-two
+    scales, then exact attention) on batch 0 of B=4 H=16 N=4096 d=128. Value:
+    the sample's metric flops over the oracle's time."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -675,11 +690,11 @@ def cpu_baseline():
     t0 = time.perf_counter()
     oracle.attention(q, k, v, False)
     oracle.attention(q, k, v, True)
-    oracle.fake_quant_attention(q8, k8, v8, signs, 128, False)
+    oracle.fake_quant_attention(q8, k8, v8, signs, 128, False, prescaled=True)
     el = time.perf_counter() - t0
     return {"value": fl / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"bf16 B=1 (of 2) H=16 N=8192 d=128 non-causal and causal; fp8 fake-quant "
-                      f"(Hadamard + block e4m3) B=1 (of 4) H=16 N=4096 d=128 outlier inputs; "
+                      f"(Hadamard + block e4m3, Q prescaled) B=1 (of 4) H=16 N=4096 d=128 outlier inputs; "
                       f"float64 numpy oracle, {el:.1f} s"}
 
 

@@ -19,6 +19,7 @@ FA_MX_ALONG_D, FA_MX_ALONG_N = 0, 1
 FA_OUT_F32 = 0x100
 FA_SCALE_POW2 = 0x200
 FA_FWD_PIPELINED = 0x400
+FA_FP8_QSCALED = 0x800
 FA_ROPE_NONE, FA_ROPE_INTERLEAVED, FA_ROPE_HALF = 0, 1, 2
 ROPE_STYLES = {"interleaved": FA_ROPE_INTERLEAVED, "half": FA_ROPE_HALF}
 
@@ -68,6 +69,10 @@ def lib():
     L.fa_mx_packed_bytes.restype = ctypes.c_size_t
     L.fa_fp8_prep_rope.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
     L.fa_fp8_prep_rope.restype = i
+    L.fa_fp8_prep_scaled.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, f, i, f, vp]
+    L.fa_fp8_prep_scaled.restype = i
+    L.fa_mx_prep_scaled.argtypes = [vp, vp, vp, i, i, i, i, i, i, f, vp]
+    L.fa_mx_prep_scaled.restype = i
     L.fa_fp8_prep.restype = i
     L.fa_fp8_packed_bytes.argtypes = [i, i, i, i]
     L.fa_fp8_packed_bytes.restype = ctypes.c_size_t
@@ -142,8 +147,26 @@ def fp8_prep_rope_raw(x, x8, signs, B, H, N, d, block_rows, in_dtype, rope_style
                                   float(rope_base), int(pos0), stream)
 
 
+def fp8_prep_scaled_raw(x, x8, signs, B, H, N, d, block_rows, in_dtype, rope_style, rope_base,
+                        pos0, prescale, stream=None):
+    return lib().fa_fp8_prep_scaled(x, x8, signs, B, H, N, d, block_rows, in_dtype,
+                                    int(rope_style), float(rope_base), int(pos0), float(prescale),
+                                    stream)
+
+
 def mx_prep_raw(x, x8, signs, B, H, N, d, axis, in_dtype, stream=None):
     return lib().fa_mx_prep(x, x8, signs, B, H, N, d, int(axis), in_dtype, stream)
+
+
+def mx_prep_scaled_raw(x, x8, signs, B, H, N, d, axis, in_dtype, prescale, stream=None):
+    return lib().fa_mx_prep_scaled(x, x8, signs, B, H, N, d, int(axis), in_dtype,
+                                   float(prescale), stream)
+
+
+def qk_prescale(softmax_scale):
+    """The prescale that makes a prepared q carry softmax_scale * log2(e)
+    (for fwd_fp8(..., qscaled=True))."""
+    return softmax_scale * math.log2(math.e)
 
 
 def mx_packed_bytes(B, H, N, d):
@@ -308,15 +331,18 @@ def fp8_scales_view(packed, B, H, N, d):
     return packed[off: off + 4 * B * H * nb].view(torch.float32).view(B, H, nb)
 
 
-def fp8_prep(x, signs=None, block_rows=128, out=None, rope=None, pow2_scale=False):
+def fp8_prep(x, signs=None, block_rows=128, out=None, rope=None, pow2_scale=False, prescale=None):
     """Random-sign Hadamard (when signs is given) + fp8 e4m3 block quantisation.
 
     x: 16-bit [B,H,N,d] device tensor; signs: int8 [H,d] device tensor of +-1
     or None; block_rows: 128, or 0 for one scale per tensor; rope: None, or
     (style, base, pos0) with style "interleaved" or "half" to apply the
     rotary embedding first, in the same pass; pow2_scale: round the scales up
-    to powers of two (the form fwd_fp8 applies exactly for V). Returns the
-    packed uint8 tensor (codes then float32 scales) that fwd_fp8 consumes.
+    to powers of two (the form fwd_fp8 applies exactly for V); prescale:
+    None, or a factor the values are multiplied by before quantisation (then
+    the scales are always powers of two; q for fwd_fp8(..., qscaled=True)
+    takes qk_prescale(softmax_scale)). Returns the packed uint8 tensor
+    (codes then float32 scales) that fwd_fp8 consumes.
     """
     B, H, N, d = x.shape
     if out is None:
@@ -329,7 +355,13 @@ def fp8_prep(x, signs=None, block_rows=128, out=None, rope=None, pow2_scale=Fals
     else:
         _check_device(x, out)
     code = _dtype_code(x) | (FA_SCALE_POW2 if pow2_scale else 0)
-    if rope is None:
+    if prescale is not None:
+        style, base, pos0 = rope if rope is not None else (None, 1.0, 0)
+        _check(style is None or style in ROPE_STYLES, f"rope style must be one of {sorted(ROPE_STYLES)}")
+        st = fp8_prep_scaled_raw(_ptr(x), _ptr(out), _ptr(signs), B, H, N, d, block_rows, code,
+                                 ROPE_STYLES[style] if style else 0, base, pos0, prescale,
+                                 _stream(x.device))
+    elif rope is None:
         st = fp8_prep_raw(_ptr(x), _ptr(out), _ptr(signs), B, H, N, d, block_rows,
                           code, _stream(x.device))
     else:
@@ -342,11 +374,14 @@ def fp8_prep(x, signs=None, block_rows=128, out=None, rope=None, pow2_scale=Fals
     return out
 
 
-def mx_prep(x, signs=None, axis="d", out=None):
+def mx_prep(x, signs=None, axis="d", out=None, prescale=None):
     """fp8 e4m3 quantisation with a power-of-two scale per 32 elements,
     along d (axis "d": Q and K, optionally after the random-sign Hadamard)
-    or along the sequence (axis "n": V). Returns the packed uint8 tensor
-    (codes, then E8M0 scale bytes) that fwd_fp8(..., mx=True) consumes."""
+    or along the sequence (axis "n": V). prescale (axis "d" only): None, or
+    a factor the values are multiplied by first (q for fwd_fp8(...,
+    mx=True, qscaled=True) takes qk_prescale(softmax_scale)). Returns the
+    packed uint8 tensor (codes, then E8M0 scale bytes) that
+    fwd_fp8(..., mx=True) consumes."""
     B, H, N, d = x.shape
     _check(axis in ("d", "n"), "axis must be 'd' or 'n'")
     if out is None:
@@ -358,9 +393,13 @@ def mx_prep(x, signs=None, axis="d", out=None):
         _check_device(x, out, signs)
     else:
         _check_device(x, out)
-    st = mx_prep_raw(_ptr(x), _ptr(out), _ptr(signs), B, H, N, d,
-                     FA_MX_ALONG_D if axis == "d" else FA_MX_ALONG_N, _dtype_code(x),
-                     _stream(x.device))
+    ax = FA_MX_ALONG_D if axis == "d" else FA_MX_ALONG_N
+    if prescale is not None:
+        st = mx_prep_scaled_raw(_ptr(x), _ptr(out), _ptr(signs), B, H, N, d, ax, _dtype_code(x),
+                                prescale, _stream(x.device))
+    else:
+        st = mx_prep_raw(_ptr(x), _ptr(out), _ptr(signs), B, H, N, d, ax, _dtype_code(x),
+                         _stream(x.device))
     if st != FA_OK:
         raise FaError(st, "fa_mx_prep")
     return out
@@ -379,9 +418,11 @@ def mx_scales_view(packed, B, H, N, d, axis):
 
 
 def fwd_fp8(q8, k8, v8, B, H, N, d, causal=False, softmax_scale=None, out_f32=False,
-            out=None, lse=None, mx=False):
+            out=None, lse=None, mx=False, qscaled=False):
     """Attention forward on packed fp8 tensors made by fp8_prep (mx=False)
-    or by mx_prep (mx=True: q and k along d, v along n).
+    or by mx_prep (mx=True: q and k along d, v along n). qscaled: q was
+    prepared with prescale=qk_prescale(softmax_scale) (block-scaled inputs:
+    k and v with power-of-two scales too), so the logits need no multiply.
 
     Returns (o, lse) with o bf16 (float32 with out_f32=True).
     """
@@ -392,7 +433,8 @@ def fwd_fp8(q8, k8, v8, B, H, N, d, causal=False, softmax_scale=None, out_f32=Fa
         out = torch.empty((B, H, N, d), dtype=odt, device=q8.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
-    code = (FA_FP8_MX if mx else FA_FP8_E4M3) | (FA_OUT_F32 if out_f32 else 0)
+    code = ((FA_FP8_MX if mx else FA_FP8_E4M3) | (FA_OUT_F32 if out_f32 else 0)
+            | (FA_FP8_QSCALED if qscaled else 0))
     need = mx_packed_bytes(B, H, N, d) if mx else fp8_packed_bytes(B, H, N, d)
     for t in (q8, k8, v8):
         _check(t.dtype == torch.uint8 and t.numel() >= need, "packed fp8 input too small")

@@ -58,9 +58,10 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
            int d, int causal, float softmax_scale, int dtype, void* stream) {
     const int base = dtype & 0xff;
     const int flags = dtype & ~0xff;
-    if ((flags & ~(FA_OUT_F32 | FA_FWD_PIPELINED)) != 0) return FA_ERR_INVALID_ARG;
+    if ((flags & ~(FA_OUT_F32 | FA_FWD_PIPELINED | FA_FP8_QSCALED)) != 0) return FA_ERR_INVALID_ARG;
     if (base != FA_F16 && base != FA_BF16 && base != FA_FP8_E4M3 && base != FA_FP8_MX)
         return FA_ERR_INVALID_ARG;
+    if ((flags & FA_FP8_QSCALED) && base != FA_FP8_E4M3 && base != FA_FP8_MX) return FA_ERR_INVALID_ARG;
     if (!sizes_ok(B, H, N, d)) return FA_ERR_INVALID_ARG;
     if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return FA_ERR_INVALID_ARG;
     if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
@@ -84,6 +85,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     a.scales_off = fa_fp8_scales_offset(B, H, N, d);
     a.mx = base == FA_FP8_MX;
     a.pipelined = (flags & FA_FWD_PIPELINED) != 0;
+    a.qscaled = (flags & FA_FP8_QSCALED) != 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();   // do not report an earlier, unrelated error
     if (fp8) return from_hip(fa::launch_fwd_fp8(a, s));
@@ -183,6 +185,44 @@ int decode_args(const void* q, const void* k, const void* v, void* o, float* lse
     return FA_OK;
 }
 
+int prep_rope(const void* x, void* x8, const int8_t* signs, int B, int H, int N, int d,
+              int block_rows, int in_dtype, int rope_style, float rope_base, int pos0,
+              float prescale, void* stream) {
+    const int pow2 = (in_dtype & FA_SCALE_POW2) != 0;
+    in_dtype &= ~FA_SCALE_POW2;
+    if (in_dtype != FA_BF16 && in_dtype != FA_F16) return FA_ERR_INVALID_ARG;
+    if (!sizes_ok(B, H, N, d)) return FA_ERR_INVALID_ARG;
+    if (rope_style != FA_ROPE_NONE && rope_style != FA_ROPE_INTERLEAVED && rope_style != FA_ROPE_HALF)
+        return FA_ERR_INVALID_ARG;
+    if (rope_style != FA_ROPE_NONE) {
+        if (!(rope_base > 0.0f) || !isfinite(rope_base)) return FA_ERR_INVALID_ARG;
+        if (pos0 < 0 || (long long)pos0 + N > (1LL << 24)) return FA_ERR_INVALID_ARG;
+    }
+    if (block_rows != 0 && block_rows != fa::kQuantBlockRows) return FA_ERR_UNSUPPORTED;
+    if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * H * ((N + 127) / 128) > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0 || N == 0) return FA_OK;
+    if (!x || !x8) return FA_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(x8, 256)) return FA_ERR_INVALID_ARG;
+
+    fa::PrepArgs a;
+    a.x = x; a.x8 = static_cast<uint8_t*>(x8); a.signs = signs;
+    a.B = B; a.H = H; a.N = N; a.d = d;
+    a.block_rows = block_rows;
+    a.bf16 = in_dtype == FA_BF16;
+    a.scales_off = fa_fp8_scales_offset(B, H, N, d);
+    a.rope_style = rope_style;
+    a.mx = fa::kMxNone;
+    a.pow2 = pow2;
+    a.prescale = prescale;
+    a.rope.pos0 = pos0;
+    for (int i = 0; i < 128; ++i)
+        a.rope.w[i] = i < d / 2 ? (float)pow((double)rope_base, -2.0 * i / d) : 0.0f;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    return from_hip(fa::launch_fp8_prep(a, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -223,41 +263,19 @@ int fa_fwd_decode_noalloc(const void* q, const void* k, const void* v, void* o, 
     return from_hip(fa::launch_decode16(a, (dtype & 0xff) == FA_BF16, s));
 }
 
+int fa_fp8_prep_scaled(const void* x, void* x8, const int8_t* signs, int B, int H, int N, int d,
+                       int block_rows, int in_dtype, int rope_style, float rope_base, int pos0,
+                       float prescale, void* stream) {
+    if (!(prescale > 0.0f) || !isfinite(prescale)) return FA_ERR_INVALID_ARG;
+    return prep_rope(x, x8, signs, B, H, N, d, block_rows, in_dtype | FA_SCALE_POW2, rope_style,
+                     rope_base, pos0, prescale, stream);
+}
+
 int fa_fp8_prep_rope(const void* x, void* x8, const int8_t* signs, int B, int H, int N, int d,
                      int block_rows, int in_dtype, int rope_style, float rope_base, int pos0,
                      void* stream) {
-    const int pow2 = (in_dtype & FA_SCALE_POW2) != 0;
-    in_dtype &= ~FA_SCALE_POW2;
-    if (in_dtype != FA_BF16 && in_dtype != FA_F16) return FA_ERR_INVALID_ARG;
-    if (!sizes_ok(B, H, N, d)) return FA_ERR_INVALID_ARG;
-    if (rope_style != FA_ROPE_NONE && rope_style != FA_ROPE_INTERLEAVED && rope_style != FA_ROPE_HALF)
-        return FA_ERR_INVALID_ARG;
-    if (rope_style != FA_ROPE_NONE) {
-        if (!(rope_base > 0.0f) || !isfinite(rope_base)) return FA_ERR_INVALID_ARG;
-        if (pos0 < 0 || (long long)pos0 + N > (1LL << 24)) return FA_ERR_INVALID_ARG;
-    }
-    if (block_rows != 0 && block_rows != fa::kQuantBlockRows) return FA_ERR_UNSUPPORTED;
-    if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
-    if ((long long)B * H * ((N + 127) / 128) > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
-    if (B == 0 || H == 0 || N == 0) return FA_OK;
-    if (!x || !x8) return FA_ERR_INVALID_ARG;
-    if (!aligned(x, 16) || !aligned(x8, 256)) return FA_ERR_INVALID_ARG;
-
-    fa::PrepArgs a;
-    a.x = x; a.x8 = static_cast<uint8_t*>(x8); a.signs = signs;
-    a.B = B; a.H = H; a.N = N; a.d = d;
-    a.block_rows = block_rows;
-    a.bf16 = in_dtype == FA_BF16;
-    a.scales_off = fa_fp8_scales_offset(B, H, N, d);
-    a.rope_style = rope_style;
-    a.mx = fa::kMxNone;
-    a.pow2 = pow2;
-    a.rope.pos0 = pos0;
-    for (int i = 0; i < 128; ++i)
-        a.rope.w[i] = i < d / 2 ? (float)pow((double)rope_base, -2.0 * i / d) : 0.0f;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    (void)hipGetLastError();
-    return from_hip(fa::launch_fp8_prep(a, s));
+    return prep_rope(x, x8, signs, B, H, N, d, block_rows, in_dtype, rope_style, rope_base, pos0,
+                     1.0f, stream);
 }
 
 size_t fa_mx_packed_bytes(int B, int H, int N, int d) {
@@ -267,8 +285,8 @@ size_t fa_mx_packed_bytes(int B, int H, int N, int d) {
     return fa::round_up(fa_fp8_scales_offset(B, H, N, d) + (rows > cols ? rows : cols), 256);
 }
 
-int fa_mx_prep(const void* x, void* x8, const int8_t* signs, int B, int H, int N, int d, int axis,
-               int in_dtype, void* stream) {
+static int mx_prep_impl(const void* x, void* x8, const int8_t* signs, int B, int H, int N, int d,
+                        int axis, int in_dtype, float prescale, void* stream) {
     if (in_dtype != FA_BF16 && in_dtype != FA_F16) return FA_ERR_INVALID_ARG;
     if (axis != FA_MX_ALONG_D && axis != FA_MX_ALONG_N) return FA_ERR_INVALID_ARG;
     if (axis == FA_MX_ALONG_N && signs) return FA_ERR_INVALID_ARG;
@@ -289,9 +307,22 @@ int fa_mx_prep(const void* x, void* x8, const int8_t* signs, int B, int H, int N
     a.rope.pos0 = 0;
     for (int i = 0; i < 128; ++i) a.rope.w[i] = 0.0f;
     a.mx = axis == FA_MX_ALONG_D ? fa::kMxAlongD : fa::kMxAlongN;
+    a.prescale = prescale;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     return from_hip(fa::launch_fp8_prep(a, s));
+}
+
+int fa_mx_prep(const void* x, void* x8, const int8_t* signs, int B, int H, int N, int d, int axis,
+               int in_dtype, void* stream) {
+    return mx_prep_impl(x, x8, signs, B, H, N, d, axis, in_dtype, 1.0f, stream);
+}
+
+int fa_mx_prep_scaled(const void* x, void* x8, const int8_t* signs, int B, int H, int N, int d,
+                      int axis, int in_dtype, float prescale, void* stream) {
+    if (!(prescale > 0.0f) || !isfinite(prescale)) return FA_ERR_INVALID_ARG;
+    if (axis != FA_MX_ALONG_D) return FA_ERR_INVALID_ARG;
+    return mx_prep_impl(x, x8, signs, B, H, N, d, axis, in_dtype, prescale, stream);
 }
 
 int fa_fp8_prep(const void* x, void* x8, const int8_t* signs, int B, int H, int N, int d,

@@ -310,6 +310,13 @@ __device__ __forceinline__ float uniform_f(float x) {
     return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
 }
 
+// E8M0 byte (127 + k) of f = 2^k, a normal float32 power of two; -1 for any
+// other value (frexp: f = 0.5 * 2^(k + 1), k + 1 in [-125, 128] when normal).
+__device__ __forceinline__ int e8m0_of_pow2(float f) {
+    const int e = __builtin_amdgcn_frexp_expf(f);
+    return (__builtin_amdgcn_frexp_mantf(f) == 0.5f && e >= -125 && e <= 128) ? 126 + e : -1;
+}
+
 // s_waitcnt immediate (gfx9 encoding) for vmcnt(0), other counters ignored.
 constexpr int kVmcnt0 = 0x0f70;
 

@@ -16,6 +16,9 @@
 // across lanes (xor-partner exchange). The block is held in registers until
 // its amax is known, so the input is read once and the codes written once.
 //
+// y is the row after the optional rotary step and transform, times the
+// caller's prescale (1 by default; Q for the fp8 forward's multiply-free
+// logits carries softmax_scale * log2(e) this way).
 // Per block: amax = max |y|, scale = amax / 448 (IEEE float32 division; 1 if
 // amax is 0), code = e4m3 round-to-nearest-even of y / scale after clamping to
 // +-448 (the clamp only absorbs the rounding of the scale). After the
@@ -157,7 +160,7 @@ template <typename T, int D, bool HAD, int MODE, int ROPE, int HB = 1>
 __global__ void __launch_bounds__((quant_threads<D, ROPE>()))
 fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t* __restrict__ signs,
                 float* __restrict__ scales, unsigned* __restrict__ gamax, int N, int H, int nblk,
-                RopeFreqs rf, int pow2)
+                RopeFreqs rf, int pow2, float prescale)
 {
     constexpr int NT = quant_threads<D, ROPE>();
     constexpr int LPR = D / 8;                 // lanes per row
@@ -288,6 +291,9 @@ fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t*
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[p][e] *= rs;
             }
+            // the prescale: its own float32 multiply of the rotated value
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[p][e] *= prescale;
             if (row < N) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[p][e]));
@@ -457,7 +463,7 @@ static hipError_t prep_t(const PrepArgs& a, hipStream_t s) {
         if constexpr (ROPE != 0) return hipErrorInvalidValue;     // fa_mx_prep has no rotary step
         hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 3, 0>), dim3((unsigned)grid),
                            dim3(quant_threads<D, 0>()), 0, s, x, a.x8, a.signs, scales, nullptr, a.N, a.H, nblk,
-                           a.rope, a.pow2);
+                           a.rope, a.pow2, a.prescale);
         return hipGetLastError();
     }
     if (a.block_rows != 0) {
@@ -472,15 +478,15 @@ static hipError_t prep_t(const PrepArgs& a, hipStream_t s) {
         if (ROPE != 0 && heads % 4 == 0 && grid / 4 >= 512)
             hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 0, ROPE, ROPE != 0 ? 4 : 1>), dim3((unsigned)(grid / 4)),
                                dim3(quant_threads<D, ROPE>()), 0, s, x, a.x8, a.signs, scales, nullptr, a.N,
-                               a.H, nblk, a.rope, a.pow2);
+                               a.H, nblk, a.rope, a.pow2, a.prescale);
         else if (ROPE != 0 && heads % 2 == 0 && grid / 2 >= 512)
             hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 0, ROPE, ROPE != 0 ? 2 : 1>), dim3((unsigned)(grid / 2)),
                                dim3(quant_threads<D, ROPE>()), 0, s, x, a.x8, a.signs, scales, nullptr, a.N,
-                               a.H, nblk, a.rope, a.pow2);
+                               a.H, nblk, a.rope, a.pow2, a.prescale);
         else
             hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 0, ROPE>), dim3((unsigned)grid),
                                dim3(quant_threads<D, ROPE>()), 0, s, x, a.x8, a.signs, scales, nullptr, a.N,
-                               a.H, nblk, a.rope, a.pow2);
+                               a.H, nblk, a.rope, a.pow2, a.prescale);
         return hipGetLastError();
     }
     // Per-tensor: the first scale slot serves as the amax accumulator; the
@@ -488,9 +494,9 @@ static hipError_t prep_t(const PrepArgs& a, hipStream_t s) {
     unsigned* gamax = reinterpret_cast<unsigned*>(scales);
     hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(1), 0, s, gamax);
     hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 1, ROPE>), dim3((unsigned)grid), dim3(quant_threads<D, ROPE>()),
-                       0, s, x, a.x8, a.signs, scales, gamax, a.N, a.H, nblk, a.rope, a.pow2);
+                       0, s, x, a.x8, a.signs, scales, gamax, a.N, a.H, nblk, a.rope, a.pow2, a.prescale);
     hipLaunchKernelGGL((fp8_prep_kernel<T, D, HAD, 2, ROPE>), dim3((unsigned)grid), dim3(quant_threads<D, ROPE>()),
-                       0, s, x, a.x8, a.signs, scales, gamax, a.N, a.H, nblk, a.rope, a.pow2);
+                       0, s, x, a.x8, a.signs, scales, gamax, a.N, a.H, nblk, a.rope, a.pow2, a.prescale);
     hipLaunchKernelGGL(fill_scales_kernel, dim3(1), dim3(1024), 0, s, scales,
                        (const unsigned*)gamax, grid, a.pow2);
     return hipGetLastError();

@@ -99,6 +99,9 @@ struct TileScales {
     // block-scaled path: E8M0 byte of the power-of-two part of the tile's V
     // block scale relative to the head's largest (see tile_scales)
     int vblk = 127;
+    // block-scaled path with base-2 logits from the product: E8M0 byte of
+    // the tile's K block scale (a power of two)
+    int kblk = 127;
     __device__ __forceinline__ int kbyte(int kb, int ch) const {
         return (k[kb][ch >> 1] >> (16 * (ch & 1))) & 0xff;
     }
@@ -107,7 +110,7 @@ struct TileScales {
 
 // ACC: O lives in the accumulation registers (one wave per SIMD); its rare
 // rescale then runs in place.
-template <int D, int BC, bool MX, bool ACC>
+template <int D, int BC, bool MX, bool ACC, bool QS>
 struct Wave8 {
     static constexpr int RB = D;           // bytes per K / V row in LDS
     static constexpr int NCH = D / 64;     // k-steps of S^T = K Q^T
@@ -119,12 +122,19 @@ struct Wave8 {
     static_assert(NKB == 2 * NPV, "one PV MFMA per two score blocks");
     using TS = TileScales<NKB, (D + 127) / 128>;
 
-    // Score MFMA with the tile's scales (microscaled) or unit scales.
+    // Score MFMA with the tile's scales (microscaled; or block-scaled with
+    // base-2 logits, QS: the K and Q block scales as E8M0 bytes) or unit
+    // scales.
     __device__ __forceinline__ f32x16 mm(const i32x8& a, const i32x8& b, const f32x16& c, int sa,
                                          int sb) const {
-        if constexpr (MX) return mfma32_fp8s(a, b, c, sa, sb);
+        if constexpr (MX || QS) return mfma32_fp8s(a, b, c, sa, sb);
         else return mfma32_fp8s(a, b, c, usc, usc);
     }
+    // K scale operand of the score MFMA (key block kb, k-step ch)
+    static __device__ __forceinline__ int kscale(const TS& ts, int kb, int ch) {
+        return MX ? ts.kbyte(kb, ch) : (QS ? ts.kblk : 127);
+    }
+    static constexpr bool KS_HELD = MX || QS;   // per-tile K scale operands
     // P V MFMA of d-block db: microscaled, the V bytes of the block and 2^-3
     // for P'; block-scaled, the power-of-two part of the tile's V scale
     // (exact) and unit P'.
@@ -173,6 +183,21 @@ struct Wave8 {
 
     f32x16 o[NDB];
     float m, l;
+    // QS (d = 128 only): the first score MFMA of every pipelined tile
+    // starts from nmv = log2(8) - m instead of zero, so the product is the
+    // exponent itself and the exponentials take no multiply-add (nmv kept
+    // current across every move of m). (At d = 64 the 16 registers cost the
+    // kernel its third wave per SIMD, at d = 256 they crowd the
+    // accumulation registers, and the per-tile K scale operands cost more
+    // than the multiply-adds they save: measured 2-4 % slower. Prescaled
+    // inputs at those d take the plain kernel with unit logit multiplier.)
+    static constexpr bool BAKE = QS;
+    static_assert(!QS || D == 128, "the multiply-free form is built for d = 128");
+    f32x16 nmv;
+    __device__ __forceinline__ void set_nmv(float x) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) nmv[i] = x;
+    }
 
     __device__ __forceinline__ void init() {
         m = -INFINITY;
@@ -187,6 +212,7 @@ struct Wave8 {
         usc = 127;
         psc = MX ? kPScaleE8M0 : 127;
         asm volatile("" : "+v"(usc), "+v"(psc));
+        if constexpr (BAKE) set_nmv(0.f);
     }
 
     // K fragment (ch, kb): row perm(l32) + 32*kb, 16-byte logical chunks
@@ -214,14 +240,14 @@ struct Wave8 {
         for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                ks[ch][kb] = MX ? ts.kbyte(kb, ch) : 127;
-                if (MX) asm volatile("" : "+v"(ks[ch][kb]));
+                ks[ch][kb] = kscale(ts, kb, ch);
+                if (KS_HELD) asm volatile("" : "+v"(ks[ch][kb]));
             }
 #pragma unroll
         for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) s[kb] = mm(kf[kb][ch], qf[ch], s[kb], ks[ch][kb], qs[ch]);
-        if constexpr (MX) {
+        if constexpr (KS_HELD) {
             const int r = __builtin_amdgcn_readfirstlane(__float_as_int(s[NKB - 1][0]));
             asm volatile("" ::"s"(r));
 #pragma unroll
@@ -293,15 +319,18 @@ struct Wave8 {
     // P' for score blocks 2t, 2t+1 -> PV operand t. Dword g of the operand
     // holds the e4m3 bytes of registers 4*(g%4)..+3 of score block 2t + g/4;
     // group q = 8t + g of the tile.
+    // FMA: p' = exp2(s cj + nm) (nm = log2(8 f_j) - m); otherwise the scores
+    // already are that exponent (BAKE pipelined tiles) and p' = exp2(s).
+    template <bool FMA = true>
     __device__ __forceinline__ void prob_group(const f32x16 (&s)[NKB], uint32_t (&w)[NPV][8], int q,
-                                               float cj, float bj, float (&ls)[2]) {
+                                               float cj, float nm, float (&ls)[2]) {
         const int t = q / 8, g = q % 8;
         const int kb = 2 * t + g / 4, r = 4 * (g % 4);
-        const float nm = bj - m;
-        const float p0 = exp2_hw(fmaf(s[kb][r], cj, nm));
-        const float p1 = exp2_hw(fmaf(s[kb][r + 1], cj, nm));
-        const float p2 = exp2_hw(fmaf(s[kb][r + 2], cj, nm));
-        const float p3 = exp2_hw(fmaf(s[kb][r + 3], cj, nm));
+        auto ex = [&](float x) { return exp2_hw(FMA ? fmaf(x, cj, nm) : x); };
+        const float p0 = ex(s[kb][r]);
+        const float p1 = ex(s[kb][r + 1]);
+        const float p2 = ex(s[kb][r + 2]);
+        const float p3 = ex(s[kb][r + 3]);
         ls[g & 1] += (p0 + p1) + (p2 + p3);
         w[t][g] = cvt4_e4m3(p0, p1, p2, p3);
     }
@@ -317,14 +346,27 @@ struct Wave8 {
     // rescaling O and l). Then l takes the tile's unquantised row sum.
     // The redo reads this tile's scores, so they stay in registers until
     // here, next to the next tile's (step pins those MFMAs before this
-    // branch).
-    __device__ __forceinline__ void settle(const f32x16 (&s)[NKB], uint32_t (&w)[NPV][8], float cj,
-                                           float bj, float lscale, float (&ls)[2]) {
+    // branch). The exponents are s cj + nm (nm = bj - m, or 0 for BAKE scores
+    // that carry it); a score's logit in the units of m is that plus
+    // m - bj. FIX (BAKE pipelined step): the next tile's scores sn, issued
+    // with the old m, and nmv move with m.
+    template <bool FIX>
+    __device__ __forceinline__ void settle(const f32x16 (&s)[NKB], f32x16 (&sn)[NKB],
+                                           uint32_t (&w)[NPV][8], float cj, float nm, float bj,
+                                           float lscale, float (&ls)[2]) {
         if (wave_any(ls[0] + ls[1] > kBig8)) {
-            raise_max(tile_max(s, cj));
+            const float m0 = m;
+            raise_max(BAKE ? tile_max(s, cj) + (nm + m0 - bj) : tile_max(s, cj));
+            const float delta = m0 - m;                        // <= 0
+            const float nmr = BAKE ? nm + delta : bj - m;
             ls[0] = ls[1] = 0.f;
 #pragma unroll
-            for (int q = 0; q < 8 * NPV; ++q) prob_group(s, w, q, cj, bj, ls);
+            for (int q = 0; q < 8 * NPV; ++q) prob_group(s, w, q, cj, nmr, ls);
+            if constexpr (BAKE && FIX) {
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) sn[kb] += delta;
+                nmv += delta;
+            }
         }
         l += (ls[0] + ls[1]) * lscale;
     }
@@ -343,15 +385,17 @@ struct Wave8 {
                      (int)r2[0], (int)r2[1], (int)r3[0], (int)r3[1]};
     }
 
-    // Softmax + PV of the tile in s (no overlap).
-    __device__ __forceinline__ void finish(const f32x16 (&s)[NKB], const char* vl,
+    // Softmax + PV of the tile in s (no overlap). baked: the scores carry
+    // log2(8) - m already (BAKE, issued by a pipelined step).
+    __device__ __forceinline__ void finish(f32x16 (&s)[NKB], const char* vl,
                                            const int (&va)[NVA], float cj, float bj, float lscale,
-                                           const TS& ts) {
+                                           const TS& ts, bool baked = false) {
         uint32_t w[NPV][8];
         float ls[2] = {0.f, 0.f};
+        const float nm = baked ? 0.f : bj - m;
 #pragma unroll
-        for (int q = 0; q < 8 * NPV; ++q) prob_group(s, w, q, cj, bj, ls);
-        settle(s, w, cj, bj, lscale, ls);
+        for (int q = 0; q < 8 * NPV; ++q) prob_group(s, w, q, cj, nm, ls);
+        settle<false>(s, s, w, cj, nm, bj, lscale, ls);
         i32x8 pf[NPV];
         pack_p(w, pf);
         i32x8 vf[NPV][NDB];
@@ -397,11 +441,15 @@ struct Wave8 {
         int ks[NKF];
 #pragma unroll
         for (int i = 0; i < NKF; ++i) {
-            ks[i] = MX ? tsn.kbyte(i % NKB, i / NKB) : 127;
-            if (MX) asm volatile("" : "+v"(ks[i]));
+            ks[i] = kscale(tsn, i % NKB, i / NKB);
+            if (KS_HELD) asm volatile("" : "+v"(ks[i]));
         }
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) sn[kb] = f32x16{};
+        for (int kb = 0; kb < NKB; ++kb) {
+            if constexpr (BAKE) sn[kb] = nmv;
+            else sn[kb] = f32x16{};
+        }
+        const float nm = bj - m;
         if (FA8_PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int f = 0; f < KPD; ++f) kf[f % NKB][f / NKB] = kfrag(kn, ka, f / NKB, f % NKB);
@@ -418,7 +466,7 @@ struct Wave8 {
             const int ch = i / NKB, kb = i % NKB;
             sn[kb] = mm(kf[kb][ch], qf[ch], sn[kb], ks[i], qs[ch]);
 #pragma unroll
-            for (int q = i * NG / NKF; q < (i + 1) * NG / NKF; ++q) prob_group(s, w, q, cj, bj, ls);
+            for (int q = i * NG / NKF; q < (i + 1) * NG / NKF; ++q) prob_group<!BAKE>(s, w, q, cj, nm, ls);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (FA8_PRIO) __builtin_amdgcn_s_setprio(0);
@@ -435,10 +483,10 @@ struct Wave8 {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) asm volatile("" ::"v"(sn[kb][0]));
         }
-        settle(s, w, cj, bj, lscale, ls);
+        settle<true>(s, sn, w, cj, BAKE ? 0.f : nm, bj, lscale, ls);
         i32x8 pf[NPV];
         pack_p(w, pf);
-        if (MX) {
+        if (KS_HELD) {
 #pragma unroll
             for (int i = 0; i < NKF; ++i) asm volatile("" ::"v"(ks[i]));
         }
@@ -455,18 +503,21 @@ struct Wave8 {
     }
 };
 
-template <int D, bool CAUSAL, bool OUT_F32, bool MX>
+template <int D, bool CAUSAL, bool OUT_F32, bool MX, bool QS>
 __global__ void __launch_bounds__(Cfg8<D>::NW * 64, Cfg8<D>::WPE)
 fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg,
                   const uint8_t* __restrict__ Vg, void* __restrict__ Og, float* __restrict__ LSEg,
                   int N, int num_qtiles, int num_blocks, int nsb, size_t scales_off, float c)
 {
     constexpr int NW = Cfg8<D>::NW, BC = Cfg8<D>::BC;
-    using W = Wave8<D, BC, MX, Cfg8<D>::WPE == 1>;
+    using W = Wave8<D, BC, MX, Cfg8<D>::WPE == 1, QS>;
     using TS = typename W::TS;
     constexpr int SBY = D / 32;            // microscaling: scale bytes per row of Q or K
     static_assert(!MX || W::NPV == 1, "microscaled V scales are held for one PV k-step per tile");
     constexpr int QW = 32, BR = NW * QW;
+    // QS block-scaled: the waves of a workgroup share one Q scale block, so
+    // the scale checks below agree across them
+    static_assert(!QS || MX || kQuantBlockRows % BR == 0, "one Q scale block per workgroup");
     constexpr int NCH = W::NCH, NDB = W::NDB, NKB = W::NKB, NVA = W::NVA, RB = W::RB;
     constexpr int TB = BC * RB;            // bytes per K (or V) tile
     constexpr int NIW = TB / 1024 / NW;    // 1 KB direct loads per wave per tile
@@ -518,13 +569,30 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     // Block-scaled path: largest V block scale of the head. Microscaled
     // path: the matrix instructions apply every scale, the logits only take
     // softmax_scale * log2(e).
-    float svmax = 1.f, cq = c;
+    // QS (q carries softmax_scale * log2(e), power-of-two block scales): the
+    // logits need no multiplier; the Q and K block scales go to the score
+    // MFMAs as E8M0 bytes, which needs every Q, K and V block scale of the
+    // head to be a normal power of two (checked here; rows of a workgroup
+    // whose scales are not get NaN).
+    float svmax = 1.f, cq = QS ? 1.f : c;
+    bool qs_ok = true;
+    int qblk = 127;
     if constexpr (!MX) {
         svmax = 0.f;
-        for (int i = lane; i < nsb; i += 64) svmax = fmaxf(svmax, Vs[i]);
+        for (int i = lane; i < nsb; i += 64) {
+            svmax = fmaxf(svmax, Vs[i]);
+            if (QS) qs_ok = qs_ok && e8m0_of_pow2(Vs[i]) >= 0 && e8m0_of_pow2(Ks[i]) >= 0;
+        }
 #pragma unroll
         for (int mm = 32; mm >= 1; mm /= 2) svmax = fmaxf(svmax, __shfl_xor(svmax, mm, 64));
-        cq = Qs[min(q0, N - 1) / kQuantBlockRows] * c;
+        const float sq = Qs[min(q0, N - 1) / kQuantBlockRows];
+        if constexpr (QS) {
+            qblk = e8m0_of_pow2(sq);
+            qs_ok = !wave_any(!qs_ok || qblk < 0);
+            qblk = wave_uniform(qblk);
+        } else {
+            cq = sq * c;
+        }
     }
     const float rsvmax = 1.0f / svmax;
 
@@ -608,6 +676,16 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
             tvs = uniform_f(*reinterpret_cast<const float*>(smem + 2 * R * TB + s * BSB + 256));
         }
     };
+    // QS block-scaled: E8M0 byte of K block scale idx of slot s (the slot of
+    // tile t holds the scales of blocks t*BC/128 + 0, 1, ...; the tile's own
+    // block and the next one)
+    auto read_kblk = [&](TS& ts, int s, int idx) {
+        if constexpr (QS && !MX) {
+            const float f = uniform_f(*reinterpret_cast<const float*>(smem + 2 * R * TB + s * BSB + 4 * idx));
+            ts.kblk = wave_uniform(e8m0_of_pow2(f));
+        }
+    };
+    auto blk_of = [](int t) { return t * BC / kQuantBlockRows; };
     const int nkt_total = (N + BC - 1) / BC;
     const uint32_t sbase = lds_addr(smem);
     // copy of K (V = false) or V tile t into its ring slot
@@ -626,7 +704,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     // block-scaled path also the V scale byte of the PV MFMAs (into vt)
     auto tile_scales = [&](float& cj, float& bj, float& lscale, TS& vt) {
         if constexpr (MX) {
-            cj = c;
+            cj = QS ? 1.0f : c;
             bj = 3.0f;                                         // log2(kPScale)
             lscale = 1.0f / kPScale;
         } else {
@@ -641,9 +719,15 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
             const float wv = fmaxf(tvs * rsvmax, 0x1p-126f);
             const int ex = __builtin_amdgcn_frexp_expf(wv);                 // >= -125
             const float f = 2.0f * __builtin_amdgcn_frexp_mantf(wv);       // [1, 2)
-            cj = uniform_f(cq * tks);
-            bj = uniform_f(__builtin_amdgcn_logf(kPScale * f));          // log2(8 f)
-            lscale = uniform_f(__builtin_amdgcn_rcpf(kPScale * f));
+            if constexpr (QS) {                                      // w a power of two: f = 1
+                cj = 1.0f;
+                bj = 3.0f;
+                lscale = 1.0f / kPScale;
+            } else {
+                cj = uniform_f(cq * tks);
+                bj = uniform_f(__builtin_amdgcn_logf(kPScale * f));      // log2(8 f)
+                lscale = uniform_f(__builtin_amdgcn_rcpf(kPScale * f));
+            }
             vt.vblk = wave_uniform(126 + ex);                            // 2^(ex - 1)
         }
     };
@@ -677,7 +761,8 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
             }
         }
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) qs[ch] = (qw[ch >> 1] >> (16 * (ch & 1) + 8 * hi)) & 0xff;
+        for (int ch = 0; ch < NCH; ++ch)
+            qs[ch] = MX ? (qw[ch >> 1] >> (16 * (ch & 1) + 8 * hi)) & 0xff : qblk;
 #pragma unroll
         for (int ch = 0; ch < NCH; ++ch) {
             u32x4 a = u32x4{0, 0, 0, 0}, b = u32x4{0, 0, 0, 0};
@@ -693,6 +778,21 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     // Q and the first tile copies have landed (a wait the compiler sees; see
     // fa_fwd16_kernel).
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    if constexpr (QS && !MX) {
+        if (!qs_ok) {                      // scales unusable as E8M0 bytes: NaN rows
+            const int row = q0 + l32;
+            if (row < N) {
+                const float nan = __builtin_nanf("");
+                if (hi == 0) LSEg[(size_t)bh * N + row] = nan;
+                for (int col = hi; col < D; col += 2) {
+                    const size_t off = head + (size_t)row * D + col;
+                    if (OUT_F32) static_cast<float*>(Og)[off] = nan;
+                    else static_cast<__bf16*>(Og)[off] = (__bf16)nan;
+                }
+            }
+            return;
+        }
+    }
 
     // Lane offsets into swizzled tiles.
     int ka[W::NKA][2], va[NVA];
@@ -731,12 +831,21 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
         read_v(tv, 0);
     }
     read_bs(0);
+    read_kblk(tk, 0, 0);
     if (nfull > 0) {
         float cj, bj, ls;
         tile_scales(cj, bj, ls, tv);
         st.scores(s, ktile(0), ka, qf, tk, qs);
         st.raise_max(W::tile_max(s, cj));    // first reference maximum: exact
+        if constexpr (W::BAKE) {
+            // from here on the pipelined scores carry log2(8) - m
+            const float nm = bj - st.m;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) s[kb] += nm;
+            st.set_nmv(nm);
+        }
         if constexpr (MX) read_k(tk, 1);
+        read_kblk(tk, 0, blk_of(1) - blk_of(0));
         __syncthreads();                     // all waves done reading K_0's slot
     }
     int t = 0;
@@ -766,6 +875,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
             read_v(tv, ring(t + 1));           // tile t + 1
         }
         if (!PAIR || (t & 1) == 1) read_bs(ring(t + 1));
+        read_kblk(tk, ring(t + 1), blk_of(t + 2) - blk_of(t + 1));   // tile t + 2
         ++t;
     };
     for (; t + R < nfull; ) {
@@ -794,11 +904,12 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
         if (R == 2) load_kv(vrs, t + 1, true);     // (with R = 4 already copied)
         float cj, bj, lscale;
         tile_scales(cj, bj, lscale, tv);
-        st.finish(s, vtile(t), va, cj, bj, lscale, tv);
+        st.finish(s, vtile(t), va, cj, bj, lscale, tv, W::BAKE);
         wait_vm_all();
         __syncthreads();
         if constexpr (MX) read_v(tv, ring(t + 1));   // the K scales of t + 1 are in tk already
         read_bs(ring(t + 1));
+        read_kblk(tk, ring(t + 1), 0);
         ++t;
     }
     for (; t < nkt; ++t) {                    // ragged end / causal diagonal
@@ -822,6 +933,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
             read_v(tv, ring(t + 1));
         }
         read_bs(ring(t + 1));
+        read_kblk(tk, ring(t + 1), 0);
     }
 
     // ---- epilogue: O = O_acc * sv_max / (8 l) (microscaled: O_acc / l, the
@@ -851,30 +963,36 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     }
 }
 
-template <int D, bool CAUSAL, bool OUT_F32, bool MX>
+template <int D, bool CAUSAL, bool OUT_F32, bool MX, bool QS>
 static hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
     constexpr int BR = Cfg8<D>::NW * 32;
     const int num_qtiles = (a.N + BR - 1) / BR;
     const long long nblk = (long long)num_qtiles * a.B * a.H;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const int nsb = (a.N + kQuantBlockRows - 1) / kQuantBlockRows;
-    hipLaunchKernelGGL((fa_fwd_fp8_kernel<D, CAUSAL, OUT_F32, MX>), dim3((unsigned)nblk),
+    hipLaunchKernelGGL((fa_fwd_fp8_kernel<D, CAUSAL, OUT_F32, MX, QS>), dim3((unsigned)nblk),
                        dim3(Cfg8<D>::NW * 64), 0, s, static_cast<const uint8_t*>(a.q),
                        static_cast<const uint8_t*>(a.k), static_cast<const uint8_t*>(a.v), a.o,
-                       a.lse, a.N, num_qtiles, (int)nblk, nsb, a.scales_off, a.scale * kLog2e);
+                       a.lse, a.N, num_qtiles, (int)nblk, nsb, a.scales_off, a.qscaled ? 1.0f : a.scale * kLog2e);
     return hipGetLastError();
 }
 
-template <int D, bool MX>
+template <int D, bool MX, bool QS>
 static hipError_t launch_m(const FwdArgs& a, hipStream_t s) {
     if (a.causal)
-        return a.out_f32 ? launch_t<D, true, true, MX>(a, s) : launch_t<D, true, false, MX>(a, s);
-    return a.out_f32 ? launch_t<D, false, true, MX>(a, s) : launch_t<D, false, false, MX>(a, s);
+        return a.out_f32 ? launch_t<D, true, true, MX, QS>(a, s) : launch_t<D, true, false, MX, QS>(a, s);
+    return a.out_f32 ? launch_t<D, false, true, MX, QS>(a, s) : launch_t<D, false, false, MX, QS>(a, s);
 }
 
+// Prescaled q (FA_FP8_QSCALED): the multiply-free kernel at d = 128; at
+// other d the plain kernel, whose logit multiplier sq * sk * c then takes
+// c = 1 (q already carries softmax_scale * log2(e)).
 template <int D>
 static hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
-    return a.mx ? launch_m<D, true>(a, s) : launch_m<D, false>(a, s);
+    if constexpr (D == 128) {
+        if (a.qscaled) return a.mx ? launch_m<D, true, true>(a, s) : launch_m<D, false, true>(a, s);
+    }
+    return a.mx ? launch_m<D, true, false>(a, s) : launch_m<D, false, false>(a, s);
 }
 
 hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t s) {

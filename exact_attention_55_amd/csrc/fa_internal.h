@@ -25,6 +25,7 @@ struct FwdArgs {
     // FP8 only: byte offset of the scale array inside q/k/v
     size_t scales_off;
     bool mx = false;    // FP8: microscaled inputs (E8M0 scales per 32 elements)
+    bool qscaled = false;   // FP8: q carries softmax_scale * log2(e) (power-of-two block scales)
     bool pipelined = false;   // 16-bit, d = 128: the 64-rows-per-wave pipelined kernel
 };
 
@@ -55,6 +56,7 @@ struct PrepArgs {
     RopeFreqs rope;
     int mx;             // kMxNone: fp32 block scales; microscaling along d or n
     int pow2 = 0;       // fp32 block scales rounded up to powers of two
+    float prescale = 1.0f;   // factor on the (rotated) values before the block maximum
 };
 hipError_t launch_fp8_prep(const PrepArgs& a, hipStream_t s);
 

@@ -63,7 +63,11 @@ enum fa_status {
  * that overlaps the next block's score MFMAs, this block's exponentials and
  * the previous block's PV MFMAs inside one wave (same results up to
  * rounding; ignored for other inputs). FA_SCALE_POW2 may be OR-ed into
- * fa_fp8_prep's in_dtype: block scales are rounded up to powers of two. */
+ * fa_fp8_prep's in_dtype: block scales are rounded up to powers of two.
+ * FA_FP8_QSCALED may be OR-ed into fa_fwd's FP8 dtypes: q was prepared with
+ * prescale softmax_scale * log2(e) (fa_fp8_prep_scaled, fa_mx_prep_scaled),
+ * so the product Q K^T already is the base-2 exponent of the softmax; see
+ * fa_fwd. */
 enum fa_dtype {
     FA_F16 = 0,
     FA_BF16 = 1,
@@ -71,7 +75,8 @@ enum fa_dtype {
     FA_FP8_MX = 3,       /* e4m3 with microscaling (fa_mx_prep): q, k along d, v along N */
     FA_OUT_F32 = 0x100,
     FA_SCALE_POW2 = 0x200,
-    FA_FWD_PIPELINED = 0x400
+    FA_FWD_PIPELINED = 0x400,
+    FA_FP8_QSCALED = 0x800
 };
 
 /*
@@ -93,8 +98,25 @@ enum fa_dtype {
  *  softmax_scale  finite and > 0 (usually 1/sqrt(d)); multiplies S before the
  *           softmax.
  *  dtype    FA_F16 | FA_BF16 | FA_FP8_E4M3 | FA_FP8_MX, optionally
- *           | FA_OUT_F32 and (16-bit inputs) | FA_FWD_PIPELINED.
+ *           | FA_OUT_F32, (16-bit inputs) | FA_FWD_PIPELINED and (FP8
+ *           inputs) | FA_FP8_QSCALED.
  *  stream   hipStream_t or NULL.
+ *
+ * FA_FP8_QSCALED (the fp8 forward's fast form, "FlashAttention-3: Fast &
+ * Accurate Attention with Asynchrony & Low-Precision", "New GPU Features on
+ * Hopper": the exponentials, not the products, bound the FP8 softmax): q's
+ * values carry softmax_scale * log2(e) (prepared with that prescale), so
+ * the logits reach exp2 straight from the matrix product, which also
+ * applies the block scales as E8M0 exponents. softmax_scale is then not
+ * used. FA_FP8_E4M3 inputs must have power-of-two block scales (q from
+ * fa_fp8_prep_scaled, which always rounds them so; k and v prepared with
+ * FA_SCALE_POW2), all normal floats: at d = 128, where the product applies
+ * them, the kernel checks the scales of each head and writes NaN to O and
+ * lse of the rows of a workgroup whose scales are not (the call still
+ * returns FA_OK); at d = 64 and 256 the logits take one multiply-add as
+ * without the flag and any scales work. FA_FP8_MX inputs need q from
+ * fa_mx_prep_scaled. A q prepared without the prescale gives wrong results
+ * that are not detected.
  *
  * q, k, v must be 16-byte aligned (256-byte for the FP8 dtypes). Returns FA_OK, FA_ERR_INVALID_ARG,
  * FA_ERR_UNSUPPORTED (d not in {64,128,256}, or N*d*2 > 2^31 - 2^16 - 1:
@@ -249,6 +271,26 @@ int fa_fp8_prep(const void* x, void* x8, const int8_t* signs,
                 int B, int H, int N, int d, int block_rows, int in_dtype,
                 void* stream);
 
+/*
+ * fa_fp8_prep_scaled - fa_fp8_prep_rope with a prescale: the values
+ * quantised are (rotary, Hadamard as there) times prescale, multiplied in
+ * float32 before the block maximum, so the packed tensor represents
+ * x * prescale; block scales are always rounded up to powers of two (the
+ * form FA_FP8_QSCALED needs; FA_SCALE_POW2 in in_dtype is accepted and
+ * changes nothing). Prepare q for fa_fwd with FA_FP8_QSCALED with
+ * prescale = softmax_scale * log2(e).
+ *
+ *  prescale finite and > 0.
+ *  rope_style FA_ROPE_NONE for no rotary step (rope_base and pos0 then
+ *           unused); other arguments as for fa_fp8_prep_rope.
+ *
+ * Returns FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED or FA_ERR_HIP.
+ */
+int fa_fp8_prep_scaled(const void* x, void* x8, const int8_t* signs,
+                       int B, int H, int N, int d, int block_rows, int in_dtype,
+                       int rope_style, float rope_base, int pos0, float prescale,
+                       void* stream);
+
 /* Rotary pairings for fa_fp8_prep_rope. */
 enum fa_rope_style {
     FA_ROPE_NONE = 0,
@@ -316,6 +358,18 @@ enum fa_mx_axis {
  */
 int fa_mx_prep(const void* x, void* x8, const int8_t* signs, int B, int H, int N, int d,
                int axis, int in_dtype, void* stream);
+
+/*
+ * fa_mx_prep_scaled - fa_mx_prep along d (axis must be FA_MX_ALONG_D) of
+ * x * prescale: the (Hadamard-rotated) float32 values are multiplied by
+ * prescale before each block's maximum, so the tensor represents
+ * x * prescale. Prepare q for fa_fwd with FA_FP8_MX | FA_FP8_QSCALED with
+ * prescale = softmax_scale * log2(e). prescale finite and > 0; other
+ * arguments and returns as for fa_mx_prep (FA_ERR_INVALID_ARG for
+ * FA_MX_ALONG_N).
+ */
+int fa_mx_prep_scaled(const void* x, void* x8, const int8_t* signs, int B, int H, int N, int d,
+                      int axis, int in_dtype, float prescale, void* stream);
 
 /* Size in bytes of a packed microscaled tensor for [B][H][N][d] (either
  * axis); 0 for invalid sizes. Pure host arithmetic. */

@@ -263,3 +263,60 @@ def test_mx_sizes_and_fwd_dtype(L):
     assert fwd(dtype=fa.FA_FP8_MX, q=FAKE + 16) == fa.FA_ERR_INVALID_ARG
     assert fwd(dtype=fa.FA_FP8_MX | 0x200) == fa.FA_ERR_INVALID_ARG
     assert fwd(dtype=fa.FA_FP8_MX, B=0) == fa.FA_OK
+
+
+def prep_scaled(**kw):
+    a = dict(x=FAKE, x8=FAKE, signs=None, B=1, H=1, N=128, d=128, block_rows=128,
+             in_dtype=fa.FA_BF16, style=fa.FA_ROPE_NONE, base=10000.0, pos0=0, prescale=0.1275)
+    a.update(kw)
+    return fa.fp8_prep_scaled_raw(a["x"], a["x8"], a["signs"], a["B"], a["H"], a["N"], a["d"],
+                                  a["block_rows"], a["in_dtype"], a["style"], a["base"], a["pos0"],
+                                  a["prescale"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(prescale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(prescale=-0.5), fa.FA_ERR_INVALID_ARG),
+    (dict(prescale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(prescale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(style=3), fa.FA_ERR_INVALID_ARG),
+    (dict(style=fa.FA_ROPE_HALF, base=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(in_dtype=fa.FA_FP8_E4M3), fa.FA_ERR_INVALID_ARG),
+    (dict(block_rows=64), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(x8=FAKE + 16), fa.FA_ERR_INVALID_ARG),
+    (dict(in_dtype=fa.FA_BF16 | fa.FA_SCALE_POW2, N=0), fa.FA_OK),
+    (dict(style=fa.FA_ROPE_NONE, base=0.0, pos0=-5, N=0), fa.FA_OK),
+])
+def test_prep_scaled_validation(L, kw, status):
+    assert prep_scaled(**kw) == status
+
+
+def mx_scaled(**kw):
+    a = dict(x=FAKE, x8=FAKE, signs=None, B=1, H=1, N=128, d=128, axis=fa.FA_MX_ALONG_D,
+             in_dtype=fa.FA_BF16, prescale=0.1275)
+    a.update(kw)
+    return fa.mx_prep_scaled_raw(a["x"], a["x8"], a["signs"], a["B"], a["H"], a["N"], a["d"],
+                                 a["axis"], a["in_dtype"], a["prescale"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(axis=fa.FA_MX_ALONG_N), fa.FA_ERR_INVALID_ARG),         # prescale defined along d only
+    (dict(axis=fa.FA_MX_ALONG_N, prescale=1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(prescale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(prescale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(x8=FAKE + 64), fa.FA_ERR_INVALID_ARG),
+    (dict(B=0), fa.FA_OK),
+])
+def test_mx_prep_scaled_validation(L, kw, status):
+    assert mx_scaled(**kw) == status
+
+
+def test_qscaled_flag_only_for_fp8(L):
+    for base in (fa.FA_BF16, fa.FA_F16):
+        assert fwd(dtype=base | fa.FA_FP8_QSCALED) == fa.FA_ERR_INVALID_ARG
+    for base in (fa.FA_FP8_E4M3, fa.FA_FP8_MX):
+        assert fwd(dtype=base | fa.FA_FP8_QSCALED, B=0) == fa.FA_OK
+        assert fwd(dtype=base | fa.FA_FP8_QSCALED | fa.FA_OUT_F32, B=0) == fa.FA_OK
+        assert fwd(dtype=base | fa.FA_FP8_QSCALED, q=FAKE + 16) == fa.FA_ERR_INVALID_ARG

@@ -1,0 +1,298 @@
+"""GPU parity of the fp8 forward's multiply-free form (FA_FP8_QSCALED): q
+prepared with prescale softmax_scale * log2(e) (fa_fp8_prep_scaled,
+fa_mx_prep_scaled), so the score product is already the base-2 exponent of
+the softmax, the block scales enter the product as E8M0 exponents, and the
+first product of every pipelined key tile starts from log2(8) - m instead of
+zero.
+
+* prescaled preps against the oracle's prescaled quantisers (codes
+  bit-identical without the Hadamard, adjacent and rare with it);
+* the forward against exact attention of the unquantised inputs (the fp8
+  RMSE bound) and against the prescaled fake-quant oracle (LSE within 1e-3,
+  every element within the bound on P''s e4m3 rounding), block-scaled and
+  microscaled, causal and not, ragged N, d = 64 / 128 / 256;
+* late score jumps that force the exact-maximum redo inside the pipelined
+  step (the next tile's scores, issued with the old maximum, and the start
+  value of later tiles move with it);
+* the full-size outlier workload, every row of three heads;
+* block scales that are not powers of two give NaN rows, not wrong ones.
+
+The forward consumes codes and scales only; the random-sign Hadamard lives
+in the prep, whose float32 butterflies can leave a value within an ulp of an
+e4m3 rounding boundary on the other side of it (the prep tests hold such
+codes to adjacent and rare). One such code in Q or K moves every logit of a
+row (measured: 1-3 per head of the outlier workload, up to 3e-2 of LSE on a
+row dominated by an 8x key), so the forward's elementwise and LSE checks
+take inputs prepared without the transform, whose codes equal the oracle's
+bit for bit; the runs with the transform are held to the RMSE contract
+against exact attention.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import exact_attention_55_amd as fa
+from exact_attention_55_amd.inputs import CONFIGS, make_qkv, make_signs, to_f64
+from oracle.mx import fake_quant_attention_mx, mx_dequantize, mx_quantize
+
+from helpers import FP8_RMSE, check_lse, errors, fp8_p_rounding_bound, half_ulp, sample_rows
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+LN2 = math.log(2.0)
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def prescale_of(d):
+    return float(np.float32(1.0 / math.sqrt(d) * math.log2(math.e)))
+
+
+def gpu_prep(x, signs, block_rows, prescale=None, pow2=False, rope=None):
+    B, H, N, d = x.shape
+    sd = None if signs is None else torch.from_numpy(signs).to(DEV)
+    packed = fa.fp8_prep(x.to(DEV), sd, block_rows, rope=rope, pow2_scale=pow2, prescale=prescale)
+    torch.cuda.synchronize()
+    codes = fa.fp8_codes_view(packed, B, H, N, d).cpu().numpy()
+    scales = fa.fp8_scales_view(packed, B, H, N, d).cpu().numpy()
+    return packed, codes, scales
+
+
+def compare_codes(codes, scales, ref_codes, ref_scales, exact):
+    if exact:
+        np.testing.assert_array_equal(scales, ref_scales)
+        np.testing.assert_array_equal(codes, ref_codes)
+        return
+    np.testing.assert_allclose(scales, ref_scales, rtol=2e-6, atol=0)
+    diff = codes != ref_codes
+    assert diff.mean() <= 1e-3, f"{diff.mean():.2e} of codes differ"
+    if diff.any():
+        a = oracle.e4m3_decode(codes[diff])
+        b = oracle.e4m3_decode(ref_codes[diff])
+        mag = np.maximum(np.maximum(np.abs(a), np.abs(b)), 2.0 ** -6)
+        assert np.all(np.abs(a - b) <= 2.0 ** (np.floor(np.log2(mag)) - 3))
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("had", [False, True])
+@pytest.mark.parametrize("block_rows", [128, 0])
+def test_prep_scaled_matches_oracle(d, had, block_rows):
+    say(f"prep scaled d={d} had={had} block_rows={block_rows}")
+    B, H, N = 2, 3, 300
+    x, _, _ = make_qkv(B, H, N, d, seed=81 + d, dtype="bf16", outliers=True)
+    signs = make_signs(H, d, 81) if had else None
+    p = prescale_of(d)
+    _, codes, scales = gpu_prep(x, signs, block_rows, prescale=p)
+    rc, rs = oracle.fp8_quantize(to_f64(x), signs, block_rows, pow2=True, prescale=p)
+    compare_codes(codes, scales, rc, rs, exact=not had)
+    assert np.all(np.frexp(scales)[0] == 0.5)
+
+
+@pytest.mark.parametrize("style", ["interleaved", "half"])
+def test_prep_scaled_with_rope(style):
+    say(f"prep scaled rope {style}")
+    x, _, _ = make_qkv(2, 2, 300, 128, seed=83, dtype="bf16", outliers=True)
+    signs = make_signs(2, 128, 83)
+    rope = (style, 10000.0, 11)
+    p = prescale_of(128)
+    _, codes, scales = gpu_prep(x, signs, 128, prescale=p, rope=rope)
+    rc, rs = oracle.fp8_quantize(to_f64(x), signs, 128, rope, pow2=True, prescale=p)
+    compare_codes(codes, scales, rc, rs, exact=False)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("had", [False, True])
+def test_mx_prep_scaled_matches_oracle(d, had):
+    say(f"mx prep scaled d={d} had={had}")
+    B, H, N = 2, 2, 300
+    x, _, _ = make_qkv(B, H, N, d, seed=85 + d, dtype="bf16", outliers=True)
+    signs = make_signs(H, d, 85) if had else None
+    p = prescale_of(d)
+    sd = None if signs is None else torch.from_numpy(signs).to(DEV)
+    packed = fa.mx_prep(x.to(DEV), sd, "d", prescale=p)
+    torch.cuda.synchronize()
+    codes = packed[: B * H * N * d].view(B, H, N, d).cpu().numpy()
+    exps = fa.mx_scales_view(packed, B, H, N, d, "d").cpu().numpy().astype(np.int32) - 127
+    rc, re = mx_quantize(to_f64(x), "d", signs, prescale=p)
+    if not had:
+        np.testing.assert_array_equal(exps, re)
+        np.testing.assert_array_equal(codes, rc)
+    else:
+        bad = exps != re
+        assert bad.mean() <= 1e-3
+        diff = (codes != rc) & np.repeat(~bad, 32, axis=-1)
+        assert diff.mean() <= 1e-3
+
+
+def run_qs(q, k, v, signs, causal, mx=False, out_f32=True, pow2_k=True):
+    B, H, N, d = q.shape
+    p = prescale_of(d)
+    sd = None if signs is None else torch.from_numpy(signs).to(DEV)
+    if mx:
+        q8 = fa.mx_prep(q.to(DEV), sd, "d", prescale=p)
+        k8 = fa.mx_prep(k.to(DEV), sd, "d")
+        v8 = fa.mx_prep(v.to(DEV), None, "n")
+    else:
+        q8 = fa.fp8_prep(q.to(DEV), sd, 128, prescale=p)
+        k8 = fa.fp8_prep(k.to(DEV), sd, 128, pow2_scale=pow2_k)
+        v8 = fa.fp8_prep(v.to(DEV), None, 128, pow2_scale=True)
+    o, lse = fa.fwd_fp8(q8, k8, v8, B, H, N, d, causal=causal, out_f32=out_f32, mx=mx,
+                        qscaled=True)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def fq_inputs(q64, k64, v64, signs, mx):
+    """The oracle's dequantised prescaled inputs (logits Q K^T in base 2)."""
+    d = q64.shape[-1]
+    p = np.float32(1.0 / math.sqrt(d) * math.log2(math.e))
+    if mx:
+        qc, qe = mx_quantize(q64, "d", signs, prescale=p)
+        kc, ke = mx_quantize(k64, "d", signs)
+        vc, ve = mx_quantize(v64, "n")
+        return mx_dequantize(qc, qe, "d"), mx_dequantize(kc, ke, "d"), mx_dequantize(vc, ve, "n")
+    qc, qs = oracle.fp8_quantize(q64, signs, 128, pow2=True, prescale=p)
+    kc, ks = oracle.fp8_quantize(k64, signs, 128, pow2=True)
+    vc, vs = oracle.fp8_quantize(v64, None, 128, pow2=True)
+    return (oracle.fp8_dequantize(qc, qs), oracle.fp8_dequantize(kc, ks),
+            oracle.fp8_dequantize(vc, vs))
+
+
+@pytest.mark.parametrize("mx", [False, True])
+@pytest.mark.parametrize("B,H,N,d,causal", [
+    (1, 2, 300, 64, False), (1, 2, 300, 64, True), (2, 2, 640, 128, False),
+    (1, 2, 520, 128, True), (1, 1, 384, 256, False), (1, 1, 200, 256, True), (2, 3, 33, 128, False),
+])
+def test_qscaled_small_vs_oracles(B, H, N, d, causal, mx):
+    say(f"fp8 qscaled B={B} H={H} N={N} d={d} causal={causal} mx={mx}")
+    q, k, v = make_qkv(B, H, N, d, seed=91 + N, dtype="bf16")
+    q64, k64, v64 = to_f64(q), to_f64(k), to_f64(v)
+    o_ref, _ = oracle.attention(q64, k64, v64, causal)
+    o, _ = run_qs(q, k, v, make_signs(H, d, 91), causal, mx)        # with the transform
+    assert np.all(np.isfinite(o))
+    _, rmse = errors(o, o_ref)
+    assert rmse <= FP8_RMSE, f"fp8 RMSE {rmse:.3e}"
+    signs = None
+    o, lse = run_qs(q, k, v, signs, causal, mx)
+    _, rmse = errors(o, o_ref)
+    assert rmse <= FP8_RMSE, f"fp8 RMSE {rmse:.3e}"
+    qd, kd, vd = fq_inputs(q64, k64, v64, signs, mx)
+    o_fq, lse_fq = oracle.attention(qd, kd, vd, causal, LN2)
+    check_lse(lse, lse_fq)
+    _, rmse_fq = errors(o, o_fq)
+    assert rmse_fq <= FP8_RMSE / 2, f"RMSE vs fake-quant {rmse_fq:.3e}"
+    rows = np.arange(N)
+    for b in range(B):
+        for h in range(H):
+            bound = fp8_p_rounding_bound(qd, kd, vd, b, h, rows, causal, None, LN2) + 1e-5
+            err = np.abs(o[b, h] - o_fq[b, h])
+            assert np.all(err <= bound), f"({b},{h}) worst excess {np.max(err - bound):.3e}"
+
+
+JUMP_KEYS = [300, 301, 455, 700, 1000]      # in tiles 4, 4, 7, 10, 15: keys scaled by 8
+
+
+@pytest.mark.parametrize("mx", [False, True])
+@pytest.mark.parametrize("causal,d", [(False, 128), (True, 128), (False, 256), (True, 64), (False, 64)])
+def test_qscaled_late_score_jump(causal, d, mx):
+    """Keys eight times longer in later tiles push some rows' scores many
+    log2 units above the first tile's maximum, so tiles inside the
+    pipelined loop take the exact-maximum redo; with several jump tiles the
+    next tile's scores, already issued from the old maximum, must move with
+    it. Every element within the P' rounding bound of the prescaled
+    fake-quant oracle, LSE within 1e-3."""
+    B, H, N = 1, 2, 1100
+    say(f"fp8 qscaled late score jump causal={causal} d={d} mx={mx}")
+    q, k, v = make_qkv(B, H, N, d, seed=97, dtype="bf16")
+    k = k.clone()
+    k[:, :, JUMP_KEYS] *= 8
+    signs = None
+    q64, k64, v64 = to_f64(q), to_f64(k), to_f64(v)
+    o, lse = run_qs(q, k, v, signs, causal, mx)
+    assert np.all(np.isfinite(o))
+    qd, kd, vd = fq_inputs(q64, k64, v64, signs, mx)
+    o_fq, lse_fq = oracle.attention(qd, kd, vd, causal, LN2)
+    s = np.einsum("bhid,bhjd->bhij", qd, kd)          # base-2 logits
+    assert np.max(lse_fq / LN2 - s[..., :64].max(-1)) > 8
+    check_lse(lse, lse_fq)
+    rows = np.arange(N)
+    for h in range(H):
+        bound = fp8_p_rounding_bound(qd, kd, vd, 0, h, rows, causal, None, LN2) + 1e-5
+        err = np.abs(o[0, h] - o_fq[0, h])
+        assert np.all(err <= bound), f"head {h}: worst excess {np.max(err - bound):.3e}"
+
+
+def test_qscaled_workload_all_rows():
+    """The outlier workload at full size (the launch the bench times, plus
+    float32 output), every row of three heads, with the transform: RMSE
+    against exact attention within the fp8 bound and within 10 % of the
+    prescaled fake-quant oracle's own. The same shape on N(0, 1) inputs
+    without the transform: elementwise within the P' rounding bound of the
+    fake-quant oracle and LSE within 1e-3, non-causal and causal with bf16
+    output. (The outlier inputs without the transform give rows with base-2
+    logits near 100, where the matrix unit's own accumulation moves the LSE
+    by up to ~7e-3 in the plain fp8 form too, measured; the transform is
+    what keeps the workload's logits small.)"""
+    cfg = CONFIGS["fp8_b4h16n4k_d128"]
+    B, H, N, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
+    say("fp8 qscaled outlier workload, all rows of three heads")
+    q, k, v = make_qkv(**cfg)
+    signs = make_signs(H, d, cfg["seed"])
+    o, _ = run_qs(q, k, v, signs, False)
+    sq = {"gpu": [], "fq": [], "gpu_fq": []}
+    for b, h in ((0, 0), (1, 7), (B - 1, H - 1)):
+        q64, k64, v64 = (to_f64(t[b:b + 1, h:h + 1]) for t in (q, k, v))
+        o_ex, _ = oracle.attention(q64, k64, v64, False)
+        qd, kd, vd = fq_inputs(q64, k64, v64, signs[h:h + 1], False)
+        o_fq, _ = oracle.attention(qd, kd, vd, False, LN2)
+        sq["gpu"].append((o[b, h] - o_ex[0, 0]) ** 2)
+        sq["fq"].append((o_fq[0, 0] - o_ex[0, 0]) ** 2)
+    say("fp8 qscaled N(0,1) inputs of the workload shape, no transform")
+    q, k, v = make_qkv(**dict(cfg, outliers=False))
+    o0, lse0 = run_qs(q, k, v, None, False)
+    for b, h in ((0, 0), (1, 7), (B - 1, H - 1)):
+        q64, k64, v64 = (to_f64(t[b:b + 1, h:h + 1]) for t in (q, k, v))
+        qd, kd, vd = fq_inputs(q64, k64, v64, None, False)
+        o_fq, lse_fq = oracle.attention(qd, kd, vd, False, LN2)
+        err = np.abs(o0[b, h] - o_fq[0, 0])
+        bound = fp8_p_rounding_bound(qd, kd, vd, 0, 0, np.arange(N), False, None, LN2) + 1e-5
+        assert np.all(err <= bound), f"head {b},{h}: worst excess {np.max(err - bound):.3e}"
+        check_lse(lse0[b, h], lse_fq[0, 0])
+        sq["gpu_fq"].append(err ** 2)
+    rmse = {n: float(np.sqrt(np.mean(np.concatenate(v)))) for n, v in sq.items()}
+    say(f"fp8 qscaled all-rows RMSE: {rmse}")
+    assert rmse["gpu"] <= FP8_RMSE
+    assert rmse["gpu"] <= 1.10 * rmse["fq"]
+    assert rmse["gpu_fq"] <= 3.5e-3
+    # causal, bf16 output
+    signs = None
+    o, lse = run_qs(q, k, v, signs, True, out_f32=False)
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        q64, k64, v64 = (to_f64(t[b:b + 1, h:h + 1]) for t in (q, k, v))
+        qd, kd, vd = fq_inputs(q64, k64, v64, signs, False)
+        o_fq, lse_fq = oracle.attention(qd, kd, vd, True, LN2)
+        rows = sample_rows(N, seed=b + h)
+        bound = fp8_p_rounding_bound(qd, kd, vd, 0, 0, rows, True, None, LN2)
+        bound += half_ulp(np.abs(o_fq[0, 0, rows]) + bound, "bf16") + 1e-6
+        err = np.abs(o[b, h, rows] - o_fq[0, 0, rows])
+        assert np.all(err <= bound), f"causal head {b},{h}: worst excess {np.max(err - bound):.3e}"
+        check_lse(lse[b, h, rows], lse_fq[0, 0, rows])
+
+
+def test_qscaled_rejects_scales_not_powers_of_two():
+    """k prepared with amax / 448 block scales cannot enter the product as
+    E8M0 exponents: every row comes back NaN (O and LSE), none wrong."""
+    say("fp8 qscaled with k scales not powers of two")
+    B, H, N, d = 1, 2, 300, 128
+    q, k, v = make_qkv(B, H, N, d, seed=99, dtype="bf16")
+    signs = make_signs(H, d, 99)
+    o, lse = run_qs(q, k, v, signs, False, pow2_k=False)
+    assert np.all(np.isnan(o)) and np.all(np.isnan(lse))
