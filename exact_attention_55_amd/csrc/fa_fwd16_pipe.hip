@@ -56,6 +56,9 @@ constexpr float kBigP = 16384.0f;   // per-lane sum of p that forces the exact-m
 #ifndef FA16P_NPF
 #define FA16P_NPF 3                  // fragments read ahead of their first MFMA
 #endif
+#ifndef FA16P_QB                     // 32-row query blocks per wave: 2 (one wave per SIMD,
+#define FA16P_QB 2                   // 4 per workgroup) or 1 (two per SIMD, 8 per workgroup)
+#endif
 
 // O^T += V^T P^T with O held in the accumulation registers (mfma_acc, see
 // the file header): the compiler does not treat these as MFMAs.
@@ -64,7 +67,7 @@ template <typename T, int D>
 struct PipeWave {
     using X8 = typename Elt<T>::x8;
     using X2 = typename Elt<T>::x2;
-    static constexpr int QB = 2;           // 32-row query blocks per wave
+    static constexpr int QB = FA16P_QB;    // 32-row query blocks per wave
     static constexpr int RB = 2 * D;       // bytes per K / V row in LDS
     static constexpr int NCH = D / 16;     // k-steps of the score MFMA (K fragments per block)
     static constexpr int NDB = D / 32;     // 32-row blocks of O^T
@@ -424,7 +427,7 @@ struct PipeWave {
 
 
 template <typename T, int D, bool CAUSAL, bool OUT_F32>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(64 * 8 / FA16P_QB, 1)
 fa_fwd16_pipe_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
                      void* __restrict__ Og, float* __restrict__ LSEg, int N, int num_qtiles,
                      int num_blocks, float c)
@@ -433,7 +436,7 @@ fa_fwd16_pipe_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
     using X8 = typename W::X8;
     using X2 = typename W::X2;
     constexpr int QB = W::QB, NCH = W::NCH, NDB = W::NDB, RB = W::RB, NPF = W::NPF;
-    constexpr int NW = 4;                  // waves per workgroup, one per SIMD
+    constexpr int NW = 8 / QB;             // waves per workgroup: 256 query rows
     constexpr int QW = 32 * QB;            // query rows per wave
     constexpr int BR = NW * QW;            // query rows per workgroup
     constexpr int BC = 64;                 // keys per tile: two half steps
@@ -623,9 +626,8 @@ fa_fwd16_pipe_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
 
     // ---- epilogue: O = O^T / l~, LSE = ln2 * (m + log2 l) ----
     // O was written by asm MFMAs: wait for the last of them before reading.
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4"
-                 : "+a"(st.o[0][0]), "+a"(st.o[0][1]), "+a"(st.o[0][2]), "+a"(st.o[0][3]),
-                   "+a"(st.o[1][0]), "+a"(st.o[1][1]), "+a"(st.o[1][2]), "+a"(st.o[1][3]));
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) acc_settle(st.o[qb][0], st.o[qb][1], st.o[qb][2], st.o[qb][3]);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const float l = pair_sum(st.l[qb]);
@@ -662,7 +664,8 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
     const long long nblk = (long long)num_qtiles * a.B * a.H;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const float c = a.scale * kLog2e;
-    hipLaunchKernelGGL((fa_fwd16_pipe_kernel<T, D, CAUSAL, OUT_F32>), dim3((unsigned)nblk), dim3(256), 0, s,
+    hipLaunchKernelGGL((fa_fwd16_pipe_kernel<T, D, CAUSAL, OUT_F32>), dim3((unsigned)nblk),
+                       dim3(64 * 8 / FA16P_QB), 0, s,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                        a.o, a.lse, a.N, num_qtiles, (int)nblk, c);
     return hipGetLastError();
