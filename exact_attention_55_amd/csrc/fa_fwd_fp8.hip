@@ -24,14 +24,18 @@
 //    factor folded into the exponent, p' = exp2(s*c - m + log2(8 f_j)), so
 //    the V block scale costs no extra VALU work. V prepared with
 //    power-of-two block scales (fa_fp8_prep with FA_SCALE_POW2) has f_j = 1:
-//    P' = 8 p, and a row dominated by the key at the reference maximum
-//    (p = 1) takes that key's weight exactly. Other f_j leave every P' with
-//    its e4m3 rounding of 2^-4 relative, including that dominant one. (Folding
-//    all of w_j into P' would also push blocks with small V scales into
-//    e4m3's subnormal range.) A
-//    tile whose P' sum in some lane exceeds kBig8 = 448 (the e4m3 maximum)
-//    is redone with its exact maximum, so every P' is <= 448; at the exact
-//    maximum every P' is below 16, and P' >= 8 p keeps p >= 2^-9 normal;
+//    P' = 8 p, and a row dominated by the key at its exact maximum (p =
+//    2^-kMaxMargin there, see below) takes that key's weight exactly. Other
+//    f_j leave every P' with its e4m3 rounding of 2^-4 relative, including
+//    that dominant one. (Folding all of w_j into P' would also push blocks
+//    with small V scales into e4m3's subnormal range.) A tile whose P' sum
+//    in some lane exceeds kBig8 = 448 (the e4m3 maximum) is redone with its
+//    exact maximum, so every P' is <= 448. The reference maximum is set
+//    kMaxMargin = 2 (log2 units) above an exact one, at the first tile and
+//    at each redo: a row whose scores just jumped keeps two more powers of
+//    two of headroom before the next redo (on the 0.1 % outlier inputs
+//    5.2 -> 2.6 % of tiles redone), so at that point every P' is below 4
+//    (f_j < 2), and P' >= 2 p keeps p >= 2^-7 normal;
 //  * the row sum l accumulates the unquantised p (rowsum(P') / (8 f_j));
 //  * epilogue: O = O_acc * sv_max / (8 l).
 // Microscaled inputs (fa_mx_prep: one power-of-two E8M0 scale per 32
@@ -50,6 +54,7 @@ namespace fa {
 constexpr float kPScale = 8.0f;     // P multiplier before e4m3 rounding
 constexpr int kPScaleE8M0 = 124;    // 2^-3: the microscaled PV MFMA undoes kPScale
 constexpr float kBig8 = 448.0f;     // per-lane tile sum of P' that forces the exact-maximum path
+constexpr float kMaxMargin = 2.0f;  // reference maximum above the exact one it is set from (log2 units)
 
 #ifndef FA8_PRIO                   // 0: the score phase runs at normal wave priority
 #define FA8_PRIO 1
@@ -301,9 +306,10 @@ struct Wave8 {
         return pair_max(part[0]) * cj;
     }
 
-    // Moves the reference maximum to max(m, mt), rescaling O and l.
+    // Moves the reference maximum to max(m, mt + kMaxMargin) (mt: an exact
+    // tile maximum), rescaling O and l.
     __device__ __forceinline__ void raise_max(float mt) {
-        const float mnew = fmaxf(m, mt);
+        const float mnew = fmaxf(m, mt + kMaxMargin);
         const float alpha = (mnew == -INFINITY) ? 1.f : exp2_hw(m - mnew);
         m = mnew;
         l *= alpha;
@@ -836,7 +842,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
         float cj, bj, ls;
         tile_scales(cj, bj, ls, tv);
         st.scores(s, ktile(0), ka, qf, tk, qs);
-        st.raise_max(W::tile_max(s, cj));    // first reference maximum: exact
+        st.raise_max(W::tile_max(s, cj));    // first reference maximum: from the exact one
         if constexpr (W::BAKE) {
             // from here on the pipelined scores carry log2(8) - m
             const float nm = bj - st.m;
@@ -923,7 +929,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
             tile_scales(cj, bj, lscale, tv);
             st.scores(s, ktile(t), ka, qf, tk, qs);
             W::template mask<CAUSAL>(s, k0, q0, N, hi, l32);
-            if (t == 0) st.raise_max(W::tile_max(s, cj));   // first reference maximum: exact
+            if (t == 0) st.raise_max(W::tile_max(s, cj));   // first reference maximum: from the exact one
             st.finish(s, vtile(t), va, cj, bj, lscale, tv);
         }
         wait_vm_all();

@@ -77,20 +77,26 @@ def fp8_p_factor(vs, N, block_rows=128):
     return np.repeat(2.0 * m, block_rows)[:N]
 
 
+# The fp8 kernels take exponentials against a reference maximum set this
+# many log2 units above an exact tile maximum (never more above the row's
+# maximum than that), so their p are at least 2^-FP8_REF_MARGIN of p
+# against the row maximum.
+FP8_REF_MARGIN = 2
+
+
 def fp8_p_rounding_bound(q, k, v, b, h, rows, causal, w=None, scale=None):
     """Elementwise bound on |O_gpu - O_dq| for query rows `rows` of head
     (b, h), where O_dq is exact attention of the dequantised inputs q, k, v
     (float64 [B,H,N,d]) and the GPU differs from it only by rounding the
-    weights P' = 8 p_j w_j to e4m3 before the PV product (p_j relative to
-    the row maximum, the row sum taken from the unrounded p, the factor w_j
-    undone exactly afterwards). An e4m3 rounding moves x by at most
-    max(2^-4 x, 2^-10) (half a step of a normal, half the subnormal spacing
-    2^-9), so
-        |dO_ic| <= sum_j max(2^-4 p_j, 2^-13 / w_j) |V_jc| / sum_j p_j.
+    weights P' = 8 p'_j w_j to e4m3 before the PV product (p'_j relative to
+    the kernel's reference maximum, the row sum taken from the unrounded p',
+    the factor w_j undone exactly afterwards). An e4m3 rounding moves x by
+    at most max(2^-4 x, 2^-10) (half a step of a normal, half the subnormal
+    spacing 2^-9); with p_j against the row maximum and p'_j >= 2^-M p_j
+    (M = FP8_REF_MARGIN),
+        |dO_ic| <= sum_j max(2^-4 p_j, 2^(M-13) / w_j) |V_jc| / sum_j p_j.
     w: per-key factor of P' (the block-scaled path: fp8_p_factor; None: 1,
-    the microscaled path). Returns [len(rows), d]. Taking p against the true
-    row maximum only loosens the subnormal term (the GPU's p are never
-    smaller)."""
+    the microscaled path). Returns [len(rows), d]."""
     qh = np.asarray(q[b, h], dtype=np.float64)[rows]
     kh = np.asarray(k[b, h], dtype=np.float64)
     vh = np.abs(np.asarray(v[b, h], dtype=np.float64))
@@ -102,7 +108,7 @@ def fp8_p_rounding_bound(q, k, v, b, h, rows, causal, w=None, scale=None):
         s = np.where(np.arange(N)[None, :] <= np.asarray(rows)[:, None], s, -np.inf)
     p = np.exp(s - s.max(axis=1, keepdims=True))
     wj = np.ones(N) if w is None else np.asarray(w, dtype=np.float64)
-    err = np.maximum(2.0 ** -4 * p, np.where(p > 0, 2.0 ** -13 / wj[None, :], 0.0))
+    err = np.maximum(2.0 ** -4 * p, np.where(p > 0, 2.0 ** (FP8_REF_MARGIN - 13) / wj[None, :], 0.0))
     return (err @ vh) / p.sum(axis=1, keepdims=True)
 
 
