@@ -684,11 +684,12 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     };
     // QS block-scaled: E8M0 byte of K block scale idx of slot s (the slot of
     // tile t holds the scales of blocks t*BC/128 + 0, 1, ...; the tile's own
-    // block and the next one)
+    // block and the next one). Every K scale of the head was checked to be a
+    // normal power of two above, so its exponent is the byte.
     auto read_kblk = [&](TS& ts, int s, int idx) {
         if constexpr (QS && !MX) {
             const float f = uniform_f(*reinterpret_cast<const float*>(smem + 2 * R * TB + s * BSB + 4 * idx));
-            ts.kblk = wave_uniform(e8m0_of_pow2(f));
+            ts.kblk = wave_uniform(126 + __builtin_amdgcn_frexp_expf(f));
         }
     };
     auto blk_of = [](int t) { return t * BC / kQuantBlockRows; };
@@ -881,7 +882,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
             read_v(tv, ring(t + 1));           // tile t + 1
         }
         if (!PAIR || (t & 1) == 1) read_bs(ring(t + 1));
-        read_kblk(tk, ring(t + 1), blk_of(t + 2) - blk_of(t + 1));   // tile t + 2
+        if (blk_of(t + 2) != blk_of(t + 1)) read_kblk(tk, ring(t + 1), 1);   // tile t + 2
         ++t;
     };
     for (; t + R < nfull; ) {
