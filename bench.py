@@ -326,7 +326,8 @@ ABLATIONS = {
     "pipelined_64_rows": (None, "_pipelined"),
     "fp8_default": (None, "fp8"),          # the fp8 forward's counters
     "fp8_unpinned_scores": (["-DFA8_KEEP=0"], "fp8"),
-    "fp8_ring_4": (["-DFA8_RING=4"], "fp8"),
+    "fp8_multiply_per_score": (["-DFA8_QS=0"], "fp8"),
+    "fp8_exact_reference": (["-DFA8_MARGIN=0.0f"], "fp8"),
 }
 ABLATION_LEGS = ["bf16_fwd_b8h16n2k_d128", "bf16_fwd_b2h16n8k_d128_causal"]
 

@@ -54,7 +54,13 @@ namespace fa {
 constexpr float kPScale = 8.0f;     // P multiplier before e4m3 rounding
 constexpr int kPScaleE8M0 = 124;    // 2^-3: the microscaled PV MFMA undoes kPScale
 constexpr float kBig8 = 448.0f;     // per-lane tile sum of P' that forces the exact-maximum path
-constexpr float kMaxMargin = 2.0f;  // reference maximum above the exact one it is set from (log2 units)
+#ifndef FA8_MARGIN                 // reference maximum above the exact one it is set from (log2 units)
+#define FA8_MARGIN 2.0f
+#endif
+#ifndef FA8_QS                     // 0: prescaled q runs the kernel with a multiply per score too
+#define FA8_QS 1
+#endif
+constexpr float kMaxMargin = FA8_MARGIN;
 
 #ifndef FA8_PRIO                   // 0: the score phase runs at normal wave priority
 #define FA8_PRIO 1
@@ -535,8 +541,9 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     // for K and R for V, of SCB bytes each. Copies run R - 1 tiles ahead of
     // use. The key loop runs R tiles per trip, so every slot is a
     // compile-time offset there.
-    // (d = 256 keeps 2: with 4 the microscaled kernel runs out of registers)
-    constexpr int R = D == 256 ? 2 : FA8_RING;
+    // (d = 256 and the multiply-free form keep 2: with 4 they run out of
+    // registers)
+    constexpr int R = (D == 256 || QS) ? 2 : FA8_RING;
     static_assert(R == 2 || R == 4, "ring depth");
     auto ring = [](int t) { return t & (R - 1); };
     constexpr int KSB = BC * (D / 32);     // K scale bytes of a tile (one row per key)
@@ -996,7 +1003,7 @@ static hipError_t launch_m(const FwdArgs& a, hipStream_t s) {
 // c = 1 (q already carries softmax_scale * log2(e)).
 template <int D>
 static hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
-    if constexpr (D == 128) {
+    if constexpr (D == 128 && FA8_QS) {
         if (a.qscaled) return a.mx ? launch_m<D, true, true>(a, s) : launch_m<D, false, true>(a, s);
     }
     return a.mx ? launch_m<D, true, false>(a, s) : launch_m<D, false, false>(a, s);
