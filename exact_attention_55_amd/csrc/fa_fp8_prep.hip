@@ -14,7 +14,10 @@
 // 16-byte load). The Sylvester
 // Walsh-Hadamard butterflies of span 1, 2, 4 run inside a lane, spans 8 .. d/2
 // across lanes (xor-partner exchange). The block is held in registers until
-// its amax is known, so the input is read once and the codes written once.
+// its amax is known, so the input is read once and the codes written once,
+// with streaming (nontemporal) stores: the codes are not read again by this
+// kernel, and keeping them out of the way in the caches measured 15 % faster
+// for three [4,16,4096,128] tensors (2 % at [8,16,8192,128]).
 //
 // y is the row after the optional rotary step and transform, times the
 // caller's prescale (1 by default; Q for the fp8 forward's multiply-free
@@ -318,7 +321,8 @@ fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t*
                         w[h] = e4m3x2(__builtin_ldexpf(x[0], -ex), __builtin_ldexpf(x[1], -ex)) |
                                (e4m3x2(__builtin_ldexpf(x[2], -ex), __builtin_ldexpf(x[3], -ex)) << 16);
                     }
-                    *reinterpret_cast<u32x2*>(X8 + head + (size_t)row * D + 8 * j) = u32x2{w[0], w[1]};
+                    __builtin_nontemporal_store(u32x2{w[0], w[1]},
+                                                reinterpret_cast<u32x2*>(X8 + head + (size_t)row * D + 8 * j));
                     if ((j & 3) == 0)
                         reinterpret_cast<uint8_t*>(scales)[((size_t)bh * N + row) * (D / 32) + j / 4] =
                             (uint8_t)(ex + 127);
@@ -364,10 +368,10 @@ fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t*
                                     (e4m3x2(qs(v[p][6]), qs(v[p][7])) << 16);
                 uint8_t* xr = X8 + head + (size_t)row * D;
                 if constexpr (SPLIT) {
-                    *reinterpret_cast<uint32_t*>(xr + c0) = w0;
-                    *reinterpret_cast<uint32_t*>(xr + c1) = w1;
+                    __builtin_nontemporal_store(w0, reinterpret_cast<uint32_t*>(xr + c0));
+                    __builtin_nontemporal_store(w1, reinterpret_cast<uint32_t*>(xr + c1));
                 } else {
-                    *reinterpret_cast<u32x2*>(xr + c0) = u32x2{w0, w1};
+                    __builtin_nontemporal_store(u32x2{w0, w1}, reinterpret_cast<u32x2*>(xr + c0));
                 }
             }
         }
@@ -422,7 +426,7 @@ mx_prep_cols_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, uint8_t* 
             for (int e = 0; e < 8; ++e) y[e] = __builtin_ldexpf(to_f(x[e]), -ex[e]);
             const uint32_t w0 = e4m3x2(y[0], y[1]) | (e4m3x2(y[2], y[3]) << 16);
             const uint32_t w1 = e4m3x2(y[4], y[5]) | (e4m3x2(y[6], y[7]) << 16);
-            *reinterpret_cast<u32x2*>(X8 + base + (size_t)r * D) = u32x2{w0, w1};
+            __builtin_nontemporal_store(u32x2{w0, w1}, reinterpret_cast<u32x2*>(X8 + base + (size_t)r * D));
         }
     }
     uint8_t* sc = scales + (size_t)gb * D;
