@@ -328,6 +328,7 @@ ABLATIONS = {
     "fp8_unpinned_scores": (["-DFA8_KEEP=0"], "fp8"),
     "fp8_multiply_per_score": (["-DFA8_QS=0"], "fp8"),
     "fp8_exact_reference": (["-DFA8_MARGIN=0.0f"], "fp8"),
+    "fp8_barrier_per_tile": (["-DFA8_PAIRSYNC=0"], "fp8"),
 }
 ABLATION_LEGS = ["bf16_fwd_b8h16n2k_d128", "bf16_fwd_b2h16n8k_d128_causal"]
 

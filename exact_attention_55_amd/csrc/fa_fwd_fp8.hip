@@ -60,6 +60,9 @@ constexpr float kBig8 = 448.0f;     // per-lane tile sum of P' that forces the e
 #ifndef FA8_QS                     // 0: prescaled q runs the kernel with a multiply per score too
 #define FA8_QS 1
 #endif
+#ifndef FA8_PAIRSYNC               // 0: block-scaled d = 128 key loop with a barrier per tile
+#define FA8_PAIRSYNC 1
+#endif
 constexpr float kMaxMargin = FA8_MARGIN;
 
 #ifndef FA8_PRIO                   // 0: the score phase runs at normal wave priority
@@ -543,7 +546,16 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     // compile-time offset there.
     // (d = 256 and the multiply-free form keep 2: with 4 they run out of
     // registers)
-    constexpr int R = (D == 256 || QS) ? 2 : FA8_RING;
+    // PS (block-scaled, d = 128): the pipelined tiles go in pairs with one
+    // barrier per pair; a pair starting at even tile t copies K t+3, t+4 and
+    // V t+2, t+3 into the slots the previous pair finished with (ring of 4),
+    // and its closing barrier publishes them, so each copy has two steps to
+    // land and a wave that falls behind (a redo) holds the others up once
+    // per two tiles. Measured +2.5 % non-causal, neutral causal; the
+    // microscaled kernel spills two registers with it and loses 2-3 %
+    // causal, so it keeps a barrier per tile.
+    constexpr bool PS = FA8_PAIRSYNC && D == 128 && !MX;
+    constexpr int R = PS ? 4 : ((D == 256 || QS) ? 2 : FA8_RING);
     static_assert(R == 2 || R == 4, "ring depth");
     auto ring = [](int t) { return t & (R - 1); };
     constexpr int KSB = BC * (D / 32);     // K scale bytes of a tile (one row per key)
@@ -749,10 +761,11 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     // overlap (the wait below covers both).
     load_kv(krs, 0, false);
     load_kv(vrs, 0, true);
+    // per-step loop: K 1 .. R-1 and V 1 .. R-2 ahead; pairs: K 1, 2 and V 1
 #pragma unroll
-    for (int i = 1; i < R; ++i) {
+    for (int i = 1; i < (PS ? 3 : R); ++i) {
         load_kv(krs, i, false);
-        if (i < R - 1) load_kv(vrs, i, true);
+        if (i < (PS ? 2 : R - 1)) load_kv(vrs, i, true);
     }
     // Q^T fragments: query q0 + l32, bytes [64*ch + 32*hi, +32) (microscaled:
     // [64*ch + 16*hi, +16) and [64*ch + 32 + 16*hi, +16), the chunk order of
@@ -838,6 +851,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
     // next; the scales of a tile are requested with its copy and read after
     // the barrier that publishes it.
     TS tk, tv;
+    TS tk2, tv2;                           // pairs: the same for the pair's second step
     wait_vm_all();
     __syncthreads();
     if constexpr (MX) {
@@ -860,6 +874,13 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
         }
         if constexpr (MX) read_k(tk, 1);
         read_kblk(tk, 0, blk_of(1) - blk_of(0));
+        if constexpr (PS) {                  // the second step of the first pair
+            if constexpr (MX) {
+                read_k(tk2, 2);
+                read_v(tv2, 1);
+            }
+            read_kblk(tk2, 0, blk_of(2) - blk_of(0));
+        }
         __syncthreads();                     // all waves done reading K_0's slot
     }
     int t = 0;
@@ -892,11 +913,52 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg
         if (blk_of(t + 2) != blk_of(t + 1)) read_kblk(tk, ring(t + 1), 1);   // tile t + 2
         ++t;
     };
-    for (; t + R < nfull; ) {
+    // Tile pairs (t even): steps t and t + 1 use K t+1, t+2 and V t, t+1,
+    // published by the previous pair's barrier (tk, tk2, tv, tv2 hold their
+    // scales); the copies of K t+3, t+4 and V t+2, t+3 go into the slots of
+    // K t-1, t and V t-2, t-1, which that barrier released.
+    auto pair_steps = [&]() {
+        static_assert(!PS || PAIR || MX, "a pair shares one scale block");
+        load_kv(krs, t + 3, false);
+        load_kv(krs, t + 4, false);
+        load_kv(vrs, t + 2, true);
+        load_kv(vrs, t + 3, true);
+        tile_scales(pcj, pbj, pls, tv);      // block-scaled: tile t's block, shared by t + 1
+        st.step(s, s2, ktile(t + 1), ka, vtile(t), va, qf, pcj, pbj, pls, tk, tv, qs);
+        st.step(s2, s, ktile(t + 2), ka, vtile(t + 1), va, qf, pcj, pbj, pls, tk2, MX ? tv2 : tv, qs);
+        wait_vm_all();
+        __syncthreads();
+        if constexpr (MX) {
+            read_k(tk, ring(t + 3));
+            read_k(tk2, ring(t + 4));
+            read_v(tv, ring(t + 2));
+            read_v(tv2, ring(t + 3));
+        }
+        read_bs(ring(t + 2));
+        read_kblk(tk, ring(t + 2), blk_of(t + 3) - blk_of(t + 2));
+        read_kblk(tk2, ring(t + 2), blk_of(t + 4) - blk_of(t + 2));
+        t += 2;
+    };
+    if constexpr (PS) {
+        // a pair at t needs full tiles t .. t+2 (its steps take the scores
+        // of t+1 and t+2)
+        for (; t + 4 < nfull; ) {            // two pairs per trip: every slot a constant
+            pair_steps();
+            pair_steps();
+        }
+        if (t + 2 < nfull) pair_steps();
+        // back to the per-step invariant (K up to t+3, V up to t+2 copied):
+        // K t+3 into the slot of K t-1, V t+2 into that of V t-2, both
+        // released by the last barrier
+        load_kv(krs, t + 3, false);
+        load_kv(vrs, t + 2, true);
+    } else {
+        for (; t + R < nfull; ) {
 #pragma unroll
-        for (int u = 0; u < R; u += 2) {
-            full_step(s, s2);
-            full_step(s2, s);
+            for (int u = 0; u < R; u += 2) {
+                full_step(s, s2);
+                full_step(s2, s);
+            }
         }
     }
     // fewer than R full steps left; after an odd number of them the scores
