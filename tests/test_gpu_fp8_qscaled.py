@@ -40,7 +40,8 @@ import exact_attention_55_amd as fa
 from exact_attention_55_amd.inputs import CONFIGS, make_qkv, make_signs, to_f64
 from oracle.mx import fake_quant_attention_mx, mx_dequantize, mx_quantize
 
-from helpers import FP8_RMSE, check_lse, errors, fp8_p_rounding_bound, half_ulp, sample_rows
+from helpers import (FP8_RMSE, check_lse, errors, fp8_p_factor, fp8_p_rounding_bound, half_ulp,
+                     sample_rows)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -195,6 +196,51 @@ def test_qscaled_small_vs_oracles(B, H, N, d, causal, mx):
             bound = fp8_p_rounding_bound(qd, kd, vd, b, h, rows, causal, None, LN2) + 1e-5
             err = np.abs(o[b, h] - o_fq[b, h])
             assert np.all(err <= bound), f"({b},{h}) worst excess {np.max(err - bound):.3e}"
+
+
+@pytest.mark.parametrize("qscaled", [True, False])
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_tile_counts_d128(causal, qscaled):
+    """The block-scaled d = 128 forward runs its full key tiles in pairs
+    with one barrier per pair (two pairs per trip, then one pair, then
+    single steps, the last full tile and the ragged end). Sequence lengths
+    of 1 .. 9 key tiles, whole and ragged, walk every one of those
+    transitions (causal: every query block its own count); each against the
+    fake-quant oracle without the transform, elementwise and LSE, with and
+    without the prescale."""
+    d, H = 128, 2
+    for n in range(1, 10):
+        for r in (0, 17):
+            N = 64 * n + r
+            if N > 576:
+                continue
+            say(f"fp8 tile counts N={N} causal={causal} qscaled={qscaled}")
+            q, k, v = make_qkv(1, H, N, d, seed=200 + N, dtype="bf16")
+            q64, k64, v64 = to_f64(q), to_f64(k), to_f64(v)
+            if qscaled:
+                o, lse = run_qs(q, k, v, None, causal)
+                qd, kd, vd = fq_inputs(q64, k64, v64, None, False)
+                scale = LN2
+            else:
+                q8 = fa.fp8_prep(q.to(DEV), None, 128)
+                k8 = fa.fp8_prep(k.to(DEV), None, 128)
+                v8 = fa.fp8_prep(v.to(DEV), None, 128, pow2_scale=True)
+                ot, lt = fa.fwd_fp8(q8, k8, v8, 1, H, N, d, causal=causal, out_f32=True)
+                torch.cuda.synchronize()
+                o, lse = ot.cpu().numpy(), lt.cpu().numpy()
+                qc, qs = oracle.fp8_quantize(q64, None, 128)
+                kc, ks = oracle.fp8_quantize(k64, None, 128)
+                vc, vs = oracle.fp8_quantize(v64, None, 128, pow2=True)
+                qd, kd, vd = (oracle.fp8_dequantize(c, sc) for c, sc in ((qc, qs), (kc, ks), (vc, vs)))
+                scale = None
+            o_fq, lse_fq = oracle.attention(qd, kd, vd, causal, scale)
+            check_lse(lse, lse_fq, f"N={N}")
+            rows = np.arange(N)
+            for h in range(H):
+                w = None if qscaled else fp8_p_factor(vs[0, h], N)
+                bound = fp8_p_rounding_bound(qd, kd, vd, 0, h, rows, causal, w, scale) + 1e-5
+                err = np.abs(o[0, h] - o_fq[0, h])
+                assert np.all(err <= bound), f"N={N} head {h}: worst excess {np.max(err - bound):.3e}"
 
 
 JUMP_KEYS = [300, 301, 455, 700, 1000]      # in tiles 4, 4, 7, 10, 15: keys scaled by 8
