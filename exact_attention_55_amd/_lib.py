@@ -204,7 +204,8 @@ def fwd(q, k, v, causal=False, softmax_scale=None, out=None, lse=None, out_f32=F
 
     Returns (o, lse): o has q's dtype (float32 with out_f32=True), lse is
     float32 [B,H,N]. pipelined: at d = 128, run the 64-rows-per-wave kernel
-    with the in-wave pipeline instead of the default one.
+    with the in-wave pipeline instead of the default one (non-causal
+    forwards with N >= 8192 run it without the flag).
     """
     B, H, N, d = q.shape
     if softmax_scale is None:

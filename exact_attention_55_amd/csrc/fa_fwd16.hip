@@ -1039,13 +1039,18 @@ static hipError_t launch_ty(const FwdArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-// d = 128 with FA_FWD_PIPELINED goes to the 64-rows-per-wave pipelined
-// kernel (fa_fwd16_pipe.hip, one wave per SIMD). It halves the LDS fragment
-// reads per MFMA but a single wave issues the softmax alone; on MI355X it
-// measured slower than this file's kernel (two waves per SIMD) on most
-// shapes, so it is a selectable variant rather than the default.
+// d = 128 goes to the 64-rows-per-wave pipelined kernel (fa_fwd16_pipe.hip,
+// one wave per SIMD) with FA_FWD_PIPELINED, and by itself when the mask is
+// off and N >= kPipeMinN. That kernel halves the LDS fragment reads per MFMA
+// but a single wave issues the softmax alone. On MI355X it measured 1.5-2 %
+// faster than this file's kernel (two waves per SIMD) on long non-causal
+// sequences (N = 8192, 16384), level at N = 4096 and about 7 % slower with
+// the causal mask, whose diagonal blocks it runs unpipelined.
+constexpr int kPipeMinN = 8192;
+
 hipError_t launch_fwd16(const FwdArgs& a, bool bf16, hipStream_t s) {
-    if (a.pipelined && a.d == 128) return launch_fwd16_pipe(a, bf16, s);
+    if (a.d == 128 && (a.pipelined || (!a.causal && a.N >= kPipeMinN)))
+        return launch_fwd16_pipe(a, bf16, s);
     return bf16 ? launch_ty<__bf16>(a, s) : launch_ty<_Float16>(a, s);
 }
 

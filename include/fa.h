@@ -62,7 +62,9 @@ enum fa_status {
  * fa_fwd's dtype: 16-bit inputs at d = 128 run the 64-rows-per-wave kernel
  * that overlaps the next block's score MFMAs, this block's exponentials and
  * the previous block's PV MFMAs inside one wave (same results up to
- * rounding; ignored for other inputs). FA_SCALE_POW2 may be OR-ed into
+ * rounding; ignored for other inputs). Without the flag that kernel still
+ * runs 16-bit d = 128 forwards with causal = 0 and N >= 8192, where it is
+ * the faster one. FA_SCALE_POW2 may be OR-ed into
  * fa_fp8_prep's in_dtype: block scales are rounded up to powers of two.
  * FA_FP8_QSCALED may be OR-ed into fa_fwd's FP8 dtypes: q was prepared with
  * prescale softmax_scale * log2(e) (fa_fp8_prep_scaled, fa_mx_prep_scaled),

@@ -270,6 +270,28 @@ def test_pipe_d128_large_logits_and_constant_v(dt):
     assert np.max(np.abs(o - 0.7109375)) <= 2e-6
 
 
+@pytest.mark.parametrize("N,causal", [(8192 + 37, False), (8192 + 37, True), (8191, False)])
+def test_long_d128_dispatch(N, causal):
+    """Non-causal d = 128 forwards with N >= 8192 run the pipelined kernel
+    without FA_FWD_PIPELINED: the default call then equals the flagged one
+    bit for bit, and both meet the oracle on sampled rows of a ragged N;
+    causal ones, and shorter sequences, stay on the default kernel."""
+    say(f"long d=128 dispatch N={N} causal={causal}")
+    q, k, v = make_qkv(1, 4, N, 128, seed=300 + N, dtype="bf16")
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    o, lse = fa.fwd(qd, kd, vd, causal=causal, out_f32=True)
+    op, lsep = fa.fwd(qd, kd, vd, causal=causal, out_f32=True, pipelined=True)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(o, op)) and bool(torch.equal(lse, lsep))
+    assert same == (not causal and N >= 8192)
+    q64, k64, v64 = to_f64(q), to_f64(k), to_f64(v)
+    for h in (0, 3):
+        rows = sample_rows(N, seed=h)
+        o_ref, lse_ref = oracle.attention_rows(q64, k64, v64, 0, h, rows, causal)
+        check_o(o[0, h, rows].cpu().numpy(), o_ref, "f32", f"head {h}")
+        check_lse(lse[0, h, rows].cpu().numpy(), lse_ref, f"head {h}")
+
+
 def test_many_heads_grid():
     """B*H large with a ragged N: grid indexing over heads and tiles."""
     say("many heads")
