@@ -8,10 +8,11 @@ resident in HBM, one launch per leg:
     and non-causal (the long-context d=128 regime), B=8 H=16 N=2048 d=128
     non-causal and causal, B=4 H=32 N=4096 d=64 non-causal, B=2 H=8 N=16384
     d=256 causal;
-  * the fp8 path on B=4 H=16 N=4096 d=128 (0.1 % outliers): fa_fp8_prep of Q
-    and K (random-sign Hadamard + 128-row power-of-two block scales, Q
-    prescaled by softmax_scale * log2(e)) and V (power-of-two block scales),
-    then the fp8 forward in its multiply-free form (FA_FP8_QSCALED).
+  * the fp8 path on B=4 H=16 N=4096 d=128 (0.1 % outliers): fa_fp8_prep_qkv,
+    one launch that prepares Q and K (random-sign Hadamard + 128-row
+    power-of-two block scales, Q prescaled by softmax_scale * log2(e)) and V
+    (power-of-two block scales), then the fp8 forward in its multiply-free
+    form (FA_FP8_QSCALED).
 Each leg is timed with HIP events on the stream it is launched on.
 
 Headlines, one per precision (work 4*B*H*N^2*d, halved for causal):
@@ -490,9 +491,7 @@ def build_legs(dev, only=None):
     prescale = fa.qk_prescale(1.0 / d8 ** 0.5)
 
     def prep():
-        fa.fp8_prep(q8, signs, 128, out=pq, prescale=prescale)
-        fa.fp8_prep(k8, signs, 128, out=pk, pow2_scale=True)
-        fa.fp8_prep(v8, None, 128, out=pv, pow2_scale=True)
+        fa.fp8_prep_qkv(q8, k8, v8, signs, q_prescale=prescale, out=(pq, pk, pv))
 
     prep()                      # the forward leg alone still reads prepared inputs
     if not only or FP8_PREP_LEG in only:
@@ -516,7 +515,8 @@ def build_next_legs(dev):
     prescaled, and V along the sequence, GB/s; the forward on its output,
     non-causal and causal); the block-scaled fp8 forward, causal; the fp8
     forward on inputs prepared without the prescale (amax / 448 scales for Q
-    and K, one multiply-add per score); and the decode-shaped
+    and K, one multiply-add per score); the step's fp8 prep as three
+    separate fa_fp8_prep calls (GB/s); and the decode-shaped
     forward on its two workloads, in GB/s of the bytes it must move (K and V
     of every sequence's keys, Q, O, LSE); the backward at d = 256 on the
     B=2 H=8 N=16384 causal workload; and, as an ablation, the pipelined
@@ -603,6 +603,14 @@ def build_next_legs(dev):
                                        qscaled=True),
                     attention_flops(B8, H8, N8, d8, True), peak=PEAK_FP8))
     uq, uk = (fa.fp8_prep(t, signs, 128) for t in (q8, k8))
+
+    def prep_separate():
+        fa.fp8_prep(q8, signs, 128, out=bq, prescale=prescale)
+        fa.fp8_prep(k8, signs, 128, out=bk, pow2_scale=True)
+        fa.fp8_prep(v8, None, 128, out=bv, pow2_scale=True)
+
+    legs.append(Leg("fp8_prep_qkv_separate_b4h16n4k_d128", prep_separate, 0.0,
+                    3 * (nel * 2 + nel + B8 * H8 * (N8 // 128) * 4)))
     legs.append(Leg("fp8_fwd_b4h16n4k_d128_unscaled",
                     lambda: fa.fwd_fp8(uq, uk, bv, B8, H8, N8, d8, False, out=o8, lse=lse8),
                     attention_flops(B8, H8, N8, d8, False), peak=PEAK_FP8))

@@ -139,6 +139,9 @@ __device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
 // the rotary step (4 passes of 32 rows at d = 128), so a thread's rows in
 // flight and the sine / cosine temporaries stay within a register budget
 // that leaves several waves per SIMD to hide memory latency; 256 otherwise.
+#ifndef FA_PREP_POW2_MUL            // 0: always divide by a block scale without the Hadamard
+#define FA_PREP_POW2_MUL 1
+#endif
 #ifndef FA_PREP_WIDE                // 1: 512 threads at d = 128 without the rotary step too
 #define FA_PREP_WIDE 0
 #endif
@@ -157,13 +160,15 @@ __device__ __forceinline__ float block_scale(float amax, int pow2) {
     return __builtin_amdgcn_ldexpf(1.0f, __builtin_amdgcn_frexp_expf(s));
 }
 
-// HB heads per workgroup (rotary step: the same 128-row block of HB
-// consecutive heads, which share every row's cosines and sines).
+// One workgroup's share of the prep: workgroup index bid of a grid over
+// (head, 128-row block). HB heads per workgroup (rotary step: the same
+// 128-row block of HB consecutive heads, which share every row's cosines and
+// sines).
 template <typename T, int D, bool HAD, int MODE, int ROPE, int HB = 1>
-__global__ void __launch_bounds__((quant_threads<D, ROPE>()))
-fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t* __restrict__ signs,
-                float* __restrict__ scales, unsigned* __restrict__ gamax, int N, int H, int nblk,
-                RopeFreqs rf, int pow2, float prescale)
+__device__ __forceinline__ void
+quant_rows(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t* __restrict__ signs,
+           float* __restrict__ scales, unsigned* __restrict__ gamax, int N, int H, int nblk,
+           const RopeFreqs& rf, int pow2, float prescale, int bid)
 {
     constexpr int NT = quant_threads<D, ROPE>();
     constexpr int LPR = D / 8;                 // lanes per row
@@ -181,13 +186,13 @@ fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t*
     const int tid = threadIdx.x;
     const int j = tid % LPR, rp = tid / LPR;
     const int c0 = SPLIT ? 4 * j : 8 * j, c1 = SPLIT ? D / 2 + 4 * j : 8 * j + 4;
-    const int blk = blockIdx.x % nblk;
+    const int blk = bid % nblk;
     // rotary terms of the thread's rows, computed once for the HB heads
     float rsn[ROPE != 0 ? NPASS : 1][4], rcs[ROPE != 0 ? NPASS : 1][4];
     bool rope_ready = false;
 #pragma unroll 1
     for (int hh = 0; hh < HB; ++hh) {
-        const int bh = (blockIdx.x / nblk) * HB + hh;
+        const int bh = (bid / nblk) * HB + hh;
         const int gslot = bh * nblk + blk;            // scale slot of this (head, block)
         const int h = bh % H;
         const size_t head = (size_t)bh * N * D;
@@ -356,26 +361,74 @@ fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t*
         // multiply by the rounded reciprocal, at most one float32 ulp away, adds
         // only more of the same; it replaces ~10 instructions per element in a
         // kernel that is VALU-bound with the transform.
+        // A normal power-of-two scale (pow2 scales, mostly) has an exact
+        // reciprocal, and x * (1 / scale) is then the division itself.
         const float inv = 1.0f / scale;
-        auto qs = [&](float x) { return HAD ? x * inv : x / scale; };
+        auto store_codes = [&](auto qs) {
 #pragma unroll
-        for (int p = 0; p < NPASS; ++p) {
-            const int row = blk * kQuantBlockRows + p * RPP + rp;
-            if (row < N) {
-                const uint32_t w0 = e4m3x2(qs(v[p][0]), qs(v[p][1])) |
-                                    (e4m3x2(qs(v[p][2]), qs(v[p][3])) << 16);
-                const uint32_t w1 = e4m3x2(qs(v[p][4]), qs(v[p][5])) |
-                                    (e4m3x2(qs(v[p][6]), qs(v[p][7])) << 16);
-                uint8_t* xr = X8 + head + (size_t)row * D;
-                if constexpr (SPLIT) {
-                    __builtin_nontemporal_store(w0, reinterpret_cast<uint32_t*>(xr + c0));
-                    __builtin_nontemporal_store(w1, reinterpret_cast<uint32_t*>(xr + c1));
-                } else {
-                    __builtin_nontemporal_store(u32x2{w0, w1}, reinterpret_cast<u32x2*>(xr + c0));
+            for (int p = 0; p < NPASS; ++p) {
+                const int row = blk * kQuantBlockRows + p * RPP + rp;
+                if (row < N) {
+                    const uint32_t w0 = e4m3x2(qs(v[p][0]), qs(v[p][1])) |
+                                        (e4m3x2(qs(v[p][2]), qs(v[p][3])) << 16);
+                    const uint32_t w1 = e4m3x2(qs(v[p][4]), qs(v[p][5])) |
+                                        (e4m3x2(qs(v[p][6]), qs(v[p][7])) << 16);
+                    uint8_t* xr = X8 + head + (size_t)row * D;
+                    if constexpr (SPLIT) {
+                        __builtin_nontemporal_store(w0, reinterpret_cast<uint32_t*>(xr + c0));
+                        __builtin_nontemporal_store(w1, reinterpret_cast<uint32_t*>(xr + c1));
+                    } else {
+                        __builtin_nontemporal_store(u32x2{w0, w1}, reinterpret_cast<u32x2*>(xr + c0));
+                    }
                 }
             }
-        }
+        };
+#if FA_PREP_POW2_MUL
+        const bool exact_inv = __builtin_amdgcn_frexp_mantf(scale) == 0.5f && scale >= 0x1p-126f;
+#else
+        const bool exact_inv = false;
+#endif
+        if (HAD || exact_inv)
+            store_codes([&](float x) { return x * inv; });
+        else
+            store_codes([&](float x) { return x / scale; });
     }   // heads of the workgroup
+}
+
+template <typename T, int D, bool HAD, int MODE, int ROPE, int HB = 1>
+__global__ void __launch_bounds__((quant_threads<D, ROPE>()))
+fp8_prep_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, const int8_t* __restrict__ signs,
+                float* __restrict__ scales, unsigned* __restrict__ gamax, int N, int H, int nblk,
+                RopeFreqs rf, int pow2, float prescale)
+{
+    quant_rows<T, D, HAD, MODE, ROPE, HB>(X, X8, signs, scales, gamax, N, H, nblk, rf, pow2, prescale,
+                                          blockIdx.x);
+}
+
+// Q, K and V of one attention call in a single launch: workgroups
+// [0, grid1) take Q (the transform when signs is given, times q_prescale),
+// [grid1, 2 grid1) K (the same transform), the rest V (no transform); all
+// with power-of-two block scales. Each workgroup runs the same steps as in
+// fp8_prep_kernel, so the codes and scales are those of three separate
+// preps; one launch three times the size leaves a smaller share of the time
+// to the last, partly filled round of workgroups.
+template <typename T, int D>
+__global__ void __launch_bounds__((quant_threads<D, 0>()))
+fp8_prep_qkv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+                    uint8_t* __restrict__ Q8, uint8_t* __restrict__ K8, uint8_t* __restrict__ V8,
+                    const int8_t* __restrict__ signs, size_t scales_off, int N, int H, int nblk,
+                    int grid1, float q_prescale)
+{
+    const int t = blockIdx.x / grid1, bid = blockIdx.x - t * grid1;
+    const T* X = t == 0 ? Q : t == 1 ? K : V;
+    uint8_t* X8 = t == 0 ? Q8 : t == 1 ? K8 : V8;
+    float* scales = reinterpret_cast<float*>(X8 + scales_off);
+    const float prescale = t == 0 ? q_prescale : 1.0f;
+    const RopeFreqs rf{};
+    if (t < 2 && signs != nullptr)
+        quant_rows<T, D, true, 0, 0>(X, X8, signs, scales, nullptr, N, H, nblk, rf, 1, prescale, bid);
+    else
+        quant_rows<T, D, false, 0, 0>(X, X8, nullptr, scales, nullptr, N, H, nblk, rf, 1, prescale, bid);
 }
 
 // Microscaling along the sequence (V): each thread owns 8 adjacent columns
@@ -532,6 +585,31 @@ static hipError_t prep_ty(const PrepArgs& a, hipStream_t s) {
 
 hipError_t launch_fp8_prep(const PrepArgs& a, hipStream_t s) {
     return a.bf16 ? prep_ty<__bf16>(a, s) : prep_ty<_Float16>(a, s);
+}
+
+template <typename T, int D>
+static hipError_t prep_qkv_d(const PrepQkvArgs& a, hipStream_t s) {
+    const int nblk = (a.N + kQuantBlockRows - 1) / kQuantBlockRows;
+    const long long grid1 = (long long)a.B * a.H * nblk;
+    hipLaunchKernelGGL((fp8_prep_qkv_kernel<T, D>), dim3((unsigned)(3 * grid1)), dim3(quant_threads<D, 0>()),
+                       0, s, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                       static_cast<const T*>(a.v), a.q8, a.k8, a.v8, a.signs, a.scales_off, a.N, a.H, nblk,
+                       (int)grid1, a.q_prescale);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t prep_qkv_ty(const PrepQkvArgs& a, hipStream_t s) {
+    switch (a.d) {
+        case 64: return prep_qkv_d<T, 64>(a, s);
+        case 128: return prep_qkv_d<T, 128>(a, s);
+        case 256: return prep_qkv_d<T, 256>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_fp8_prep_qkv(const PrepQkvArgs& a, hipStream_t s) {
+    return a.bf16 ? prep_qkv_ty<__bf16>(a, s) : prep_qkv_ty<_Float16>(a, s);
 }
 
 }  // namespace fa

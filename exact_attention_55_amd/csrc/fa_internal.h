@@ -60,6 +60,23 @@ struct PrepArgs {
 };
 hipError_t launch_fp8_prep(const PrepArgs& a, hipStream_t s);
 
+// Q, K and V prepared in one launch (block scales, powers of two; Q and K
+// through the transform when signs is set, Q times q_prescale).
+struct PrepQkvArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    uint8_t* q8;
+    uint8_t* k8;
+    uint8_t* v8;
+    const int8_t* signs;
+    int B, H, N, d;
+    bool bf16;
+    size_t scales_off;
+    float q_prescale;
+};
+hipError_t launch_fp8_prep_qkv(const PrepQkvArgs& a, hipStream_t s);
+
 struct BwdArgs {
     const void* q;
     const void* k;

@@ -293,6 +293,38 @@ int fa_fp8_prep_scaled(const void* x, void* x8, const int8_t* signs,
                        int rope_style, float rope_base, int pos0, float prescale,
                        void* stream);
 
+/*
+ * fa_fp8_prep_qkv - the three preps of one FP8 attention call in a single
+ * launch ("FlashAttention-3: Fast & Accurate Attention with Asynchrony &
+ * Low-Precision", "Incoherent Processing for FP8 Accuracy" and block
+ * quantisation): q with the rotation by signs and prescale q_prescale, k
+ * with the same rotation, v without one, all with 128-row blocks and
+ * power-of-two scales. The three packed outputs equal, byte for byte, those
+ * of fa_fp8_prep_scaled(q, q8, signs, ..., 128, in_dtype, FA_ROPE_NONE, 1,
+ * 0, q_prescale), fa_fp8_prep(k, k8, signs, ..., 128, in_dtype |
+ * FA_SCALE_POW2) and fa_fp8_prep(v, v8, NULL, ..., 128, in_dtype |
+ * FA_SCALE_POW2); one launch three times the size fills the GPU better than
+ * three in turn. With q_prescale = qk prescale softmax_scale * log2(e) the
+ * outputs are the inputs of fa_fwd with FA_FP8_E4M3 | FA_FP8_QSCALED; with
+ * q_prescale = 1 those of the plain FA_FP8_E4M3 forward.
+ *
+ *  q, k, v     16-bit inputs [B][H][N][d] (in_dtype FA_BF16 or FA_F16,
+ *              FA_SCALE_POW2 may be set and changes nothing), 16-byte
+ *              aligned.
+ *  q8, k8, v8  packed outputs as fa_fp8_prep's x8, each of
+ *              fa_fp8_packed_bytes(B,H,N,d) bytes, 256-byte aligned, owned by
+ *              the caller; the three must not overlap one another or the
+ *              inputs (overlapping outputs are rejected).
+ *  signs       int8 [H][d] of +1/-1, or NULL for no rotation of q and k.
+ *  q_prescale  finite and > 0.
+ *  d           64, 128 or 256; 3 * B * H * ceil(N/128) < 2^31.
+ * Returns FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED or FA_ERR_HIP.
+ */
+int fa_fp8_prep_qkv(const void* q, const void* k, const void* v,
+                    void* q8, void* k8, void* v8, const int8_t* signs,
+                    int B, int H, int N, int d, int in_dtype, float q_prescale,
+                    void* stream);
+
 /* Rotary pairings for fa_fp8_prep_rope. */
 enum fa_rope_style {
     FA_ROPE_NONE = 0,

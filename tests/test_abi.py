@@ -320,3 +320,35 @@ def test_qscaled_flag_only_for_fp8(L):
         assert fwd(dtype=base | fa.FA_FP8_QSCALED, B=0) == fa.FA_OK
         assert fwd(dtype=base | fa.FA_FP8_QSCALED | fa.FA_OUT_F32, B=0) == fa.FA_OK
         assert fwd(dtype=base | fa.FA_FP8_QSCALED, q=FAKE + 16) == fa.FA_ERR_INVALID_ARG
+
+
+P8 = 1 << 24   # spacing of the fake packed outputs: apart, they do not overlap
+
+
+def prep_qkv(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, q8=FAKE, k8=FAKE + P8, v8=FAKE + 2 * P8, signs=None, B=1, H=1,
+             N=128, d=128, in_dtype=fa.FA_BF16, p=0.1275)
+    a.update(kw)
+    return fa.fp8_prep_qkv_raw(a["q"], a["k"], a["v"], a["q8"], a["k8"], a["v8"], a["signs"], a["B"],
+                               a["H"], a["N"], a["d"], a["in_dtype"], a["p"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(p=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(p=-1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(p=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(p=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(in_dtype=fa.FA_FP8_E4M3), fa.FA_ERR_INVALID_ARG),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=1 << 14, H=1 << 10, N=1 << 13), fa.FA_ERR_UNSUPPORTED),   # 3 x 2^30 workgroups
+    (dict(q8=FAKE + 16), fa.FA_ERR_INVALID_ARG),
+    (dict(k=FAKE + 4), fa.FA_ERR_INVALID_ARG),
+    (dict(v=None), fa.FA_ERR_INVALID_ARG),
+    (dict(v8=None), fa.FA_ERR_INVALID_ARG),
+    (dict(k8=FAKE), fa.FA_ERR_INVALID_ARG),                 # k8 is q8
+    (dict(v8=FAKE + P8 + 256), fa.FA_ERR_INVALID_ARG),      # v8 inside k8
+    (dict(B=0, k8=FAKE), fa.FA_OK),
+    (dict(N=0, in_dtype=fa.FA_F16 | fa.FA_SCALE_POW2), fa.FA_OK),
+])
+def test_prep_qkv_validation(L, kw, status):
+    assert prep_qkv(**kw) == status
