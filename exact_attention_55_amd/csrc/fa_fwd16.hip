@@ -1042,10 +1042,12 @@ static hipError_t launch_ty(const FwdArgs& a, hipStream_t s) {
 // d = 128 goes to the 64-rows-per-wave pipelined kernel (fa_fwd16_pipe.hip,
 // one wave per SIMD) with FA_FWD_PIPELINED, and by itself when the mask is
 // off and N >= kPipeMinN. That kernel halves the LDS fragment reads per MFMA
-// but a single wave issues the softmax alone. On MI355X it measured 1.5-2 %
-// faster than this file's kernel (two waves per SIMD) on long non-causal
-// sequences (N = 8192, 16384), level at N = 4096 and about 7 % slower with
-// the causal mask, whose diagonal blocks it runs unpipelined.
+// but a single wave issues the softmax alone, and with one 256-row
+// workgroup per CU nothing hides a workgroup's fixed cost (Q loads, first
+// tile, O stores). On MI355X it measured 1.5-2 % faster than this file's
+// kernel (two waves per SIMD) on long non-causal sequences (N = 8192,
+// 16384), level at N = 4096 and about 6 % slower with the causal mask,
+// where the average workgroup sees half the keys.
 constexpr int kPipeMinN = 8192;
 
 hipError_t launch_fwd16(const FwdArgs& a, bool bf16, hipStream_t s) {

@@ -42,9 +42,11 @@
 // exact maximum of block 0; a block whose sum of exponentials passes kBig in
 // some lane is redone with its exact maximum (moving m, rescaling O and the
 // sums), as in fa_fwd16.hip. Tiles that cross the causal diagonal or the end
-// of the sequence run afterwards, one 32-key block at a time, unpipelined;
-// the first key tile also goes through the exact split of P (P~ plus its
-// rounding residue) for rows that see few keys.
+// of the sequence go through the same pipelined steps with their scores
+// masked, when the workgroup has at least one full tile before them;
+// otherwise (rows that see at most 256 keys) they run one 32-key block at a
+// time, unpipelined, and the first key tile also goes through the exact
+// split of P (P~ plus its rounding residue) for rows that see few keys.
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -55,6 +57,9 @@ constexpr float kBigP = 16384.0f;   // per-lane sum of p that forces the exact-m
 
 #ifndef FA16P_NPF
 #define FA16P_NPF 3                  // fragments read ahead of their first MFMA
+#endif
+#ifndef FA16P_MASKED_PIPE            // 0: masked tiles always one 32-key block at a time
+#define FA16P_MASKED_PIPE 1
 #endif
 #ifndef FA16P_QB                     // 32-row query blocks per wave: 2 (one wave per SIMD,
 #define FA16P_QB 2                   // 4 per workgroup) or 1 (two per SIMD, 8 per workgroup)
@@ -530,9 +535,23 @@ fa_fwd16_pipe_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
         }
     }
 
-    // Tiles [0, nfull) need no mask for any wave of the workgroup.
+    // Tiles [0, nfull) need no mask for any wave of the workgroup. When there
+    // is at least one, the masked tiles after them (the causal diagonal, the
+    // ragged end) also run through the pipelined steps, their scores masked
+    // between the step that computes them and the one that takes their
+    // exponentials; a workgroup with none (its rows see at most 256 keys)
+    // takes the one-block-at-a-time path below, with the exact split of P.
     const int nkt = (kend + BC - 1) / BC;
     const int nfull = (CAUSAL ? min(qtile0 + 1, N) : N) / BC;
+#if FA16P_MASKED_PIPE
+    const int nloop = nfull > 0 ? nkt : 0;
+#else
+    const int nloop = nfull;
+#endif
+    // scores of 32-key block kb of tile t, before their exponentials
+    auto mask_if = [&](f32x16 (&s)[QB], int t, int kb) {
+        if (t >= nfull) W::template mask<CAUSAL>(s, t * BC + 32 * kb, q0, N, hi, l32);
+    };
 
     // the copies of iteration j (K j+3 and V j+2: NIW pieces each, one
     // piece per call) into their ring slots
@@ -552,7 +571,7 @@ fa_fwd16_pipe_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
     f32x16 sA[QB], sB[QB];
     X8 pA[QB][2], pB[QB][2];
     X8 pre[NPF];
-    if (nfull > 0) {
+    if (nloop > 0) {
         // block 0: scores, and the reference maximum from them (exact)
         st.scores(sA, ktile(0), 0, qf);
         float mt[QB];
@@ -564,7 +583,7 @@ fa_fwd16_pipe_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
         // tile 0: half step 0 (scores of block 1, exponentials of block 0),
         // half step 1 (scores of block 2, exponentials of 1, P V of 0)
         const auto cp0 = copies(0);
-        if (nfull > 1) {
+        if (nloop > 1) {
             st.template step<true, false, true, true, true, 2 * NIW>(
                 sB, sA, pA, pB, pre, qf, ktile(0), 1, nullptr, 0, ktile(1), 0, vtile(0), 0, c, cp0);
             st.template step<true, true, true, true, true>(
@@ -578,29 +597,34 @@ fa_fwd16_pipe_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
         // tiles 1 .. nfull-2: both half steps full; the tile copies of an
         // iteration are spread over its first half step
         int j = 1;
-        for (; j + 1 < nfull; ++j) {
+        for (; j + 1 < nloop; ++j) {
             sync_tiles<2 * NIW>();             // K j+2, V j+1 landed; K j-1, V j-2 free
+            mask_if(sA, j, 0);
             st.template step<true, true, true, true, true, 2 * NIW>(
                 sB, sA, pA, pB, pre, qf, ktile(j), 1, vtile(j - 1), 1, ktile(j + 1), 0, vtile(j), 0, c,
                 copies(j));
+            mask_if(sB, j, 1);
             st.template step<true, true, true, true, true>(
                 sA, sB, pB, pA, pre, qf, ktile(j + 1), 0, vtile(j), 0, ktile(j + 1), 1, vtile(j), 1, c);
         }
-        if (j < nfull) {                     // last full tile: no scores after it
+        if (j < nloop) {                     // last tile: no scores after it
             sync_tiles<2 * NIW>();
+            mask_if(sA, j, 0);
             st.template step<true, true, true, false, true, 2 * NIW>(
                 sB, sA, pA, pB, pre, qf, ktile(j), 1, vtile(j - 1), 1, nullptr, 0, vtile(j), 0, c, copies(j));
+            mask_if(sB, j, 1);
             st.template step<false, true, true, false, true>(
                 sA, sB, pB, pA, pre, qf, nullptr, 0, vtile(j), 0, nullptr, 0, vtile(j), 1, c);
             ++j;
         }
         // drain: P V of the last block
         st.template step<false, true, false, false, false>(sA, sB, pA, pB, pre, qf, nullptr, 0,
-                                                          vtile(nfull - 1), 1, nullptr, 0, nullptr, 0, c);
+                                                          vtile(nloop - 1), 1, nullptr, 0, nullptr, 0, c);
     }
 
-    // Masked tiles (causal diagonal, ragged end): one 32-key block at a time.
-    for (int t = nfull; t < nkt; ++t) {
+    // Masked tiles (causal diagonal, ragged end) of a workgroup without a
+    // full tile: one 32-key block at a time.
+    for (int t = nloop; t < nkt; ++t) {
         sync_tiles<0>();                       // every copy issued so far has landed
         issue(krs, t + 3, 0);                  // K t-1, V t-2 are free
         issue(vrs, t + 2, 1);
