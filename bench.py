@@ -511,9 +511,10 @@ def build_next_legs(dev):
     d=128, work 10*B*H*N^2*d (the five GEMMs of the gradient, halved for
     causal); the fused rotary + Hadamard + fp8 block quantisation of Q and K
     of the fp8 workload (half pairing, GB/s of bytes read and written); the
-    microscaled fp8 variant (fa_mx_prep of Q, K along d with the Hadamard, Q
-    prescaled, and V along the sequence, GB/s; the forward on its output,
-    non-causal and causal); the block-scaled fp8 forward, causal; the fp8
+    microscaled fp8 variant (fa_mx_prep_qkv: Q, K along d with the Hadamard,
+    Q prescaled, and V along the sequence in one launch, GB/s, and the same
+    as three fa_mx_prep calls; the forward on its output, non-causal and
+    causal); the block-scaled fp8 forward, causal; the fp8
     forward on inputs prepared without the prescale (amax / 448 scales for Q
     and K, one multiply-add per score); the step's fp8 prep as three
     separate fa_fp8_prep calls (GB/s); and the decode-shaped
@@ -581,11 +582,15 @@ def build_next_legs(dev):
     prescale = fa.qk_prescale(1.0 / d8 ** 0.5)
 
     def prep_mx():
+        fa.mx_prep_qkv(q8, k8, v8, signs, q_prescale=prescale, out=(mq, mk, mv))
+
+    def prep_mx_separate():
         fa.mx_prep(q8, signs, "d", out=mq, prescale=prescale)
         fa.mx_prep(k8, signs, "d", out=mk)
         fa.mx_prep(v8, None, "n", out=mv)
 
     legs.append(Leg("fp8_mx_prep_qkv_b4h16n4k_d128", prep_mx, 0.0, mx_bytes))
+    legs.append(Leg("fp8_mx_prep_qkv_separate_b4h16n4k_d128", prep_mx_separate, 0.0, mx_bytes))
     prep_mx()
     o8 = torch.empty((B8, H8, N8, d8), dtype=torch.bfloat16, device=dev)
     lse8 = torch.empty((B8, H8, N8), dtype=torch.float32, device=dev)

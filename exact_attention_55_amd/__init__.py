@@ -19,5 +19,5 @@ from ._lib import (  # noqa: F401
     fp8_prep_rope_raw, FA_ROPE_NONE, FA_ROPE_INTERLEAVED, FA_ROPE_HALF,
     FA_FP8_MX, FA_MX_ALONG_D, FA_MX_ALONG_N, mx_prep, mx_prep_raw, mx_packed_bytes, mx_scales_view,
     FA_FP8_QSCALED, fp8_prep_scaled_raw, mx_prep_scaled_raw, qk_prescale,
-    fp8_prep_qkv, fp8_prep_qkv_raw,
+    fp8_prep_qkv, fp8_prep_qkv_raw, mx_prep_qkv, mx_prep_qkv_raw,
 )

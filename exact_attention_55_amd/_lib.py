@@ -75,6 +75,8 @@ def lib():
     L.fa_mx_prep_scaled.restype = i
     L.fa_fp8_prep_qkv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
     L.fa_fp8_prep_qkv.restype = i
+    L.fa_mx_prep_qkv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    L.fa_mx_prep_qkv.restype = i
     L.fa_fp8_prep.restype = i
     L.fa_fp8_packed_bytes.argtypes = [i, i, i, i]
     L.fa_fp8_packed_bytes.restype = ctypes.c_size_t
@@ -159,6 +161,11 @@ def fp8_prep_scaled_raw(x, x8, signs, B, H, N, d, block_rows, in_dtype, rope_sty
 def fp8_prep_qkv_raw(q, k, v, q8, k8, v8, signs, B, H, N, d, in_dtype, q_prescale, stream=None):
     return lib().fa_fp8_prep_qkv(q, k, v, q8, k8, v8, signs, B, H, N, d, in_dtype,
                                  float(q_prescale), stream)
+
+
+def mx_prep_qkv_raw(q, k, v, q8, k8, v8, signs, B, H, N, d, in_dtype, q_prescale, stream=None):
+    return lib().fa_mx_prep_qkv(q, k, v, q8, k8, v8, signs, B, H, N, d, in_dtype,
+                                float(q_prescale), stream)
 
 
 def mx_prep_raw(x, x8, signs, B, H, N, d, axis, in_dtype, stream=None):
@@ -339,6 +346,28 @@ def fp8_scales_view(packed, B, H, N, d):
     return packed[off: off + 4 * B * H * nb].view(torch.float32).view(B, H, nb)
 
 
+def _prep_qkv(raw, packed_bytes, name, q, k, v, signs, q_prescale, out):
+    B, H, N, d = q.shape
+    _check(q.dim() == 4 and k.shape == q.shape and v.shape == q.shape, "q, k, v shapes differ")
+    _check(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v dtypes differ")
+    nbytes = packed_bytes(B, H, N, d)
+    if out is None:
+        out = tuple(torch.empty(nbytes, dtype=torch.uint8, device=q.device) for _ in range(3))
+    _check(len(out) == 3, "out must hold three packed tensors")
+    for o in out:
+        _check(o.dtype == torch.uint8 and o.numel() >= nbytes, "packed output too small")
+    if signs is not None:
+        _check(signs.dtype == torch.int8 and tuple(signs.shape) == (H, d), "signs must be int8 [H, d]")
+        _check_device(q, k, v, *out, signs)
+    else:
+        _check_device(q, k, v, *out)
+    st = raw(_ptr(q), _ptr(k), _ptr(v), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _ptr(signs),
+             B, H, N, d, _dtype_code(q), q_prescale, _stream(q.device))
+    if st != FA_OK:
+        raise FaError(st, name)
+    return tuple(out)
+
+
 def fp8_prep_qkv(q, k, v, signs=None, q_prescale=1.0, out=None):
     """The three fp8 preps of one attention call in a single launch: q and k
     rotated by signs (when given), q times q_prescale, v plain, all with
@@ -347,25 +376,19 @@ def fp8_prep_qkv(q, k, v, signs=None, q_prescale=1.0, out=None):
     fp8_prep(k, signs, pow2_scale=True) and fp8_prep(v, pow2_scale=True); out
     may hold three such tensors to write into. With q_prescale =
     qk_prescale(softmax_scale) they feed fwd_fp8(..., qscaled=True)."""
-    B, H, N, d = q.shape
-    _check(q.dim() == 4 and k.shape == q.shape and v.shape == q.shape, "q, k, v shapes differ")
-    _check(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v dtypes differ")
-    if out is None:
-        out = tuple(fp8_alloc_packed(B, H, N, d, q.device) for _ in range(3))
-    _check(len(out) == 3, "out must hold three packed tensors")
-    for o in out:
-        _check(o.dtype == torch.uint8 and o.numel() >= fp8_packed_bytes(B, H, N, d),
-               "packed output too small")
-    if signs is not None:
-        _check(signs.dtype == torch.int8 and tuple(signs.shape) == (H, d), "signs must be int8 [H, d]")
-        _check_device(q, k, v, *out, signs)
-    else:
-        _check_device(q, k, v, *out)
-    st = fp8_prep_qkv_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]),
-                          _ptr(signs), B, H, N, d, _dtype_code(q), q_prescale, _stream(q.device))
-    if st != FA_OK:
-        raise FaError(st, "fa_fp8_prep_qkv")
-    return tuple(out)
+    return _prep_qkv(fp8_prep_qkv_raw, fp8_packed_bytes, "fa_fp8_prep_qkv", q, k, v, signs,
+                     q_prescale, out)
+
+
+def mx_prep_qkv(q, k, v, signs=None, q_prescale=1.0, out=None):
+    """The three microscaled preps of one attention call in a single launch:
+    q and k along d, rotated by signs (when given), q times q_prescale; v
+    along the sequence. Returns (q8, k8, v8) equal to mx_prep(q, signs, "d",
+    prescale=q_prescale), mx_prep(k, signs, "d") and mx_prep(v, None, "n");
+    with q_prescale = qk_prescale(softmax_scale) they feed fwd_fp8(...,
+    mx=True, qscaled=True)."""
+    return _prep_qkv(mx_prep_qkv_raw, mx_packed_bytes, "fa_mx_prep_qkv", q, k, v, signs,
+                     q_prescale, out)
 
 
 def fp8_prep(x, signs=None, block_rows=128, out=None, rope=None, pow2_scale=False, prescale=None):

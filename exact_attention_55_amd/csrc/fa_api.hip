@@ -223,6 +223,48 @@ int prep_rope(const void* x, void* x8, const int8_t* signs, int B, int H, int N,
     return from_hip(fa::launch_fp8_prep(a, s));
 }
 
+// Shared checks and arguments of the one-launch Q/K/V preps; returns
+// FA_OK with a filled, or a status (empty problems: FA_OK with *empty set).
+int qkv_args(const void* q, const void* k, const void* v, void* q8, void* k8, void* v8,
+             const int8_t* signs, int B, int H, int N, int d, int in_dtype, float q_prescale, bool mx,
+             fa::PrepQkvArgs& a, bool* empty) {
+    *empty = false;
+    in_dtype &= ~FA_SCALE_POW2;
+    if (in_dtype != FA_BF16 && in_dtype != FA_F16) return FA_ERR_INVALID_ARG;
+    if (!(q_prescale > 0.0f) || !isfinite(q_prescale)) return FA_ERR_INVALID_ARG;
+    if (!sizes_ok(B, H, N, d)) return FA_ERR_INVALID_ARG;
+    if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
+    // workgroups of the launch (bounded above): Q and K one per 128-row
+    // block; V the same (block scales) or at most one per 32-row block (MX)
+    const long long bh = (long long)B * H;
+    const long long wgs = 2 * bh * ((N + 127) / 128) + bh * (mx ? (N + 31) / 32 : (N + 127) / 128);
+    if (wgs > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+    const size_t out_bytes = mx ? fa_mx_packed_bytes(B, H, N, d) : fa_fp8_packed_bytes(B, H, N, d);
+    if (B == 0 || H == 0 || N == 0) {
+        *empty = true;
+        return FA_OK;
+    }
+    const void* in[3] = {q, k, v};
+    void* out[3] = {q8, k8, v8};
+    for (int i = 0; i < 3; ++i) {
+        if (!in[i] || !out[i]) return FA_ERR_INVALID_ARG;
+        if (!aligned(in[i], 16) || !aligned(out[i], 256)) return FA_ERR_INVALID_ARG;
+    }
+    for (int i = 0; i < 3; ++i)
+        for (int j = i + 1; j < 3; ++j) {
+            const uintptr_t x = (uintptr_t)out[i], y = (uintptr_t)out[j];
+            if (x < y + out_bytes && y < x + out_bytes) return FA_ERR_INVALID_ARG;
+        }
+    a.q = q; a.k = k; a.v = v;
+    a.q8 = static_cast<uint8_t*>(q8); a.k8 = static_cast<uint8_t*>(k8); a.v8 = static_cast<uint8_t*>(v8);
+    a.signs = signs;
+    a.B = B; a.H = H; a.N = N; a.d = d;
+    a.bf16 = in_dtype == FA_BF16;
+    a.scales_off = fa_fp8_scales_offset(B, H, N, d);
+    a.q_prescale = q_prescale;
+    return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -271,37 +313,24 @@ int fa_fp8_prep_scaled(const void* x, void* x8, const int8_t* signs, int B, int 
                      rope_base, pos0, prescale, stream);
 }
 
+int fa_mx_prep_qkv(const void* q, const void* k, const void* v, void* q8, void* k8, void* v8,
+                   const int8_t* signs, int B, int H, int N, int d, int in_dtype, float q_prescale,
+                   void* stream) {
+    fa::PrepQkvArgs a;
+    bool empty;
+    const int st = qkv_args(q, k, v, q8, k8, v8, signs, B, H, N, d, in_dtype, q_prescale, true, a, &empty);
+    if (st != FA_OK || empty) return st;
+    (void)hipGetLastError();
+    return from_hip(fa::launch_mx_prep_qkv(a, static_cast<hipStream_t>(stream)));
+}
+
 int fa_fp8_prep_qkv(const void* q, const void* k, const void* v, void* q8, void* k8, void* v8,
                     const int8_t* signs, int B, int H, int N, int d, int in_dtype, float q_prescale,
                     void* stream) {
-    in_dtype &= ~FA_SCALE_POW2;
-    if (in_dtype != FA_BF16 && in_dtype != FA_F16) return FA_ERR_INVALID_ARG;
-    if (!(q_prescale > 0.0f) || !isfinite(q_prescale)) return FA_ERR_INVALID_ARG;
-    if (!sizes_ok(B, H, N, d)) return FA_ERR_INVALID_ARG;
-    if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
-    if (3LL * B * H * ((N + 127) / 128) > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
-    if (B == 0 || H == 0 || N == 0) return FA_OK;
-    const void* in[3] = {q, k, v};
-    void* out[3] = {q8, k8, v8};
-    for (int i = 0; i < 3; ++i) {
-        if (!in[i] || !out[i]) return FA_ERR_INVALID_ARG;
-        if (!aligned(in[i], 16) || !aligned(out[i], 256)) return FA_ERR_INVALID_ARG;
-    }
-    const size_t bytes = fa_fp8_packed_bytes(B, H, N, d);
-    for (int i = 0; i < 3; ++i)
-        for (int j = i + 1; j < 3; ++j) {
-            const uintptr_t a = (uintptr_t)out[i], b = (uintptr_t)out[j];
-            if (a < b + bytes && b < a + bytes) return FA_ERR_INVALID_ARG;
-        }
-
     fa::PrepQkvArgs a;
-    a.q = q; a.k = k; a.v = v;
-    a.q8 = static_cast<uint8_t*>(q8); a.k8 = static_cast<uint8_t*>(k8); a.v8 = static_cast<uint8_t*>(v8);
-    a.signs = signs;
-    a.B = B; a.H = H; a.N = N; a.d = d;
-    a.bf16 = in_dtype == FA_BF16;
-    a.scales_off = fa_fp8_scales_offset(B, H, N, d);
-    a.q_prescale = q_prescale;
+    bool empty;
+    const int st = qkv_args(q, k, v, q8, k8, v8, signs, B, H, N, d, in_dtype, q_prescale, false, a, &empty);
+    if (st != FA_OK || empty) return st;
     (void)hipGetLastError();
     return from_hip(fa::launch_fp8_prep_qkv(a, static_cast<hipStream_t>(stream)));
 }

@@ -431,48 +431,56 @@ fp8_prep_qkv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* _
         quant_rows<T, D, false, 0, 0>(X, X8, nullptr, scales, nullptr, N, H, nblk, rf, 1, prescale, bid);
 }
 
-// Microscaling along the sequence (V): each thread owns 8 adjacent columns
-// of one 32-row block and holds the block's 32 rows of them in registers
-// (16-byte row loads, so the threads of a block together read whole rows),
-// takes the 8 column maxima, then writes 8 code bytes per row; a workgroup
-// covers kPrepThreads / (D / 8) blocks, and rows past the head's end are
-// neither read nor written. The block's scale for column c is stored at byte
-// (c % 32) * (D / 32) + c / 32 of the block's D scale bytes, the order in
-// which a lane of the PV matrix instruction wants its column scales.
+// Microscaling along the sequence (V): one wave per 32-row block. Lane
+// (q, cg) owns 8 adjacent columns (cg) of rows q R .. q R + R - 1 of the
+// block, R = 32 / (64 / (D / 8)) (8 rows at d = 128), so one load
+// instruction of the wave reads 64 / (D / 8) whole rows; the column maxima
+// of the block combine over the lanes that share cg (lane xor over the
+// higher lane bits), then each lane writes the codes of its rows. Rows past
+// the head's end are neither read nor written. The block's scale for column
+// c is stored at byte (c % 32) * (D / 32) + c / 32 of the block's D scale
+// bytes, the order in which a lane of the PV matrix instruction wants its
+// column scales. gb: the (head, block) index of this wave.
 template <typename T, int D>
-__global__ void __launch_bounds__(kPrepThreads)
-mx_prep_cols_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, uint8_t* __restrict__ scales,
-                    int N, int nkb, long long nblocks)
+__device__ __forceinline__ void mx_cols_block(const T* __restrict__ X, uint8_t* __restrict__ X8,
+                                              uint8_t* __restrict__ scales, int N, int nkb, long long gb)
 {
     constexpr int CG = D / 8;                      // column groups of a block
-    constexpr int BPW = kPrepThreads / CG;         // blocks per workgroup
-    const int cg = threadIdx.x % CG;
-    const long long gb = (long long)blockIdx.x * BPW + threadIdx.x / CG;   // (head, block) index
-    if (gb >= nblocks) return;
+    constexpr int RQ = 64 / CG;                    // row groups (lanes per column group)
+    constexpr int R = 32 / RQ;                     // rows per lane
+    const int lane = threadIdx.x & 63;
+    const int cg = lane % CG, rq = lane / CG;
     const long long bh = gb / nkb;
     const int r0 = (int)(gb - bh * nkb) * 32;
     const int nr = min(32, N - r0);
-    const size_t base = ((size_t)bh * N + r0) * D + 8 * cg;
+    const size_t base = ((size_t)bh * N + r0 + rq * R) * D + 8 * cg;
     typedef __attribute__((ext_vector_type(8))) T T8;
-    u32x4 raw[32];
+    u32x4 raw[R];
 #pragma unroll
-    for (int r = 0; r < 32; ++r)
-        raw[r] = r < nr ? *reinterpret_cast<const u32x4*>(X + base + (size_t)r * D) : u32x4{0, 0, 0, 0};
+    for (int r = 0; r < R; ++r)
+        raw[r] = rq * R + r < nr ? *reinterpret_cast<const u32x4*>(X + base + (size_t)r * D) : u32x4{0, 0, 0, 0};
     float a[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) a[e] = 0.f;
 #pragma unroll
-    for (int r = 0; r < 32; ++r) {
+    for (int r = 0; r < R; ++r) {
         const T8 x = __builtin_bit_cast(T8, raw[r]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) a[e] = fmaxf(a[e], fabsf(to_f(x[e])));
     }
+    static_for<0, 3>([&](auto mc) {
+        constexpr int m = CG << decltype(mc)::value;
+        if constexpr (m < 64) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a[e] = fmaxf(a[e], lane_xor<m>(a[e]));
+        }
+    });
     int ex[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) ex[e] = mx_exponent(a[e]);
 #pragma unroll
-    for (int r = 0; r < 32; ++r) {
-        if (r < nr) {
+    for (int r = 0; r < R; ++r) {
+        if (rq * R + r < nr) {
             const T8 x = __builtin_bit_cast(T8, raw[r]);
             float y[8];
 #pragma unroll
@@ -482,12 +490,56 @@ mx_prep_cols_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, uint8_t* 
             __builtin_nontemporal_store(u32x2{w0, w1}, reinterpret_cast<u32x2*>(X8 + base + (size_t)r * D));
         }
     }
-    uint8_t* sc = scales + (size_t)gb * D;
+    if (rq == 0) {
+        uint8_t* sc = scales + (size_t)gb * D;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int col = 8 * cg + e;
-        sc[(col % 32) * (D / 32) + col / 32] = (uint8_t)(ex[e] + 127);
+        for (int e = 0; e < 8; ++e) {
+            const int col = 8 * cg + e;
+            sc[(col % 32) * (D / 32) + col / 32] = (uint8_t)(ex[e] + 127);
+        }
     }
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(kPrepThreads)
+mx_prep_cols_kernel(const T* __restrict__ X, uint8_t* __restrict__ X8, uint8_t* __restrict__ scales,
+                    int N, int nkb, long long nblocks)
+{
+    const long long gb = (long long)blockIdx.x * (kPrepThreads / 64) + (threadIdx.x >> 6);
+    if (gb >= nblocks) return;
+    mx_cols_block<T, D>(X, X8, scales, N, nkb, gb);
+}
+
+// The microscaled Q, K and V of one attention call in a single launch:
+// workgroups [0, grid1) take Q (along d: the transform when signs is given,
+// times q_prescale), [grid1, 2 grid1) K (the same transform), the rest V
+// (along the sequence, one wave per 32-row block). Each workgroup runs the
+// steps of the single-tensor kernels, so the outputs are theirs byte for
+// byte.
+template <typename T, int D>
+__global__ void __launch_bounds__((quant_threads<D, 0>()))
+mx_prep_qkv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+                   uint8_t* __restrict__ Q8, uint8_t* __restrict__ K8, uint8_t* __restrict__ V8,
+                   const int8_t* __restrict__ signs, size_t scales_off, int N, int H, int nblk,
+                   int grid1, int nkb, long long nvblocks, float q_prescale)
+{
+    constexpr int NT = quant_threads<D, 0>();
+    const int bid = blockIdx.x;
+    if (bid >= 2 * grid1) {
+        const long long gb = (long long)(bid - 2 * grid1) * (NT / 64) + (threadIdx.x >> 6);
+        if (gb < nvblocks) mx_cols_block<T, D>(V, V8, V8 + scales_off, N, nkb, gb);
+        return;
+    }
+    const int t = bid / grid1, b = bid - t * grid1;
+    const T* X = t == 0 ? Q : K;
+    uint8_t* X8 = t == 0 ? Q8 : K8;
+    float* scales = reinterpret_cast<float*>(X8 + scales_off);
+    const float prescale = t == 0 ? q_prescale : 1.0f;
+    const RopeFreqs rf{};
+    if (signs != nullptr)
+        quant_rows<T, D, true, 3, 0>(X, X8, signs, scales, nullptr, N, H, nblk, rf, 0, prescale, b);
+    else
+        quant_rows<T, D, false, 3, 0>(X, X8, nullptr, scales, nullptr, N, H, nblk, rf, 0, prescale, b);
 }
 
 __global__ void zero_u32_kernel(unsigned* p) { *p = 0u; }
@@ -511,7 +563,7 @@ static hipError_t prep_t(const PrepArgs& a, hipStream_t s) {
     if (a.mx == kMxAlongN) {
         const int nkb = (a.N + 31) / 32;
         const long long nblocks = (long long)a.B * a.H * nkb;
-        constexpr int BPW = kPrepThreads / (D / 8);
+        constexpr int BPW = kPrepThreads / 64;
         hipLaunchKernelGGL((mx_prep_cols_kernel<T, D>), dim3((unsigned)((nblocks + BPW - 1) / BPW)),
                            dim3(kPrepThreads), 0, s, x, a.x8, a.x8 + a.scales_off, a.N, nkb, nblocks);
         return hipGetLastError();
@@ -610,6 +662,35 @@ static hipError_t prep_qkv_ty(const PrepQkvArgs& a, hipStream_t s) {
 
 hipError_t launch_fp8_prep_qkv(const PrepQkvArgs& a, hipStream_t s) {
     return a.bf16 ? prep_qkv_ty<__bf16>(a, s) : prep_qkv_ty<_Float16>(a, s);
+}
+
+template <typename T, int D>
+static hipError_t mx_prep_qkv_d(const PrepQkvArgs& a, hipStream_t s) {
+    constexpr int NT = quant_threads<D, 0>();
+    const int nblk = (a.N + kQuantBlockRows - 1) / kQuantBlockRows;
+    const long long grid1 = (long long)a.B * a.H * nblk;
+    const int nkb = (a.N + 31) / 32;
+    const long long nvblocks = (long long)a.B * a.H * nkb;
+    const long long gridv = (nvblocks + NT / 64 - 1) / (NT / 64);
+    hipLaunchKernelGGL((mx_prep_qkv_kernel<T, D>), dim3((unsigned)(2 * grid1 + gridv)), dim3(NT), 0, s,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                       a.q8, a.k8, a.v8, a.signs, a.scales_off, a.N, a.H, nblk, (int)grid1, nkb, nvblocks,
+                       a.q_prescale);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t mx_prep_qkv_ty(const PrepQkvArgs& a, hipStream_t s) {
+    switch (a.d) {
+        case 64: return mx_prep_qkv_d<T, 64>(a, s);
+        case 128: return mx_prep_qkv_d<T, 128>(a, s);
+        case 256: return mx_prep_qkv_d<T, 256>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_mx_prep_qkv(const PrepQkvArgs& a, hipStream_t s) {
+    return a.bf16 ? mx_prep_qkv_ty<__bf16>(a, s) : mx_prep_qkv_ty<_Float16>(a, s);
 }
 
 }  // namespace fa

@@ -76,6 +76,8 @@ struct PrepQkvArgs {
     float q_prescale;
 };
 hipError_t launch_fp8_prep_qkv(const PrepQkvArgs& a, hipStream_t s);
+// The same for microscaled inputs (q, k along d; v along the sequence).
+hipError_t launch_mx_prep_qkv(const PrepQkvArgs& a, hipStream_t s);
 
 struct BwdArgs {
     const void* q;

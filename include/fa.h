@@ -405,6 +405,36 @@ int fa_mx_prep(const void* x, void* x8, const int8_t* signs, int B, int H, int N
 int fa_mx_prep_scaled(const void* x, void* x8, const int8_t* signs, int B, int H, int N, int d,
                       int axis, int in_dtype, float prescale, void* stream);
 
+/*
+ * fa_mx_prep_qkv - the three microscaled preps of one FA_FP8_MX attention
+ * call in a single launch ("FlashAttention-3: Fast & Accurate Attention with
+ * Asynchrony & Low-Precision", "Incoherent Processing for FP8 Accuracy",
+ * and block quantisation at 32-element blocks): q along d with the rotation
+ * by signs and prescale q_prescale, k along d with the same rotation, v
+ * along N without one. The three packed outputs equal, byte for byte, those
+ * of fa_mx_prep_scaled(q, q8, signs, ..., FA_MX_ALONG_D, in_dtype,
+ * q_prescale), fa_mx_prep(k, k8, signs, ..., FA_MX_ALONG_D, in_dtype) and
+ * fa_mx_prep(v, v8, NULL, ..., FA_MX_ALONG_N, in_dtype). With q_prescale =
+ * softmax_scale * log2(e) the outputs are the inputs of fa_fwd with
+ * FA_FP8_MX | FA_FP8_QSCALED; with q_prescale = 1 those of plain FA_FP8_MX.
+ *
+ *  q, k, v     16-bit inputs [B][H][N][d] (in_dtype FA_BF16 or FA_F16),
+ *              16-byte aligned.
+ *  q8, k8, v8  packed outputs as fa_mx_prep's x8, each of
+ *              fa_mx_packed_bytes(B,H,N,d) bytes, 256-byte aligned, owned by
+ *              the caller; the three must not overlap one another or the
+ *              inputs (overlapping outputs are rejected).
+ *  signs       int8 [H][d] of +1/-1, or NULL for no rotation of q and k.
+ *  q_prescale  finite and > 0.
+ *  d           64, 128 or 256; 2 * B * H * ceil(N/128) + B * H * ceil(N/32)
+ *              < 2^31.
+ * Returns FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED or FA_ERR_HIP.
+ */
+int fa_mx_prep_qkv(const void* q, const void* k, const void* v,
+                   void* q8, void* k8, void* v8, const int8_t* signs,
+                   int B, int H, int N, int d, int in_dtype, float q_prescale,
+                   void* stream);
+
 /* Size in bytes of a packed microscaled tensor for [B][H][N][d] (either
  * axis); 0 for invalid sizes. Pure host arithmetic. */
 size_t fa_mx_packed_bytes(int B, int H, int N, int d);

@@ -352,3 +352,28 @@ def prep_qkv(**kw):
 ])
 def test_prep_qkv_validation(L, kw, status):
     assert prep_qkv(**kw) == status
+
+
+def mx_prep_qkv(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, q8=FAKE, k8=FAKE + P8, v8=FAKE + 2 * P8, signs=None, B=1, H=1,
+             N=128, d=128, in_dtype=fa.FA_BF16, p=0.1275)
+    a.update(kw)
+    return fa.mx_prep_qkv_raw(a["q"], a["k"], a["v"], a["q8"], a["k8"], a["v8"], a["signs"], a["B"],
+                              a["H"], a["N"], a["d"], a["in_dtype"], a["p"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(p=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(p=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(in_dtype=fa.FA_FP8_MX), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=1 << 14, H=1 << 10, N=1 << 13), fa.FA_ERR_UNSUPPORTED),   # 2^32 V blocks
+    (dict(q8=FAKE + 64), fa.FA_ERR_INVALID_ARG),
+    (dict(v=FAKE + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(v8=FAKE), fa.FA_ERR_INVALID_ARG),                 # v8 is q8
+    (dict(k8=FAKE + 2 * P8 - 256), fa.FA_ERR_INVALID_ARG),  # k8 runs into v8
+    (dict(H=0, v8=FAKE), fa.FA_OK),
+])
+def test_mx_prep_qkv_validation(L, kw, status):
+    assert mx_prep_qkv(**kw) == status
