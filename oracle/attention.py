@@ -7,7 +7,7 @@ FlashAttention (all three versions) is an exact rewrite of this computation:
 the review "FlashAttention-3: почему внимание стало быстрее", sections
 "Коротко" and "FAQ", states that the formula itself is unchanged.
 
-Readings where the pages are silent (all listed in the design doc):
+Readings where the pages are silent:
 * layout [B, H, N, d] for q, k, v and o; [B, H, N] for the log-sum-exp;
 * softmax_scale multiplies S before the row max is taken;
 * causal means key j is visible to query i iff j <= i (N_q == N_k);
