@@ -81,6 +81,10 @@ FP8_FWD_LEG = "fp8_fwd_b4h16n4k_d128"
 FP8_PREP_LEG = "fp8_prep_qkv_b4h16n4k_d128"
 FP8_SYMBOL = "_ZN2fa17fa_fwd_fp8_kernelILi128ELb0ELb0ELb0ELb1EEEvPKhS2_S2_PvPfiiiimf"
 KERNEL_OF = {**{k: v[1] for k, v in FWD16_LEGS.items()}, FP8_FWD_LEG: FP8_SYMBOL}
+# the HBM-bound kernel of the step (Q, K, V fp8 prep in one launch)
+PREP_SYMBOL = "_ZN2fa19fp8_prep_qkv_kernelIDF16bLi128EEEvPKT_S3_S3_PhS4_S4_PKamiiiif"
+# kernels whose HBM traffic is measured: the forward legs' and the prep's
+TRAFFIC_OF = {**KERNEL_OF, FP8_PREP_LEG: PREP_SYMBOL}
 HEADLINE = ["bf16_fwd_b2h16n8k_d128_causal", "bf16_fwd_b2h16n8k_d128"]
 ROOF_LEG = "bf16_fwd_b2h16n8k_d128"
 
@@ -162,14 +166,19 @@ def measured_traffic(leg):
             t = json.load(f)["legs"][leg]
     except (OSError, ValueError, KeyError):
         return None
-    if t.get("code_sha256") != source_hash(KERNEL_OF[leg]):
+    if t.get("code_sha256") != source_hash(TRAFFIC_OF[leg]):
         return None
     return t.get("hbm_bytes_per_launch")
 
 
 def algorithmic_bytes(leg):
-    """Bytes a forward must move per launch: Q, K, V in, O out, LSE out (and
-    the fp8 scales)."""
+    """Bytes a kernel must move per launch. Forward: Q, K, V in, O out, LSE
+    out (and the fp8 scales). fp8 prep: the three 16-bit tensors in, their
+    codes and block scales out."""
+    if leg == FP8_PREP_LEG:
+        c = CONFIGS[FP8]
+        nel = c["B"] * c["H"] * c["N"] * c["d"]
+        return 3 * (2 * nel + nel + 4 * c["B"] * c["H"] * ((c["N"] + 127) // 128))
     if leg == FP8_FWD_LEG:
         c = CONFIGS[FP8]
         nel = c["B"] * c["H"] * c["N"] * c["d"]
@@ -183,7 +192,7 @@ def algorithmic_bytes(leg):
 def traffic_commands():
     cmds = []
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
-        for leg in KERNEL_OF:
+        for leg in TRAFFIC_OF:
             cmds.append(f"rocprofv3 --pmc {c} -d <out>/pmc_{c} -o {leg} -f csv -- python3 bench.py "
                         f"--only {leg} --steps 3 --warmup 1 --no-cpu --no-next")
         cmds.append(f"rocprofv3 --pmc {c} -d <out>/pmc_{c} -o copy -f csv -- python3 bench.py --copy-calib")
@@ -211,7 +220,7 @@ def traffic_summary(run_dir):
         copy_kib = sorted(copy.values())[-2]          # median of the three 1 GiB copies
         scale[c] = {"copy_kib": copy_kib, "scale": (1 << 30) / 1024.0 / copy_kib}
     legs = {}
-    for leg, sym in KERNEL_OF.items():
+    for leg, sym in TRAFFIC_OF.items():
         part = _short_kernel_name(sym).split("<")[0]
         e = {"kernel_symbol": sym}
         try:
@@ -659,6 +668,8 @@ def time_legs(legs, steps, warmup):
 def leg_summary(L):
     t = float(np.mean(L.times))
     e = {"ms": t * 1e3, "ms_min": float(np.min(L.times)) * 1e3}
+    if L.name == FP8_PREP_LEG:
+        e["traffic"] = measured_traffic(L.name)
     if L.flops:
         e["tflops"] = L.flops / t / 1e12
         e["frac_of_peak"] = e["tflops"] / L.peak
